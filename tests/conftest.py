@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+@pytest.fixture(scope="session")
+def oracle_lib():
+    """The oracle package, built if its library is missing."""
+    from oracle import build as oracle_build
+    if not os.path.exists(oracle_build.LIBRARY):
+        oracle_build.build()
+    import oracle
+    return oracle
