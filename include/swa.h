@@ -1,0 +1,166 @@
+/*
+ * swa.h - C ABI of the shifted-window multi-head self-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  The TERRA page ("TERRA: A Hierarchical Parallel Training
+ * and Memory Orchestration Framework for High-Resolution AI-based Earth
+ * Modeling") describes Earth-forecasting models whose Transformer layers are
+ * window-based (Swin) attention with shifted-window execution: tokens of a
+ * (time,) latitude, longitude grid leave their spatial layout for a window
+ * layout, attend inside windows, and return (abstract; Fig. 5 caption, shift
+ * token routes).  Its Table I names the real resolution H, W, the padded
+ * resolution H^, W^ and the embedding d; its Table V gives heads N_h and
+ * window size w.  The library computes the forward pass of that layer:
+ *
+ *   for every batch b, head h and real query token i = (t, y, x):
+ *     K(i)  = keys sharing i's shifted window, on the same side of the wrap of
+ *             every masked axis, excluding pad tokens;
+ *     logit = scale * <q_i, k_j> + table[l_t(i)-l_t(j)+w_t-1]
+ *                                       [l_y(i)-l_y(j)+w_y-1]
+ *                                       [l_x(i)-l_x(j)+w_x-1][h];
+ *     o_i   = sum over j in K(i) of softmax_j(logit) * v_j,
+ *
+ * where the grid is padded at the end of each masked axis, rolled by -shift
+ * (rolled[c'] = padded[(c' + s) mod P]), cut into windows, and l_a(c) =
+ * ((c - s_a) mod P_a) mod w_a is the position inside the rolled window.
+ * Longitude is cyclic (wrapped neighbours attend each other); time and
+ * latitude are masked (no attention across the wrap, none to padding).
+ *
+ * Layouts (all C-contiguous, all device memory):
+ *   q, k, v, out : [B][T][H][W][heads][head_dim] over the REAL extents T, H, W,
+ *                  element type cfg.dtype (fp32 or bf16);
+ *   bias_table   : fp32 [2*w_t-1][2*w_y-1][2*w_x-1][heads];
+ *   window-major : [B][nW_t][nW_y][nW_x][N][heads][head_dim], N = w_t*w_y*w_x,
+ *                  windows and their tokens in row-major (t, y, x) order of
+ *                  the rolled, padded grid; pad slots hold zeros.
+ *
+ * Ownership.  The caller owns every buffer passed in; they must stay valid
+ * until the work queued on the given stream has finished.  A handle owns only
+ * its constants and, for the staged variant, a workspace it allocates in
+ * swa_create and frees in swa_destroy.  swa_forward never allocates.
+ *
+ * Errors.  Every call validates its arguments before touching the GPU and
+ * returns SWA_ERR_INVALID_ARGUMENT or SWA_ERR_UNSUPPORTED without side
+ * effects.  SWA_ERR_HIP means a HIP runtime call or kernel launch failed (for
+ * swa_create: no usable gfx950 device); the text of the last failure is
+ * available from swa_last_error().  No C++ exception crosses this ABI.
+ * All device work is asynchronous on the stream passed in (a hipStream_t;
+ * NULL is the default stream).  A handle may be used from one thread at a
+ * time; the staged variant's workspace is shared by all calls on a handle.
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum swa_status {
+    SWA_OK = 0,
+    SWA_ERR_INVALID_ARGUMENT = 1,
+    SWA_ERR_UNSUPPORTED = 2,
+    SWA_ERR_OUT_OF_MEMORY = 3,
+    SWA_ERR_HIP = 4
+} swa_status;
+
+typedef enum swa_dtype {
+    SWA_F32 = 0, /* fp32 in and out; fp32 arithmetic throughout */
+    SWA_BF16 = 1 /* bf16 in and out; bf16 matrix-core products, fp32 accumulation and softmax */
+} swa_dtype;
+
+typedef enum swa_variant {
+    SWA_VARIANT_FUSED = 0, /* one kernel: gather and scatter folded into the attention kernel */
+    SWA_VARIANT_STAGED = 1 /* gather -> window attention -> scatter, through a window-major workspace */
+} swa_variant;
+
+typedef struct swa_config {
+    int batch;     /* B >= 1 */
+    int heads;     /* N_h >= 1 (TERRA, Table V) */
+    int head_dim;  /* d / N_h; 32 or 64 for SWA_BF16, 1..128 for SWA_F32 */
+    int grid[3];   /* real extents (T, H, W): time, latitude, longitude (TERRA, Table I) */
+    int padded[3]; /* padded extents (T^, H^, W^) >= grid; must equal grid on cyclic axes */
+    int window[3]; /* window (w_t, w_y, w_x); 1 <= w <= padded, padded % w == 0 */
+    int shift[3];  /* shift (s_t, s_y, s_x); 0 <= s < w */
+    int cyclic[3]; /* 1: cyclic axis, 0: masked axis.  Usual setting {0, 0, 1} */
+    swa_dtype dtype;
+    float scale;   /* logit scale; 0 selects 1/sqrt(head_dim) */
+    swa_variant variant;
+} swa_config;
+
+typedef struct swa_handle swa_handle;
+
+/* Derived sizes of a configured handle. */
+typedef struct swa_info {
+    int64_t windows;            /* B * nW_t * nW_y * nW_x */
+    int32_t window_tokens;      /* N = w_t * w_y * w_x */
+    int64_t tokens;             /* real tokens B * T * H * W */
+    int64_t window_major_elems; /* windows * N * heads * head_dim */
+    size_t workspace_bytes;     /* device bytes owned by the handle (staged variant) */
+    double nominal_flops;       /* 4 * N^2 * head_dim per (window, head), all windows */
+    double algorithmic_bytes;   /* q, k, v read and out written once, real tokens, plus the table */
+} swa_info;
+
+/*
+ * Validates cfg, checks that the current HIP device is a gfx950, and creates
+ * a handle.  The staged variant allocates its workspace (four window-major
+ * tensors) here.  On failure *out is set to NULL.
+ * Errors: INVALID_ARGUMENT (NULL pointers, malformed tiling),
+ * UNSUPPORTED (head_dim or window size outside the kernels' range),
+ * HIP (no gfx950 device), OUT_OF_MEMORY (workspace).
+ */
+swa_status swa_create(const swa_config* cfg, swa_handle** out);
+
+/*
+ * The forward pass defined at the top of this header, queued on `stream`.
+ * q, k, v, out: device pointers in the layout above, 16-byte aligned; out
+ * must not overlap q, k, v or bias_table.  bias_table: device pointer, fp32,
+ * 4-byte aligned.  Every real output token is written; nothing else is.
+ * Errors: INVALID_ARGUMENT (NULL handle or pointer, misalignment, overlap),
+ * HIP (launch failure).
+ */
+swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* v,
+                       const float* bias_table, void* out, void* stream);
+
+/* Frees the handle and its workspace (synchronising the device first when a
+ * workspace exists).  NULL is a no-op returning SWA_OK. */
+swa_status swa_destroy(swa_handle* h);
+
+/* Sizes derived from the handle's configuration. */
+swa_status swa_get_info(const swa_handle* h, swa_info* info);
+
+/* Static text for a status code. */
+const char* swa_status_string(swa_status s);
+
+/* Text of the most recent failure on this thread ("" if none). */
+const char* swa_last_error(void);
+
+/*
+ * The route into the window layout alone (pad, roll by -shift, partition):
+ * src [B][T][H][W][heads][head_dim] -> dst window-major (pad slots zeroed).
+ * Same pointer rules as swa_forward; dst holds info.window_major_elems elements.
+ */
+swa_status swa_gather(swa_handle* h, const void* src, void* dst_window_major, void* stream);
+
+/*
+ * The route back alone (un-partition, roll by +shift, crop): window-major src
+ * -> dst [B][T][H][W][heads][head_dim].  Pad slots of src are not read.
+ */
+swa_status swa_scatter(swa_handle* h, const void* src_window_major, void* dst, void* stream);
+
+/*
+ * The attention mask of one window, as the attention kernels evaluate it:
+ * dev_out[n * N + m] = 1 when key m may be attended by query n of window
+ * `window_index` (0 <= window_index < info.windows), else 0; pad queries get
+ * all-zero rows.  dev_out: device buffer of N * N bytes.
+ */
+swa_status swa_debug_visibility(swa_handle* h, int64_t window_index, uint8_t* dev_out,
+                                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

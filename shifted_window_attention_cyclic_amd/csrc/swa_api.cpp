@@ -1,0 +1,284 @@
+// C ABI of the shifted-window attention library: validation, handles,
+// variant dispatch and error reporting.  Declarations and the contract of
+// every entry point are in include/swa.h.
+#include "swa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "swa_geometry.h"
+
+struct swa_handle {
+    swa_config cfg;
+    swa::Geometry g;
+    int elem_bytes;
+    int device;
+    size_t wm_bytes;    // bytes of one window-major tensor
+    void* workspace;    // staged variant: q, k, v, o window-major tensors
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+swa_status fail(swa_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+swa_status fail_hip(hipError_t e, const char* what) {
+    return fail(SWA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Validation that needs no device.  Fills g on success.
+swa_status validate(const swa_config* c, swa::Geometry* g, int* elem_bytes) {
+    if (c->batch < 1 || c->heads < 1) return fail(SWA_ERR_INVALID_ARGUMENT, "batch and heads must be >= 1");
+    if (c->dtype != SWA_F32 && c->dtype != SWA_BF16) return fail(SWA_ERR_INVALID_ARGUMENT, "unknown dtype");
+    if (c->variant != SWA_VARIANT_FUSED && c->variant != SWA_VARIANT_STAGED)
+        return fail(SWA_ERR_INVALID_ARGUMENT, "unknown variant");
+    if (c->head_dim < 1) return fail(SWA_ERR_INVALID_ARGUMENT, "head_dim must be >= 1");
+    if (!(isfinite(c->scale))) return fail(SWA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    static const char* axis[3] = {"time", "latitude", "longitude"};
+    int64_t tokens = c->batch;
+    int N = 1, table = 1;
+    int64_t windows = c->batch;
+    for (int a = 0; a < 3; a++) {
+        char buf[160];
+        if (c->grid[a] < 1) {
+            snprintf(buf, sizeof buf, "%s extent must be >= 1", axis[a]);
+            return fail(SWA_ERR_INVALID_ARGUMENT, buf);
+        }
+        if (c->cyclic[a] != 0 && c->cyclic[a] != 1) {
+            snprintf(buf, sizeof buf, "%s cyclic flag must be 0 or 1", axis[a]);
+            return fail(SWA_ERR_INVALID_ARGUMENT, buf);
+        }
+        if (c->padded[a] < c->grid[a]) {
+            snprintf(buf, sizeof buf, "%s padded extent %d is below the extent %d", axis[a], c->padded[a], c->grid[a]);
+            return fail(SWA_ERR_INVALID_ARGUMENT, buf);
+        }
+        if (c->cyclic[a] && c->padded[a] != c->grid[a]) {
+            snprintf(buf, sizeof buf, "%s is cyclic and cannot be padded", axis[a]);
+            return fail(SWA_ERR_INVALID_ARGUMENT, buf);
+        }
+        if (c->window[a] < 1 || c->window[a] > c->padded[a]) {
+            snprintf(buf, sizeof buf, "%s window %d outside [1, %d]", axis[a], c->window[a], c->padded[a]);
+            return fail(SWA_ERR_INVALID_ARGUMENT, buf);
+        }
+        if (c->padded[a] % c->window[a] != 0) {
+            snprintf(buf, sizeof buf, "%s padded extent %d is not a multiple of the window %d", axis[a], c->padded[a], c->window[a]);
+            return fail(SWA_ERR_INVALID_ARGUMENT, buf);
+        }
+        if (c->shift[a] < 0 || c->shift[a] >= c->window[a]) {
+            snprintf(buf, sizeof buf, "%s shift %d outside [0, %d)", axis[a], c->shift[a], c->window[a]);
+            return fail(SWA_ERR_INVALID_ARGUMENT, buf);
+        }
+        tokens *= c->grid[a];
+        N *= c->window[a];
+        table *= 2 * c->window[a] - 1;
+        windows *= c->padded[a] / c->window[a];
+        if (tokens > (int64_t)1 << 40 || windows > (int64_t)1 << 40)
+            return fail(SWA_ERR_UNSUPPORTED, "grid too large");
+    }
+    if (c->head_dim != 32 && c->head_dim != 64)
+        return fail(SWA_ERR_UNSUPPORTED, "head_dim must be 32 or 64");
+    if (c->heads > 4096) return fail(SWA_ERR_UNSUPPORTED, "at most 4096 heads");
+    if (table >= 1 << 16) return fail(SWA_ERR_UNSUPPORTED, "bias table too large (window too large)");
+    const int64_t row = (int64_t)c->heads * c->head_dim;
+    // row indices are 32-bit inside the kernels
+    if (tokens >= ((int64_t)1 << 31) || windows * N >= ((int64_t)1 << 31))
+        return fail(SWA_ERR_UNSUPPORTED, "more than 2^31 tokens");
+    if (windows * c->heads >= ((int64_t)1 << 31)) return fail(SWA_ERR_UNSUPPORTED, "too many (window, head) pairs");
+
+    swa::Geometry& G = *g;
+    G.batch = c->batch;
+    G.heads = c->heads;
+    G.head_dim = c->head_dim;
+    G.N = N;
+    G.nW = 1;
+    for (int a = 0; a < 3; a++) {
+        G.ext[a] = c->grid[a];
+        G.pad[a] = c->padded[a];
+        G.win[a] = c->window[a];
+        G.shift[a] = c->shift[a];
+        G.cyc[a] = c->cyclic[a];
+        G.nwin[a] = c->padded[a] / c->window[a];
+        G.nW *= G.nwin[a];
+    }
+    G.windows = windows;
+    G.row = (int)row;
+    G.tdy = 2 * c->window[1] - 1;
+    G.tdx = 2 * c->window[2] - 1;
+    G.table_size = table;
+    G.scale = c->scale != 0.f ? c->scale : (float)(1.0 / sqrt((double)c->head_dim));
+    *elem_bytes = c->dtype == SWA_F32 ? 4 : 2;
+
+    const size_t lds = swa::attention_lds_bytes(G, c->dtype == SWA_BF16);
+    if (c->dtype == SWA_BF16 && N > 512) return fail(SWA_ERR_UNSUPPORTED, "bf16 kernels take windows of at most 512 tokens");
+    if (lds > 160 * 1024) return fail(SWA_ERR_UNSUPPORTED, "window too large for the LDS of one workgroup");
+    return SWA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+} // namespace
+
+extern "C" {
+
+const char* swa_status_string(swa_status s) {
+    switch (s) {
+    case SWA_OK: return "ok";
+    case SWA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SWA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SWA_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case SWA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* swa_last_error(void) { return g_last_error.c_str(); }
+
+swa_status swa_create(const swa_config* cfg, swa_handle** out) {
+    if (out) *out = nullptr;
+    if (!cfg || !out) return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    swa::Geometry g;
+    int eb = 0;
+    swa_status st = validate(cfg, &g, &eb);
+    if (st != SWA_OK) return st;
+
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count < 1) {
+        (void)hipGetLastError();
+        return fail(SWA_ERR_HIP, "no HIP device");
+    }
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return fail_hip(e, "hipGetDevice");
+    hipDeviceProp_t prop;
+    if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess) return fail_hip(e, "hipGetDeviceProperties");
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(SWA_ERR_HIP, std::string("device is ") + prop.gcnArchName + ", kernels are built for gfx950");
+    if ((e = swa::prepare_kernels()) != hipSuccess) return fail_hip(e, "hipFuncSetAttribute");
+
+    swa_handle* h = new (std::nothrow) swa_handle();
+    if (!h) return fail(SWA_ERR_OUT_OF_MEMORY, "host allocation");
+    h->cfg = *cfg;
+    h->g = g;
+    h->elem_bytes = eb;
+    h->device = dev;
+    h->wm_bytes = (size_t)g.windows * g.N * g.row * eb;
+    h->workspace = nullptr;
+    if (cfg->variant == SWA_VARIANT_STAGED) {
+        e = hipMalloc(&h->workspace, 4 * h->wm_bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            delete h;
+            return fail(SWA_ERR_OUT_OF_MEMORY, "staged workspace");
+        }
+    }
+    *out = h;
+    return SWA_OK;
+}
+
+swa_status swa_destroy(swa_handle* h) {
+    if (!h) return SWA_OK;
+    swa_status st = SWA_OK;
+    if (h->workspace) {
+        hipError_t e = hipDeviceSynchronize();
+        if (e == hipSuccess) e = hipFree(h->workspace);
+        if (e != hipSuccess) st = fail_hip(e, "releasing the workspace");
+    }
+    delete h;
+    return st;
+}
+
+swa_status swa_get_info(const swa_handle* h, swa_info* info) {
+    if (!h || !info) return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    const swa::Geometry& g = h->g;
+    info->windows = g.windows;
+    info->window_tokens = g.N;
+    info->tokens = (int64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
+    info->window_major_elems = g.windows * g.N * (int64_t)g.row;
+    info->workspace_bytes = h->workspace ? 4 * h->wm_bytes : 0;
+    info->nominal_flops = 4.0 * g.N * (double)g.N * g.head_dim * (double)g.windows * g.heads;
+    info->algorithmic_bytes = 4.0 * (double)info->tokens * g.row * h->elem_bytes + 4.0 * g.table_size * g.heads;
+    return SWA_OK;
+}
+
+static size_t io_bytes(const swa_handle* h) {
+    return (size_t)h->g.batch * h->g.ext[0] * h->g.ext[1] * h->g.ext[2] * h->g.row * h->elem_bytes;
+}
+
+swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* v,
+                       const float* bias_table, void* out, void* stream) {
+    if (!h || !q || !k || !v || !bias_table || !out) return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(bias_table, 4))
+        return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned pointer (q, k, v, out need 16 bytes)");
+    const size_t n = io_bytes(h);
+    const size_t nt = (size_t)h->g.table_size * h->g.heads * sizeof(float);
+    if (overlap(out, n, q, n) || overlap(out, n, k, n) || overlap(out, n, v, n) || overlap(out, n, bias_table, nt))
+        return fail(SWA_ERR_INVALID_ARGUMENT, "out overlaps an input");
+    hipStream_t s = (hipStream_t)stream;
+    const swa::Geometry& g = h->g;
+    const bool bf16 = h->cfg.dtype == SWA_BF16;
+    hipError_t e;
+    if (h->cfg.variant == SWA_VARIANT_FUSED) {
+        e = bf16 ? swa::launch_attention_bf16(g, false, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                              bias_table, (uint16_t*)out, s)
+                 : swa::launch_attention_f32(g, false, (const float*)q, (const float*)k, (const float*)v,
+                                             bias_table, (float*)out, s);
+        return e == hipSuccess ? SWA_OK : fail_hip(e, "attention launch");
+    }
+    char* ws = (char*)h->workspace;
+    void* wq = ws;
+    void* wk = ws + h->wm_bytes;
+    void* wv = ws + 2 * h->wm_bytes;
+    void* wo = ws + 3 * h->wm_bytes;
+    if ((e = swa::launch_gather(g, h->elem_bytes, q, wq, s)) != hipSuccess) return fail_hip(e, "gather launch");
+    if ((e = swa::launch_gather(g, h->elem_bytes, k, wk, s)) != hipSuccess) return fail_hip(e, "gather launch");
+    if ((e = swa::launch_gather(g, h->elem_bytes, v, wv, s)) != hipSuccess) return fail_hip(e, "gather launch");
+    e = bf16 ? swa::launch_attention_bf16(g, true, (const uint16_t*)wq, (const uint16_t*)wk, (const uint16_t*)wv,
+                                          bias_table, (uint16_t*)wo, s)
+             : swa::launch_attention_f32(g, true, (const float*)wq, (const float*)wk, (const float*)wv, bias_table,
+                                         (float*)wo, s);
+    if (e != hipSuccess) return fail_hip(e, "attention launch");
+    if ((e = swa::launch_scatter(g, h->elem_bytes, wo, out, s)) != hipSuccess) return fail_hip(e, "scatter launch");
+    return SWA_OK;
+}
+
+swa_status swa_gather(swa_handle* h, const void* src, void* dst_window_major, void* stream) {
+    if (!h || !src || !dst_window_major) return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (!aligned(src, 16) || !aligned(dst_window_major, 16)) return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+    if (overlap(src, io_bytes(h), dst_window_major, h->wm_bytes))
+        return fail(SWA_ERR_INVALID_ARGUMENT, "dst overlaps src");
+    hipError_t e = swa::launch_gather(h->g, h->elem_bytes, src, dst_window_major, (hipStream_t)stream);
+    return e == hipSuccess ? SWA_OK : fail_hip(e, "gather launch");
+}
+
+swa_status swa_scatter(swa_handle* h, const void* src_window_major, void* dst, void* stream) {
+    if (!h || !src_window_major || !dst) return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (!aligned(src_window_major, 16) || !aligned(dst, 16)) return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+    if (overlap(dst, io_bytes(h), src_window_major, h->wm_bytes))
+        return fail(SWA_ERR_INVALID_ARGUMENT, "dst overlaps src");
+    hipError_t e = swa::launch_scatter(h->g, h->elem_bytes, src_window_major, dst, (hipStream_t)stream);
+    return e == hipSuccess ? SWA_OK : fail_hip(e, "scatter launch");
+}
+
+swa_status swa_debug_visibility(swa_handle* h, int64_t window_index, uint8_t* dev_out, void* stream) {
+    if (!h || !dev_out) return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (window_index < 0 || window_index >= h->g.windows) return fail(SWA_ERR_INVALID_ARGUMENT, "window index out of range");
+    hipError_t e = swa::launch_visibility(h->g, window_index, dev_out, (hipStream_t)stream);
+    return e == hipSuccess ? SWA_OK : fail_hip(e, "visibility launch");
+}
+
+} // extern "C"

@@ -1,0 +1,119 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/swa.h declares, and rejects malformed arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from shifted_window_attention_cyclic_amd import binding
+from shifted_window_attention_cyclic_amd.inputs import WORKLOADS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "swa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("swa_create", "swa_forward", "swa_destroy"):
+        assert n in names
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.swa_status_string(s)
+    assert lib.swa_status_string(99) == b"unknown status"
+
+
+def test_null_handles(lib):
+    assert lib.swa_destroy(None) == binding.SWA_OK
+    assert lib.swa_forward(None, None, None, None, None, None, None) == binding.SWA_ERR_INVALID_ARGUMENT
+    assert lib.swa_gather(None, None, None, None) == binding.SWA_ERR_INVALID_ARGUMENT
+    assert lib.swa_scatter(None, None, None, None) == binding.SWA_ERR_INVALID_ARGUMENT
+    assert lib.swa_debug_visibility(None, 0, None, None) == binding.SWA_ERR_INVALID_ARGUMENT
+    assert lib.swa_get_info(None, None) == binding.SWA_ERR_INVALID_ARGUMENT
+    h = ctypes.c_void_p(1234)
+    assert lib.swa_create(None, ctypes.byref(h)) == binding.SWA_ERR_INVALID_ARGUMENT
+    assert h.value is None  # *out cleared on failure
+
+
+def create_status(lib, problem, variant="fused"):
+    cfg = binding.make_config(problem, variant)
+    h = ctypes.c_void_p()
+    st = lib.swa_create(ctypes.byref(cfg), ctypes.byref(h))
+    if st == binding.SWA_OK:
+        lib.swa_destroy(h)
+    return st, lib.swa_last_error().decode()
+
+
+BASE = WORKLOADS["c3_bf16_540x1080"]
+BAD = [
+    ("batch0", BASE.with_(batch=0), binding.SWA_ERR_INVALID_ARGUMENT),
+    ("heads0", BASE.with_(heads=0), binding.SWA_ERR_INVALID_ARGUMENT),
+    ("shift_eq_window", BASE.with_(shift=(0, 12, 6)), binding.SWA_ERR_INVALID_ARGUMENT),
+    ("negative_shift", BASE.with_(shift=(0, -1, 6)), binding.SWA_ERR_INVALID_ARGUMENT),
+    ("window_gt_extent", BASE.with_(window=(1, 600, 12)), binding.SWA_ERR_INVALID_ARGUMENT),
+    ("window0", BASE.with_(window=(1, 0, 12)), binding.SWA_ERR_INVALID_ARGUMENT),
+    ("not_divisible", BASE.with_(extent=(1, 545, 1080), padded=(1, 545, 1080)), binding.SWA_ERR_INVALID_ARGUMENT),
+    ("padded_below_extent", BASE.with_(padded=(1, 530, 1080)), binding.SWA_ERR_INVALID_ARGUMENT),
+    ("pad_on_cyclic_axis", BASE.with_(extent=(1, 540, 1070), padded=(1, 540, 1080)), binding.SWA_ERR_INVALID_ARGUMENT),
+    ("extent0", BASE.with_(extent=(0, 540, 1080)), binding.SWA_ERR_INVALID_ARGUMENT),
+    ("head_dim48", BASE.with_(head_dim=48), binding.SWA_ERR_UNSUPPORTED),
+    ("head_dim128", BASE.with_(head_dim=128), binding.SWA_ERR_UNSUPPORTED),
+    ("window_27x27_bf16", BASE.with_(window=(1, 27, 27)), binding.SWA_ERR_UNSUPPORTED),
+    ("bf16_window_over_512", BASE.with_(extent=(1, 540, 1080), window=(1, 20, 27)), binding.SWA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,problem,status", BAD, ids=[b[0] for b in BAD])
+def test_invalid_configs_rejected_before_hip(lib, name, problem, status):
+    st, msg = create_status(lib, problem)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_bad_dtype_and_variant(lib):
+    cfg = binding.make_config(BASE)
+    cfg.dtype = 7
+    h = ctypes.c_void_p()
+    assert lib.swa_create(ctypes.byref(cfg), ctypes.byref(h)) == binding.SWA_ERR_INVALID_ARGUMENT
+    cfg = binding.make_config(BASE)
+    cfg.variant = 5
+    assert lib.swa_create(ctypes.byref(cfg), ctypes.byref(h)) == binding.SWA_ERR_INVALID_ARGUMENT
+    cfg = binding.make_config(BASE)
+    cfg.cyclic[2] = 2
+    assert lib.swa_create(ctypes.byref(cfg), ctypes.byref(h)) == binding.SWA_ERR_INVALID_ARGUMENT
+    cfg = binding.make_config(BASE)
+    cfg.scale = float("nan")
+    assert lib.swa_create(ctypes.byref(cfg), ctypes.byref(h)) == binding.SWA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_valid_configs_need_a_device(lib, name):
+    st, msg = create_status(lib, WORKLOADS[name])
+    assert st == binding.SWA_ERR_HIP, msg
+
+
+def test_binding_refuses_cpu_tensors():
+    t = torch.zeros(4)
+    with pytest.raises(ValueError):
+        binding._dev(t, "q")
