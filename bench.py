@@ -1,0 +1,226 @@
+"""Benchmark of the shifted-window attention forward pass on one MI355X.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one swa_forward call over the whole workload (gather, window
+attention with bias and mask, softmax, PV and scatter), inputs already in HBM.
+Default workload: bf16, B=1, 540x1080 grid (1/12 degree field at patch 4),
+8 heads x 64, window 12x12, shift 6.  Prints one JSON line.
+
+The CPU-baseline leg times the fp64 oracle on the host cores over a bounded
+sample of the same workload (whole latitude rows) and reports the GPU's
+relative max-abs error on that sample.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "shifted-window attention fwd TFLOP/s + tokens/s, % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+MALL_BYTES = 256 << 20     # Infinity Cache; rotate inputs until the working set is 3x this
+KERNEL_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_kernels.hip",
+                  "shifted_window_attention_cyclic_amd/csrc/swa_geometry.h"]
+KERNEL_NAME = {"bf16": "attn_bf16_kernel", "f32": "attn_f32_kernel"}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if the summary in
+    profiles/ was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^traffic_json:\s*(\{.*\})\s*$", open(path).read(), flags=re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def useful_pairs(p) -> int:
+    """Visible (query, key) pairs summed over real queries: per axis, the key
+    segment sizes multiply, so the sum factorises over the three axes."""
+    total = p.batch
+    for a in range(3):
+        E, P, w, s, cyc = p.extent[a], p.padded[a], p.window[a], p.shift[a], p.cyclic[a]
+
+        def label(c):
+            if cyc:
+                return ((c - s) % E) // w
+            return -1 if c < s else (c - s) // w
+
+        counts = {}
+        for c in range(E):
+            counts[label(c)] = counts.get(label(c), 0) + 1
+        total *= sum(n * n for n in counts.values())
+    return total
+
+
+def cpu_baseline(p, x, out_gpu, rows):
+    import numpy as np
+
+    import oracle
+
+    T, H, W = p.extent
+    rows = min(rows, H)
+    idx = np.array([((b * T + t) * H + y) * W + xx for b in range(p.batch) for t in range(T)
+                    for y in range(rows) for xx in range(W)], dtype=np.int64)
+    host = {n: x[n].float().numpy() for n in ("q", "k", "v", "table")}
+    t0 = time.perf_counter()
+    ref, used = oracle.direct_forward(p, host["q"], host["k"], host["v"], host["table"],
+                                      query_index=idx)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * p.window_tokens * p.head_dim * p.heads * len(idx)  # nominal, per query
+    got = out_gpu.float().cpu().numpy().reshape(p.tokens, p.heads, p.head_dim)[idx]
+    err = float(np.abs(got - ref).max() / np.abs(ref).max())
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
+        "sample": (f"fp64 direct-form oracle over latitude rows 0..{rows - 1} of every time step "
+                   f"and batch item ({len(idx)} of {p.tokens} query tokens, all {p.heads} heads)"),
+        "seconds": dt, "tokens_per_s": len(idx) / dt,
+        "gpu_rel_max_abs_err_on_sample": err,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3_bf16_540x1080")
+    ap.add_argument("--variant", default="fused", choices=["fused", "staged"])
+    ap.add_argument("--cpu-rows", type=int, default=1 << 30,
+                    help="latitude rows in the CPU-baseline sample (default: all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the forward pass is measured "
+                                   "on one MI355X; multi-GPU sharding is not implemented",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from shifted_window_attention_cyclic_amd import WindowAttention, swa_forward
+    from shifted_window_attention_cyclic_amd.inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    p = WORKLOADS[args.workload]
+    x = make_inputs(p)
+    att = WindowAttention(p, args.variant)
+    info = att.info
+    set_bytes = info.algorithmic_bytes
+    nsets = max(1, min(8, math.ceil(3 * MALL_BYTES / set_bytes)))
+    sets = []
+    for i in range(nsets):
+        xi = x if i == 0 else make_inputs(p, seed=p.seed + 7919 * i)
+        d = {n: t.cuda() for n, t in xi.items()}
+        d["out"] = torch.empty_like(d["q"])
+        sets.append(d)
+
+    def step(i):
+        s = sets[i % nsets]
+        swa_forward(att.handle, s["q"], s["k"], s["v"], s["table"], s["out"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    tflops = info.nominal_flops / (ms_per_step * 1e-3) / 1e12
+    useful = 4.0 * useful_pairs(p) * p.head_dim * p.heads
+    achieved_gbs = info.algorithmic_bytes / (avg_launch_ms * 1e-3) / 1e9
+    peak_tf = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
+    traffic = traffic_from_profiles(p.name) if args.variant == "fused" else None
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, N(0,0.02^2) bias table)",
+        "config": {
+            "workload": p.name, "batch": p.batch, "grid_thw": list(p.extent),
+            "padded_thw": list(p.padded), "window": list(p.window), "shift": list(p.shift),
+            "heads": p.heads, "head_dim": p.head_dim, "variant": args.variant,
+            "input_sets_rotated": nsets,
+        },
+        "tokens_per_s": round(info.tokens / (ms_per_step * 1e-3), 1),
+        "mfma_peak_frac": round(tflops / peak_tf, 5),
+        "useful_tflops": round(useful / (ms_per_step * 1e-3) / 1e12, 3),
+        "kernel": {"name": KERNEL_NAME[p.dtype] if args.variant == "fused" else "gather+attn+scatter",
+                   "avg_launch_ms": round(avg_launch_ms, 5),
+                   "p10_ms": round(launch_ms[len(launch_ms) // 10], 5),
+                   "p90_ms": round(launch_ms[(9 * len(launch_ms)) // 10], 5),
+                   "source_sha256_16": kernel_source_hash()},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": info.algorithmic_bytes,
+            "nominal_flops_per_launch": info.nominal_flops,
+            "mfma_ceiling_frac_at_hbm_roof": round(
+                min(1.0, info.nominal_flops / info.algorithmic_bytes * PEAK_HBM_GBS * 1e9
+                    / (peak_tf * 1e12)), 4),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p, x, sets[0]["out"], args.cpu_rows)
+    att.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
