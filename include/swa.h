@@ -79,14 +79,14 @@ typedef enum swa_variant {
 typedef struct swa_config {
     int batch;     /* B >= 1 */
     int heads;     /* N_h >= 1 (TERRA, Table V) */
-    int head_dim;  /* d / N_h; 32 or 64 for SWA_BF16, 1..128 for SWA_F32 */
+    int head_dim;  /* d / N_h: 32 or 64 */
     int grid[3];   /* real extents (T, H, W): time, latitude, longitude (TERRA, Table I) */
     int padded[3]; /* padded extents (T^, H^, W^) >= grid; must equal grid on cyclic axes */
     int window[3]; /* window (w_t, w_y, w_x); 1 <= w <= padded, padded % w == 0 */
     int shift[3];  /* shift (s_t, s_y, s_x); 0 <= s < w */
     int cyclic[3]; /* 1: cyclic axis, 0: masked axis.  Usual setting {0, 0, 1} */
     swa_dtype dtype;
-    float scale;   /* logit scale; 0 selects 1/sqrt(head_dim) */
+    float scale;   /* logit scale, > 0; 0 selects 1/sqrt(head_dim) */
     swa_variant variant;
 } swa_config;
 

@@ -19,6 +19,9 @@ ARCH = "gfx950"
 def hipcc_flags():
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep MFMA operands and results in VGPRs (no AGPR copies), and let
+            # fmaxf skip NaN canonicalisation (inputs are finite; masks use -inf)
+            "-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans",
             "-I", INCLUDE, "-I", CSRC]
 
 

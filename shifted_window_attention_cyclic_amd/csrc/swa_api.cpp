@@ -43,7 +43,8 @@ swa_status validate(const swa_config* c, swa::Geometry* g, int* elem_bytes) {
     if (c->variant != SWA_VARIANT_FUSED && c->variant != SWA_VARIANT_STAGED)
         return fail(SWA_ERR_INVALID_ARGUMENT, "unknown variant");
     if (c->head_dim < 1) return fail(SWA_ERR_INVALID_ARGUMENT, "head_dim must be >= 1");
-    if (!(isfinite(c->scale))) return fail(SWA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (!(isfinite(c->scale)) || c->scale < 0.f)
+        return fail(SWA_ERR_INVALID_ARGUMENT, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
     static const char* axis[3] = {"time", "latitude", "longitude"};
     int64_t tokens = c->batch;
     int N = 1, table = 1;
@@ -115,7 +116,14 @@ swa_status validate(const swa_config* c, swa::Geometry* g, int* elem_bytes) {
     G.tdy = 2 * c->window[1] - 1;
     G.tdx = 2 * c->window[2] - 1;
     G.table_size = table;
+    G.c0 = ((c->window[0] - 1) * G.tdy + (c->window[1] - 1)) * G.tdx + (c->window[2] - 1);
     G.scale = c->scale != 0.f ? c->scale : (float)(1.0 / sqrt((double)c->head_dim));
+    G.fd_heads = swa::make_fastdiv((uint32_t)c->heads);
+    G.fd_nW = swa::make_fastdiv((uint32_t)G.nW);
+    G.fd_nwin1 = swa::make_fastdiv((uint32_t)G.nwin[1]);
+    G.fd_nwin2 = swa::make_fastdiv((uint32_t)G.nwin[2]);
+    G.fd_win1 = swa::make_fastdiv((uint32_t)c->window[1]);
+    G.fd_win2 = swa::make_fastdiv((uint32_t)c->window[2]);
     *elem_bytes = c->dtype == SWA_F32 ? 4 : 2;
 
     const size_t lds = swa::attention_lds_bytes(G, c->dtype == SWA_BF16);
@@ -168,7 +176,26 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
     if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess) return fail_hip(e, "hipGetDeviceProperties");
     if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
         return fail(SWA_ERR_HIP, std::string("device is ") + prop.gcnArchName + ", kernels are built for gfx950");
-    if ((e = swa::prepare_kernels()) != hipSuccess) return fail_hip(e, "hipFuncSetAttribute");
+    // LDS a workgroup may use: gfx950 has 160 KB per CU
+    int optin = 0, per_cu = 0;
+    (void)hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev);
+    (void)hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    (void)hipGetLastError();
+    int max_lds = optin > per_cu ? optin : per_cu;
+    if (max_lds < 64 * 1024) max_lds = 64 * 1024;
+    if (max_lds > 160 * 1024) max_lds = 160 * 1024;
+    const size_t need = swa::attention_lds_bytes(g, cfg->dtype == SWA_BF16);
+    if (need > (size_t)max_lds) {
+        char buf[160];
+        snprintf(buf, sizeof buf, "window needs %zu bytes of LDS, the device allows %d", need, max_lds);
+        return fail(SWA_ERR_UNSUPPORTED, buf);
+    }
+    if ((e = swa::prepare_kernels(max_lds)) != hipSuccess) return fail_hip(e, "hipFuncSetAttribute");
+    if (cfg->dtype == SWA_BF16) {
+        int per_cu = 0;
+        if ((e = swa::bf16_check_fits(g, &per_cu)) != hipSuccess) return fail_hip(e, "occupancy query");
+        if (per_cu < 1) return fail(SWA_ERR_UNSUPPORTED, "attention kernel does not fit on a compute unit");
+    }
 
     swa_handle* h = new (std::nothrow) swa_handle();
     if (!h) return fail(SWA_ERR_OUT_OF_MEMORY, "host allocation");

@@ -21,6 +21,25 @@
 
 namespace swa {
 
+// n / d for 0 <= n < 2^31 and 1 <= d < 2^31 by multiply-high and shift
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): t = mulhi(m, n), q = (t + n) >> l.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) l++;
+    const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return FastDiv{d, (uint32_t)m, l};
+}
+
+__host__ __device__ inline uint32_t fdiv(const FastDiv& f, uint32_t n) {
+    const uint32_t t = (uint32_t)(((uint64_t)f.m * n) >> 32);
+    return (t + n) >> f.l;
+}
+
 struct Geometry {
     int batch, heads, head_dim;
     int ext[3];   // real extents (T, H, W)
@@ -35,8 +54,26 @@ struct Geometry {
     int row;      // elements per token: heads * head_dim
     int tdy, tdx; // 2 w_y - 1, 2 w_x - 1
     int table_size; // (2 w_t - 1) * tdy * tdx
+    int c0;       // qb - kb of any token (see above)
     float scale;  // logit scale
+    FastDiv fd_heads, fd_nW, fd_nwin1, fd_nwin2, fd_win1, fd_win2;
 };
+
+// Whether any key of window (wc) can be hidden from some query: the window
+// holds the wrapped part of a masked axis, or pad tokens.  A rolled window
+// [lo, lo + w) takes sources [lo + s, min(lo + w + s, P)) and, past the wrap,
+// [0, lo + w + s - P); pad is any source >= E.
+__host__ __device__ inline bool window_maybe_masked(const Geometry& g, const int wc[3]) {
+    for (int a = 0; a < 3; a++) {
+        if (g.cyc[a]) continue;
+        const int lo = wc[a] * g.win[a];
+        const int hi = lo + g.win[a] + g.shift[a];
+        if (g.shift[a] > 0 && wc[a] == g.nwin[a] - 1) return true;
+        if ((hi < g.pad[a] ? hi : g.pad[a]) > g.ext[a]) return true;
+        if (hi - g.pad[a] > g.ext[a]) return true;
+    }
+    return false;
+}
 
 // Mask words.  A key word holds kb in bits 0..15, the wrapped flags of the
 // masked axes in bits 16..18 and the pad flag in bit 19.  A query word holds
@@ -109,9 +146,12 @@ hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, 
 hipError_t launch_attention_bf16(const Geometry& g, bool staged, const uint16_t* q,
                                  const uint16_t* k, const uint16_t* v, const float* table,
                                  uint16_t* out, hipStream_t s);
-// LDS bytes the attention kernels need for g (0 when g is outside their range).
+// LDS bytes the attention kernels need for g.
 size_t attention_lds_bytes(const Geometry& g, bool bf16);
-// One-time per-device kernel attributes (large dynamic LDS).
-hipError_t prepare_kernels();
+// Workgroups of the bf16 attention kernel one compute unit can hold (0: the
+// kernel does not fit).
+hipError_t bf16_check_fits(const Geometry& g, int* blocks_per_cu);
+// Lets every attention kernel take up to max_lds bytes of dynamic LDS.
+hipError_t prepare_kernels(int max_lds);
 
 } // namespace swa

@@ -275,170 +275,355 @@ hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, 
 // --------------------------------------------------------------------------
 // bf16 attention on MFMA.
 //
-// Block = (window, head), 4 waves.  K of the window goes to LDS as [key][d];
-// V goes to LDS transposed, [d][key], so the PV product can read 4 keys of
-// one d-row with one 8-byte load.  Each wave takes query tiles of 16 queries
-// and computes, per tile:
-//   S^T = K Q^T   with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS,
-//                 B = Q rows straight from global memory); lane l then holds
-//                 scores of query (l % 16) against keys 4*(l/16) + 0..3 of
-//                 every 16-key tile,
-//   bias + mask   from LDS tables, in base-2 units (scaled by log2 e),
-//   softmax       online over blocks of kKeyTilesPerBlock key tiles: running
-//                 max and sum per query, reduced across the 4 lanes that share
-//                 a query,
-//   O^T = V^T P^T with the same MFMA (A = V^T from LDS, B = bf16 P straight
-//                 from the score registers: two 16-key tiles give the 8 keys
-//                 of one 32-deep step; an odd last tile uses 16x16x16),
-//   epilogue      divide by the sum, round to bf16, store 4 d-values per lane.
-// Both products use the same key order on both operands, so any order of
-// the 32 reduction slots the hardware uses gives the same sums.
+// Block = (window, head), one wave per 16-query tile (two tiles per wave past
+// 16 tiles), so the window's K and V in LDS serve as many waves as possible
+// and several blocks share a compute unit.  Phases:
+//   A  per-window token tables in LDS: mask field and source row of each
+//      token, and the bias offset kb of every 4-key group;
+//   B  every global load of the block issued back to back: K and V of the
+//      window (4 keys x 16 bytes per item), this head's bias table slice and
+//      each wave's Q tiles; then K to LDS ([key][d], 16-byte chunks XOR-
+//      swizzled by row so 8 consecutive rows hit distinct banks), V to LDS
+//      transposed ([d][key], 4 keys per 8-byte write) and the bias times
+//      log2(e);
+//   C  per 16-query tile of a wave:
+//        S^T = K Q^T     v_mfma_f32_16x16x32_bf16, A = K from LDS, B = Q tile
+//                        in registers, C = 0; lane l holds query (l % 16)
+//                        against keys 4*(l/16) + 0..3 of every 16-key tile;
+//                        all tiles of a key block are issued before any
+//                        result is read.  The accumulator input is never a
+//                        register a load may still overwrite during the MFMA;
+//        logits          (scale * S + bias) * log2(e) by one FMA; the bias of
+//                        query n and key m sits at qb(n) - kb(m), and when the
+//                        window's longitude extent is a multiple of 4 the 4
+//                        keys of a lane are neighbours in one window row, so
+//                        their 4 biases are 4 consecutive table entries read
+//                        with two ds_read2_b32;
+//        mask            -inf where the key is pad, past N or on the other
+//                        side of a masked wrap; only on windows / tiles that
+//                        can hold such keys;
+//        softmax         online over key blocks, in base 2: p = exp2(l - m),
+//                        running max per query (reduced across the 4 lanes
+//                        that share it);
+//        O^T = V^T P^T   same MFMA, A = V^T from LDS, B = bf16 P straight
+//                        from registers (two key tiles make one 32-deep step;
+//                        an odd last tile uses 16x16x16); the row sum of the
+//                        bf16 P comes from the same product with A = 1;
+//        epilogue        divide by the sum, round to bf16, store 4 d-values
+//                        per lane at the token's address.
+// Both products use the same key order on both operands, so whatever order
+// the hardware gives the 32 reduction slots the sums are the same.
+// The kernel is specialised on the key-tile count of common window sizes
+// (KT_FIXED > 0: straight-line code); KT_FIXED = 0 handles any count.
 // --------------------------------------------------------------------------
-constexpr int kBf16Waves = 4;
 constexpr int kKeyTilesPerBlock = 9;
+constexpr int kLdsBytes = 160 * 1024; // gfx950 LDS per compute unit
+#ifndef SWA_MFMA_K32
+#define SWA_MFMA_K32 0
+#endif
+// 1: 32-deep v_mfma_f32_16x16x32_bf16; 0: pairs of 16-deep v_mfma_f32_16x16x16_bf16
+// fed from the same 16-byte fragments (low and high 8 bytes as two k-steps)
+constexpr bool kMfmaK32 = SWA_MFMA_K32 != 0;
+
+__device__ inline i16x4 half_lo(bf16x8 x) {
+    const u32x4 u = __builtin_bit_cast(u32x4, x);
+    return __builtin_bit_cast(i16x4, u32x2{u[0], u[1]});
+}
+__device__ inline i16x4 half_hi(bf16x8 x) {
+    const u32x4 u = __builtin_bit_cast(u32x4, x);
+    return __builtin_bit_cast(i16x4, u32x2{u[2], u[3]});
+}
+// acc += A B over a 32-deep step, A and B as 16-byte lane fragments
+__device__ inline f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 acc) {
+    if (kMfmaK32) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(half_lo(a), half_lo(b), acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(half_hi(a), half_hi(b), acc, 0, 0, 0);
+}
 
 struct Bf16Lds {
-    int NP, KSTR, VSTR;
-    size_t ks, vt, bias, kword, qword, rowi, total;
+    int NP, VSTR;
+    size_t ks, vt, bias, kb4, rg, rowi, total;
 };
 
 __host__ __device__ inline Bf16Lds bf16_lds(const Geometry& g) {
     Bf16Lds L;
     L.NP = (g.N + 15) / 16 * 16;
-    L.KSTR = g.head_dim + 8; // bf16 elements per K row (16-byte pad against bank conflicts)
-    L.VSTR = L.NP + 4;       // bf16 elements per V^T row
+    L.VSTR = L.NP + 4; // bf16 elements per V^T row: 8-byte aligned, rows 16 apart hit distinct banks
     L.ks = 0;
-    L.vt = L.ks + (size_t)L.NP * L.KSTR * 2;
+    L.vt = L.ks + (size_t)L.NP * g.head_dim * 2;
     L.bias = L.vt + (size_t)g.head_dim * L.VSTR * 2;
-    L.bias = (L.bias + 15) / 16 * 16;
-    L.kword = L.bias + (size_t)g.table_size * 4;
-    L.qword = L.kword + (size_t)L.NP * 4;
-    L.rowi = L.qword + (size_t)L.NP * 4;
+    L.kb4 = L.bias + ((size_t)g.table_size * 4 + 15) / 16 * 16;
+    L.rg = L.kb4 + (size_t)L.NP * 4;
+    L.rowi = L.rg + (size_t)L.NP * 4;
     L.total = L.rowi + (size_t)L.NP * 4;
     return L;
 }
 
-__device__ inline bf16x8 load_bf16x8(const uint16_t* p) {
-    return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
-}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline unsigned pack_bf16x2(float a, float b) {
-    __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (unsigned)__builtin_bit_cast(uint16_t, x) | ((unsigned)__builtin_bit_cast(uint16_t, y) << 16);
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
+// 16-byte chunk slot of logical chunk c in K row m (rows of D bf16)
 template <int D>
-__global__ __launch_bounds__(kBf16Waves * 64) void attn_bf16_kernel(
+__device__ inline int k_slot(int m, int c) {
+    constexpr int CH = D / 8;
+    constexpr int ROWS_PER_128B = 128 / (D * 2);
+    return c ^ ((m / ROWS_PER_128B) % CH);
+}
+
+// window-local coordinates of local index n
+__device__ inline void local_coords(const Geometry& g, int n, int& lt, int& ly, int& lx) {
+    const uint32_t r = fdiv(g.fd_win2, (uint32_t)n);
+    lx = n - (int)r * g.win[2];
+    lt = (int)fdiv(g.fd_win1, r);
+    ly = (int)r - lt * g.win[1];
+}
+
+template <int D, int NWAVES, int QT_MAX, int KT_FIXED, bool BIAS_VEC>
+__global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
     Geometry g, int staged, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ table, uint16_t* __restrict__ out) {
-    constexpr int KSTEPS = D / 32; // 32-deep steps of Q K^T
+    constexpr int THREADS = NWAVES * 64;
+    constexpr int KSTEPS = D / 32; // 32-deep steps of K Q^T
     constexpr int DT = D / 16;     // 16-row d tiles of O^T
     constexpr int CH = D / 8;      // 16-byte chunks per (token, head)
-    constexpr int KB = kKeyTilesPerBlock;
+    constexpr int KT_MAX = KT_FIXED > 0 ? KT_FIXED : NWAVES * QT_MAX;
+    static_assert(KT_MAX <= NWAVES * QT_MAX, "every query tile needs a wave");
+    constexpr int LOAD_IT = ((KT_MAX * 4) * CH + THREADS - 1) / THREADS;
+    constexpr int KB = (KT_FIXED > 0 && KT_FIXED <= kKeyTilesPerBlock) ? KT_FIXED : kKeyTilesPerBlock;
+    static_assert(KT_FIXED == 0 || KT_FIXED % KB == 0, "fixed tile counts split into equal key blocks");
+    constexpr int KB_UNROLL = KT_FIXED > 0 ? KT_FIXED / KB : 1;
+    constexpr int BIAS_UNROLL = 4;
     extern __shared__ __align__(16) unsigned char smem[];
     const Bf16Lds L = bf16_lds(g);
     uint16_t* Ks = (uint16_t*)(smem + L.ks);
     uint16_t* Vt = (uint16_t*)(smem + L.vt);
     float* bias = (float*)(smem + L.bias);
-    int* kword = (int*)(smem + L.kword);
-    int* qword = (int*)(smem + L.qword);
+    int* kb4 = (int*)(smem + L.kb4); // 4 * kb, per key (BIAS_VEC: per 4-key group, at index 4g)
+    int* rg = (int*)(smem + L.rg);
     int* rowi = (int*)(smem + L.rowi);
-    const int N = g.N, NP = L.NP, KT = NP / 16;
+    const int N = g.N, NP = L.NP;
+    const int KT = KT_FIXED > 0 ? KT_FIXED : NP / 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
 
-    const int64_t total = g.windows * g.heads;
-    const int64_t work = xcd_work_index(blockIdx.x, total);
-    const int64_t wi = work / g.heads;
-    const int h = (int)(work - wi * g.heads);
+    // block -> (window, head); blocks are dealt to XCDs round-robin, so this
+    // keeps the heads of a window and neighbouring windows on one XCD
+    const uint32_t total = (uint32_t)(g.windows * g.heads);
+    const uint32_t work = (uint32_t)xcd_work_index(blockIdx.x, total);
+    const uint32_t wi = fdiv(g.fd_heads, work);
+    const int h = (int)(work - wi * (uint32_t)g.heads);
+    const int b = (int)fdiv(g.fd_nW, wi);
+    int wc[3];
+    {
+        const uint32_t r = wi - (uint32_t)b * (uint32_t)g.nW;
+        const uint32_t r2 = fdiv(g.fd_nwin2, r);
+        wc[2] = (int)(r - r2 * (uint32_t)g.nwin[2]);
+        wc[0] = (int)fdiv(g.fd_nwin1, r2);
+        wc[1] = (int)(r2 - (uint32_t)wc[0] * (uint32_t)g.nwin[1]);
+    }
+    const bool masked_window = window_maybe_masked(g, wc);
 
-    fill_token_tables(g, wi, staged != 0, NP, kword, qword, rowi);
-    for (int i = threadIdx.x; i < g.table_size; i += blockDim.x)
-        bias[i] = table[(int64_t)i * g.heads + h] * kLog2e;
-    __syncthreads();
-
-    // K rows and V^T columns into LDS; pad keys are zeros (their P is 0, and
-    // 0 * 0 keeps the PV sums finite).
-    for (int i = threadIdx.x; i < NP * CH; i += blockDim.x) {
-        int m = i / CH, c = i % CH;
-        int r = rowi[m];
-        u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-        if (r >= 0) {
-            int64_t off = (int64_t)r * g.row + (int64_t)h * D + c * 8;
-            kv = *(const u32x4*)(k + off);
-            vv = *(const u32x4*)(v + off);
-        }
-        *(u32x4*)(Ks + m * L.KSTR + c * 8) = kv;
-        for (int j = 0; j < 4; j++) {
-            Vt[(c * 8 + 2 * j) * L.VSTR + m] = (uint16_t)(vv[j] & 0xFFFF);
-            Vt[(c * 8 + 2 * j + 1) * L.VSTR + m] = (uint16_t)(vv[j] >> 16);
+    // ---- A: token tables
+    for (int n = tid; n < NP; n += THREADS) {
+        if (n < N) {
+            int l[3];
+            local_coords(g, n, l[0], l[1], l[2]);
+            int region = 0, tok = b;
+            bool is_pad = false;
+#pragma unroll
+            for (int a = 0; a < 3; a++) {
+                const int cr = wc[a] * g.win[a] + l[a];
+                int c = cr + g.shift[a];
+                if (c >= g.pad[a]) c -= g.pad[a];
+                is_pad |= c >= g.ext[a];
+                if (!g.cyc[a] && cr >= g.pad[a] - g.shift[a]) region |= 1 << a;
+                tok = tok * g.ext[a] + c;
+            }
+            rg[n] = region | (is_pad ? 8 : 0);
+            rowi[n] = is_pad ? -1 : (staged ? (int)(wi * (uint32_t)N + n) : tok);
+            kb4[n] = ((l[0] * g.tdy + l[1]) * g.tdx + l[2]) * 4;
+        } else {
+            rg[n] = 15;
+            rowi[n] = -1;
+            kb4[n] = BIAS_VEC ? 12 : 0; // keeps qb - kb (- 3) inside the table
         }
     }
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = lane & 15, grp = lane >> 4;
-    const float sl2 = g.scale * kLog2e;
-
-    for (int qt = wave; qt < KT; qt += kBf16Waves) {
-        const int n = qt * 16 + col;
-        const int qw = qword[n];
-        const int qb = qw & 0xFFFF;
-        const int r = rowi[n];
-        bf16x8 qop[KSTEPS];
-        for (int ks = 0; ks < KSTEPS; ks++) {
-            if (r >= 0)
-                qop[ks] = load_bf16x8(q + (int64_t)r * g.row + (int64_t)h * D + ks * 32 + grp * 8);
-            else
-                qop[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    // ---- B: all loads in flight together
+    u32x4 kr[LOAD_IT][4], vr[LOAD_IT][4];
+    const int items = (NP / 4) * CH;
+    const uint16_t* kh = k + h * D;
+    const uint16_t* vh = v + h * D;
+#pragma unroll
+    for (int it = 0; it < LOAD_IT; it++) {
+        const int i = tid + it * THREADS;
+        const int g4 = i / CH, c = i % CH;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int r = i < items ? rowi[g4 * 4 + j] : -1;
+            if (r >= 0) {
+                const uint32_t off = (uint32_t)r * (uint32_t)g.row + c * 8;
+                kr[it][j] = *(const u32x4*)(kh + off);
+                vr[it][j] = *(const u32x4*)(vh + off);
+            } else {
+                kr[it][j] = u32x4{0, 0, 0, 0};
+                vr[it][j] = u32x4{0, 0, 0, 0};
+            }
         }
-        f32x4 o[DT];
-        for (int dt = 0; dt < DT; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float mrun = -INFINITY, lsum = 0.f;
+    }
+    bf16x8 qop[QT_MAX][KSTEPS];
+    int qn[QT_MAX];
+#pragma unroll
+    for (int t = 0; t < QT_MAX; t++) {
+        const int qt = wave + t * NWAVES;
+        qn[t] = qt * 16 + col;
+        const int r = qt < KT ? rowi[qn[t]] : -1;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ks++) {
+            u32x4 val = {0, 0, 0, 0};
+            if (r >= 0) val = *(const u32x4*)(q + (uint32_t)r * (uint32_t)g.row + h * D + ks * 32 + grp * 8);
+            qop[t][ks] = __builtin_bit_cast(bf16x8, val);
+        }
+    }
+    for (int base = 0; base < g.table_size; base += BIAS_UNROLL * THREADS) {
+        float bv[BIAS_UNROLL];
+#pragma unroll
+        for (int u = 0; u < BIAS_UNROLL; u++) {
+            const int i = base + u * THREADS + tid;
+            bv[u] = i < g.table_size ? table[i * g.heads + h] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < BIAS_UNROLL; u++) {
+            const int i = base + u * THREADS + tid;
+            if (i < g.table_size) bias[i] = bv[u] * kLog2e;
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < LOAD_IT; it++) {
+        const int i = tid + it * THREADS;
+        if (i < items) {
+            const int g4 = i / CH, c = i % CH;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int m = g4 * 4 + j;
+                *(u32x4*)(Ks + m * D + k_slot<D>(m, c) * 8) = kr[it][j];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                // bf16 e of 4 consecutive keys: low or high halves of dword e / 2
+                const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                const unsigned lo = __builtin_amdgcn_perm(vr[it][1][e >> 1], vr[it][0][e >> 1], sel);
+                const unsigned hi = __builtin_amdgcn_perm(vr[it][3][e >> 1], vr[it][2][e >> 1], sel);
+                *(u32x2*)(Vt + (c * 8 + e) * L.VSTR + g4 * 4) = u32x2{lo, hi};
+            }
+        }
+    }
+    __syncthreads();
 
-        for (int kb0 = 0; kb0 < KT; kb0 += KB) {
-            float s[KB][4];
-            float bmax = -INFINITY;
+    // ---- C: query tiles
+    const float cl2 = g.scale * kLog2e;
+    const unsigned one2 = 0x3F803F80u; // two bf16 ones
+    const bf16x8 ones8 = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
+    const i16x4 ones4 = __builtin_bit_cast(i16x4, u32x2{one2, one2});
+    const unsigned char* bias_bytes = (const unsigned char*)bias;
+#pragma unroll
+    for (int t = 0; t < QT_MAX; t++) {
+        const int qt = wave + t * NWAVES;
+        if (qt >= KT) break;
+        const int n = qn[t];
+        const int qreg = rg[n];
+        const int r = rowi[n];
+        int qb4;
+        if (n < N) {
+            int lt, ly, lx;
+            local_coords(g, n, lt, ly, lx);
+            qb4 = (((lt * g.tdy + ly) * g.tdx + lx) + g.c0) * 4;
+        } else {
+            qb4 = (g.table_size - 1) * 4; // largest qb keeps qb - kb inside the table
+        }
+        const unsigned char* qbias = bias_bytes + qb4;
+        f32x4 o[DT], osum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float mrun = -INFINITY;
+
+#pragma unroll KB_UNROLL
+        for (int kb0 = 0; kb0 < (KT_FIXED > 0 ? KT_FIXED : KT); kb0 += KB) {
+            f32x4 s[KB];
 #pragma unroll
             for (int kt = 0; kt < KB; kt++) {
-                if (kb0 + kt < KT) {
-                    const int key0 = (kb0 + kt) * 16;
+                const int key0 = (kb0 + kt) * 16;
+                if (KT_FIXED > 0 || kb0 + kt < KT) {
+                    const int krow = key0 + col;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KSTEPS; ks++) {
-                        bf16x8 a = load_bf16x8(Ks + (key0 + col) * L.KSTR + ks * 32 + grp * 8);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], acc, 0, 0, 0);
+                        const bf16x8 a = __builtin_bit_cast(
+                            bf16x8, *(const u32x4*)(Ks + krow * D + k_slot<D>(krow, ks * 4 + grp) * 8));
+                        acc = mfma32(a, qop[t][ks], acc);
                     }
+                    s[kt] = acc;
+                }
+            }
+            float bmax = -INFINITY;
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        int kw = kword[key0 + grp * 4 + i];
-                        float val = acc[i] * sl2 + bias[qb - (kw & 0xFFFF)];
-                        val = visible(qw, kw) ? val : -INFINITY;
-                        s[kt][i] = val;
-                        bmax = fmaxf(bmax, val);
+            for (int kt = 0; kt < KB; kt++) {
+                const int key0 = (kb0 + kt) * 16;
+                if (KT_FIXED > 0 || kb0 + kt < KT) {
+                    float bb[4];
+                    if (BIAS_VEC) {
+                        // keys key0 + 4*grp + i share a window row: biases at qb - kb0 - i
+                        const float* bp = (const float*)(qbias - kb4[key0 + grp * 4]) - 3;
+                        bb[3] = bp[0];
+                        bb[2] = bp[1];
+                        bb[1] = bp[2];
+                        bb[0] = bp[3];
+                    } else {
+                        const int4 kq = *(const int4*)(kb4 + key0 + grp * 4);
+                        bb[0] = *(const float*)(qbias - kq.x);
+                        bb[1] = *(const float*)(qbias - kq.y);
+                        bb[2] = *(const float*)(qbias - kq.z);
+                        bb[3] = *(const float*)(qbias - kq.w);
                     }
+                    // logits in base-2 units: (scale * q.k + bias) * log2(e)
+                    f32x4 lg = {fmaf(s[kt][0], cl2, bb[0]), fmaf(s[kt][1], cl2, bb[1]),
+                                fmaf(s[kt][2], cl2, bb[2]), fmaf(s[kt][3], cl2, bb[3])};
+                    if (masked_window || key0 + 16 > N) {
+                        const int4 kr4 = *(const int4*)(rg + key0 + grp * 4);
+                        lg[0] = kr4.x == qreg ? lg[0] : -INFINITY;
+                        lg[1] = kr4.y == qreg ? lg[1] : -INFINITY;
+                        lg[2] = kr4.z == qreg ? lg[2] : -INFINITY;
+                        lg[3] = kr4.w == qreg ? lg[3] : -INFINITY;
+                    }
+                    s[kt] = lg;
+                    bmax = fmaxf(bmax, fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
                 } else {
-#pragma unroll
-                    for (int i = 0; i < 4; i++) s[kt][i] = -INFINITY;
+                    s[kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
                 }
             }
             bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
             bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
             const float mnew = fmaxf(mrun, bmax);
-            const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(mrun - msafe);
-            lsum *= alpha;
+            const float mc = mnew == -INFINITY ? 0.f : mnew;
+            if (kb0 > 0) { // rescale what earlier key blocks accumulated
+                const float alpha = __builtin_amdgcn_exp2f(mrun - mc);
+                osum *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < DT; dt++) o[dt] *= alpha;
+                for (int dt = 0; dt < DT; dt++) o[dt] *= alpha;
+            }
             mrun = mnew;
 
-            unsigned pk[KB][2]; // bf16 P, 4 keys per tile packed in two dwords
+            unsigned pk[KB][2]; // bf16 P: 4 keys per tile in two dwords
 #pragma unroll
             for (int kt = 0; kt < KB; kt++) {
                 float p[4];
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    p[i] = __builtin_amdgcn_exp2f(s[kt][i] - msafe);
-                    lsum += p[i];
-                }
+                for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(s[kt][i] - mc);
                 pk[kt][0] = pack_bf16x2(p[0], p[1]);
                 pk[kt][1] = pack_bf16x2(p[2], p[3]);
             }
@@ -446,40 +631,41 @@ __global__ __launch_bounds__(kBf16Waves * 64) void attn_bf16_kernel(
 #pragma unroll
             for (int kt = 0; kt < KB; kt += 2) {
                 const int t0 = kb0 + kt;
-                if (kt + 1 < KB && t0 + 1 < KT) {
-                    bf16x8 b = __builtin_bit_cast(
+                const bool pair = kt + 1 < KB && (KT_FIXED > 0 || t0 + 1 < KT);
+                if (pair) {
+                    const bf16x8 bop = __builtin_bit_cast(
                         bf16x8, u32x4{pk[kt][0], pk[kt][1], pk[kt + 1][0], pk[kt + 1][1]});
 #pragma unroll
                     for (int dt = 0; dt < DT; dt++) {
-                        const uint16_t* vr = Vt + (dt * 16 + col) * L.VSTR + t0 * 16 + grp * 4;
-                        u32x2 lo = *(const u32x2*)vr;
-                        u32x2 hi = *(const u32x2*)(vr + 16);
-                        bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, o[dt], 0, 0, 0);
+                        const uint16_t* vrow = Vt + (dt * 16 + col) * L.VSTR + t0 * 16 + grp * 4;
+                        const u32x2 lo = *(const u32x2*)vrow;
+                        const u32x2 hi = *(const u32x2*)(vrow + 16);
+                        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                        o[dt] = mfma32(a, bop, o[dt]);
                     }
-                } else if (t0 < KT) {
-                    i16x4 b = __builtin_bit_cast(i16x4, u32x2{pk[kt][0], pk[kt][1]});
+                    osum = mfma32(ones8, bop, osum);
+                } else if (KT_FIXED > 0 || t0 < KT) {
+                    const i16x4 bop = __builtin_bit_cast(i16x4, u32x2{pk[kt][0], pk[kt][1]});
 #pragma unroll
                     for (int dt = 0; dt < DT; dt++) {
-                        const uint16_t* vr = Vt + (dt * 16 + col) * L.VSTR + t0 * 16 + grp * 4;
-                        i16x4 a = __builtin_bit_cast(i16x4, *(const u32x2*)vr);
-                        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, o[dt], 0, 0, 0);
+                        const uint16_t* vrow = Vt + (dt * 16 + col) * L.VSTR + t0 * 16 + grp * 4;
+                        const i16x4 a = __builtin_bit_cast(i16x4, *(const u32x2*)vrow);
+                        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bop, o[dt], 0, 0, 0);
                     }
+                    osum = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, bop, osum, 0, 0, 0);
                 }
             }
         }
-        lsum += __shfl_xor(lsum, 16);
-        lsum += __shfl_xor(lsum, 32);
 
-        int64_t orow = r;
-        if (r < 0 && staged) orow = wi * N + n; // staged: pad slots of O are written as zeros
+        int orow = r;
+        if (r < 0 && staged) orow = (int)(wi * (uint32_t)N + n); // staged: pad slots of O are zeros
         if (orow >= 0 && n < N) {
-            const float inv = r >= 0 ? 1.f / lsum : 0.f;
-            uint16_t* op = out + orow * g.row + (int64_t)h * D + grp * 4;
+            const float inv = r >= 0 ? __builtin_amdgcn_rcpf(osum[0]) : 0.f;
+            uint16_t* op = out + (uint32_t)orow * (uint32_t)g.row + h * D + grp * 4;
 #pragma unroll
             for (int dt = 0; dt < DT; dt++) {
-                u32x2 w = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
-                           pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
+                const u32x2 w = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
+                                 pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
                 *(u32x2*)(op + dt * 16) = w;
             }
         }
@@ -490,34 +676,64 @@ size_t attention_lds_bytes(const Geometry& g, bool bf16) {
     return bf16 ? bf16_lds(g).total : f32_lds_bytes(g);
 }
 
+// Kernel variant for a geometry: specialised tile counts, else the general one.
+typedef void (*bf16_kernel_t)(Geometry, int, const uint16_t*, const uint16_t*, const uint16_t*,
+                              const float*, uint16_t*);
+struct Bf16Variant {
+    bf16_kernel_t f;
+    int waves;
+};
+
+template <int D, bool BV>
+static Bf16Variant bf16_variant_b(int KT) {
+    switch (KT) {
+    case 4: return {attn_bf16_kernel<D, 4, 1, 4, BV>, 4};
+    case 7: return {attn_bf16_kernel<D, 7, 1, 7, BV>, 7};
+    case 9: return {attn_bf16_kernel<D, 9, 1, 9, BV>, 9};
+    case 18: return {attn_bf16_kernel<D, 9, 2, 18, BV>, 9};
+    default:
+        if (KT <= 8) return {attn_bf16_kernel<D, 8, 1, 0, BV>, 8};
+        return {attn_bf16_kernel<D, 8, 4, 0, BV>, 8};
+    }
+}
+
+static Bf16Variant bf16_variant_for(const Geometry& g) {
+    const int KT = (g.N + 15) / 16;
+    const bool bv = g.win[2] % 4 == 0;
+    if (g.head_dim == 32) return bv ? bf16_variant_b<32, true>(KT) : bf16_variant_b<32, false>(KT);
+    return bv ? bf16_variant_b<64, true>(KT) : bf16_variant_b<64, false>(KT);
+}
+
+hipError_t bf16_check_fits(const Geometry& g, int* blocks_per_cu) {
+    const Bf16Variant var = bf16_variant_for(g);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)var.f, var.waves * 64,
+                                                        bf16_lds(g).total);
+}
+
 hipError_t launch_attention_bf16(const Geometry& g, bool staged, const uint16_t* q,
                                  const uint16_t* k, const uint16_t* v, const float* table,
                                  uint16_t* out, hipStream_t s) {
-    size_t lds = bf16_lds(g).total;
-    dim3 grid((unsigned)(g.windows * g.heads));
-    if (g.head_dim == 32)
-        hipLaunchKernelGGL(attn_bf16_kernel<32>, grid, dim3(kBf16Waves * 64), lds, s, g,
-                           (int)staged, q, k, v, table, out);
-    else
-        hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(kBf16Waves * 64), lds, s, g,
-                           (int)staged, q, k, v, table, out);
+    const Bf16Variant var = bf16_variant_for(g);
+    hipLaunchKernelGGL(var.f, dim3((unsigned)(g.windows * g.heads)), dim3(var.waves * 64), bf16_lds(g).total,
+                       s, g, (int)staged, q, k, v, table, out);
     return hipGetLastError();
 }
 
-hipError_t prepare_kernels() {
-    const int max_lds = 160 * 1024;
-    hipError_t e;
-    if ((e = hipFuncSetAttribute((const void*)attn_f32_kernel<32>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, max_lds)) != hipSuccess)
-        return e;
-    if ((e = hipFuncSetAttribute((const void*)attn_f32_kernel<64>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, max_lds)) != hipSuccess)
-        return e;
-    if ((e = hipFuncSetAttribute((const void*)attn_bf16_kernel<32>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, max_lds)) != hipSuccess)
-        return e;
-    return hipFuncSetAttribute((const void*)attn_bf16_kernel<64>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+hipError_t prepare_kernels(int max_lds) {
+    const void* f32k[] = {(const void*)attn_f32_kernel<32>, (const void*)attn_f32_kernel<64>};
+    for (const void* f : f32k) {
+        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+        if (e != hipSuccess) return e;
+    }
+    for (int KT : {4, 7, 9, 18, 1, 32}) {
+        const bf16_kernel_t fs[] = {bf16_variant_b<32, true>(KT).f, bf16_variant_b<32, false>(KT).f,
+                                    bf16_variant_b<64, true>(KT).f, bf16_variant_b<64, false>(KT).f};
+        for (bf16_kernel_t f : fs) {
+            hipError_t e = hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
 }
 
 } // namespace swa

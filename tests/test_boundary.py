@@ -104,6 +104,8 @@ def test_bad_dtype_and_variant(lib):
     cfg = binding.make_config(BASE)
     cfg.scale = float("nan")
     assert lib.swa_create(ctypes.byref(cfg), ctypes.byref(h)) == binding.SWA_ERR_INVALID_ARGUMENT
+    cfg.scale = -0.125
+    assert lib.swa_create(ctypes.byref(cfg), ctypes.byref(h)) == binding.SWA_ERR_INVALID_ARGUMENT
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
