@@ -319,10 +319,14 @@ hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, 
 constexpr int kKeyTilesPerBlock = 9;
 constexpr int kLdsBytes = 160 * 1024; // gfx950 LDS per compute unit
 #ifndef SWA_MFMA_K32
-#define SWA_MFMA_K32 0
+#define SWA_MFMA_K32 1
 #endif
 // 1: 32-deep v_mfma_f32_16x16x32_bf16; 0: pairs of 16-deep v_mfma_f32_16x16x16_bf16
-// fed from the same 16-byte fragments (low and high 8 bytes as two k-steps)
+// fed from the same 16-byte fragments (low and high 8 bytes as two k-steps).
+// Both take 16 cycles on gfx950, so the 32-deep form has twice the throughput.
+// Every accumulator chain uses a single opcode: back-to-back dependent MFMAs of
+// different opcodes on one accumulator gave wrong sums on gfx950 with this
+// compiler's schedules, same-opcode chains do not.
 constexpr bool kMfmaK32 = SWA_MFMA_K32 != 0;
 
 __device__ inline i16x4 half_lo(bf16x8 x) {
@@ -529,7 +533,6 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
     const float cl2 = g.scale * kLog2e;
     const unsigned one2 = 0x3F803F80u; // two bf16 ones
     const bf16x8 ones8 = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
-    const i16x4 ones4 = __builtin_bit_cast(i16x4, u32x2{one2, one2});
     const unsigned char* bias_bytes = (const unsigned char*)bias;
 #pragma unroll
     for (int t = 0; t < QT_MAX; t++) {
@@ -645,14 +648,18 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
                     }
                     osum = mfma32(ones8, bop, osum);
                 } else if (KT_FIXED > 0 || t0 < KT) {
-                    const i16x4 bop = __builtin_bit_cast(i16x4, u32x2{pk[kt][0], pk[kt][1]});
+                    // a lone last tile: the same 32-deep product with the second key
+                    // tile's slots zero (P = 0, V^T = 0), so every accumulation chain
+                    // uses one MFMA opcode
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{pk[kt][0], pk[kt][1], 0u, 0u});
 #pragma unroll
                     for (int dt = 0; dt < DT; dt++) {
                         const uint16_t* vrow = Vt + (dt * 16 + col) * L.VSTR + t0 * 16 + grp * 4;
-                        const i16x4 a = __builtin_bit_cast(i16x4, *(const u32x2*)vrow);
-                        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bop, o[dt], 0, 0, 0);
+                        const u32x2 lo = *(const u32x2*)vrow;
+                        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], 0u, 0u});
+                        o[dt] = mfma32(a, bop, o[dt]);
                     }
-                    osum = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, bop, osum, 0, 0, 0);
+                    osum = mfma32(ones8, bop, osum);
                 }
             }
         }
