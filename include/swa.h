@@ -76,6 +76,12 @@ typedef enum swa_variant {
     SWA_VARIANT_STAGED = 1 /* gather -> window attention -> scatter, through a window-major workspace */
 } swa_variant;
 
+typedef enum swa_schedule {
+    SWA_SCHEDULE_AUTO = 0,   /* STREAM when it fits in LDS, else BLOCK */
+    SWA_SCHEDULE_STREAM = 1, /* bf16: persistent blocks streaming K/V into a two-stage LDS ring */
+    SWA_SCHEDULE_BLOCK = 2   /* bf16: one workgroup per (window, head) */
+} swa_schedule;
+
 typedef struct swa_config {
     int batch;     /* B >= 1 */
     int heads;     /* N_h >= 1 (TERRA, Table V) */
@@ -88,6 +94,7 @@ typedef struct swa_config {
     swa_dtype dtype;
     float scale;   /* logit scale, > 0; 0 selects 1/sqrt(head_dim) */
     swa_variant variant;
+    swa_schedule schedule; /* bf16 kernel schedule; ignored for SWA_F32 */
 } swa_config;
 
 typedef struct swa_handle swa_handle;
@@ -107,8 +114,9 @@ typedef struct swa_info {
  * Validates cfg, checks that the current HIP device is a gfx950, and creates
  * a handle.  The staged variant allocates its workspace (four window-major
  * tensors) here.  On failure *out is set to NULL.
- * Errors: INVALID_ARGUMENT (NULL pointers, malformed tiling),
- * UNSUPPORTED (head_dim or window size outside the kernels' range),
+ * Errors: INVALID_ARGUMENT (NULL pointers, malformed tiling, unknown enum),
+ * UNSUPPORTED (head_dim or window size outside the kernels' range, or
+ * SWA_SCHEDULE_STREAM for a window too large for it),
  * HIP (no gfx950 device), OUT_OF_MEMORY (workspace).
  */
 swa_status swa_create(const swa_config* cfg, swa_handle** out);

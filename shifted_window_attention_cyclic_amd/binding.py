@@ -15,6 +15,8 @@ from .build import LIBRARY
 SWA_OK, SWA_ERR_INVALID_ARGUMENT, SWA_ERR_UNSUPPORTED, SWA_ERR_OUT_OF_MEMORY, SWA_ERR_HIP = range(5)
 SWA_F32, SWA_BF16 = 0, 1
 SWA_VARIANT_FUSED, SWA_VARIANT_STAGED = 0, 1
+SWA_SCHEDULE_AUTO, SWA_SCHEDULE_STREAM, SWA_SCHEDULE_BLOCK = 0, 1, 2
+SCHEDULES = {"auto": SWA_SCHEDULE_AUTO, "stream": SWA_SCHEDULE_STREAM, "block": SWA_SCHEDULE_BLOCK}
 
 EXPORTS = ("swa_create", "swa_forward", "swa_destroy", "swa_get_info", "swa_status_string",
            "swa_last_error", "swa_gather", "swa_scatter", "swa_debug_visibility")
@@ -26,6 +28,7 @@ class swa_config(ctypes.Structure):
         ("grid", ctypes.c_int * 3), ("padded", ctypes.c_int * 3), ("window", ctypes.c_int * 3),
         ("shift", ctypes.c_int * 3), ("cyclic", ctypes.c_int * 3),
         ("dtype", ctypes.c_int), ("scale", ctypes.c_float), ("variant", ctypes.c_int),
+        ("schedule", ctypes.c_int),
     ]
 
 
@@ -84,7 +87,7 @@ def _check(status):
                                f"{lib.swa_last_error().decode()}")
 
 
-def make_config(problem, variant: str = "fused") -> swa_config:
+def make_config(problem, variant: str = "fused", schedule: str = "auto") -> swa_config:
     """swa_config from a problem description (attributes batch, heads, head_dim,
     extent, padded, window, shift, cyclic, dtype ("f32"/"bf16"), scale)."""
     c = swa_config()
@@ -98,6 +101,7 @@ def make_config(problem, variant: str = "fused") -> swa_config:
     c.dtype = SWA_F32 if problem.dtype == "f32" else SWA_BF16
     c.scale = float(problem.scale or 0.0)
     c.variant = {"fused": SWA_VARIANT_FUSED, "staged": SWA_VARIANT_STAGED}[variant]
+    c.schedule = SCHEDULES[schedule]
     return c
 
 
@@ -164,10 +168,10 @@ def swa_debug_visibility(handle, window_index: int, dev_out, stream=None) -> Non
 class WindowAttention:
     """Owns one handle for a problem; checks tensor shapes before each call."""
 
-    def __init__(self, problem, variant: str = "fused"):
+    def __init__(self, problem, variant: str = "fused", schedule: str = "auto"):
         self.problem = problem
         self.dtype = torch.float32 if problem.dtype == "f32" else torch.bfloat16
-        self.handle = swa_create(make_config(problem, variant))
+        self.handle = swa_create(make_config(problem, variant, schedule))
         self.info = swa_get_info(self.handle)
 
     @property

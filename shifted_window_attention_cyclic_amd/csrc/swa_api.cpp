@@ -19,6 +19,8 @@ struct swa_handle {
     swa::Geometry g;
     int elem_bytes;
     int device;
+    bool stream;        // bf16: streaming schedule
+    int blocks;         // bf16: workgroups per attention launch
     size_t wm_bytes;    // bytes of one window-major tensor
     void* workspace;    // staged variant: q, k, v, o window-major tensors
 };
@@ -42,6 +44,8 @@ swa_status validate(const swa_config* c, swa::Geometry* g, int* elem_bytes) {
     if (c->dtype != SWA_F32 && c->dtype != SWA_BF16) return fail(SWA_ERR_INVALID_ARGUMENT, "unknown dtype");
     if (c->variant != SWA_VARIANT_FUSED && c->variant != SWA_VARIANT_STAGED)
         return fail(SWA_ERR_INVALID_ARGUMENT, "unknown variant");
+    if (c->schedule != SWA_SCHEDULE_AUTO && c->schedule != SWA_SCHEDULE_STREAM && c->schedule != SWA_SCHEDULE_BLOCK)
+        return fail(SWA_ERR_INVALID_ARGUMENT, "unknown schedule");
     if (c->head_dim < 1) return fail(SWA_ERR_INVALID_ARGUMENT, "head_dim must be >= 1");
     if (!(isfinite(c->scale)) || c->scale < 0.f)
         return fail(SWA_ERR_INVALID_ARGUMENT, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
@@ -191,10 +195,15 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
         return fail(SWA_ERR_UNSUPPORTED, buf);
     }
     if ((e = swa::prepare_kernels(max_lds)) != hipSuccess) return fail_hip(e, "hipFuncSetAttribute");
+    bool stream = false;
+    int blocks = 0;
     if (cfg->dtype == SWA_BF16) {
-        int per_cu = 0;
-        if ((e = swa::bf16_check_fits(g, &per_cu)) != hipSuccess) return fail_hip(e, "occupancy query");
-        if (per_cu < 1) return fail(SWA_ERR_UNSUPPORTED, "attention kernel does not fit on a compute unit");
+        const bool fits = swa::bf16_stream_fits(g);
+        if (cfg->schedule == SWA_SCHEDULE_STREAM && !fits)
+            return fail(SWA_ERR_UNSUPPORTED, "window too large for the streaming schedule");
+        stream = cfg->schedule == SWA_SCHEDULE_STREAM || (cfg->schedule == SWA_SCHEDULE_AUTO && fits);
+        if ((e = swa::bf16_plan(g, stream, &blocks)) != hipSuccess) return fail_hip(e, "occupancy query");
+        if (blocks < 1) return fail(SWA_ERR_UNSUPPORTED, "attention kernel does not fit on a compute unit");
     }
 
     swa_handle* h = new (std::nothrow) swa_handle();
@@ -203,6 +212,8 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
     h->g = g;
     h->elem_bytes = eb;
     h->device = dev;
+    h->stream = stream;
+    h->blocks = blocks;
     h->wm_bytes = (size_t)g.windows * g.N * g.row * eb;
     h->workspace = nullptr;
     if (cfg->variant == SWA_VARIANT_STAGED) {
@@ -260,7 +271,7 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
     const bool bf16 = h->cfg.dtype == SWA_BF16;
     hipError_t e;
     if (h->cfg.variant == SWA_VARIANT_FUSED) {
-        e = bf16 ? swa::launch_attention_bf16(g, false, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+        e = bf16 ? swa::launch_attention_bf16(g, h->stream, h->blocks, false, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                               bias_table, (uint16_t*)out, s)
                  : swa::launch_attention_f32(g, false, (const float*)q, (const float*)k, (const float*)v,
                                              bias_table, (float*)out, s);
@@ -274,7 +285,7 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
     if ((e = swa::launch_gather(g, h->elem_bytes, q, wq, s)) != hipSuccess) return fail_hip(e, "gather launch");
     if ((e = swa::launch_gather(g, h->elem_bytes, k, wk, s)) != hipSuccess) return fail_hip(e, "gather launch");
     if ((e = swa::launch_gather(g, h->elem_bytes, v, wv, s)) != hipSuccess) return fail_hip(e, "gather launch");
-    e = bf16 ? swa::launch_attention_bf16(g, true, (const uint16_t*)wq, (const uint16_t*)wk, (const uint16_t*)wv,
+    e = bf16 ? swa::launch_attention_bf16(g, h->stream, h->blocks, true, (const uint16_t*)wq, (const uint16_t*)wk, (const uint16_t*)wv,
                                           bias_table, (uint16_t*)wo, s)
              : swa::launch_attention_f32(g, true, (const float*)wq, (const float*)wk, (const float*)wv, bias_table,
                                          (float*)wo, s);

@@ -143,14 +143,15 @@ hipError_t launch_scatter(const Geometry& g, int elem_bytes, const void* src, vo
 hipError_t launch_visibility(const Geometry& g, int64_t window, uint8_t* out, hipStream_t s);
 hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, const float* k,
                                 const float* v, const float* table, float* out, hipStream_t s);
-hipError_t launch_attention_bf16(const Geometry& g, bool staged, const uint16_t* q,
+hipError_t launch_attention_bf16(const Geometry& g, bool stream, int blocks, bool staged, const uint16_t* q,
                                  const uint16_t* k, const uint16_t* v, const float* table,
                                  uint16_t* out, hipStream_t s);
 // LDS bytes the attention kernels need for g.
 size_t attention_lds_bytes(const Geometry& g, bool bf16);
-// Workgroups of the bf16 attention kernel one compute unit can hold (0: the
-// kernel does not fit).
-hipError_t bf16_check_fits(const Geometry& g, int* blocks_per_cu);
+// Whether the streaming bf16 schedule (persistent blocks, two LDS stages) fits.
+bool bf16_stream_fits(const Geometry& g);
+// Workgroups one bf16 attention launch uses (0: the kernel does not fit).
+hipError_t bf16_plan(const Geometry& g, bool stream, int* blocks);
 // Lets every attention kernel take up to max_lds bytes of dynamic LDS.
 hipError_t prepare_kernels(int max_lds);
 

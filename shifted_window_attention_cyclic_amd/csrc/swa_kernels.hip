@@ -284,8 +284,7 @@ hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, 
 //      window (4 keys x 16 bytes per item), this head's bias table slice and
 //      each wave's Q tiles; then K to LDS ([key][d], 16-byte chunks XOR-
 //      swizzled by row so 8 consecutive rows hit distinct banks), V to LDS
-//      transposed ([d][key], 4 keys per 8-byte write) and the bias times
-//      log2(e);
+//      transposed ([d][key], 4 keys per 8-byte write) and the bias;
 //   C  per 16-query tile of a wave:
 //        S^T = K Q^T     v_mfma_f32_16x16x32_bf16, A = K from LDS, B = Q tile
 //                        in registers, C = 0; lane l holds query (l % 16)
@@ -293,7 +292,7 @@ hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, 
 //                        all tiles of a key block are issued before any
 //                        result is read.  The accumulator input is never a
 //                        register a load may still overwrite during the MFMA;
-//        logits          (scale * S + bias) * log2(e) by one FMA; the bias of
+//        logits          scale * S + bias by one FMA; the bias of
 //                        query n and key m sits at qb(n) - kb(m), and when the
 //                        window's longitude extent is a multiple of 4 the 4
 //                        keys of a lane are neighbours in one window row, so
@@ -302,7 +301,7 @@ hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, 
 //        mask            -inf where the key is pad, past N or on the other
 //                        side of a masked wrap; only on windows / tiles that
 //                        can hold such keys;
-//        softmax         online over key blocks, in base 2: p = exp2(l - m),
+//        softmax         online over key blocks: p = exp2(l*log2(e) - m*log2(e)),
 //                        running max per query (reduced across the 4 lanes
 //                        that share it);
 //        O^T = V^T P^T   same MFMA, A = V^T from LDS, B = bf16 P straight
@@ -504,7 +503,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 #pragma unroll
         for (int u = 0; u < BIAS_UNROLL; u++) {
             const int i = base + u * THREADS + tid;
-            if (i < g.table_size) bias[i] = bv[u] * kLog2e;
+            if (i < g.table_size) bias[i] = bv[u];
         }
     }
 #pragma unroll
@@ -530,7 +529,6 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
     __syncthreads();
 
     // ---- C: query tiles
-    const float cl2 = g.scale * kLog2e;
     const unsigned one2 = 0x3F803F80u; // two bf16 ones
     const bf16x8 ones8 = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
     const unsigned char* bias_bytes = (const unsigned char*)bias;
@@ -593,9 +591,9 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
                         bb[2] = *(const float*)(qbias - kq.z);
                         bb[3] = *(const float*)(qbias - kq.w);
                     }
-                    // logits in base-2 units: (scale * q.k + bias) * log2(e)
-                    f32x4 lg = {fmaf(s[kt][0], cl2, bb[0]), fmaf(s[kt][1], cl2, bb[1]),
-                                fmaf(s[kt][2], cl2, bb[2]), fmaf(s[kt][3], cl2, bb[3])};
+                    // logits, natural units: scale * q.k + bias
+                    f32x4 lg = {fmaf(s[kt][0], g.scale, bb[0]), fmaf(s[kt][1], g.scale, bb[1]),
+                                fmaf(s[kt][2], g.scale, bb[2]), fmaf(s[kt][3], g.scale, bb[3])};
                     if (masked_window || key0 + 16 > N) {
                         const int4 kr4 = *(const int4*)(rg + key0 + grp * 4);
                         lg[0] = kr4.x == qreg ? lg[0] : -INFINITY;
@@ -612,9 +610,9 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
             bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
             bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
             const float mnew = fmaxf(mrun, bmax);
-            const float mc = mnew == -INFINITY ? 0.f : mnew;
+            const float mc = (mnew == -INFINITY ? 0.f : mnew) * kLog2e;
             if (kb0 > 0) { // rescale what earlier key blocks accumulated
-                const float alpha = __builtin_amdgcn_exp2f(mrun - mc);
+                const float alpha = __builtin_amdgcn_exp2f(mrun * kLog2e - mc);
                 osum *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < DT; dt++) o[dt] *= alpha;
@@ -626,7 +624,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
             for (int kt = 0; kt < KB; kt++) {
                 float p[4];
 #pragma unroll
-                for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(s[kt][i] - mc);
+                for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(fmaf(s[kt][i], kLog2e, -mc));
                 pk[kt][0] = pack_bf16x2(p[0], p[1]);
                 pk[kt][1] = pack_bf16x2(p[2], p[3]);
             }
@@ -679,6 +677,505 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
     }
 }
 
+// --------------------------------------------------------------------------
+// bf16 attention, streaming schedule: persistent blocks with an LDS ring.
+//
+// The same per-tile arithmetic as above, instruction for instruction (both
+// schedules give bit-identical outputs), but a block stays resident and walks
+// a sequence of (window, head) units.  Each XCD (block % 8) owns a contiguous
+// range of units and its blocks interleave over it, so an XCD works on the
+// heads of a few neighbouring windows at a time.
+//
+// A block has one wave per 16-query tile plus kLoaders loader waves.  The
+// loaders build each unit's token table and copy its K and V from global
+// memory straight into LDS with global_load_lds (16 bytes per lane, no
+// registers), two units ahead, into a ring of kStages stages:
+//   K [key][d] and V [key][d], 16-byte chunks XOR-swizzled by row (the source
+//   chunk each lane fetches is chosen so the copy lands swizzled).
+// Loader wave j owns a contiguous range of key rows: it writes their table
+// words and issues their copies, so it never reads what the other loader
+// wrote.  It issues nothing but these copies, so "wait until only the next
+// unit's copies are outstanding" is an exact vmcnt count (vector memory
+// operations of a wave complete in order).
+//
+// The compute waves issue no LDS copies.  They load their Q tiles one unit
+// ahead into registers and store O through buffer instructions whose range
+// check drops the lanes of pad queries (loads of such lanes return zeros), so
+// every wave issues the same number of loads and stores per unit and the
+// compiler's own counted waits for the Q registers never wait for stores.
+// The two roles run separate loops with the same number of block barriers;
+// the barriers fence LDS only (a full fence would wait for every outstanding
+// global load and store).  Iteration i:
+//   loaders: wait for unit i's copies, barrier, table and copies of unit i+2;
+//   compute: barrier, Q loads of unit i+1, unit i (Q loaded one iteration ago).
+// The PV product reads V^T fragments with ds_read_b64_tr_b16, which hands
+// lane i of each 16-lane group element i of the 4 rows its group addresses.
+// --------------------------------------------------------------------------
+constexpr int kStages = 3;
+constexpr int kTableSlots = 3;
+constexpr int kLoaders = 2;
+
+struct StreamLds {
+    int NP, TSP;   // padded keys; bias table entries per head slice (multiple of 64)
+    bool bias_resident;
+    size_t stage_bytes, bias, kb4, slot0, slot_bytes, total;
+    // stage s: K at s * stage_bytes, V at s * stage_bytes + NP * D * 2
+};
+
+__host__ __device__ inline StreamLds stream_lds_with(const Geometry& g, bool bias_resident) {
+    StreamLds L;
+    L.NP = (g.N + 15) / 16 * 16;
+    L.TSP = (g.table_size + 63) / 64 * 64;
+    L.bias_resident = bias_resident;
+    L.stage_bytes = (size_t)2 * L.NP * g.head_dim * 2;
+    L.bias = kStages * L.stage_bytes;
+    L.kb4 = L.bias + (size_t)(bias_resident ? g.heads : kStages) * L.TSP * 4;
+    L.slot0 = L.kb4 + (size_t)L.NP * 4;
+    L.slot_bytes = (size_t)L.NP * 4; // one packed word per token: (row + 1) | mask field << 28
+    L.total = L.slot0 + kTableSlots * L.slot_bytes;
+    return L;
+}
+
+// Every head's bias stays in LDS when that costs no resident block per CU.
+__host__ __device__ inline StreamLds stream_lds(const Geometry& g) {
+    const StreamLds S = stream_lds_with(g, false);
+    const int tsp = (g.table_size + 63) / 64 * 64;
+    if ((size_t)g.heads * tsp * 4 <= (size_t)24 * 1024) {
+        const StreamLds R = stream_lds_with(g, true);
+        if (R.total <= (size_t)kLdsBytes && kLdsBytes / R.total >= kLdsBytes / S.total) return R;
+    }
+    return S;
+}
+
+constexpr int kRowMask = (1 << 28) - 1; // packed table word: source row + 1 in bits 0..27
+constexpr uint32_t kOutOfRange = 0x80000000u; // buffer offset past every tensor the schedule takes
+constexpr int kBufferWord3 = 0x00020000;     // raw buffer resource, 32-bit data format
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left unconstrained)
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
+// Waits until at most min(n, 63) vector-memory operations of this wave are
+// outstanding; n must be wave-uniform (a scalar branch picks the immediate).
+__device__ inline void wait_vmcnt_le(int n) {
+    switch (n < 63 ? n : 63) {
+#define SWA_VM(c) \
+    case c: __builtin_amdgcn_s_waitcnt(vmcnt_imm(c)); break;
+#define SWA_VM8(c) SWA_VM(c) SWA_VM(c + 1) SWA_VM(c + 2) SWA_VM(c + 3) SWA_VM(c + 4) SWA_VM(c + 5) SWA_VM(c + 6) SWA_VM(c + 7)
+        SWA_VM8(0) SWA_VM8(8) SWA_VM8(16) SWA_VM8(24) SWA_VM8(32) SWA_VM8(40) SWA_VM8(48) SWA_VM8(56)
+#undef SWA_VM8
+#undef SWA_VM
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    }
+}
+
+// Block barrier that orders LDS accesses only: waits for this wave's LDS
+// operations, not for its global loads and stores.
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// unit -> (window, head, batch item, window coordinates)
+struct Unit {
+    uint32_t wi;
+    int h, b, wc[3];
+};
+
+__device__ inline Unit decode_unit(const Geometry& g, uint32_t u) {
+    Unit U;
+    U.wi = fdiv(g.fd_heads, u);
+    U.h = (int)(u - U.wi * (uint32_t)g.heads);
+    U.b = (int)fdiv(g.fd_nW, U.wi);
+    const uint32_t r = U.wi - (uint32_t)U.b * (uint32_t)g.nW;
+    const uint32_t r2 = fdiv(g.fd_nwin2, r);
+    U.wc[2] = (int)(r - r2 * (uint32_t)g.nwin[2]);
+    U.wc[0] = (int)fdiv(g.fd_nwin1, r2);
+    U.wc[1] = (int)(r2 - (uint32_t)U.wc[0] * (uint32_t)g.nwin[1]);
+    return U;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Copies one loader wave issues per unit: its share of the K and V copies
+// (1 KB each), plus the streamed bias slice for loader 0.
+__host__ __device__ inline int loader_copies(const Geometry& g, const StreamLds& L, int j) {
+    const int ncopy = L.NP * (g.head_dim / 8) / 64;
+    const int c0 = ncopy * j / kLoaders, c1 = ncopy * (j + 1) / kLoaders;
+    return 2 * (c1 - c0) + (j == 0 && !L.bias_resident ? L.TSP / 64 : 0);
+}
+
+// Loader wave j's work for unit uu: the table words of its key rows into slot
+// s, then its K and V copies (and, for loader 0, the streamed bias) into
+// stage st.  Returns after issuing the copies.
+template <int D>
+__device__ inline void load_unit(const Geometry& g, const StreamLds& L, unsigned char* smem, int j, int lane,
+                                 uint32_t uu, int s, int st, int staged, const uint16_t* __restrict__ k,
+                                 const uint16_t* __restrict__ v, const float* __restrict__ table) {
+    constexpr int CH = D / 8;
+    constexpr int RPC = 64 / CH; // key rows per 1 KB copy
+    const int N = g.N, NP = L.NP;
+    const int ncopy = NP * CH / 64;
+    const int c0 = ncopy * j / kLoaders, c1 = ncopy * (j + 1) / kLoaders;
+    const Unit U = decode_unit(g, uu);
+    int* tw = (int*)(smem + L.slot0 + s * L.slot_bytes);
+    // table word per token: (source row + 1, 0 for pad) | mask field << 28, the mask
+    // field holding the wrapped flags with pad in bit 3 (15 past N)
+    for (int n = c0 * RPC + lane; n < c1 * RPC; n += 64) {
+        if (n < N) {
+            int l[3];
+            local_coords(g, n, l[0], l[1], l[2]);
+            int region = 0, tok = U.b;
+            bool is_pad = false;
+#pragma unroll
+            for (int a = 0; a < 3; a++) {
+                const int cr = U.wc[a] * g.win[a] + l[a];
+                int c = cr + g.shift[a];
+                if (c >= g.pad[a]) c -= g.pad[a];
+                is_pad |= c >= g.ext[a];
+                if (!g.cyc[a] && cr >= g.pad[a] - g.shift[a]) region |= 1 << a;
+                tok = tok * g.ext[a] + c;
+            }
+            const int row = is_pad ? -1 : (staged ? (int)(U.wi * (uint32_t)N + n) : tok);
+            tw[n] = (row + 1) | ((region | (is_pad ? 8 : 0)) << 28);
+        } else {
+            tw[n] = 15 << 28;
+        }
+    }
+    // the copies below read table words other lanes of this wave just wrote
+    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    for (int c = c0; c < c1; c++) {
+        const int byte = c * 1024 + lane * 16;
+        const int m = byte / (D * 2);
+        const int ch = ((byte % (D * 2)) / 16) ^ ((m / (128 / (D * 2))) % CH); // logical chunk
+        const int r1 = tw[m] & kRowMask; // row + 1; pad rows copy row 0 (finite, weight exactly 0)
+        const uint32_t off = (uint32_t)(r1 == 0 ? 0 : r1 - 1) * (uint32_t)g.row + U.h * D + ch * 8;
+        unsigned char* dst = smem + st * L.stage_bytes + c * 1024;
+        __builtin_amdgcn_global_load_lds((const void*)(k + off), (lds_void*)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(v + off), (lds_void*)(dst + (size_t)NP * D * 2), 16, 0,
+                                         0);
+    }
+    if (j == 0 && !L.bias_resident) {
+        float* bdst = (float*)(smem + L.bias) + st * L.TSP;
+        for (int jj = 0; jj * 64 < L.TSP; jj++) {
+            const int i = jj * 64 + lane;
+            const float* src = table + (i < g.table_size ? i * g.heads + U.h : 0);
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(bdst + jj * 64), 4, 0, 0);
+        }
+    }
+}
+
+// Loads the Q tiles of unit uu (token table in slot s) into qo: one 16-byte
+// buffer load per tile and 32-deep step, issued by every lane (pad queries
+// read out of range and get zeros).
+template <int D, int NWAVES, int QT_MAX, int KT_FIXED>
+__device__ inline void stream_load_q(const Geometry& g, const StreamLds& L, const unsigned char* smem,
+                                     __amdgpu_buffer_rsrc_t qrs, int wave, int col, int grp, uint32_t uu, int s,
+                                     bf16x8 (&qo)[QT_MAX][D / 32]) {
+    const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
+    const int KT = KT_FIXED > 0 ? KT_FIXED : L.NP / 16;
+    const int hh = (int)(uu - fdiv(g.fd_heads, uu) * (uint32_t)g.heads);
+#pragma unroll
+    for (int t = 0; t < QT_MAX; t++) {
+        const int qt = wave + t * NWAVES;
+        const int r = qt < KT ? (tw[qt * 16 + col] & kRowMask) - 1 : -1;
+        const uint32_t base = r >= 0 ? ((uint32_t)r * (uint32_t)g.row + hh * D + grp * 8) * 2 : kOutOfRange;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ks++)
+            qo[t][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, base + ks * 64, 0, 0));
+    }
+}
+
+// One unit's attention for the query tiles of this wave (operands in stage
+// st and table slot s of LDS, Q in qc); O leaves through ors.
+template <int D, int NWAVES, int QT_MAX, int KT_FIXED, bool BIAS_VEC>
+__device__ inline void stream_compute(const Geometry& g, const StreamLds& L, const unsigned char* smem,
+                                      __amdgpu_buffer_rsrc_t ors, int wave, int col, int grp, int staged,
+                                      uint32_t uu, int s, int st, const bf16x8 (&qc)[QT_MAX][D / 32]) {
+    constexpr int KSTEPS = D / 32;
+    constexpr int DT = D / 16;
+    constexpr int CH = D / 8;
+    constexpr int KB = (KT_FIXED > 0 && KT_FIXED <= kKeyTilesPerBlock) ? KT_FIXED : kKeyTilesPerBlock;
+    constexpr int KB_UNROLL = KT_FIXED > 0 ? KT_FIXED / KB : 1;
+    const int N = g.N;
+    const int KT = KT_FIXED > 0 ? KT_FIXED : L.NP / 16;
+    const unsigned one2 = 0x3F803F80u; // two bf16 ones
+    const bf16x8 ones8 = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
+    const Unit U = decode_unit(g, uu);
+    const bool masked_window = window_maybe_masked(g, U.wc);
+    const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
+    const int* kb4 = (const int*)(smem + L.kb4);
+    const uint16_t* Ks = (const uint16_t*)(smem + st * L.stage_bytes);
+    const unsigned char* Vb = smem + st * L.stage_bytes + (size_t)L.NP * D * 2;
+    const unsigned char* bias_bytes =
+        smem + L.bias + (size_t)(L.bias_resident ? U.h : st) * L.TSP * 4;
+#pragma unroll
+    for (int t = 0; t < QT_MAX; t++) {
+        const int qt = wave + t * NWAVES;
+        if (KT_FIXED == 0 && qt >= KT) break;
+        const int n = qt * 16 + col;
+        const int qword = tw[n];
+        const int qreg = (unsigned)qword >> 28;
+        const int r = (qword & kRowMask) - 1;
+        int qb4;
+        if (n < N) {
+            int lt, ly, lx;
+            local_coords(g, n, lt, ly, lx);
+            qb4 = (((lt * g.tdy + ly) * g.tdx + lx) + g.c0) * 4;
+        } else {
+            qb4 = (g.table_size - 1) * 4;
+        }
+        const unsigned char* qbias = bias_bytes + qb4;
+        f32x4 o[DT], osum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float mrun = -INFINITY;
+
+#pragma unroll KB_UNROLL
+        for (int kb0 = 0; kb0 < (KT_FIXED > 0 ? KT_FIXED : KT); kb0 += KB) {
+            f32x4 sc[KB];
+#pragma unroll
+            for (int kt = 0; kt < KB; kt++) {
+                const int key0 = (kb0 + kt) * 16;
+                if (KT_FIXED > 0 || kb0 + kt < KT) {
+                    const int krow = key0 + col;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KSTEPS; ks++) {
+                        const bf16x8 a = __builtin_bit_cast(
+                            bf16x8, *(const u32x4*)(Ks + krow * D + k_slot<D>(krow, ks * 4 + grp) * 8));
+                        acc = mfma32(a, qc[t][ks], acc);
+                    }
+                    sc[kt] = acc;
+                }
+            }
+            float bmax = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < KB; kt++) {
+                const int key0 = (kb0 + kt) * 16;
+                if (KT_FIXED > 0 || kb0 + kt < KT) {
+                    float bb[4];
+                    if (BIAS_VEC) {
+                        const float* bp = (const float*)(qbias - kb4[key0 + grp * 4]) - 3;
+                        bb[3] = bp[0];
+                        bb[2] = bp[1];
+                        bb[1] = bp[2];
+                        bb[0] = bp[3];
+                    } else {
+                        const int4 kq = *(const int4*)(kb4 + key0 + grp * 4);
+                        bb[0] = *(const float*)(qbias - kq.x);
+                        bb[1] = *(const float*)(qbias - kq.y);
+                        bb[2] = *(const float*)(qbias - kq.z);
+                        bb[3] = *(const float*)(qbias - kq.w);
+                    }
+                    // logits, natural units: scale * q.k + bias
+                    f32x4 lg = {fmaf(sc[kt][0], g.scale, bb[0]), fmaf(sc[kt][1], g.scale, bb[1]),
+                                fmaf(sc[kt][2], g.scale, bb[2]), fmaf(sc[kt][3], g.scale, bb[3])};
+                    if (masked_window || key0 + 16 > N) {
+                        const int4 kr4 = *(const int4*)(tw + key0 + grp * 4);
+                        lg[0] = ((unsigned)kr4.x >> 28) == (unsigned)qreg ? lg[0] : -INFINITY;
+                        lg[1] = ((unsigned)kr4.y >> 28) == (unsigned)qreg ? lg[1] : -INFINITY;
+                        lg[2] = ((unsigned)kr4.z >> 28) == (unsigned)qreg ? lg[2] : -INFINITY;
+                        lg[3] = ((unsigned)kr4.w >> 28) == (unsigned)qreg ? lg[3] : -INFINITY;
+                    }
+                    sc[kt] = lg;
+                    bmax = fmaxf(bmax, fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
+                } else {
+                    sc[kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                }
+            }
+            bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+            bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+            const float mnew = fmaxf(mrun, bmax);
+            const float mc = (mnew == -INFINITY ? 0.f : mnew) * kLog2e;
+            if (kb0 > 0) {
+                const float alpha = __builtin_amdgcn_exp2f(mrun * kLog2e - mc);
+                osum *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; dt++) o[dt] *= alpha;
+            }
+            mrun = mnew;
+
+            unsigned pk[KB][2];
+#pragma unroll
+            for (int kt = 0; kt < KB; kt++) {
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], kLog2e, -mc));
+                pk[kt][0] = pack_bf16x2(p[0], p[1]);
+                pk[kt][1] = pack_bf16x2(p[2], p[3]);
+            }
+
+            // V^T fragment of key tile t: lane (col, grp) gets keys 16t + 4grp + 0..3 at
+            // d = 16 dt + col; lane s of the group points at row 16t + 4grp + s/4, d 16dt + 4(s%4)
+            auto vt_frag = [&](int t0, int dt) __attribute__((always_inline)) {
+                const int row = t0 * 16 + grp * 4 + (col >> 2);
+                const int d = dt * 16 + (col & 3) * 4;
+                const int chunk = (d >> 3) ^ ((row / (128 / (D * 2))) % CH);
+                const unsigned char* p = Vb + row * (D * 2) + chunk * 16 + (d & 7) * 2;
+                const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)p);
+                return __builtin_bit_cast(u32x2, x);
+            };
+#pragma unroll
+            for (int kt = 0; kt < KB; kt += 2) {
+                const int t0 = kb0 + kt;
+                const bool pair = kt + 1 < KB && (KT_FIXED > 0 || t0 + 1 < KT);
+                if (pair) {
+                    const bf16x8 bop =
+                        __builtin_bit_cast(bf16x8, u32x4{pk[kt][0], pk[kt][1], pk[kt + 1][0], pk[kt + 1][1]});
+#pragma unroll
+                    for (int dt = 0; dt < DT; dt++) {
+                        const u32x2 lo = vt_frag(t0, dt);
+                        const u32x2 hi = vt_frag(t0 + 1, dt);
+                        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                        o[dt] = mfma32(a, bop, o[dt]);
+                    }
+                    osum = mfma32(ones8, bop, osum);
+                } else if (KT_FIXED > 0 || t0 < KT) {
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{pk[kt][0], pk[kt][1], 0u, 0u});
+#pragma unroll
+                    for (int dt = 0; dt < DT; dt++) {
+                        const u32x2 lo = vt_frag(t0, dt);
+                        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], 0u, 0u});
+                        o[dt] = mfma32(a, bop, o[dt]);
+                    }
+                    osum = mfma32(ones8, bop, osum);
+                }
+            }
+        }
+
+        // O rows: the real token, or in the staged layout also pad slots (zeros);
+        // other lanes store out of range, which the buffer range check drops
+        int orow = r;
+        if (r < 0 && staged) orow = (int)(U.wi * (uint32_t)N + n);
+        const bool keep = orow >= 0 && n < N;
+        const float inv = r >= 0 ? __builtin_amdgcn_rcpf(osum[0]) : 0.f;
+        const uint32_t obase = keep ? ((uint32_t)orow * (uint32_t)g.row + U.h * D + grp * 4) * 2 : kOutOfRange;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            const u32x2 w = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
+            __builtin_amdgcn_raw_buffer_store_b64(w, ors, obase + dt * 32, 0, 0);
+        }
+    }
+}
+
+// Bytes of each tensor the streaming schedule reads or writes through
+// buffer resources (real-token layout, or window-major when staged).
+__host__ __device__ inline uint64_t stream_tensor_bytes(const Geometry& g, bool staged) {
+    const uint64_t rows = staged ? (uint64_t)g.windows * g.N
+                                 : (uint64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
+    return rows * (uint64_t)g.row * 2;
+}
+
+template <int D, int NWAVES, int QT_MAX, int KT_FIXED, bool BIAS_VEC>
+__global__ __launch_bounds__((NWAVES + kLoaders) * 64) void attn_bf16_stream_kernel(
+    Geometry g, int staged, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ table, uint16_t* __restrict__ out) {
+    constexpr int THREADS = (NWAVES + kLoaders) * 64;
+    constexpr int KSTEPS = D / 32;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const StreamLds L = stream_lds(g);
+    float* bias_lds = (float*)(smem + L.bias);
+    int* kb4 = (int*)(smem + L.kb4);
+    const int N = g.N, NP = L.NP;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+
+    const uint32_t units = (uint32_t)(g.windows * g.heads);
+    const uint32_t per = gridDim.x / kXcds;
+    const uint32_t xcd = blockIdx.x % kXcds;
+    const uint32_t ubeg = (uint32_t)((uint64_t)units * xcd / kXcds);
+    const uint32_t uend = (uint32_t)((uint64_t)units * (xcd + 1) / kXcds);
+    const uint32_t u0 = ubeg + blockIdx.x / kXcds;
+    if (u0 >= uend) return;
+
+    // ---- window-independent tables; every head's bias when resident
+    for (int n = tid; n < NP; n += THREADS) {
+        if (n < N) {
+            int lt, ly, lx;
+            local_coords(g, n, lt, ly, lx);
+            kb4[n] = ((lt * g.tdy + ly) * g.tdx + lx) * 4;
+        } else {
+            kb4[n] = BIAS_VEC ? 12 : 0; // keeps qb - kb (- 3) inside the table
+        }
+    }
+    if (L.bias_resident) {
+        for (int hh = 0; hh < g.heads; hh++)
+            for (int i = tid; i < g.table_size; i += THREADS) bias_lds[hh * L.TSP + i] = table[i * g.heads + hh];
+    }
+
+    if (wave >= NWAVES) {
+        // ---- loader waves
+        const int j = wave - NWAVES;
+        const int copies = loader_copies(g, L, j);
+        load_unit<D>(g, L, smem, j, lane, u0, 0, 0, staged, k, v, table);
+        if (u0 + per < uend) load_unit<D>(g, L, smem, j, lane, u0 + per, 1, 1, staged, k, v, table);
+        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): table words of units 0 and 1
+        lds_barrier();                      // prologue
+        uint32_t u = u0;
+        for (int iter = 0;; iter++) {
+            const uint32_t un = u + per;
+            // unit u's copies have landed once at most the next unit's remain
+            wait_vmcnt_le(un < uend ? copies : 0);
+            lds_barrier();
+            if (un + per < uend)
+                load_unit<D>(g, L, smem, j, lane, un + per, (iter + 2) % kTableSlots, (iter + 2) % kStages, staged,
+                             k, v, table);
+            if (un >= uend) break;
+            u = un;
+        }
+    } else {
+        // ---- compute waves
+        const __amdgpu_buffer_rsrc_t qrs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)q, 0, (int)stream_tensor_bytes(g, staged), kBufferWord3);
+        const __amdgpu_buffer_rsrc_t ors =
+            __builtin_amdgcn_make_buffer_rsrc((void*)out, 0, (int)stream_tensor_bytes(g, staged), kBufferWord3);
+        bf16x8 qa[QT_MAX][KSTEPS], qb[QT_MAX][KSTEPS];
+        lds_barrier(); // prologue: unit 0's table is in slot 0
+        stream_load_q<D, NWAVES, QT_MAX, KT_FIXED>(g, L, smem, qrs, wave, col, grp, u0, 0, qa);
+        // as many stores as a unit's epilogue issues, all out of range (dropped): the
+        // loop is then entered with the same vector-memory history from both sides,
+        // and the compiler's wait for qa leaves the previous unit's stores in flight
+        for (int t = 0; t < QT_MAX; t++) {
+            if (KT_FIXED == 0 && wave + t * NWAVES >= L.NP / 16) break;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; dt++)
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, ors, kOutOfRange + dt * 32, 0, 0);
+        }
+        uint32_t u = u0;
+        for (int iter = 0;; iter += 2) {
+            // two iterations per trip, so that the Q registers swap roles without copies
+            {
+                const uint32_t un = u + per;
+                const bool has_next = un < uend;
+                lds_barrier();
+                stream_load_q<D, NWAVES, QT_MAX, KT_FIXED>(g, L, smem, qrs, wave, col, grp, has_next ? un : u,
+                                                           (iter + (has_next ? 1 : 0)) % kTableSlots, qb);
+                stream_compute<D, NWAVES, QT_MAX, KT_FIXED, BIAS_VEC>(g, L, smem, ors, wave, col, grp, staged, u,
+                                                                      iter % kTableSlots, iter % kStages, qa);
+                if (!has_next) break;
+                u = un;
+            }
+            {
+                const uint32_t un = u + per;
+                const bool has_next = un < uend;
+                lds_barrier();
+                stream_load_q<D, NWAVES, QT_MAX, KT_FIXED>(g, L, smem, qrs, wave, col, grp, has_next ? un : u,
+                                                           (iter + 1 + (has_next ? 1 : 0)) % kTableSlots, qa);
+                stream_compute<D, NWAVES, QT_MAX, KT_FIXED, BIAS_VEC>(g, L, smem, ors, wave, col, grp, staged, u,
+                                                                      (iter + 1) % kTableSlots,
+                                                                      (iter + 1) % kStages, qb);
+                if (!has_next) break;
+                u = un;
+            }
+        }
+    }
+}
+
 size_t attention_lds_bytes(const Geometry& g, bool bf16) {
     return bf16 ? bf16_lds(g).total : f32_lds_bytes(g);
 }
@@ -704,25 +1201,70 @@ static Bf16Variant bf16_variant_b(int KT) {
     }
 }
 
-static Bf16Variant bf16_variant_for(const Geometry& g) {
+// (stream variants: .waves counts the compute waves; the block has kLoaders more)
+template <int D, bool BV>
+static Bf16Variant stream_variant_b(int KT) {
+    switch (KT) {
+    case 4: return {attn_bf16_stream_kernel<D, 4, 1, 4, BV>, 4};
+    case 7: return {attn_bf16_stream_kernel<D, 7, 1, 7, BV>, 7};
+    case 9: return {attn_bf16_stream_kernel<D, 9, 1, 9, BV>, 9};
+    default: // up to 16 tiles (larger windows take the block schedule)
+        if (KT <= 8) return {attn_bf16_stream_kernel<D, 8, 1, 0, BV>, 8};
+        return {attn_bf16_stream_kernel<D, 8, 2, 0, BV>, 8};
+    }
+}
+
+static Bf16Variant bf16_variant_for(const Geometry& g, bool stream) {
     const int KT = (g.N + 15) / 16;
     const bool bv = g.win[2] % 4 == 0;
+    if (stream) {
+        if (g.head_dim == 32) return bv ? stream_variant_b<32, true>(KT) : stream_variant_b<32, false>(KT);
+        return bv ? stream_variant_b<64, true>(KT) : stream_variant_b<64, false>(KT);
+    }
     if (g.head_dim == 32) return bv ? bf16_variant_b<32, true>(KT) : bf16_variant_b<32, false>(KT);
     return bv ? bf16_variant_b<64, true>(KT) : bf16_variant_b<64, false>(KT);
 }
 
-hipError_t bf16_check_fits(const Geometry& g, int* blocks_per_cu) {
-    const Bf16Variant var = bf16_variant_for(g);
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)var.f, var.waves * 64,
-                                                        bf16_lds(g).total);
+bool bf16_stream_fits(const Geometry& g) {
+    const int64_t rows = (int64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
+    const int64_t wrows = g.windows * g.N;
+    const int KT = (g.N + 15) / 16;
+    // rows + 1 fit the packed table word; buffer offsets of both layouts stay below 2^31
+    return stream_lds(g).total <= (size_t)kLdsBytes && KT <= 16 &&
+           (rows > wrows ? rows : wrows) < kRowMask && stream_tensor_bytes(g, false) < kOutOfRange &&
+           stream_tensor_bytes(g, true) < kOutOfRange;
 }
 
-hipError_t launch_attention_bf16(const Geometry& g, bool staged, const uint16_t* q,
+hipError_t bf16_plan(const Geometry& g, bool stream, int* blocks) {
+    const Bf16Variant var = bf16_variant_for(g, stream);
+    const size_t lds = stream ? stream_lds(g).total : bf16_lds(g).total;
+    int per_cu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)var.f,
+                                                                (var.waves + (stream ? kLoaders : 0)) * 64, lds);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1) {
+        *blocks = 0;
+        return hipSuccess;
+    }
+    if (!stream) {
+        *blocks = (int)(g.windows * g.heads);
+        return hipSuccess;
+    }
+    int dev = 0, cus = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int64_t n = (int64_t)per_cu * cus / kXcds * kXcds; // a multiple of the XCD count
+    *blocks = (int)(n < kXcds ? kXcds : n);
+    return hipSuccess;
+}
+
+hipError_t launch_attention_bf16(const Geometry& g, bool stream, int blocks, bool staged, const uint16_t* q,
                                  const uint16_t* k, const uint16_t* v, const float* table,
                                  uint16_t* out, hipStream_t s) {
-    const Bf16Variant var = bf16_variant_for(g);
-    hipLaunchKernelGGL(var.f, dim3((unsigned)(g.windows * g.heads)), dim3(var.waves * 64), bf16_lds(g).total,
-                       s, g, (int)staged, q, k, v, table, out);
+    const Bf16Variant var = bf16_variant_for(g, stream);
+    const size_t lds = stream ? stream_lds(g).total : bf16_lds(g).total;
+    hipLaunchKernelGGL(var.f, dim3((unsigned)blocks), dim3((var.waves + (stream ? kLoaders : 0)) * 64), lds, s, g,
+                       (int)staged, q, k, v, table, out);
     return hipGetLastError();
 }
 
@@ -732,12 +1274,18 @@ hipError_t prepare_kernels(int max_lds) {
         hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
         if (e != hipSuccess) return e;
     }
-    for (int KT : {4, 7, 9, 18, 1, 32}) {
-        const bf16_kernel_t fs[] = {bf16_variant_b<32, true>(KT).f, bf16_variant_b<32, false>(KT).f,
-                                    bf16_variant_b<64, true>(KT).f, bf16_variant_b<64, false>(KT).f};
-        for (bf16_kernel_t f : fs) {
-            hipError_t e = hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-            if (e != hipSuccess) return e;
+    for (int stream = 0; stream < 2; stream++) {
+        for (int KT : {4, 7, 9, 18, 1, 32}) {
+            const bf16_kernel_t fs[] = {
+                stream ? stream_variant_b<32, true>(KT).f : bf16_variant_b<32, true>(KT).f,
+                stream ? stream_variant_b<32, false>(KT).f : bf16_variant_b<32, false>(KT).f,
+                stream ? stream_variant_b<64, true>(KT).f : bf16_variant_b<64, true>(KT).f,
+                stream ? stream_variant_b<64, false>(KT).f : bf16_variant_b<64, false>(KT).f};
+            for (bf16_kernel_t f : fs) {
+                hipError_t e =
+                    hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+                if (e != hipSuccess) return e;
+            }
         }
     }
     return hipSuccess;

@@ -21,8 +21,8 @@ def say(*a):
     print(*a, flush=True)
 
 
-def run(p, d, variant="fused"):
-    att = WindowAttention(p, variant)
+def run(p, d, variant="fused", schedule="auto"):
+    att = WindowAttention(p, variant, schedule)
     out = att.forward(d["q"], d["k"], d["v"], d["table"])
     torch.cuda.synchronize()
     att.close()
@@ -57,13 +57,13 @@ EDGE = {
 
 
 @pytest.mark.parametrize("name", list(SMALL) + list(EDGE))
-@pytest.mark.parametrize("variant", ["fused", "staged"])
-def test_parity_small_full_grid(name, variant):
+@pytest.mark.parametrize("variant,schedule", [("fused", "auto"), ("staged", "auto"), ("fused", "block")])
+def test_parity_small_full_grid(name, variant, schedule):
     p = SMALL.get(name) or EDGE[name]
-    say(f"[parity] {name} {variant} dtype={p.dtype} B={p.batch} grid={p.extent} pad={p.padded} "
+    say(f"[parity] {name} {variant} {schedule} dtype={p.dtype} B={p.batch} grid={p.extent} pad={p.padded} "
         f"win={p.window} shift={p.shift} heads={p.heads}x{p.head_dim} seed={p.seed}")
     x, d = device_inputs(p)
-    out = run(p, d, variant)
+    out = run(p, d, variant, schedule)
     ref = oracle_full(p, x)
     err = rel_err(host_f32(out), ref)
     say(f"  rel err {err:.3e}")
@@ -92,6 +92,9 @@ def test_parity_full_size_sampled(name):
     # the staged variant runs the same attention arithmetic on window-major copies
     out2 = run(p, d, "staged")
     assert torch.equal(out, out2)
+    # the per-window-block schedule computes the same sums in the same order
+    out3 = run(p, d, "fused", "block")
+    assert torch.equal(out, out3)
 
 
 def test_fp32_full_workload_matches_oracle_everywhere():
