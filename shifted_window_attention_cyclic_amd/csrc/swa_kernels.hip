@@ -686,40 +686,39 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 // range of units and its blocks interleave over it, so an XCD works on the
 // heads of a few neighbouring windows at a time.
 //
-// A block has one wave per 16-query tile plus kLoaders loader waves.  The
-// loaders build each unit's token table and copy its K and V from global
-// memory straight into LDS with global_load_lds (16 bytes per lane, no
-// registers), two units ahead, into a ring of kStages stages:
-//   K [key][d] and V [key][d], 16-byte chunks XOR-swizzled by row (the source
-//   chunk each lane fetches is chosen so the copy lands swizzled).
-// Loader wave j owns a contiguous range of key rows: it writes their table
-// words and issues their copies, so it never reads what the other loader
-// wrote.  It issues nothing but these copies, so "wait until only the next
-// unit's copies are outstanding" is an exact vmcnt count (vector memory
-// operations of a wave complete in order).
+// A block has one wave per 16-query tile plus kLoaders loader waves.  Only
+// the loaders read global memory: they build each unit's token table and copy
+// its K, V and Q straight into LDS with global_load_lds (16 bytes per lane,
+// eight lanes per 128-byte token row, so every request is a whole line):
+//   K, V  two units ahead, into a ring of kStages stages;
+//   Q     one unit ahead, into kQSlots slots;
+// all [token][d] with 16-byte chunks XOR-swizzled by row (the source chunk a
+// lane fetches is chosen so that the copy lands swizzled).  Loader wave j
+// owns a contiguous range of token rows: it writes their table words and
+// issues their copies, so it never reads what the other loader wrote.  It
+// issues nothing but copies, in the order Q(i+1), K/V(i+2) during unit i, so
+// "wait until only the newest unit's K/V copies are outstanding" is an exact
+// vmcnt count (vector memory operations of a wave complete in order).
 //
-// The compute waves issue no LDS copies.  They load their Q tiles one unit
-// ahead into registers and store O through buffer instructions whose range
-// check drops the lanes of pad queries (loads of such lanes return zeros), so
-// every wave issues the same number of loads and stores per unit and the
-// compiler's own counted waits for the Q registers never wait for stores.
-// The two roles run separate loops with the same number of block barriers;
-// the barriers fence LDS only (a full fence would wait for every outstanding
-// global load and store).  Iteration i:
-//   loaders: wait for unit i's copies, barrier, table and copies of unit i+2;
-//   compute: barrier, Q loads of unit i+1, unit i (Q loaded one iteration ago).
+// The compute waves read Q, K and V^T fragments from LDS, and write their O
+// tile into their own Q tile's LDS rows (free once Q is in registers) so that
+// it leaves as whole 128-byte token rows through buffer stores; lanes of pad
+// queries store out of range, which the buffer range check drops.  The two
+// roles run separate loops with the same number of block barriers, and the
+// barriers fence LDS only: a full fence would wait for every store in flight.
 // The PV product reads V^T fragments with ds_read_b64_tr_b16, which hands
 // lane i of each 16-lane group element i of the 4 rows its group addresses.
 // --------------------------------------------------------------------------
 constexpr int kStages = 3;
+constexpr int kQSlots = 2;
 constexpr int kTableSlots = 3;
 constexpr int kLoaders = 2;
 
 struct StreamLds {
     int NP, TSP;   // padded keys; bias table entries per head slice (multiple of 64)
     bool bias_resident;
-    size_t stage_bytes, bias, kb4, slot0, slot_bytes, total;
-    // stage s: K at s * stage_bytes, V at s * stage_bytes + NP * D * 2
+    size_t stage_bytes, q0, q_bytes, bias, kb4, slot0, slot_bytes, total;
+    // stage s: K at s * stage_bytes, V at s * stage_bytes + NP * D * 2; Q slot s at q0 + s * q_bytes
 };
 
 __host__ __device__ inline StreamLds stream_lds_with(const Geometry& g, bool bias_resident) {
@@ -727,8 +726,10 @@ __host__ __device__ inline StreamLds stream_lds_with(const Geometry& g, bool bia
     L.NP = (g.N + 15) / 16 * 16;
     L.TSP = (g.table_size + 63) / 64 * 64;
     L.bias_resident = bias_resident;
-    L.stage_bytes = (size_t)2 * L.NP * g.head_dim * 2;
-    L.bias = kStages * L.stage_bytes;
+    L.q_bytes = (size_t)L.NP * g.head_dim * 2;
+    L.stage_bytes = 2 * L.q_bytes;
+    L.q0 = kStages * L.stage_bytes;
+    L.bias = L.q0 + kQSlots * L.q_bytes;
     L.kb4 = L.bias + (size_t)(bias_resident ? g.heads : kStages) * L.TSP * 4;
     L.slot0 = L.kb4 + (size_t)L.NP * 4;
     L.slot_bytes = (size_t)L.NP * 4; // one packed word per token: (row + 1) | mask field << 28
@@ -799,31 +800,35 @@ __device__ inline Unit decode_unit(const Geometry& g, uint32_t u) {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// Copies one loader wave issues per unit: its share of the K and V copies
-// (1 KB each), plus the streamed bias slice for loader 0.
-__host__ __device__ inline int loader_copies(const Geometry& g, const StreamLds& L, int j) {
+// The 1 KB copies (per tensor) of loader wave j: [c0, c1), covering token rows
+// [c0 * RPC, c1 * RPC) with RPC = 64 / (D / 8) rows per copy.
+struct LoaderRange {
+    int c0, c1;
+};
+
+__host__ __device__ inline LoaderRange loader_range(const Geometry& g, const StreamLds& L, int j) {
     const int ncopy = L.NP * (g.head_dim / 8) / 64;
-    const int c0 = ncopy * j / kLoaders, c1 = ncopy * (j + 1) / kLoaders;
-    return 2 * (c1 - c0) + (j == 0 && !L.bias_resident ? L.TSP / 64 : 0);
+    return LoaderRange{ncopy * j / kLoaders, ncopy * (j + 1) / kLoaders};
 }
 
-// Loader wave j's work for unit uu: the table words of its key rows into slot
-// s, then its K and V copies (and, for loader 0, the streamed bias) into
-// stage st.  Returns after issuing the copies.
+// Copies loader wave j issues with a unit's K and V: K and V of its rows,
+// plus the streamed bias slice for loader 0.
+__host__ __device__ inline int loader_kv_copies(const Geometry& g, const StreamLds& L, int j) {
+    const LoaderRange R = loader_range(g, L, j);
+    return 2 * (R.c1 - R.c0) + (j == 0 && !L.bias_resident ? L.TSP / 64 : 0);
+}
+
+// Table words of loader j's rows of unit uu, into slot s: (source row + 1, 0
+// for pad) | mask field << 28, the mask field holding the wrapped flags with
+// pad in bit 3 (15 past N).
 template <int D>
-__device__ inline void load_unit(const Geometry& g, const StreamLds& L, unsigned char* smem, int j, int lane,
-                                 uint32_t uu, int s, int st, int staged, const uint16_t* __restrict__ k,
-                                 const uint16_t* __restrict__ v, const float* __restrict__ table) {
-    constexpr int CH = D / 8;
-    constexpr int RPC = 64 / CH; // key rows per 1 KB copy
-    const int N = g.N, NP = L.NP;
-    const int ncopy = NP * CH / 64;
-    const int c0 = ncopy * j / kLoaders, c1 = ncopy * (j + 1) / kLoaders;
+__device__ inline void stream_table(const Geometry& g, const StreamLds& L, unsigned char* smem, LoaderRange R,
+                                    int lane, uint32_t uu, int s, int staged) {
+    constexpr int RPC = 64 / (D / 8);
+    const int N = g.N;
     const Unit U = decode_unit(g, uu);
     int* tw = (int*)(smem + L.slot0 + s * L.slot_bytes);
-    // table word per token: (source row + 1, 0 for pad) | mask field << 28, the mask
-    // field holding the wrapped flags with pad in bit 3 (15 past N)
-    for (int n = c0 * RPC + lane; n < c1 * RPC; n += 64) {
+    for (int n = R.c0 * RPC + lane; n < R.c1 * RPC; n += 64) {
         if (n < N) {
             int l[3];
             local_coords(g, n, l[0], l[1], l[2]);
@@ -844,62 +849,95 @@ __device__ inline void load_unit(const Geometry& g, const StreamLds& L, unsigned
             tw[n] = 15 << 28;
         }
     }
-    // the copies below read table words other lanes of this wave just wrote
+    // the copies read table words other lanes of this wave just wrote
     __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
-    for (int c = c0; c < c1; c++) {
-        const int byte = c * 1024 + lane * 16;
-        const int m = byte / (D * 2);
-        const int ch = ((byte % (D * 2)) / 16) ^ ((m / (128 / (D * 2))) % CH); // logical chunk
-        const int r1 = tw[m] & kRowMask; // row + 1; pad rows copy row 0 (finite, weight exactly 0)
-        const uint32_t off = (uint32_t)(r1 == 0 ? 0 : r1 - 1) * (uint32_t)g.row + U.h * D + ch * 8;
-        unsigned char* dst = smem + st * L.stage_bytes + c * 1024;
-        __builtin_amdgcn_global_load_lds((const void*)(k + off), (lds_void*)dst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(v + off), (lds_void*)(dst + (size_t)NP * D * 2), 16, 0,
-                                         0);
-    }
+}
+
+// Most 1 KB copies per tensor a loader wave issues for a unit.
+template <int D, int KT_FIXED>
+constexpr int loader_max_copies() {
+    return ((KT_FIXED > 0 ? KT_FIXED : 16) * 16 * (D / 8) / 64 + kLoaders - 1) / kLoaders;
+}
+
+// Source element offsets (within a head's slice of a token row) of loader j's
+// copies for the unit whose table is in slot s: 1 KB per copy, 8 lanes per
+// 128-byte token row, the source chunk chosen so that the row lands swizzled.
+// Pad rows copy row 0 (finite values that get weight exactly 0, or outputs
+// that are never stored).  All table reads are issued before any is used.
+template <int D, int MAXC>
+__device__ inline void stream_offsets(const Geometry& g, const StreamLds& L, const unsigned char* smem, LoaderRange R,
+                                      int lane, int s, uint32_t (&off)[MAXC]) {
+    constexpr int CH = D / 8;
+    constexpr int RPC = 64 / CH;
+    const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
+    const int m0 = lane / CH; // row within a copy
+    const int ch = (lane % CH) ^ ((m0 / (128 / (D * 2))) % CH); // RPC is a multiple of 128 / (2 D)
+    int r1[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; i++) r1[i] = R.c0 + i < R.c1 ? tw[(R.c0 + i) * RPC + m0] & kRowMask : 0;
+#pragma unroll
+    for (int i = 0; i < MAXC; i++)
+        off[i] = (uint32_t)(r1[i] == 0 ? 0 : r1[i] - 1) * (uint32_t)g.row + ch * 8;
+}
+
+template <int D, int MAXC>
+__device__ inline void stream_issue(const StreamLds& L, LoaderRange R, int lane, int hh, const uint32_t (&off)[MAXC],
+                                    const uint16_t* __restrict__ src, unsigned char* dst) {
+    const uint16_t* sh = src + hh * D;
+#pragma unroll
+    for (int i = 0; i < MAXC; i++)
+        if (R.c0 + i < R.c1)
+            __builtin_amdgcn_global_load_lds((const void*)(sh + off[i]), (lds_void*)(dst + (R.c0 + i) * 1024), 16, 0,
+                                             0);
+}
+
+// K and V of unit uu (table in slot s) into stage st, and for loader 0 the
+// streamed bias.
+template <int D, int MAXC>
+__device__ inline void stream_copy_kv(const Geometry& g, const StreamLds& L, unsigned char* smem, int j,
+                                      LoaderRange R, int lane, uint32_t uu, int s, int st,
+                                      const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                      const float* __restrict__ table) {
+    const int hh = (int)(uu - fdiv(g.fd_heads, uu) * (uint32_t)g.heads);
+    unsigned char* kd = smem + st * L.stage_bytes;
+    uint32_t off[MAXC];
+    stream_offsets<D, MAXC>(g, L, smem, R, lane, s, off);
+    stream_issue<D, MAXC>(L, R, lane, hh, off, k, kd);
+    stream_issue<D, MAXC>(L, R, lane, hh, off, v, kd + L.q_bytes);
     if (j == 0 && !L.bias_resident) {
         float* bdst = (float*)(smem + L.bias) + st * L.TSP;
         for (int jj = 0; jj * 64 < L.TSP; jj++) {
             const int i = jj * 64 + lane;
-            const float* src = table + (i < g.table_size ? i * g.heads + U.h : 0);
+            const float* src = table + (i < g.table_size ? i * g.heads + hh : 0);
             __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(bdst + jj * 64), 4, 0, 0);
         }
     }
 }
 
-// Loads the Q tiles of unit uu (token table in slot s) into qo: one 16-byte
-// buffer load per tile and 32-deep step, issued by every lane (pad queries
-// read out of range and get zeros).
-template <int D, int NWAVES, int QT_MAX, int KT_FIXED>
-__device__ inline void stream_load_q(const Geometry& g, const StreamLds& L, const unsigned char* smem,
-                                     __amdgpu_buffer_rsrc_t qrs, int wave, int col, int grp, uint32_t uu, int s,
-                                     bf16x8 (&qo)[QT_MAX][D / 32]) {
-    const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
-    const int KT = KT_FIXED > 0 ? KT_FIXED : L.NP / 16;
+// Q of unit uu (table in slot s) into LDS at dst.
+template <int D, int MAXC>
+__device__ inline void stream_copy_q(const Geometry& g, const StreamLds& L, unsigned char* smem, LoaderRange R,
+                                     int lane, uint32_t uu, int s, const uint16_t* __restrict__ q,
+                                     unsigned char* dst) {
     const int hh = (int)(uu - fdiv(g.fd_heads, uu) * (uint32_t)g.heads);
-#pragma unroll
-    for (int t = 0; t < QT_MAX; t++) {
-        const int qt = wave + t * NWAVES;
-        const int r = qt < KT ? (tw[qt * 16 + col] & kRowMask) - 1 : -1;
-        const uint32_t base = r >= 0 ? ((uint32_t)r * (uint32_t)g.row + hh * D + grp * 8) * 2 : kOutOfRange;
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ks++)
-            qo[t][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, base + ks * 64, 0, 0));
-    }
+    uint32_t off[MAXC];
+    stream_offsets<D, MAXC>(g, L, smem, R, lane, s, off);
+    stream_issue<D, MAXC>(L, R, lane, hh, off, q, dst);
 }
 
-// One unit's attention for the query tiles of this wave (operands in stage
-// st and table slot s of LDS, Q in qc); O leaves through ors.
+// One unit's attention for the query tiles of this wave: Q in slot qs, K, V
+// (and streamed bias) in stage st, table in slot s; O leaves through ors.
 template <int D, int NWAVES, int QT_MAX, int KT_FIXED, bool BIAS_VEC>
-__device__ inline void stream_compute(const Geometry& g, const StreamLds& L, const unsigned char* smem,
-                                      __amdgpu_buffer_rsrc_t ors, int wave, int col, int grp, int staged,
-                                      uint32_t uu, int s, int st, const bf16x8 (&qc)[QT_MAX][D / 32]) {
+__device__ inline void stream_compute(const Geometry& g, const StreamLds& L, unsigned char* smem,
+                                      __amdgpu_buffer_rsrc_t ors, int wave, int lane, int staged, uint32_t uu,
+                                      int s, int st, int qs) {
     constexpr int KSTEPS = D / 32;
     constexpr int DT = D / 16;
     constexpr int CH = D / 8;
     constexpr int KB = (KT_FIXED > 0 && KT_FIXED <= kKeyTilesPerBlock) ? KT_FIXED : kKeyTilesPerBlock;
     constexpr int KB_UNROLL = KT_FIXED > 0 ? KT_FIXED / KB : 1;
+    const int col = lane & 15, grp = lane >> 4;
     const int N = g.N;
     const int KT = KT_FIXED > 0 ? KT_FIXED : L.NP / 16;
     const unsigned one2 = 0x3F803F80u; // two bf16 ones
@@ -909,7 +947,8 @@ __device__ inline void stream_compute(const Geometry& g, const StreamLds& L, con
     const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
     const int* kb4 = (const int*)(smem + L.kb4);
     const uint16_t* Ks = (const uint16_t*)(smem + st * L.stage_bytes);
-    const unsigned char* Vb = smem + st * L.stage_bytes + (size_t)L.NP * D * 2;
+    const unsigned char* Vb = smem + st * L.stage_bytes + L.q_bytes;
+    uint16_t* Qs = (uint16_t*)(smem + L.q0 + qs * L.q_bytes);
     const unsigned char* bias_bytes =
         smem + L.bias + (size_t)(L.bias_resident ? U.h : st) * L.TSP * 4;
 #pragma unroll
@@ -929,6 +968,10 @@ __device__ inline void stream_compute(const Geometry& g, const StreamLds& L, con
             qb4 = (g.table_size - 1) * 4;
         }
         const unsigned char* qbias = bias_bytes + qb4;
+        bf16x8 qf[KSTEPS]; // B operand: query n, d = 32 ks + 8 grp + 0..7
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ks++)
+            qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Qs + n * D + k_slot<D>(n, ks * 4 + grp) * 8));
         f32x4 o[DT], osum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -947,7 +990,7 @@ __device__ inline void stream_compute(const Geometry& g, const StreamLds& L, con
                     for (int ks = 0; ks < KSTEPS; ks++) {
                         const bf16x8 a = __builtin_bit_cast(
                             bf16x8, *(const u32x4*)(Ks + krow * D + k_slot<D>(krow, ks * 4 + grp) * 8));
-                        acc = mfma32(a, qc[t][ks], acc);
+                        acc = mfma32(a, qf[ks], acc);
                     }
                     sc[kt] = acc;
                 }
@@ -1047,23 +1090,32 @@ __device__ inline void stream_compute(const Geometry& g, const StreamLds& L, con
             }
         }
 
-        // O rows: the real token, or in the staged layout also pad slots (zeros);
-        // other lanes store out of range, which the buffer range check drops
-        int orow = r;
-        if (r < 0 && staged) orow = (int)(U.wi * (uint32_t)N + n);
-        const bool keep = orow >= 0 && n < N;
+        // O tile into this tile's Q rows (same swizzle), then out as whole token rows
         const float inv = r >= 0 ? __builtin_amdgcn_rcpf(osum[0]) : 0.f;
-        const uint32_t obase = keep ? ((uint32_t)orow * (uint32_t)g.row + U.h * D + grp * 4) * 2 : kOutOfRange;
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
             const u32x2 w = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
-            __builtin_amdgcn_raw_buffer_store_b64(w, ors, obase + dt * 32, 0, 0);
+            const int c = dt * 2 + (grp >> 1); // 16-byte chunk of d = 16 dt + 4 grp
+            *(u32x2*)(Qs + n * D + k_slot<D>(n, c) * 8 + (grp & 1) * 4) = w;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): the tile is written
+        __builtin_amdgcn_wave_barrier();
+        constexpr int RPI = 64 / CH; // token rows per store instruction
+#pragma unroll
+        for (int i = 0; i < 16 / RPI; i++) {
+            const int m = qt * 16 + i * RPI + lane / CH, c = lane % CH;
+            const u32x4 val = *(const u32x4*)(Qs + m * D + k_slot<D>(m, c) * 8);
+            const int rm = (tw[m] & kRowMask) - 1;
+            // the real token, or in the staged layout also pad slots (zeros)
+            const int orow = rm >= 0 ? rm : (staged && m < N ? (int)(U.wi * (uint32_t)N + m) : -1);
+            const uint32_t ob = orow >= 0 ? ((uint32_t)orow * (uint32_t)g.row + U.h * D + c * 8) * 2 : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(val, ors, ob, 0, 0);
         }
     }
 }
 
-// Bytes of each tensor the streaming schedule reads or writes through
-// buffer resources (real-token layout, or window-major when staged).
+// Bytes of each tensor the streaming schedule writes through a buffer
+// resource (real-token layout, or window-major when staged).
 __host__ __device__ inline uint64_t stream_tensor_bytes(const Geometry& g, bool staged) {
     const uint64_t rows = staged ? (uint64_t)g.windows * g.N
                                  : (uint64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
@@ -1075,7 +1127,6 @@ __global__ __launch_bounds__((NWAVES + kLoaders) * 64) void attn_bf16_stream_ker
     Geometry g, int staged, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ table, uint16_t* __restrict__ out) {
     constexpr int THREADS = (NWAVES + kLoaders) * 64;
-    constexpr int KSTEPS = D / 32;
     extern __shared__ __align__(16) unsigned char smem[];
     const StreamLds L = stream_lds(g);
     float* bias_lds = (float*)(smem + L.bias);
@@ -1083,7 +1134,6 @@ __global__ __launch_bounds__((NWAVES + kLoaders) * 64) void attn_bf16_stream_ker
     const int N = g.N, NP = L.NP;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int col = lane & 15, grp = lane >> 4;
 
     const uint32_t units = (uint32_t)(g.windows * g.heads);
     const uint32_t per = gridDim.x / kXcds;
@@ -1109,69 +1159,50 @@ __global__ __launch_bounds__((NWAVES + kLoaders) * 64) void attn_bf16_stream_ker
     }
 
     if (wave >= NWAVES) {
-        // ---- loader waves
+        // ---- loader waves.  Issue order: K/V(0), Q(0), K/V(1) | Q(i+1), K/V(i+2) after barrier i
+        constexpr int MAXC = loader_max_copies<D, KT_FIXED>();
         const int j = wave - NWAVES;
-        const int copies = loader_copies(g, L, j);
-        load_unit<D>(g, L, smem, j, lane, u0, 0, 0, staged, k, v, table);
-        if (u0 + per < uend) load_unit<D>(g, L, smem, j, lane, u0 + per, 1, 1, staged, k, v, table);
-        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): table words of units 0 and 1
-        lds_barrier();                      // prologue
+        const LoaderRange R = loader_range(g, L, j);
+        const int kv_copies = loader_kv_copies(g, L, j);
+        const uint32_t u1 = u0 + per;
+        stream_table<D>(g, L, smem, R, lane, u0, 0, staged);
+        stream_copy_kv<D, MAXC>(g, L, smem, j, R, lane, u0, 0, 0, k, v, table);
+        stream_copy_q<D, MAXC>(g, L, smem, R, lane, u0, 0, q, smem + L.q0);
+        if (u1 < uend) {
+            stream_table<D>(g, L, smem, R, lane, u1, 1, staged);
+            stream_copy_kv<D, MAXC>(g, L, smem, j, R, lane, u1, 1, 1, k, v, table);
+        }
+        lds_barrier(); // prologue: window-independent tables and the first token tables
         uint32_t u = u0;
         for (int iter = 0;; iter++) {
-            const uint32_t un = u + per;
-            // unit u's copies have landed once at most the next unit's remain
-            wait_vmcnt_le(un < uend ? copies : 0);
+            const uint32_t un = u + per, un2 = un + per;
+            // unit u's K, V and Q have landed once at most the K/V copies of unit un remain
+            wait_vmcnt_le(un < uend ? kv_copies : 0);
             lds_barrier();
-            if (un + per < uend)
-                load_unit<D>(g, L, smem, j, lane, un + per, (iter + 2) % kTableSlots, (iter + 2) % kStages, staged,
-                             k, v, table);
+            if (un < uend)
+                stream_copy_q<D, MAXC>(g, L, smem, R, lane, un, (iter + 1) % kTableSlots, q,
+                                       smem + L.q0 + ((iter + 1) % kQSlots) * L.q_bytes);
+            if (un2 < uend) {
+                stream_table<D>(g, L, smem, R, lane, un2, (iter + 2) % kTableSlots, staged);
+                stream_copy_kv<D, MAXC>(g, L, smem, j, R, lane, un2, (iter + 2) % kTableSlots, (iter + 2) % kStages,
+                                        k, v, table);
+            }
             if (un >= uend) break;
             u = un;
         }
     } else {
         // ---- compute waves
-        const __amdgpu_buffer_rsrc_t qrs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)q, 0, (int)stream_tensor_bytes(g, staged), kBufferWord3);
         const __amdgpu_buffer_rsrc_t ors =
             __builtin_amdgcn_make_buffer_rsrc((void*)out, 0, (int)stream_tensor_bytes(g, staged), kBufferWord3);
-        bf16x8 qa[QT_MAX][KSTEPS], qb[QT_MAX][KSTEPS];
-        lds_barrier(); // prologue: unit 0's table is in slot 0
-        stream_load_q<D, NWAVES, QT_MAX, KT_FIXED>(g, L, smem, qrs, wave, col, grp, u0, 0, qa);
-        // as many stores as a unit's epilogue issues, all out of range (dropped): the
-        // loop is then entered with the same vector-memory history from both sides,
-        // and the compiler's wait for qa leaves the previous unit's stores in flight
-        for (int t = 0; t < QT_MAX; t++) {
-            if (KT_FIXED == 0 && wave + t * NWAVES >= L.NP / 16) break;
-#pragma unroll
-            for (int dt = 0; dt < D / 16; dt++)
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, ors, kOutOfRange + dt * 32, 0, 0);
-        }
+        lds_barrier(); // prologue
         uint32_t u = u0;
-        for (int iter = 0;; iter += 2) {
-            // two iterations per trip, so that the Q registers swap roles without copies
-            {
-                const uint32_t un = u + per;
-                const bool has_next = un < uend;
-                lds_barrier();
-                stream_load_q<D, NWAVES, QT_MAX, KT_FIXED>(g, L, smem, qrs, wave, col, grp, has_next ? un : u,
-                                                           (iter + (has_next ? 1 : 0)) % kTableSlots, qb);
-                stream_compute<D, NWAVES, QT_MAX, KT_FIXED, BIAS_VEC>(g, L, smem, ors, wave, col, grp, staged, u,
-                                                                      iter % kTableSlots, iter % kStages, qa);
-                if (!has_next) break;
-                u = un;
-            }
-            {
-                const uint32_t un = u + per;
-                const bool has_next = un < uend;
-                lds_barrier();
-                stream_load_q<D, NWAVES, QT_MAX, KT_FIXED>(g, L, smem, qrs, wave, col, grp, has_next ? un : u,
-                                                           (iter + 1 + (has_next ? 1 : 0)) % kTableSlots, qa);
-                stream_compute<D, NWAVES, QT_MAX, KT_FIXED, BIAS_VEC>(g, L, smem, ors, wave, col, grp, staged, u,
-                                                                      (iter + 1) % kTableSlots,
-                                                                      (iter + 1) % kStages, qb);
-                if (!has_next) break;
-                u = un;
-            }
+        for (int iter = 0;; iter++) {
+            lds_barrier();
+            stream_compute<D, NWAVES, QT_MAX, KT_FIXED, BIAS_VEC>(g, L, smem, ors, wave, lane, staged, u,
+                                                                  iter % kTableSlots, iter % kStages,
+                                                                  iter % kQSlots);
+            u += per;
+            if (u >= uend) break;
         }
     }
 }
