@@ -30,7 +30,13 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 MALL_BYTES = 256 << 20     # Infinity Cache; rotate inputs until the working set is 3x this
 KERNEL_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_kernels.hip",
                   "shifted_window_attention_cyclic_amd/csrc/swa_geometry.h"]
-KERNEL_NAME = {"bf16": "attn_bf16_kernel", "f32": "attn_f32_kernel"}
+SCHEDULE_STREAM, SCHEDULE_BLOCK = 1, 2  # swa_info.schedule
+
+
+def kernel_name(p, info) -> str:
+    if p.dtype == "f32":
+        return "attn_f32_kernel"
+    return "attn_bf16_stream_kernel" if info.schedule == SCHEDULE_STREAM else "attn_bf16_kernel"
 
 
 def kernel_source_hash() -> str:
@@ -196,7 +202,8 @@ def main():
         "tokens_per_s": round(info.tokens / (ms_per_step * 1e-3), 1),
         "mfma_peak_frac": round(tflops / peak_tf, 5),
         "useful_tflops": round(useful / (ms_per_step * 1e-3) / 1e12, 3),
-        "kernel": {"name": KERNEL_NAME[p.dtype] if args.variant == "fused" else "gather+attn+scatter",
+        "kernel": {"name": kernel_name(p, info) if args.variant == "fused" else "gather+attn+scatter",
+                   "workgroups": info.workgroups,
                    "avg_launch_ms": round(avg_launch_ms, 5),
                    "p10_ms": round(launch_ms[len(launch_ms) // 10], 5),
                    "p90_ms": round(launch_ms[(9 * len(launch_ms)) // 10], 5),

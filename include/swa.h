@@ -108,6 +108,8 @@ typedef struct swa_info {
     size_t workspace_bytes;     /* device bytes owned by the handle (staged variant) */
     double nominal_flops;       /* 4 * N^2 * head_dim per (window, head), all windows */
     double algorithmic_bytes;   /* q, k, v read and out written once, real tokens, plus the table */
+    int32_t schedule;           /* bf16: the schedule in use (SWA_SCHEDULE_STREAM or _BLOCK); fp32: 0 */
+    int32_t workgroups;         /* bf16: workgroups per attention launch; fp32: 0 */
 } swa_info;
 
 /*

@@ -37,6 +37,7 @@ class swa_info(ctypes.Structure):
         ("windows", ctypes.c_int64), ("window_tokens", ctypes.c_int32), ("tokens", ctypes.c_int64),
         ("window_major_elems", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
         ("nominal_flops", ctypes.c_double), ("algorithmic_bytes", ctypes.c_double),
+        ("schedule", ctypes.c_int32), ("workgroups", ctypes.c_int32),
     ]
 
 

@@ -250,6 +250,9 @@ swa_status swa_get_info(const swa_handle* h, swa_info* info) {
     info->workspace_bytes = h->workspace ? 4 * h->wm_bytes : 0;
     info->nominal_flops = 4.0 * g.N * (double)g.N * g.head_dim * (double)g.windows * g.heads;
     info->algorithmic_bytes = 4.0 * (double)info->tokens * g.row * h->elem_bytes + 4.0 * g.table_size * g.heads;
+    const bool bf16 = h->cfg.dtype == SWA_BF16;
+    info->schedule = bf16 ? (h->stream ? SWA_SCHEDULE_STREAM : SWA_SCHEDULE_BLOCK) : 0;
+    info->workgroups = bf16 ? h->blocks : 0;
     return SWA_OK;
 }
 

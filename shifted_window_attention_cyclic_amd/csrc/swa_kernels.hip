@@ -470,7 +470,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
         for (int j = 0; j < 4; j++) {
             const int r = i < items ? rowi[g4 * 4 + j] : -1;
             if (r >= 0) {
-                const uint32_t off = (uint32_t)r * (uint32_t)g.row + c * 8;
+                const uint64_t off = (uint64_t)(uint32_t)r * (uint32_t)g.row + c * 8;
                 kr[it][j] = *(const u32x4*)(kh + off);
                 vr[it][j] = *(const u32x4*)(vh + off);
             } else {
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ks++) {
             u32x4 val = {0, 0, 0, 0};
-            if (r >= 0) val = *(const u32x4*)(q + (uint32_t)r * (uint32_t)g.row + h * D + ks * 32 + grp * 8);
+            if (r >= 0) val = *(const u32x4*)(q + (uint64_t)(uint32_t)r * (uint32_t)g.row + h * D + ks * 32 + grp * 8);
             qop[t][ks] = __builtin_bit_cast(bf16x8, val);
         }
     }
@@ -666,7 +666,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
         if (r < 0 && staged) orow = (int)(wi * (uint32_t)N + n); // staged: pad slots of O are zeros
         if (orow >= 0 && n < N) {
             const float inv = r >= 0 ? __builtin_amdgcn_rcpf(osum[0]) : 0.f;
-            uint16_t* op = out + (uint32_t)orow * (uint32_t)g.row + h * D + grp * 4;
+            uint16_t* op = out + (uint64_t)(uint32_t)orow * (uint32_t)g.row + h * D + grp * 4;
 #pragma unroll
             for (int dt = 0; dt < DT; dt++) {
                 const u32x2 w = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
