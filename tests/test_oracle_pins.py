@@ -391,3 +391,79 @@ def test_masked_latitude_does_not_wrap_but_longitude_does(oracle_lib):
 def test_workload_shapes_are_valid_tilings(oracle_lib):
     for p in WORKLOADS.values():
         assert oracle_lib.check(p) == 0, p.name
+
+
+# --------------------------------------------------------------------------- roll direction and pad values
+
+
+def _roll_plus_attention(p, x):
+    """Brute force with the OTHER roll direction, written here from the steps:
+    pad at the end, roll by +s (rolled[c'] = padded[(c' - s) mod P]), cut into
+    windows, mask pairs across the wrap (now the first s rolled rows of a
+    masked axis) and pad keys, bias by the position inside the window."""
+    B, (T, H, W), (Pt, Ph, Pw) = p.batch, p.extent, p.padded
+    w, s = np.array(p.window), np.array(p.shift)
+    scale = 1.0 / math.sqrt(p.head_dim)
+    q, k, v, tab = (f64(x[n]) for n in ("q", "k", "v", "table"))
+    out = np.zeros_like(q)
+    for b in range(B):
+        # per rolled coordinate: source (or None for pad), wrapped flags, window, local
+        info = {}
+        for ct in range(Pt):
+            for cy in range(Ph):
+                for cx in range(Pw):
+                    cr = np.array([ct, cy, cx])
+                    src = (cr - s) % np.array([Pt, Ph, Pw])
+                    real = src[0] < T and src[1] < H and src[2] < W
+                    wrapped = tuple(bool(cr[a] < s[a]) and not p.cyclic[a] for a in range(3))
+                    info[(ct, cy, cx)] = (tuple(src) if real else None, wrapped, tuple(cr // w), cr % w)
+        for crq, (srcq, wq, winq, lq) in info.items():
+            if srcq is None:
+                continue
+            keys = [(srck, lk) for crk, (srck, wk, wink, lk) in info.items()
+                    if wink == winq and wk == wq and srck is not None]
+            for h in range(p.heads):
+                qi = q[(b,) + srcq + (h,)]
+                lg = np.array([scale * qi @ k[(b,) + sk + (h,)]
+                               + tab[tuple(lq - lk + w - 1) + (h,)] for sk, lk in keys])
+                e = np.exp(lg - lg.max())
+                out[(b,) + srcq + (h,)] = sum(ei * v[(b,) + sk + (h,)] for ei, (sk, _) in zip(e / e.sum(), keys))
+    return out
+
+
+def test_roll_direction_is_immaterial_at_half_window_shift(oracle_lib):
+    """With s = w/2 and the padded extent a multiple of w, rolling by +s or -s
+    gives the same windows, masks and window-local positions, so the same output."""
+    p = P((1, 7, 8), (1, 8, 8), (1, 4, 4), (0, 2, 2), heads=2, head_dim=4)
+    x = make_inputs(p, seed=31)
+    assert np.abs(_roll_plus_attention(p, x) - run_direct(oracle_lib, p, x)).max() < 1e-12
+
+
+def test_roll_direction_matters_off_half_window(oracle_lib):
+    """The same brute force with s != w/2 must NOT match: the test above can fail."""
+    p = P((1, 7, 8), (1, 8, 8), (1, 4, 4), (0, 1, 1), heads=1, head_dim=4)
+    x = make_inputs(p, seed=32)
+    assert np.abs(_roll_plus_attention(p, x) - run_direct(oracle_lib, p, x)).max() > 1e-3
+
+
+def test_pad_values_do_not_matter(oracle_lib, monkeypatch):
+    """Pad tokens get weight exactly 0: filling the pad slots of the literal form
+    with large random values instead of zeros leaves every real output unchanged."""
+    from oracle import literal
+
+    p = P((1, 13, 8), (1, 16, 8), (1, 4, 4), (0, 2, 2), heads=2, head_dim=4)
+    x = make_inputs(p, seed=33)
+    base = run_literal(oracle_lib, p, x)
+    orig = literal._pad
+    rng = np.random.default_rng(5)
+
+    def noisy_pad(prob, a):
+        out = orig(prob, a)
+        T, H, W = prob.extent
+        noise = rng.normal(0.0, 50.0, out.shape)
+        noise[:, :T, :H, :W] = 0.0
+        return out + noise
+
+    monkeypatch.setattr(literal, "_pad", noisy_pad)
+    noisy = run_literal(oracle_lib, p, x)
+    assert np.array_equal(noisy, base)
