@@ -377,6 +377,17 @@ __device__ inline int k_slot(int m, int c) {
     return c ^ ((m / ROWS_PER_128B) % CH);
 }
 
+// 16-byte chunk slot of logical chunk c in V row m, for rows read through
+// ds_read_b64_tr_b16: a 16-lane group reads 2 adjacent chunks of 4
+// consecutive rows, and XOR with 2 * (row index within 128-byte groups, mod
+// CH / 2) gives those 8 (row, chunk) pairs distinct banks.
+template <int D>
+__device__ inline int v_slot(int m, int c) {
+    constexpr int CH = D / 8;
+    constexpr int ROWS_PER_128B = 128 / (D * 2);
+    return c ^ (2 * ((m / ROWS_PER_128B) % (CH / 2)));
+}
+
 // window-local coordinates of local index n
 __device__ inline void local_coords(const Geometry& g, int n, int& lt, int& ly, int& lx) {
     const uint32_t r = fdiv(g.fd_win2, (uint32_t)n);
@@ -678,7 +689,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 }
 
 // --------------------------------------------------------------------------
-// bf16 attention, streaming schedule: persistent blocks with an LDS ring.
+// bf16 attention, streaming schedule: persistent blocks with LDS double buffers.
 //
 // The same per-tile arithmetic as above, instruction for instruction (both
 // schedules give bit-identical outputs), but a block stays resident and walks
@@ -686,39 +697,47 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 // range of units and its blocks interleave over it, so an XCD works on the
 // heads of a few neighbouring windows at a time.
 //
-// A block has one wave per 16-query tile plus kLoaders loader waves.  Only
-// the loaders read global memory: they build each unit's token table and copy
-// its K, V and Q straight into LDS with global_load_lds (16 bytes per lane,
-// eight lanes per 128-byte token row, so every request is a whole line):
-//   K, V  two units ahead, into a ring of kStages stages;
-//   Q     one unit ahead, into kQSlots slots;
-// all [token][d] with 16-byte chunks XOR-swizzled by row (the source chunk a
-// lane fetches is chosen so that the copy lands swizzled).  Loader wave j
-// owns a contiguous range of token rows: it writes their table words and
-// issues their copies, so it never reads what the other loader wrote.  It
-// issues nothing but copies, in the order Q(i+1), K/V(i+2) during unit i, so
-// "wait until only the newest unit's K/V copies are outstanding" is an exact
-// vmcnt count (vector memory operations of a wave complete in order).
+// A block has one wave per 16-query tile (windows of up to 9 tiles) plus
+// kLoaders loader waves.  Only the loaders read global memory: they build
+// each unit's token table and copy its K, Q and V straight into LDS with
+// global_load_lds (16 bytes per lane, eight lanes per 128-byte token row, so
+// every request is a whole line), [token][d] with 16-byte chunks
+// XOR-swizzled by row (the source chunk a lane fetches is chosen so that the
+// copy lands swizzled).  Loader wave j owns a contiguous range of token rows:
+// it writes their table words and issues their copies, so it never reads
+// what the other loader wrote.
 //
-// The compute waves read Q, K and V^T fragments from LDS, and write their O
-// tile into their own Q tile's LDS rows (free once Q is in registers) so that
-// it leaves as whole 128-byte token rows through buffer stores; lanes of pad
-// queries store out of range, which the buffer range check drops.  The two
-// roles run separate loops with the same number of block barriers, and the
-// barriers fence LDS only: a full fence would wait for every store in flight.
-// The PV product reads V^T fragments with ds_read_b64_tr_b16, which hands
-// lane i of each 16-lane group element i of the 4 rows its group addresses.
+// Unit i takes two block barriers: A_i (its K and Q are in LDS) and B_i (its
+// V is in LDS; its K and Q are no longer read).  K, Q and V have two buffers
+// each, so a copy can start 1.5 units before its data is needed:
+//   after A_i  the loaders issue V(i+1)          (its buffer held V(i-1));
+//   after B_i  they build the table of unit i+2 and issue K(i+2), Q(i+2)
+//              (their buffers held K(i), Q(i)).
+// Copies are issued in the order K0 Q0 V0 K1 Q1 | V(i+1) K(i+2) Q(i+2) ...,
+// and a loader issues nothing else, so each wait is an exact vmcnt count
+// (vector memory operations of a wave complete in order): before A_i at most
+// V(i) and K/Q(i+1) may be outstanding, before B_i at most K/Q(i+1) and V(i+1).
+//
+// Compute waves: between A_i and B_i, S^T = K Q^T, bias, mask and softmax,
+// leaving bf16 P in registers; between B_i and A_(i+1), O^T = V^T P^T, then
+// the O tile goes to the wave's rows of an LDS staging buffer and leaves as
+// whole 128-byte token rows through buffer stores (lanes of pad queries store
+// out of range, which the buffer range check drops).  The two roles run
+// separate loops with the same number of barriers, and the barriers fence LDS
+// only: a full fence would wait for every store in flight.  The PV product
+// reads V^T fragments with ds_read_b64_tr_b16, which hands lane i of each
+// 16-lane group element i of the 4 rows its group addresses.
 // --------------------------------------------------------------------------
-constexpr int kStages = 3;
-constexpr int kQSlots = 2;
-constexpr int kTableSlots = 3;
+constexpr int kBufs = 2;       // buffers each of K, Q and V
+constexpr int kTableSlots = 3; // token tables of units i, i+1, i+2
 constexpr int kLoaders = 2;
+constexpr int kStreamMaxTiles = 9;
 
 struct StreamLds {
     int NP, TSP;   // padded keys; bias table entries per head slice (multiple of 64)
     bool bias_resident;
-    size_t stage_bytes, q0, q_bytes, bias, kb4, slot0, slot_bytes, total;
-    // stage s: K at s * stage_bytes, V at s * stage_bytes + NP * D * 2; Q slot s at q0 + s * q_bytes
+    size_t tb;     // bytes of one [NP][D] bf16 buffer
+    size_t k0, q0, v0, o0, bias, kb4, slot0, slot_bytes, total;
 };
 
 __host__ __device__ inline StreamLds stream_lds_with(const Geometry& g, bool bias_resident) {
@@ -726,11 +745,13 @@ __host__ __device__ inline StreamLds stream_lds_with(const Geometry& g, bool bia
     L.NP = (g.N + 15) / 16 * 16;
     L.TSP = (g.table_size + 63) / 64 * 64;
     L.bias_resident = bias_resident;
-    L.q_bytes = (size_t)L.NP * g.head_dim * 2;
-    L.stage_bytes = 2 * L.q_bytes;
-    L.q0 = kStages * L.stage_bytes;
-    L.bias = L.q0 + kQSlots * L.q_bytes;
-    L.kb4 = L.bias + (size_t)(bias_resident ? g.heads : kStages) * L.TSP * 4;
+    L.tb = (size_t)L.NP * g.head_dim * 2;
+    L.k0 = 0;
+    L.q0 = L.k0 + kBufs * L.tb;
+    L.v0 = L.q0 + kBufs * L.tb;
+    L.o0 = L.v0 + kBufs * L.tb;
+    L.bias = L.o0 + L.tb;
+    L.kb4 = L.bias + (size_t)(bias_resident ? g.heads : kTableSlots) * L.TSP * 4;
     L.slot0 = L.kb4 + (size_t)L.NP * 4;
     L.slot_bytes = (size_t)L.NP * 4; // one packed word per token: (row + 1) | mask field << 28
     L.total = L.slot0 + kTableSlots * L.slot_bytes;
@@ -778,6 +799,18 @@ __device__ inline void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The same barrier for the loader waves, whose only LDS writes are table
+// words (covered by the lgkmcnt wait) and copies they have already waited for
+// with vmcnt.  A release fence here would make the compiler wait for every
+// LDS copy in flight (vmcnt(0)), which drains the pipeline; the empty asm
+// statements only keep the compiler from moving LDS accesses across it.
+__device__ inline void loader_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // unit -> (window, head, batch item, window coordinates)
 struct Unit {
     uint32_t wi;
@@ -811,11 +844,15 @@ __host__ __device__ inline LoaderRange loader_range(const Geometry& g, const Str
     return LoaderRange{ncopy * j / kLoaders, ncopy * (j + 1) / kLoaders};
 }
 
-// Copies loader wave j issues with a unit's K and V: K and V of its rows,
-// plus the streamed bias slice for loader 0.
-__host__ __device__ inline int loader_kv_copies(const Geometry& g, const StreamLds& L, int j) {
+// Copies loader wave j issues with a unit's K and Q (plus the streamed bias
+// slice for loader 0), and with its V.
+__host__ __device__ inline int loader_kq_copies(const Geometry& g, const StreamLds& L, int j) {
     const LoaderRange R = loader_range(g, L, j);
     return 2 * (R.c1 - R.c0) + (j == 0 && !L.bias_resident ? L.TSP / 64 : 0);
+}
+__host__ __device__ inline int loader_v_copies(const Geometry& g, const StreamLds& L, int j) {
+    const LoaderRange R = loader_range(g, L, j);
+    return R.c1 - R.c0;
 }
 
 // Table words of loader j's rows of unit uu, into slot s: (source row + 1, 0
@@ -857,7 +894,7 @@ __device__ inline void stream_table(const Geometry& g, const StreamLds& L, unsig
 // Most 1 KB copies per tensor a loader wave issues for a unit.
 template <int D, int KT_FIXED>
 constexpr int loader_max_copies() {
-    return ((KT_FIXED > 0 ? KT_FIXED : 16) * 16 * (D / 8) / 64 + kLoaders - 1) / kLoaders;
+    return ((KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles) * 16 * (D / 8) / 64 + kLoaders - 1) / kLoaders;
 }
 
 // Source element offsets (within a head's slice of a token row) of loader j's
@@ -865,14 +902,15 @@ constexpr int loader_max_copies() {
 // 128-byte token row, the source chunk chosen so that the row lands swizzled.
 // Pad rows copy row 0 (finite values that get weight exactly 0, or outputs
 // that are never stored).  All table reads are issued before any is used.
-template <int D, int MAXC>
+template <int D, int MAXC, bool VROWS>
 __device__ inline void stream_offsets(const Geometry& g, const StreamLds& L, const unsigned char* smem, LoaderRange R,
                                       int lane, int s, uint32_t (&off)[MAXC]) {
     constexpr int CH = D / 8;
     constexpr int RPC = 64 / CH;
     const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
-    const int m0 = lane / CH; // row within a copy
-    const int ch = (lane % CH) ^ ((m0 / (128 / (D * 2))) % CH); // RPC is a multiple of 128 / (2 D)
+    const int m0 = lane / CH; // row within a copy; RPC is a multiple of the swizzle periods
+    // the logical chunk whose slot is this lane's (both swizzles are XORs, so self-inverse)
+    const int ch = VROWS ? v_slot<D>(m0, lane % CH) : k_slot<D>(m0, lane % CH);
     int r1[MAXC];
 #pragma unroll
     for (int i = 0; i < MAXC; i++) r1[i] = R.c0 + i < R.c1 ? tw[(R.c0 + i) * RPC + m0] & kRowMask : 0;
@@ -882,7 +920,7 @@ __device__ inline void stream_offsets(const Geometry& g, const StreamLds& L, con
 }
 
 template <int D, int MAXC>
-__device__ inline void stream_issue(const StreamLds& L, LoaderRange R, int lane, int hh, const uint32_t (&off)[MAXC],
+__device__ inline void stream_issue(LoaderRange R, int hh, const uint32_t (&off)[MAXC],
                                     const uint16_t* __restrict__ src, unsigned char* dst) {
     const uint16_t* sh = src + hh * D;
 #pragma unroll
@@ -892,21 +930,20 @@ __device__ inline void stream_issue(const StreamLds& L, LoaderRange R, int lane,
                                              0);
 }
 
-// K and V of unit uu (table in slot s) into stage st, and for loader 0 the
-// streamed bias.
+// K and Q of unit uu (table in slot s) into buffer pair b, and for loader 0
+// the streamed bias slice into bias slot s.
 template <int D, int MAXC>
-__device__ inline void stream_copy_kv(const Geometry& g, const StreamLds& L, unsigned char* smem, int j,
-                                      LoaderRange R, int lane, uint32_t uu, int s, int st,
-                                      const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+__device__ inline void stream_copy_kq(const Geometry& g, const StreamLds& L, unsigned char* smem, int j,
+                                      LoaderRange R, int lane, uint32_t uu, int s, int b,
+                                      const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                       const float* __restrict__ table) {
     const int hh = (int)(uu - fdiv(g.fd_heads, uu) * (uint32_t)g.heads);
-    unsigned char* kd = smem + st * L.stage_bytes;
     uint32_t off[MAXC];
-    stream_offsets<D, MAXC>(g, L, smem, R, lane, s, off);
-    stream_issue<D, MAXC>(L, R, lane, hh, off, k, kd);
-    stream_issue<D, MAXC>(L, R, lane, hh, off, v, kd + L.q_bytes);
+    stream_offsets<D, MAXC, false>(g, L, smem, R, lane, s, off);
+    stream_issue<D, MAXC>(R, hh, off, k, smem + L.k0 + b * L.tb);
+    stream_issue<D, MAXC>(R, hh, off, q, smem + L.q0 + b * L.tb);
     if (j == 0 && !L.bias_resident) {
-        float* bdst = (float*)(smem + L.bias) + st * L.TSP;
+        float* bdst = (float*)(smem + L.bias) + s * L.TSP;
         for (int jj = 0; jj * 64 < L.TSP; jj++) {
             const int i = jj * 64 + lane;
             const float* src = table + (i < g.table_size ? i * g.heads + hh : 0);
@@ -915,202 +952,257 @@ __device__ inline void stream_copy_kv(const Geometry& g, const StreamLds& L, uns
     }
 }
 
-// Q of unit uu (table in slot s) into LDS at dst.
+// V of unit uu (table in slot s) into buffer b.
 template <int D, int MAXC>
-__device__ inline void stream_copy_q(const Geometry& g, const StreamLds& L, unsigned char* smem, LoaderRange R,
-                                     int lane, uint32_t uu, int s, const uint16_t* __restrict__ q,
-                                     unsigned char* dst) {
+__device__ inline void stream_copy_v(const Geometry& g, const StreamLds& L, unsigned char* smem, LoaderRange R,
+                                     int lane, uint32_t uu, int s, int b, const uint16_t* __restrict__ v) {
     const int hh = (int)(uu - fdiv(g.fd_heads, uu) * (uint32_t)g.heads);
     uint32_t off[MAXC];
-    stream_offsets<D, MAXC>(g, L, smem, R, lane, s, off);
-    stream_issue<D, MAXC>(L, R, lane, hh, off, q, dst);
+    stream_offsets<D, MAXC, true>(g, L, smem, R, lane, s, off);
+    stream_issue<D, MAXC>(R, hh, off, v, smem + L.v0 + b * L.tb);
 }
 
-// One unit's attention for the query tiles of this wave: Q in slot qs, K, V
-// (and streamed bias) in stage st, table in slot s; O leaves through ors.
-template <int D, int NWAVES, int QT_MAX, int KT_FIXED, bool BIAS_VEC>
-__device__ inline void stream_compute(const Geometry& g, const StreamLds& L, unsigned char* smem,
-                                      __amdgpu_buffer_rsrc_t ors, int wave, int lane, int staged, uint32_t uu,
-                                      int s, int st, int qs) {
+// What a compute wave carries from the first half of a unit to the second.
+template <int KT>
+struct TileState {
+    unsigned pk[KT][2]; // bf16 P: 4 keys per tile in two dwords
+    int n, r;           // query index in the window; its source row (or -1)
+};
+
+// Byte offsets, within a head's bias slice, of the biases a lane adds: they
+// depend only on the positions of its query and keys inside the window, so a
+// compute wave computes them once.  With BIAS_VEC the 4 keys of a lane are
+// neighbours in one window row and one offset (of the lowest of 4 consecutive
+// entries) serves them; otherwise there is one offset per key.
+template <int KT_FIXED, bool BIAS_VEC>
+struct BiasOffsets {
+    int off[(KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles)][BIAS_VEC ? 1 : 4];
+};
+
+template <int KT_FIXED, bool BIAS_VEC>
+__device__ inline void bias_offsets(const Geometry& g, const StreamLds& L, const unsigned char* smem, int qt,
+                                    int lane, BiasOffsets<KT_FIXED, BIAS_VEC>& bo) {
+    constexpr int KB = KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles;
+    const int col = lane & 15, grp = lane >> 4;
+    const int* kb4 = (const int*)(smem + L.kb4);
+    const int n = qt * 16 + col;
+    int qb4;
+    if (n < g.N) {
+        int lt, ly, lx;
+        local_coords(g, n, lt, ly, lx);
+        qb4 = (((lt * g.tdy + ly) * g.tdx + lx) + g.c0) * 4;
+    } else {
+        qb4 = (g.table_size - 1) * 4; // largest qb keeps qb - kb inside the table
+    }
+#pragma unroll
+    for (int kt = 0; kt < KB; kt++) {
+        const int key0 = kt * 16 + grp * 4; // kb4 has NP entries, padded keys included
+        if (KT_FIXED == 0 && key0 >= L.NP) {
+#pragma unroll
+            for (int i = 0; i < (BIAS_VEC ? 1 : 4); i++) bo.off[kt][i] = 0;
+        } else if (BIAS_VEC) {
+            bo.off[kt][0] = qb4 - kb4[key0] - 12; // entries qb - kb0 - 3 .. qb - kb0
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) bo.off[kt][i] = qb4 - kb4[key0 + i];
+        }
+    }
+}
+
+// First half of unit uu for this wave's tile qt: S^T = K Q^T, logits, mask and
+// softmax, from K, Q in buffer b and the table in slot s.
+template <int D, int KT_FIXED, bool BIAS_VEC>
+__device__ inline void stream_qk(const Geometry& g, const StreamLds& L, const unsigned char* smem, int qt, int lane,
+                                 uint32_t uu, int s, int b, const BiasOffsets<KT_FIXED, BIAS_VEC>& bo,
+                                 TileState<(KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles)>& ts) {
     constexpr int KSTEPS = D / 32;
+    constexpr int KB = KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles;
+    const int col = lane & 15, grp = lane >> 4;
+    const int N = g.N;
+    const int KT = KT_FIXED > 0 ? KT_FIXED : L.NP / 16;
+    const Unit U = decode_unit(g, uu);
+    const bool masked_window = window_maybe_masked(g, U.wc);
+    const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
+    const uint16_t* Ks = (const uint16_t*)(smem + L.k0 + b * L.tb);
+    const uint16_t* Qs = (const uint16_t*)(smem + L.q0 + b * L.tb);
+    const unsigned char* bias_bytes = smem + L.bias + (size_t)(L.bias_resident ? U.h : s) * L.TSP * 4;
+    const int n = qt * 16 + col;
+    const int qword = tw[n];
+    const int qreg = (unsigned)qword >> 28;
+    ts.n = n;
+    ts.r = (qword & kRowMask) - 1;
+    // every bias this lane adds (addresses need no LDS reads); with 64-wide heads
+    // they are all read before the products, with 32-wide heads tile by tile
+    constexpr bool kBiasEarly = D == 64;
+    float bias[KB][4];
+#pragma unroll
+    for (int kt = 0; kt < KB; kt++) {
+        if (kBiasEarly && (KT_FIXED > 0 || kt < KT)) {
+            if (BIAS_VEC) {
+                const float* bp = (const float*)(bias_bytes + bo.off[kt][0]);
+                bias[kt][3] = bp[0];
+                bias[kt][2] = bp[1];
+                bias[kt][1] = bp[2];
+                bias[kt][0] = bp[3];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; i++) bias[kt][i] = *(const float*)(bias_bytes + bo.off[kt][BIAS_VEC ? 0 : i]);
+            }
+        }
+    }
+    bf16x8 qf[KSTEPS]; // B operand: query n, d = 32 ks + 8 grp + 0..7
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ks++)
+        qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Qs + n * D + k_slot<D>(n, ks * 4 + grp) * 8));
+    f32x4 sc[KB];
+#pragma unroll
+    for (int kt = 0; kt < KB; kt++) {
+        if (KT_FIXED > 0 || kt < KT) {
+            const int krow = kt * 16 + col;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ks++) {
+                const bf16x8 a =
+                    __builtin_bit_cast(bf16x8, *(const u32x4*)(Ks + krow * D + k_slot<D>(krow, ks * 4 + grp) * 8));
+                acc = mfma32(a, qf[ks], acc);
+            }
+            sc[kt] = acc;
+        }
+    }
+#pragma unroll
+    for (int kt = 0; kt < KB; kt++) {
+        if (KT_FIXED > 0 || kt < KT) {
+            if (!kBiasEarly) {
+                if (BIAS_VEC) {
+                    const float* bp = (const float*)(bias_bytes + bo.off[kt][0]);
+                    bias[kt][3] = bp[0];
+                    bias[kt][2] = bp[1];
+                    bias[kt][1] = bp[2];
+                    bias[kt][0] = bp[3];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        bias[kt][i] = *(const float*)(bias_bytes + bo.off[kt][BIAS_VEC ? 0 : i]);
+                }
+            }
+            // logits, natural units: scale * q.k + bias
+            sc[kt] = f32x4{fmaf(sc[kt][0], g.scale, bias[kt][0]), fmaf(sc[kt][1], g.scale, bias[kt][1]),
+                           fmaf(sc[kt][2], g.scale, bias[kt][2]), fmaf(sc[kt][3], g.scale, bias[kt][3])};
+        } else {
+            sc[kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        }
+    }
+    // the mask, on windows that can hold hidden keys (all tiles) or whose last
+    // tile runs past N (that tile only); a separate loop, so that windows
+    // without hidden keys read no mask words at all
+    if (masked_window || KT * 16 > N) {
+#pragma unroll
+        for (int kt = 0; kt < KB; kt++) {
+            const int key0 = kt * 16;
+            if ((KT_FIXED > 0 || kt < KT) && (masked_window || key0 + 16 > N)) {
+                const int4 kr4 = *(const int4*)(tw + key0 + grp * 4);
+                sc[kt][0] = ((unsigned)kr4.x >> 28) == (unsigned)qreg ? sc[kt][0] : -INFINITY;
+                sc[kt][1] = ((unsigned)kr4.y >> 28) == (unsigned)qreg ? sc[kt][1] : -INFINITY;
+                sc[kt][2] = ((unsigned)kr4.z >> 28) == (unsigned)qreg ? sc[kt][2] : -INFINITY;
+                sc[kt][3] = ((unsigned)kr4.w >> 28) == (unsigned)qreg ? sc[kt][3] : -INFINITY;
+            }
+        }
+    }
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KB; kt++)
+        bmax = fmaxf(bmax, fmaxf(fmaxf(sc[kt][0], sc[kt][1]), fmaxf(sc[kt][2], sc[kt][3])));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    const float mc = (bmax == -INFINITY ? 0.f : bmax) * kLog2e;
+#pragma unroll
+    for (int kt = 0; kt < KB; kt++) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], kLog2e, -mc));
+        ts.pk[kt][0] = pack_bf16x2(p[0], p[1]);
+        ts.pk[kt][1] = pack_bf16x2(p[2], p[3]);
+    }
+}
+
+// Second half: O^T = V^T P^T from V in buffer b, divide by the sum, stage the O
+// tile in the wave's rows of the LDS staging buffer and store whole token rows.
+template <int D, int KT_FIXED>
+__device__ inline void stream_pv(const Geometry& g, const StreamLds& L, unsigned char* smem,
+                                 __amdgpu_buffer_rsrc_t ors, int qt, int lane, int staged, uint32_t uu, int s, int b,
+                                 const TileState<(KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles)>& ts) {
     constexpr int DT = D / 16;
     constexpr int CH = D / 8;
-    constexpr int KB = (KT_FIXED > 0 && KT_FIXED <= kKeyTilesPerBlock) ? KT_FIXED : kKeyTilesPerBlock;
-    constexpr int KB_UNROLL = KT_FIXED > 0 ? KT_FIXED / KB : 1;
+    constexpr int KB = KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles;
     const int col = lane & 15, grp = lane >> 4;
     const int N = g.N;
     const int KT = KT_FIXED > 0 ? KT_FIXED : L.NP / 16;
     const unsigned one2 = 0x3F803F80u; // two bf16 ones
     const bf16x8 ones8 = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
-    const Unit U = decode_unit(g, uu);
-    const bool masked_window = window_maybe_masked(g, U.wc);
     const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
-    const int* kb4 = (const int*)(smem + L.kb4);
-    const uint16_t* Ks = (const uint16_t*)(smem + st * L.stage_bytes);
-    const unsigned char* Vb = smem + st * L.stage_bytes + L.q_bytes;
-    uint16_t* Qs = (uint16_t*)(smem + L.q0 + qs * L.q_bytes);
-    const unsigned char* bias_bytes =
-        smem + L.bias + (size_t)(L.bias_resident ? U.h : st) * L.TSP * 4;
+    const unsigned char* Vb = smem + L.v0 + b * L.tb;
+    uint16_t* Os = (uint16_t*)(smem + L.o0);
+    f32x4 o[DT], osum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < QT_MAX; t++) {
-        const int qt = wave + t * NWAVES;
-        if (KT_FIXED == 0 && qt >= KT) break;
-        const int n = qt * 16 + col;
-        const int qword = tw[n];
-        const int qreg = (unsigned)qword >> 28;
-        const int r = (qword & kRowMask) - 1;
-        int qb4;
-        if (n < N) {
-            int lt, ly, lx;
-            local_coords(g, n, lt, ly, lx);
-            qb4 = (((lt * g.tdy + ly) * g.tdx + lx) + g.c0) * 4;
-        } else {
-            qb4 = (g.table_size - 1) * 4;
+    for (int dt = 0; dt < DT; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // V^T fragment of key tile t: lane (col, grp) gets keys 16t + 4grp + 0..3 at
+    // d = 16 dt + col; lane s of the group points at row 16t + 4grp + s/4, d 16dt + 4(s%4)
+    auto vt_frag = [&](int t0, int dt) __attribute__((always_inline)) {
+        const int row = t0 * 16 + grp * 4 + (col >> 2);
+        const int d = dt * 16 + (col & 3) * 4;
+        const unsigned char* p = Vb + row * (D * 2) + v_slot<D>(row, d >> 3) * 16 + (d & 7) * 2;
+        const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)p);
+        return __builtin_bit_cast(u32x2, x);
+    };
+#pragma unroll
+    for (int kt = 0; kt < KB; kt += 2) {
+        const bool pair = kt + 1 < KB && (KT_FIXED > 0 || kt + 1 < KT);
+        if (pair) {
+            const bf16x8 bop =
+                __builtin_bit_cast(bf16x8, u32x4{ts.pk[kt][0], ts.pk[kt][1], ts.pk[kt + 1][0], ts.pk[kt + 1][1]});
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const u32x2 lo = vt_frag(kt, dt);
+                const u32x2 hi = vt_frag(kt + 1, dt);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                o[dt] = mfma32(a, bop, o[dt]);
+            }
+            osum = mfma32(ones8, bop, osum);
+        } else if (KT_FIXED > 0 || kt < KT) {
+            // a lone last tile: the same 32-deep product with the second key
+            // tile's slots zero, so every accumulation chain uses one opcode
+            const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{ts.pk[kt][0], ts.pk[kt][1], 0u, 0u});
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const u32x2 lo = vt_frag(kt, dt);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], 0u, 0u});
+                o[dt] = mfma32(a, bop, o[dt]);
+            }
+            osum = mfma32(ones8, bop, osum);
         }
-        const unsigned char* qbias = bias_bytes + qb4;
-        bf16x8 qf[KSTEPS]; // B operand: query n, d = 32 ks + 8 grp + 0..7
+    }
+    // O tile into the staging rows of this tile (same swizzle), then out as whole token rows
+    const int n = ts.n;
+    const float inv = ts.r >= 0 ? __builtin_amdgcn_rcpf(osum[0]) : 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ks++)
-            qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Qs + n * D + k_slot<D>(n, ks * 4 + grp) * 8));
-        f32x4 o[DT], osum = {0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; dt++) {
+        const u32x2 w = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
+        const int c = dt * 2 + (grp >> 1); // 16-byte chunk of d = 16 dt + 4 grp
+        *(u32x2*)(Os + n * D + k_slot<D>(n, c) * 8 + (grp & 1) * 4) = w;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): the tile is written
+    __builtin_amdgcn_wave_barrier();
+    const Unit U = decode_unit(g, uu);
+    constexpr int RPI = 64 / CH; // token rows per store instruction
 #pragma unroll
-        for (int dt = 0; dt < DT; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float mrun = -INFINITY;
-
-#pragma unroll KB_UNROLL
-        for (int kb0 = 0; kb0 < (KT_FIXED > 0 ? KT_FIXED : KT); kb0 += KB) {
-            f32x4 sc[KB];
-#pragma unroll
-            for (int kt = 0; kt < KB; kt++) {
-                const int key0 = (kb0 + kt) * 16;
-                if (KT_FIXED > 0 || kb0 + kt < KT) {
-                    const int krow = key0 + col;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KSTEPS; ks++) {
-                        const bf16x8 a = __builtin_bit_cast(
-                            bf16x8, *(const u32x4*)(Ks + krow * D + k_slot<D>(krow, ks * 4 + grp) * 8));
-                        acc = mfma32(a, qf[ks], acc);
-                    }
-                    sc[kt] = acc;
-                }
-            }
-            float bmax = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < KB; kt++) {
-                const int key0 = (kb0 + kt) * 16;
-                if (KT_FIXED > 0 || kb0 + kt < KT) {
-                    float bb[4];
-                    if (BIAS_VEC) {
-                        const float* bp = (const float*)(qbias - kb4[key0 + grp * 4]) - 3;
-                        bb[3] = bp[0];
-                        bb[2] = bp[1];
-                        bb[1] = bp[2];
-                        bb[0] = bp[3];
-                    } else {
-                        const int4 kq = *(const int4*)(kb4 + key0 + grp * 4);
-                        bb[0] = *(const float*)(qbias - kq.x);
-                        bb[1] = *(const float*)(qbias - kq.y);
-                        bb[2] = *(const float*)(qbias - kq.z);
-                        bb[3] = *(const float*)(qbias - kq.w);
-                    }
-                    // logits, natural units: scale * q.k + bias
-                    f32x4 lg = {fmaf(sc[kt][0], g.scale, bb[0]), fmaf(sc[kt][1], g.scale, bb[1]),
-                                fmaf(sc[kt][2], g.scale, bb[2]), fmaf(sc[kt][3], g.scale, bb[3])};
-                    if (masked_window || key0 + 16 > N) {
-                        const int4 kr4 = *(const int4*)(tw + key0 + grp * 4);
-                        lg[0] = ((unsigned)kr4.x >> 28) == (unsigned)qreg ? lg[0] : -INFINITY;
-                        lg[1] = ((unsigned)kr4.y >> 28) == (unsigned)qreg ? lg[1] : -INFINITY;
-                        lg[2] = ((unsigned)kr4.z >> 28) == (unsigned)qreg ? lg[2] : -INFINITY;
-                        lg[3] = ((unsigned)kr4.w >> 28) == (unsigned)qreg ? lg[3] : -INFINITY;
-                    }
-                    sc[kt] = lg;
-                    bmax = fmaxf(bmax, fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
-                } else {
-                    sc[kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-                }
-            }
-            bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-            bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-            const float mnew = fmaxf(mrun, bmax);
-            const float mc = (mnew == -INFINITY ? 0.f : mnew) * kLog2e;
-            if (kb0 > 0) {
-                const float alpha = __builtin_amdgcn_exp2f(mrun * kLog2e - mc);
-                osum *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT; dt++) o[dt] *= alpha;
-            }
-            mrun = mnew;
-
-            unsigned pk[KB][2];
-#pragma unroll
-            for (int kt = 0; kt < KB; kt++) {
-                float p[4];
-#pragma unroll
-                for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], kLog2e, -mc));
-                pk[kt][0] = pack_bf16x2(p[0], p[1]);
-                pk[kt][1] = pack_bf16x2(p[2], p[3]);
-            }
-
-            // V^T fragment of key tile t: lane (col, grp) gets keys 16t + 4grp + 0..3 at
-            // d = 16 dt + col; lane s of the group points at row 16t + 4grp + s/4, d 16dt + 4(s%4)
-            auto vt_frag = [&](int t0, int dt) __attribute__((always_inline)) {
-                const int row = t0 * 16 + grp * 4 + (col >> 2);
-                const int d = dt * 16 + (col & 3) * 4;
-                const int chunk = (d >> 3) ^ ((row / (128 / (D * 2))) % CH);
-                const unsigned char* p = Vb + row * (D * 2) + chunk * 16 + (d & 7) * 2;
-                const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)p);
-                return __builtin_bit_cast(u32x2, x);
-            };
-#pragma unroll
-            for (int kt = 0; kt < KB; kt += 2) {
-                const int t0 = kb0 + kt;
-                const bool pair = kt + 1 < KB && (KT_FIXED > 0 || t0 + 1 < KT);
-                if (pair) {
-                    const bf16x8 bop =
-                        __builtin_bit_cast(bf16x8, u32x4{pk[kt][0], pk[kt][1], pk[kt + 1][0], pk[kt + 1][1]});
-#pragma unroll
-                    for (int dt = 0; dt < DT; dt++) {
-                        const u32x2 lo = vt_frag(t0, dt);
-                        const u32x2 hi = vt_frag(t0 + 1, dt);
-                        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                        o[dt] = mfma32(a, bop, o[dt]);
-                    }
-                    osum = mfma32(ones8, bop, osum);
-                } else if (KT_FIXED > 0 || t0 < KT) {
-                    const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{pk[kt][0], pk[kt][1], 0u, 0u});
-#pragma unroll
-                    for (int dt = 0; dt < DT; dt++) {
-                        const u32x2 lo = vt_frag(t0, dt);
-                        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], 0u, 0u});
-                        o[dt] = mfma32(a, bop, o[dt]);
-                    }
-                    osum = mfma32(ones8, bop, osum);
-                }
-            }
-        }
-
-        // O tile into this tile's Q rows (same swizzle), then out as whole token rows
-        const float inv = r >= 0 ? __builtin_amdgcn_rcpf(osum[0]) : 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; dt++) {
-            const u32x2 w = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
-            const int c = dt * 2 + (grp >> 1); // 16-byte chunk of d = 16 dt + 4 grp
-            *(u32x2*)(Qs + n * D + k_slot<D>(n, c) * 8 + (grp & 1) * 4) = w;
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): the tile is written
-        __builtin_amdgcn_wave_barrier();
-        constexpr int RPI = 64 / CH; // token rows per store instruction
-#pragma unroll
-        for (int i = 0; i < 16 / RPI; i++) {
-            const int m = qt * 16 + i * RPI + lane / CH, c = lane % CH;
-            const u32x4 val = *(const u32x4*)(Qs + m * D + k_slot<D>(m, c) * 8);
-            const int rm = (tw[m] & kRowMask) - 1;
-            // the real token, or in the staged layout also pad slots (zeros)
-            const int orow = rm >= 0 ? rm : (staged && m < N ? (int)(U.wi * (uint32_t)N + m) : -1);
-            const uint32_t ob = orow >= 0 ? ((uint32_t)orow * (uint32_t)g.row + U.h * D + c * 8) * 2 : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b128(val, ors, ob, 0, 0);
-        }
+    for (int i = 0; i < 16 / RPI; i++) {
+        const int m = qt * 16 + i * RPI + lane / CH, c = lane % CH;
+        const u32x4 val = *(const u32x4*)(Os + m * D + k_slot<D>(m, c) * 8);
+        const int rm = (tw[m] & kRowMask) - 1;
+        // the real token, or in the staged layout also pad slots (zeros)
+        const int orow = rm >= 0 ? rm : (staged && m < N ? (int)(U.wi * (uint32_t)N + m) : -1);
+        const uint32_t ob = orow >= 0 ? ((uint32_t)orow * (uint32_t)g.row + U.h * D + c * 8) * 2 : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(val, ors, ob, 0, 0);
     }
 }
 
@@ -1122,11 +1214,12 @@ __host__ __device__ inline uint64_t stream_tensor_bytes(const Geometry& g, bool 
     return rows * (uint64_t)g.row * 2;
 }
 
-template <int D, int NWAVES, int QT_MAX, int KT_FIXED, bool BIAS_VEC>
+template <int D, int NWAVES, int KT_FIXED, bool BIAS_VEC>
 __global__ __launch_bounds__((NWAVES + kLoaders) * 64) void attn_bf16_stream_kernel(
     Geometry g, int staged, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ table, uint16_t* __restrict__ out) {
     constexpr int THREADS = (NWAVES + kLoaders) * 64;
+    static_assert(KT_FIXED <= NWAVES, "one query tile per compute wave");
     extern __shared__ __align__(16) unsigned char smem[];
     const StreamLds L = stream_lds(g);
     float* bias_lds = (float*)(smem + L.bias);
@@ -1159,48 +1252,56 @@ __global__ __launch_bounds__((NWAVES + kLoaders) * 64) void attn_bf16_stream_ker
     }
 
     if (wave >= NWAVES) {
-        // ---- loader waves.  Issue order: K/V(0), Q(0), K/V(1) | Q(i+1), K/V(i+2) after barrier i
+        // ---- loader waves
         constexpr int MAXC = loader_max_copies<D, KT_FIXED>();
         const int j = wave - NWAVES;
         const LoaderRange R = loader_range(g, L, j);
-        const int kv_copies = loader_kv_copies(g, L, j);
+        const int nkq = loader_kq_copies(g, L, j), nv = loader_v_copies(g, L, j);
         const uint32_t u1 = u0 + per;
         stream_table<D>(g, L, smem, R, lane, u0, 0, staged);
-        stream_copy_kv<D, MAXC>(g, L, smem, j, R, lane, u0, 0, 0, k, v, table);
-        stream_copy_q<D, MAXC>(g, L, smem, R, lane, u0, 0, q, smem + L.q0);
+        stream_copy_kq<D, MAXC>(g, L, smem, j, R, lane, u0, 0, 0, q, k, table);
+        stream_copy_v<D, MAXC>(g, L, smem, R, lane, u0, 0, 0, v);
         if (u1 < uend) {
             stream_table<D>(g, L, smem, R, lane, u1, 1, staged);
-            stream_copy_kv<D, MAXC>(g, L, smem, j, R, lane, u1, 1, 1, k, v, table);
+            stream_copy_kq<D, MAXC>(g, L, smem, j, R, lane, u1, 1, 1, q, k, table);
         }
-        lds_barrier(); // prologue: window-independent tables and the first token tables
+        loader_barrier(); // prologue: window-independent tables and the first token tables
         uint32_t u = u0;
         for (int iter = 0;; iter++) {
             const uint32_t un = u + per, un2 = un + per;
-            // unit u's K, V and Q have landed once at most the K/V copies of unit un remain
-            wait_vmcnt_le(un < uend ? kv_copies : 0);
-            lds_barrier();
-            if (un < uend)
-                stream_copy_q<D, MAXC>(g, L, smem, R, lane, un, (iter + 1) % kTableSlots, q,
-                                       smem + L.q0 + ((iter + 1) % kQSlots) * L.q_bytes);
+            const bool has_next = un < uend;
+            // A: K, Q of unit u have landed once at most V(u) and K/Q(un) remain
+            wait_vmcnt_le(nv + (has_next ? nkq : 0));
+            loader_barrier();
+            if (has_next) stream_copy_v<D, MAXC>(g, L, smem, R, lane, un, (iter + 1) % kTableSlots, (iter + 1) % kBufs, v);
+            // B: V of unit u has landed once at most K/Q(un) and V(un) remain
+            wait_vmcnt_le(has_next ? nkq + nv : 0);
+            loader_barrier();
             if (un2 < uend) {
                 stream_table<D>(g, L, smem, R, lane, un2, (iter + 2) % kTableSlots, staged);
-                stream_copy_kv<D, MAXC>(g, L, smem, j, R, lane, un2, (iter + 2) % kTableSlots, (iter + 2) % kStages,
-                                        k, v, table);
+                stream_copy_kq<D, MAXC>(g, L, smem, j, R, lane, un2, (iter + 2) % kTableSlots, iter % kBufs, q, k,
+                                        table);
             }
-            if (un >= uend) break;
+            if (!has_next) break;
             u = un;
         }
     } else {
         // ---- compute waves
         const __amdgpu_buffer_rsrc_t ors =
             __builtin_amdgcn_make_buffer_rsrc((void*)out, 0, (int)stream_tensor_bytes(g, staged), kBufferWord3);
+        const int KT = KT_FIXED > 0 ? KT_FIXED : NP / 16;
+        const bool active = wave < KT;
+        TileState<(KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles)> ts;
+        BiasOffsets<KT_FIXED, BIAS_VEC> bo;
         lds_barrier(); // prologue
+        if (active) bias_offsets<KT_FIXED, BIAS_VEC>(g, L, smem, wave, lane, bo);
         uint32_t u = u0;
         for (int iter = 0;; iter++) {
-            lds_barrier();
-            stream_compute<D, NWAVES, QT_MAX, KT_FIXED, BIAS_VEC>(g, L, smem, ors, wave, lane, staged, u,
-                                                                  iter % kTableSlots, iter % kStages,
-                                                                  iter % kQSlots);
+            const int s = iter % kTableSlots, b = iter % kBufs;
+            lds_barrier(); // A
+            if (active) stream_qk<D, KT_FIXED, BIAS_VEC>(g, L, smem, wave, lane, u, s, b, bo, ts);
+            lds_barrier(); // B
+            if (active) stream_pv<D, KT_FIXED>(g, L, smem, ors, wave, lane, staged, u, s, b, ts);
             u += per;
             if (u >= uend) break;
         }
@@ -1236,12 +1337,10 @@ static Bf16Variant bf16_variant_b(int KT) {
 template <int D, bool BV>
 static Bf16Variant stream_variant_b(int KT) {
     switch (KT) {
-    case 4: return {attn_bf16_stream_kernel<D, 4, 1, 4, BV>, 4};
-    case 7: return {attn_bf16_stream_kernel<D, 7, 1, 7, BV>, 7};
-    case 9: return {attn_bf16_stream_kernel<D, 9, 1, 9, BV>, 9};
-    default: // up to 16 tiles (larger windows take the block schedule)
-        if (KT <= 8) return {attn_bf16_stream_kernel<D, 8, 1, 0, BV>, 8};
-        return {attn_bf16_stream_kernel<D, 8, 2, 0, BV>, 8};
+    case 4: return {attn_bf16_stream_kernel<D, 4, 4, BV>, 4};
+    case 7: return {attn_bf16_stream_kernel<D, 7, 7, BV>, 7};
+    case 9: return {attn_bf16_stream_kernel<D, 9, 9, BV>, 9};
+    default: return {attn_bf16_stream_kernel<D, kStreamMaxTiles, 0, BV>, kStreamMaxTiles};
     }
 }
 
@@ -1261,7 +1360,7 @@ bool bf16_stream_fits(const Geometry& g) {
     const int64_t wrows = g.windows * g.N;
     const int KT = (g.N + 15) / 16;
     // rows + 1 fit the packed table word; buffer offsets of both layouts stay below 2^31
-    return stream_lds(g).total <= (size_t)kLdsBytes && KT <= 16 &&
+    return stream_lds(g).total <= (size_t)kLdsBytes && KT <= kStreamMaxTiles &&
            (rows > wrows ? rows : wrows) < kRowMask && stream_tensor_bytes(g, false) < kOutOfRange &&
            stream_tensor_bytes(g, true) < kOutOfRange;
 }
