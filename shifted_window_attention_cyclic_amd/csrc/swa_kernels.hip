@@ -730,7 +730,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 // --------------------------------------------------------------------------
 constexpr int kBufs = 2;       // buffers each of K, Q and V
 constexpr int kTableSlots = 3; // token tables of units i, i+1, i+2
-constexpr int kLoaders = 2;
+constexpr int kLoaders = 3;
 constexpr int kStreamMaxTiles = 9;
 
 struct StreamLds {
@@ -772,6 +772,7 @@ __host__ __device__ inline StreamLds stream_lds(const Geometry& g) {
 constexpr int kRowMask = (1 << 28) - 1; // packed table word: source row + 1 in bits 0..27
 constexpr uint32_t kOutOfRange = 0x80000000u; // buffer offset past every tensor the schedule takes
 constexpr int kBufferWord3 = 0x00020000;     // raw buffer resource, 32-bit data format
+constexpr int kNonTemporal = 2;              // cache policy of read-once / write-once traffic (nt)
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left unconstrained)
@@ -927,7 +928,7 @@ __device__ inline void stream_issue(LoaderRange R, int hh, const uint32_t (&off)
     for (int i = 0; i < MAXC; i++)
         if (R.c0 + i < R.c1)
             __builtin_amdgcn_global_load_lds((const void*)(sh + off[i]), (lds_void*)(dst + (R.c0 + i) * 1024), 16, 0,
-                                             0);
+                                             kNonTemporal);
 }
 
 // K and Q of unit uu (table in slot s) into buffer pair b, and for loader 0
@@ -1202,7 +1203,7 @@ __device__ inline void stream_pv(const Geometry& g, const StreamLds& L, unsigned
         // the real token, or in the staged layout also pad slots (zeros)
         const int orow = rm >= 0 ? rm : (staged && m < N ? (int)(U.wi * (uint32_t)N + m) : -1);
         const uint32_t ob = orow >= 0 ? ((uint32_t)orow * (uint32_t)g.row + U.h * D + c * 8) * 2 : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b128(val, ors, ob, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(val, ors, ob, 0, kNonTemporal);
     }
 }
 
