@@ -203,6 +203,11 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
             return fail(SWA_ERR_UNSUPPORTED, "window too large for the streaming schedule");
         stream = cfg->schedule == SWA_SCHEDULE_STREAM || (cfg->schedule == SWA_SCHEDULE_AUTO && fits);
         if ((e = swa::bf16_plan(g, stream, &blocks)) != hipSuccess) return fail_hip(e, "occupancy query");
+        if (blocks < 1 && stream && cfg->schedule == SWA_SCHEDULE_AUTO) {
+            // the streaming workgroup cannot be resident: take the per-unit schedule
+            stream = false;
+            if ((e = swa::bf16_plan(g, stream, &blocks)) != hipSuccess) return fail_hip(e, "occupancy query");
+        }
         if (blocks < 1) return fail(SWA_ERR_UNSUPPORTED, "attention kernel does not fit on a compute unit");
     }
 

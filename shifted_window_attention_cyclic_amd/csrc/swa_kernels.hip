@@ -698,7 +698,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 // heads of a few neighbouring windows at a time.
 //
 // A block has one wave per 16-query tile (windows of up to 9 tiles) plus
-// kLoaders loader waves.  Only the loaders read global memory: they build
+// NL loader waves.  Only the loaders read global memory: they build
 // each unit's token table and copy its K, Q and V straight into LDS with
 // global_load_lds (16 bytes per lane, eight lanes per 128-byte token row, so
 // every request is a whole line), [token][d] with 16-byte chunks
@@ -711,8 +711,10 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 // V is in LDS; its K and Q are no longer read).  K, Q and V have two buffers
 // each, so a copy can start 1.5 units before its data is needed:
 //   after A_i  the loaders issue V(i+1)          (its buffer held V(i-1));
-//   after B_i  they build the table of unit i+2 and issue K(i+2), Q(i+2)
-//              (their buffers held K(i), Q(i)).
+//   after B_i  they issue K(i+2), Q(i+2)         (their buffers held K(i), Q(i)).
+// Token tables are built three units ahead and the source offsets of each
+// batch are read from its table while the batch before it is awaited, so the
+// copies leave right after each barrier.
 // Copies are issued in the order K0 Q0 V0 K1 Q1 | V(i+1) K(i+2) Q(i+2) ...,
 // and a loader issues nothing else, so each wait is an exact vmcnt count
 // (vector memory operations of a wave complete in order): before A_i at most
@@ -729,8 +731,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 // 16-lane group element i of the 4 rows its group addresses.
 // --------------------------------------------------------------------------
 constexpr int kBufs = 2;       // buffers each of K, Q and V
-constexpr int kTableSlots = 3; // token tables of units i, i+1, i+2
-constexpr int kLoaders = 3;
+constexpr int kTableSlots = 4; // token tables of units i .. i+3
 constexpr int kStreamMaxTiles = 9;
 
 struct StreamLds {
@@ -840,19 +841,19 @@ struct LoaderRange {
     int c0, c1;
 };
 
-__host__ __device__ inline LoaderRange loader_range(const Geometry& g, const StreamLds& L, int j) {
+__host__ __device__ inline LoaderRange loader_range(const Geometry& g, const StreamLds& L, int j, int nl) {
     const int ncopy = L.NP * (g.head_dim / 8) / 64;
-    return LoaderRange{ncopy * j / kLoaders, ncopy * (j + 1) / kLoaders};
+    return LoaderRange{ncopy * j / nl, ncopy * (j + 1) / nl};
 }
 
 // Copies loader wave j issues with a unit's K and Q (plus the streamed bias
 // slice for loader 0), and with its V.
-__host__ __device__ inline int loader_kq_copies(const Geometry& g, const StreamLds& L, int j) {
-    const LoaderRange R = loader_range(g, L, j);
+__host__ __device__ inline int loader_kq_copies(const Geometry& g, const StreamLds& L, int j, int nl) {
+    const LoaderRange R = loader_range(g, L, j, nl);
     return 2 * (R.c1 - R.c0) + (j == 0 && !L.bias_resident ? L.TSP / 64 : 0);
 }
-__host__ __device__ inline int loader_v_copies(const Geometry& g, const StreamLds& L, int j) {
-    const LoaderRange R = loader_range(g, L, j);
+__host__ __device__ inline int loader_v_copies(const Geometry& g, const StreamLds& L, int j, int nl) {
+    const LoaderRange R = loader_range(g, L, j, nl);
     return R.c1 - R.c0;
 }
 
@@ -893,9 +894,9 @@ __device__ inline void stream_table(const Geometry& g, const StreamLds& L, unsig
 }
 
 // Most 1 KB copies per tensor a loader wave issues for a unit.
-template <int D, int KT_FIXED>
+template <int D, int KT_FIXED, int NL>
 constexpr int loader_max_copies() {
-    return ((KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles) * 16 * (D / 8) / 64 + kLoaders - 1) / kLoaders;
+    return ((KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles) * 16 * (D / 8) / 64 + NL - 1) / NL;
 }
 
 // Source element offsets (within a head's slice of a token row) of loader j's
@@ -931,16 +932,13 @@ __device__ inline void stream_issue(LoaderRange R, int hh, const uint32_t (&off)
                                              kNonTemporal);
 }
 
-// K and Q of unit uu (table in slot s) into buffer pair b, and for loader 0
-// the streamed bias slice into bias slot s.
+// K and Q of a unit of head hh (source offsets off from its table) into
+// buffer pair b, and for loader 0 the streamed bias slice into bias slot s.
 template <int D, int MAXC>
 __device__ inline void stream_copy_kq(const Geometry& g, const StreamLds& L, unsigned char* smem, int j,
-                                      LoaderRange R, int lane, uint32_t uu, int s, int b,
+                                      LoaderRange R, int lane, int hh, const uint32_t (&off)[MAXC], int s, int b,
                                       const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                       const float* __restrict__ table) {
-    const int hh = (int)(uu - fdiv(g.fd_heads, uu) * (uint32_t)g.heads);
-    uint32_t off[MAXC];
-    stream_offsets<D, MAXC, false>(g, L, smem, R, lane, s, off);
     stream_issue<D, MAXC>(R, hh, off, k, smem + L.k0 + b * L.tb);
     stream_issue<D, MAXC>(R, hh, off, q, smem + L.q0 + b * L.tb);
     if (j == 0 && !L.bias_resident) {
@@ -951,16 +949,6 @@ __device__ inline void stream_copy_kq(const Geometry& g, const StreamLds& L, uns
             __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(bdst + jj * 64), 4, 0, 0);
         }
     }
-}
-
-// V of unit uu (table in slot s) into buffer b.
-template <int D, int MAXC>
-__device__ inline void stream_copy_v(const Geometry& g, const StreamLds& L, unsigned char* smem, LoaderRange R,
-                                     int lane, uint32_t uu, int s, int b, const uint16_t* __restrict__ v) {
-    const int hh = (int)(uu - fdiv(g.fd_heads, uu) * (uint32_t)g.heads);
-    uint32_t off[MAXC];
-    stream_offsets<D, MAXC, true>(g, L, smem, R, lane, s, off);
-    stream_issue<D, MAXC>(R, hh, off, v, smem + L.v0 + b * L.tb);
 }
 
 // What a compute wave carries from the first half of a unit to the second.
@@ -1215,11 +1203,11 @@ __host__ __device__ inline uint64_t stream_tensor_bytes(const Geometry& g, bool 
     return rows * (uint64_t)g.row * 2;
 }
 
-template <int D, int NWAVES, int KT_FIXED, bool BIAS_VEC>
-__global__ __launch_bounds__((NWAVES + kLoaders) * 64) void attn_bf16_stream_kernel(
+template <int D, int NWAVES, int NL, int KT_FIXED, bool BIAS_VEC>
+__global__ __launch_bounds__((NWAVES + NL) * 64) void attn_bf16_stream_kernel(
     Geometry g, int staged, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ table, uint16_t* __restrict__ out) {
-    constexpr int THREADS = (NWAVES + kLoaders) * 64;
+    constexpr int THREADS = (NWAVES + NL) * 64;
     static_assert(KT_FIXED <= NWAVES, "one query tile per compute wave");
     extern __shared__ __align__(16) unsigned char smem[];
     const StreamLds L = stream_lds(g);
@@ -1253,36 +1241,47 @@ __global__ __launch_bounds__((NWAVES + kLoaders) * 64) void attn_bf16_stream_ker
     }
 
     if (wave >= NWAVES) {
-        // ---- loader waves
-        constexpr int MAXC = loader_max_copies<D, KT_FIXED>();
+        // ---- loader waves.  Token tables are built three units ahead and the
+        // source offsets of each batch of copies while the previous batch is
+        // awaited, so that after a barrier a loader only issues copies.
+        constexpr int MAXC = loader_max_copies<D, KT_FIXED, NL>();
         const int j = wave - NWAVES;
-        const LoaderRange R = loader_range(g, L, j);
-        const int nkq = loader_kq_copies(g, L, j), nv = loader_v_copies(g, L, j);
-        const uint32_t u1 = u0 + per;
+        const LoaderRange R = loader_range(g, L, j, NL);
+        const int nkq = loader_kq_copies(g, L, j, NL), nv = loader_v_copies(g, L, j, NL);
+        auto head = [&](uint32_t uu) { return (int)(uu - fdiv(g.fd_heads, uu) * (uint32_t)g.heads); };
+        uint32_t okq[MAXC], ov[MAXC]; // source offsets of the next K/Q and V copies
+        const uint32_t u1 = u0 + per, u2 = u1 + per;
         stream_table<D>(g, L, smem, R, lane, u0, 0, staged);
-        stream_copy_kq<D, MAXC>(g, L, smem, j, R, lane, u0, 0, 0, q, k, table);
-        stream_copy_v<D, MAXC>(g, L, smem, R, lane, u0, 0, 0, v);
+        stream_offsets<D, MAXC, false>(g, L, smem, R, lane, 0, okq);
+        stream_copy_kq<D, MAXC>(g, L, smem, j, R, lane, head(u0), okq, 0, 0, q, k, table);
+        stream_offsets<D, MAXC, true>(g, L, smem, R, lane, 0, ov);
+        stream_issue<D, MAXC>(R, head(u0), ov, v, smem + L.v0);
         if (u1 < uend) {
             stream_table<D>(g, L, smem, R, lane, u1, 1, staged);
-            stream_copy_kq<D, MAXC>(g, L, smem, j, R, lane, u1, 1, 1, q, k, table);
+            stream_offsets<D, MAXC, false>(g, L, smem, R, lane, 1, okq);
+            stream_copy_kq<D, MAXC>(g, L, smem, j, R, lane, head(u1), okq, 1, 1, q, k, table);
+            stream_offsets<D, MAXC, true>(g, L, smem, R, lane, 1, ov);
         }
+        if (u2 < uend) stream_table<D>(g, L, smem, R, lane, u2, 2, staged);
         loader_barrier(); // prologue: window-independent tables and the first token tables
         uint32_t u = u0;
         for (int iter = 0;; iter++) {
-            const uint32_t un = u + per, un2 = un + per;
+            const uint32_t un = u + per, un2 = un + per, un3 = un2 + per;
             const bool has_next = un < uend;
             // A: K, Q of unit u have landed once at most V(u) and K/Q(un) remain
             wait_vmcnt_le(nv + (has_next ? nkq : 0));
             loader_barrier();
-            if (has_next) stream_copy_v<D, MAXC>(g, L, smem, R, lane, un, (iter + 1) % kTableSlots, (iter + 1) % kBufs, v);
+            if (has_next) stream_issue<D, MAXC>(R, head(un), ov, v, smem + L.v0 + ((iter + 1) % kBufs) * L.tb);
+            if (un2 < uend) stream_offsets<D, MAXC, false>(g, L, smem, R, lane, (iter + 2) % kTableSlots, okq);
             // B: V of unit u has landed once at most K/Q(un) and V(un) remain
             wait_vmcnt_le(has_next ? nkq + nv : 0);
             loader_barrier();
             if (un2 < uend) {
-                stream_table<D>(g, L, smem, R, lane, un2, (iter + 2) % kTableSlots, staged);
-                stream_copy_kq<D, MAXC>(g, L, smem, j, R, lane, un2, (iter + 2) % kTableSlots, iter % kBufs, q, k,
-                                        table);
+                stream_copy_kq<D, MAXC>(g, L, smem, j, R, lane, head(un2), okq, (iter + 2) % kTableSlots, iter % kBufs,
+                                        q, k, table);
+                stream_offsets<D, MAXC, true>(g, L, smem, R, lane, (iter + 2) % kTableSlots, ov);
             }
+            if (un3 < uend) stream_table<D>(g, L, smem, R, lane, un3, (iter + 3) % kTableSlots, staged);
             if (!has_next) break;
             u = un;
         }
@@ -1318,7 +1317,7 @@ typedef void (*bf16_kernel_t)(Geometry, int, const uint16_t*, const uint16_t*, c
                               const float*, uint16_t*);
 struct Bf16Variant {
     bf16_kernel_t f;
-    int waves;
+    int waves; // waves per workgroup
 };
 
 template <int D, bool BV>
@@ -1334,14 +1333,27 @@ static Bf16Variant bf16_variant_b(int KT) {
     }
 }
 
-// (stream variants: .waves counts the compute waves; the block has kLoaders more)
+// Loader waves of a streaming variant.  Issuing the copies is what limits a
+// loader wave, so the 64-wide variants take six where their registers allow
+// 15 or 16 waves per workgroup (four per SIMD); the others take three.
+template <int D, int KT, bool BV>
+constexpr int stream_loaders() {
+    return (D == 64 && (KT == 7 || (KT == 9 && BV))) ? 6 : 3;
+}
+
+template <int D, int NWAVES, int KT, bool BV>
+static Bf16Variant stream_variant() {
+    constexpr int NL = stream_loaders<D, KT, BV>();
+    return {attn_bf16_stream_kernel<D, NWAVES, NL, KT, BV>, NWAVES + NL};
+}
+
 template <int D, bool BV>
 static Bf16Variant stream_variant_b(int KT) {
     switch (KT) {
-    case 4: return {attn_bf16_stream_kernel<D, 4, 4, BV>, 4};
-    case 7: return {attn_bf16_stream_kernel<D, 7, 7, BV>, 7};
-    case 9: return {attn_bf16_stream_kernel<D, 9, 9, BV>, 9};
-    default: return {attn_bf16_stream_kernel<D, kStreamMaxTiles, 0, BV>, kStreamMaxTiles};
+    case 4: return stream_variant<D, 4, 4, BV>();
+    case 7: return stream_variant<D, 7, 7, BV>();
+    case 9: return stream_variant<D, 9, 9, BV>();
+    default: return stream_variant<D, kStreamMaxTiles, 0, BV>();
     }
 }
 
@@ -1370,8 +1382,7 @@ hipError_t bf16_plan(const Geometry& g, bool stream, int* blocks) {
     const Bf16Variant var = bf16_variant_for(g, stream);
     const size_t lds = stream ? stream_lds(g).total : bf16_lds(g).total;
     int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)var.f,
-                                                                (var.waves + (stream ? kLoaders : 0)) * 64, lds);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)var.f, var.waves * 64, lds);
     if (e != hipSuccess) return e;
     if (per_cu < 1) {
         *blocks = 0;
@@ -1394,7 +1405,7 @@ hipError_t launch_attention_bf16(const Geometry& g, bool stream, int blocks, boo
                                  uint16_t* out, hipStream_t s) {
     const Bf16Variant var = bf16_variant_for(g, stream);
     const size_t lds = stream ? stream_lds(g).total : bf16_lds(g).total;
-    hipLaunchKernelGGL(var.f, dim3((unsigned)blocks), dim3((var.waves + (stream ? kLoaders : 0)) * 64), lds, s, g,
+    hipLaunchKernelGGL(var.f, dim3((unsigned)blocks), dim3(var.waves * 64), lds, s, g,
                        (int)staged, q, k, v, table, out);
     return hipGetLastError();
 }

@@ -269,3 +269,16 @@ def test_larger_logits_still_match():
     d = {n: t.cuda() for n, t in x.items()}
     out = run(p, d)
     assert rel_err(host_f32(out), oracle_full(p, x)) <= TOL["bf16"]
+
+
+@pytest.mark.gpu
+def test_auto_schedule_choice():
+    """AUTO takes the streaming schedule for windows of up to 9 query tiles that
+    fit its LDS ring, and the per-(window, head) schedule otherwise."""
+    want = {"c2_bf16_180x360": 1, "c3_bf16_540x1080": 1, "c4_bf16_181x360_pad190": 1,
+            "c5_bf16_4x180x360_3d": 2}
+    for name, schedule in want.items():
+        att = WindowAttention(WORKLOADS[name])
+        assert att.info.schedule == schedule, name
+        assert att.info.workgroups >= 8, name
+        att.close()
