@@ -273,47 +273,45 @@ hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, 
 }
 
 // --------------------------------------------------------------------------
-// bf16 attention on MFMA.
+// bf16 attention on MFMA, per-unit schedule.
 //
-// Block = (window, head), one wave per 16-query tile (two tiles per wave past
-// 16 tiles), so the window's K and V in LDS serve as many waves as possible
-// and several blocks share a compute unit.  Phases:
-//   A  per-window token tables in LDS: mask field and source row of each
-//      token, and the bias offset kb of every 4-key group;
-//   B  every global load of the block issued back to back: K and V of the
-//      window (4 keys x 16 bytes per item), this head's bias table slice and
-//      each wave's Q tiles; then K to LDS ([key][d], 16-byte chunks XOR-
-//      swizzled by row so 8 consecutive rows hit distinct banks), V to LDS
-//      transposed ([d][key], 4 keys per 8-byte write) and the bias;
+// Block = (window, head); wave w takes the 16-query tiles w, w + NWAVES, ...
+// Phases:
+//   A  the window's token table in LDS: one packed word per token (source row
+//      + 1, 0 for pad, in bits 0..27; mask field in bits 28..31) and the bias
+//      offset kb of every key (16 bits);
+//   B  K and V of the window copied straight into LDS with global_load_lds
+//      ([key][d], 16-byte chunks XOR-swizzled by row; a 1 KB copy moves 8
+//      token rows of 128 bytes, every request a whole line), this head's bias
+//      slice, and each wave's Q tiles into registers;
 //   C  per 16-query tile of a wave:
 //        S^T = K Q^T     v_mfma_f32_16x16x32_bf16, A = K from LDS, B = Q tile
 //                        in registers, C = 0; lane l holds query (l % 16)
 //                        against keys 4*(l/16) + 0..3 of every 16-key tile;
-//                        all tiles of a key block are issued before any
-//                        result is read.  The accumulator input is never a
-//                        register a load may still overwrite during the MFMA;
-//        logits          scale * S + bias by one FMA; the bias of
-//                        query n and key m sits at qb(n) - kb(m), and when the
-//                        window's longitude extent is a multiple of 4 the 4
-//                        keys of a lane are neighbours in one window row, so
-//                        their 4 biases are 4 consecutive table entries read
-//                        with two ds_read2_b32;
+//        logits          scale * S + bias by one FMA; the bias of query n and
+//                        key m sits at qb(n) - kb(m), and when the window's
+//                        longitude extent is a multiple of 4 the 4 keys of a
+//                        lane are neighbours in one window row, so their 4
+//                        biases are 4 consecutive table entries;
 //        mask            -inf where the key is pad, past N or on the other
 //                        side of a masked wrap; only on windows / tiles that
 //                        can hold such keys;
-//        softmax         online over key blocks: p = exp2(l*log2(e) - m*log2(e)),
-//                        running max per query (reduced across the 4 lanes
-//                        that share it);
-//        O^T = V^T P^T   same MFMA, A = V^T from LDS, B = bf16 P straight
-//                        from registers (two key tiles make one 32-deep step;
-//                        an odd last tile uses 16x16x16); the row sum of the
-//                        bf16 P comes from the same product with A = 1;
+//        softmax         online over key blocks of up to 9 tiles:
+//                        p = exp2(l*log2(e) - m*log2(e)), running max per query
+//                        (reduced across the 4 lanes that share it);
+//        O^T = V^T P^T   same MFMA, A = V^T fragments read with the transposing
+//                        ds_read_b64_tr_b16, B = bf16 P straight from registers
+//                        (two key tiles make one 32-deep step; an odd last tile
+//                        is zero-extended); the row sum of the bf16 P comes from
+//                        the same product with A = 1;
 //        epilogue        divide by the sum, round to bf16, store 4 d-values
 //                        per lane at the token's address.
 // Both products use the same key order on both operands, so whatever order
-// the hardware gives the 32 reduction slots the sums are the same.
-// The kernel is specialised on the key-tile count of common window sizes
-// (KT_FIXED > 0: straight-line code); KT_FIXED = 0 handles any count.
+// the hardware gives the 32 reduction slots the sums are the same.  The
+// arithmetic is the streaming schedule's, so both give bit-identical outputs
+// for windows that both take.  The kernel is specialised on the key-tile
+// count of common window sizes (KT_FIXED > 0: straight-line code);
+// KT_FIXED = 0 handles any count.
 // --------------------------------------------------------------------------
 constexpr int kKeyTilesPerBlock = 9;
 constexpr int kLdsBytes = 160 * 1024; // gfx950 LDS per compute unit
@@ -343,22 +341,29 @@ __device__ inline f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(half_hi(a), half_hi(b), acc, 0, 0, 0);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kRowMask = (1 << 28) - 1; // packed table word: source row + 1 in bits 0..27
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left unconstrained)
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
 struct Bf16Lds {
-    int NP, VSTR;
-    size_t ks, vt, bias, kb4, rg, rowi, total;
+    int NP;
+    size_t ks, vs, bias, tw, kb, total;
 };
 
 __host__ __device__ inline Bf16Lds bf16_lds(const Geometry& g) {
     Bf16Lds L;
     L.NP = (g.N + 15) / 16 * 16;
-    L.VSTR = L.NP + 4; // bf16 elements per V^T row: 8-byte aligned, rows 16 apart hit distinct banks
     L.ks = 0;
-    L.vt = L.ks + (size_t)L.NP * g.head_dim * 2;
-    L.bias = L.vt + (size_t)g.head_dim * L.VSTR * 2;
-    L.kb4 = L.bias + ((size_t)g.table_size * 4 + 15) / 16 * 16;
-    L.rg = L.kb4 + (size_t)L.NP * 4;
-    L.rowi = L.rg + (size_t)L.NP * 4;
-    L.total = L.rowi + (size_t)L.NP * 4;
+    L.vs = L.ks + (size_t)L.NP * g.head_dim * 2;
+    L.bias = L.vs + (size_t)L.NP * g.head_dim * 2;
+    L.tw = L.bias + ((size_t)g.table_size * 4 + 15) / 16 * 16;
+    L.kb = L.tw + (size_t)L.NP * 4;
+    L.total = L.kb + (size_t)L.NP * 2;
     return L;
 }
 
@@ -377,17 +382,6 @@ __device__ inline int k_slot(int m, int c) {
     return c ^ ((m / ROWS_PER_128B) % CH);
 }
 
-// 16-byte chunk slot of logical chunk c in V row m, for rows read through
-// ds_read_b64_tr_b16: a 16-lane group reads 2 adjacent chunks of 4
-// consecutive rows, and XOR with 2 * (row index within 128-byte groups, mod
-// CH / 2) gives those 8 (row, chunk) pairs distinct banks.
-template <int D>
-__device__ inline int v_slot(int m, int c) {
-    constexpr int CH = D / 8;
-    constexpr int ROWS_PER_128B = 128 / (D * 2);
-    return c ^ (2 * ((m / ROWS_PER_128B) % (CH / 2)));
-}
-
 // window-local coordinates of local index n
 __device__ inline void local_coords(const Geometry& g, int n, int& lt, int& ly, int& lx) {
     const uint32_t r = fdiv(g.fd_win2, (uint32_t)n);
@@ -404,24 +398,24 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
     constexpr int KSTEPS = D / 32; // 32-deep steps of K Q^T
     constexpr int DT = D / 16;     // 16-row d tiles of O^T
     constexpr int CH = D / 8;      // 16-byte chunks per (token, head)
+    constexpr int RPC = 64 / CH;   // token rows per 1 KB copy
     constexpr int KT_MAX = KT_FIXED > 0 ? KT_FIXED : NWAVES * QT_MAX;
     static_assert(KT_MAX <= NWAVES * QT_MAX, "every query tile needs a wave");
-    constexpr int LOAD_IT = ((KT_MAX * 4) * CH + THREADS - 1) / THREADS;
     constexpr int KB = (KT_FIXED > 0 && KT_FIXED <= kKeyTilesPerBlock) ? KT_FIXED : kKeyTilesPerBlock;
     static_assert(KT_FIXED == 0 || KT_FIXED % KB == 0, "fixed tile counts split into equal key blocks");
     constexpr int KB_UNROLL = KT_FIXED > 0 ? KT_FIXED / KB : 1;
     constexpr int BIAS_UNROLL = 4;
     extern __shared__ __align__(16) unsigned char smem[];
     const Bf16Lds L = bf16_lds(g);
-    uint16_t* Ks = (uint16_t*)(smem + L.ks);
-    uint16_t* Vt = (uint16_t*)(smem + L.vt);
+    const uint16_t* Ks = (const uint16_t*)(smem + L.ks);
+    const unsigned char* Vb = smem + L.vs;
     float* bias = (float*)(smem + L.bias);
-    int* kb4 = (int*)(smem + L.kb4); // 4 * kb, per key (BIAS_VEC: per 4-key group, at index 4g)
-    int* rg = (int*)(smem + L.rg);
-    int* rowi = (int*)(smem + L.rowi);
+    int* tw = (int*)(smem + L.tw);
+    uint16_t* kb = (uint16_t*)(smem + L.kb);
     const int N = g.N, NP = L.NP;
     const int KT = KT_FIXED > 0 ? KT_FIXED : NP / 16;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;
 
     // block -> (window, head); blocks are dealt to XCDs round-robin, so this
@@ -441,7 +435,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
     }
     const bool masked_window = window_maybe_masked(g, wc);
 
-    // ---- A: token tables
+    // ---- A: token table and key bias offsets
     for (int n = tid; n < NP; n += THREADS) {
         if (n < N) {
             int l[3];
@@ -457,50 +451,41 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
                 if (!g.cyc[a] && cr >= g.pad[a] - g.shift[a]) region |= 1 << a;
                 tok = tok * g.ext[a] + c;
             }
-            rg[n] = region | (is_pad ? 8 : 0);
-            rowi[n] = is_pad ? -1 : (staged ? (int)(wi * (uint32_t)N + n) : tok);
-            kb4[n] = ((l[0] * g.tdy + l[1]) * g.tdx + l[2]) * 4;
+            const int row = is_pad ? -1 : (staged ? (int)(wi * (uint32_t)N + n) : tok);
+            tw[n] = (row + 1) | ((region | (is_pad ? 8 : 0)) << 28);
+            kb[n] = (uint16_t)((l[0] * g.tdy + l[1]) * g.tdx + l[2]);
         } else {
-            rg[n] = 15;
-            rowi[n] = -1;
-            kb4[n] = BIAS_VEC ? 12 : 0; // keeps qb - kb (- 3) inside the table
+            tw[n] = 15 << 28;
+            kb[n] = BIAS_VEC ? 3 : 0; // keeps qb - kb (- 3) inside the table
         }
     }
     __syncthreads();
 
-    // ---- B: all loads in flight together
-    u32x4 kr[LOAD_IT][4], vr[LOAD_IT][4];
-    const int items = (NP / 4) * CH;
-    const uint16_t* kh = k + h * D;
-    const uint16_t* vh = v + h * D;
-#pragma unroll
-    for (int it = 0; it < LOAD_IT; it++) {
-        const int i = tid + it * THREADS;
-        const int g4 = i / CH, c = i % CH;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int r = i < items ? rowi[g4 * 4 + j] : -1;
-            if (r >= 0) {
-                const uint64_t off = (uint64_t)(uint32_t)r * (uint32_t)g.row + c * 8;
-                kr[it][j] = *(const u32x4*)(kh + off);
-                vr[it][j] = *(const u32x4*)(vh + off);
-            } else {
-                kr[it][j] = u32x4{0, 0, 0, 0};
-                vr[it][j] = u32x4{0, 0, 0, 0};
-            }
+    // ---- B: K and V copies into LDS (pad rows copy row 0: finite values that
+    // get weight exactly 0), the bias slice, and each wave's Q tiles
+    {
+        const int ncopy = NP * CH / 64; // 1 KB copies per tensor
+        const int m0 = lane / CH;
+        const int ch = k_slot<D>(m0, lane % CH); // logical chunk landing in this lane's slot
+        for (int c = wave; c < 2 * ncopy; c += NWAVES) {
+            const bool is_v = c >= ncopy;
+            const int cc = is_v ? c - ncopy : c;
+            const int r1 = tw[cc * RPC + m0] & kRowMask;
+            const uint64_t off = (uint64_t)(uint32_t)(r1 == 0 ? 0 : r1 - 1) * (uint32_t)g.row + h * D + ch * 8;
+            __builtin_amdgcn_global_load_lds((const void*)((is_v ? v : k) + off),
+                                             (lds_void*)(smem + (is_v ? L.vs : L.ks) + cc * 1024), 16, 0, 0);
         }
     }
     bf16x8 qop[QT_MAX][KSTEPS];
-    int qn[QT_MAX];
 #pragma unroll
     for (int t = 0; t < QT_MAX; t++) {
         const int qt = wave + t * NWAVES;
-        qn[t] = qt * 16 + col;
-        const int r = qt < KT ? rowi[qn[t]] : -1;
+        const int r = qt < KT ? (tw[qt * 16 + col] & kRowMask) - 1 : -1;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ks++) {
             u32x4 val = {0, 0, 0, 0};
-            if (r >= 0) val = *(const u32x4*)(q + (uint64_t)(uint32_t)r * (uint32_t)g.row + h * D + ks * 32 + grp * 8);
+            if (r >= 0)
+                val = *(const u32x4*)(q + (uint64_t)(uint32_t)r * (uint32_t)g.row + h * D + ks * 32 + grp * 8);
             qop[t][ks] = __builtin_bit_cast(bf16x8, val);
         }
     }
@@ -517,39 +502,30 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
             if (i < g.table_size) bias[i] = bv[u];
         }
     }
-#pragma unroll
-    for (int it = 0; it < LOAD_IT; it++) {
-        const int i = tid + it * THREADS;
-        if (i < items) {
-            const int g4 = i / CH, c = i % CH;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int m = g4 * 4 + j;
-                *(u32x4*)(Ks + m * D + k_slot<D>(m, c) * 8) = kr[it][j];
-            }
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                // bf16 e of 4 consecutive keys: low or high halves of dword e / 2
-                const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                const unsigned lo = __builtin_amdgcn_perm(vr[it][1][e >> 1], vr[it][0][e >> 1], sel);
-                const unsigned hi = __builtin_amdgcn_perm(vr[it][3][e >> 1], vr[it][2][e >> 1], sel);
-                *(u32x2*)(Vt + (c * 8 + e) * L.VSTR + g4 * 4) = u32x2{lo, hi};
-            }
-        }
-    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); // this wave's LDS copies have landed
     __syncthreads();
 
     // ---- C: query tiles
     const unsigned one2 = 0x3F803F80u; // two bf16 ones
     const bf16x8 ones8 = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
     const unsigned char* bias_bytes = (const unsigned char*)bias;
+    // V^T fragment of key tile t: lane (col, grp) gets keys 16t + 4grp + 0..3 at
+    // d = 16 dt + col; lane s of the group points at row 16t + 4grp + s/4, d 16dt + 4(s%4)
+    auto vt_frag = [&](int t0, int dt) __attribute__((always_inline)) {
+        const int row = t0 * 16 + grp * 4 + (col >> 2);
+        const int d = dt * 16 + (col & 3) * 4;
+        const unsigned char* p = Vb + row * (D * 2) + k_slot<D>(row, d >> 3) * 16 + (d & 7) * 2;
+        const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)p);
+        return __builtin_bit_cast(u32x2, x);
+    };
 #pragma unroll
     for (int t = 0; t < QT_MAX; t++) {
         const int qt = wave + t * NWAVES;
         if (qt >= KT) break;
-        const int n = qn[t];
-        const int qreg = rg[n];
-        const int r = rowi[n];
+        const int n = qt * 16 + col;
+        const int qword = tw[n];
+        const int qreg = (unsigned)qword >> 28;
+        const int r = (qword & kRowMask) - 1;
         int qb4;
         if (n < N) {
             int lt, ly, lx;
@@ -590,27 +566,27 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
                     float bb[4];
                     if (BIAS_VEC) {
                         // keys key0 + 4*grp + i share a window row: biases at qb - kb0 - i
-                        const float* bp = (const float*)(qbias - kb4[key0 + grp * 4]) - 3;
+                        const float* bp = (const float*)(qbias - (int)kb[key0 + grp * 4] * 4) - 3;
                         bb[3] = bp[0];
                         bb[2] = bp[1];
                         bb[1] = bp[2];
                         bb[0] = bp[3];
                     } else {
-                        const int4 kq = *(const int4*)(kb4 + key0 + grp * 4);
-                        bb[0] = *(const float*)(qbias - kq.x);
-                        bb[1] = *(const float*)(qbias - kq.y);
-                        bb[2] = *(const float*)(qbias - kq.z);
-                        bb[3] = *(const float*)(qbias - kq.w);
+                        const u32x2 kq = *(const u32x2*)(kb + key0 + grp * 4);
+                        bb[0] = *(const float*)(qbias - (int)(kq[0] & 0xFFFF) * 4);
+                        bb[1] = *(const float*)(qbias - (int)(kq[0] >> 16) * 4);
+                        bb[2] = *(const float*)(qbias - (int)(kq[1] & 0xFFFF) * 4);
+                        bb[3] = *(const float*)(qbias - (int)(kq[1] >> 16) * 4);
                     }
                     // logits, natural units: scale * q.k + bias
                     f32x4 lg = {fmaf(s[kt][0], g.scale, bb[0]), fmaf(s[kt][1], g.scale, bb[1]),
                                 fmaf(s[kt][2], g.scale, bb[2]), fmaf(s[kt][3], g.scale, bb[3])};
                     if (masked_window || key0 + 16 > N) {
-                        const int4 kr4 = *(const int4*)(rg + key0 + grp * 4);
-                        lg[0] = kr4.x == qreg ? lg[0] : -INFINITY;
-                        lg[1] = kr4.y == qreg ? lg[1] : -INFINITY;
-                        lg[2] = kr4.z == qreg ? lg[2] : -INFINITY;
-                        lg[3] = kr4.w == qreg ? lg[3] : -INFINITY;
+                        const int4 kr4 = *(const int4*)(tw + key0 + grp * 4);
+                        lg[0] = ((unsigned)kr4.x >> 28) == (unsigned)qreg ? lg[0] : -INFINITY;
+                        lg[1] = ((unsigned)kr4.y >> 28) == (unsigned)qreg ? lg[1] : -INFINITY;
+                        lg[2] = ((unsigned)kr4.z >> 28) == (unsigned)qreg ? lg[2] : -INFINITY;
+                        lg[3] = ((unsigned)kr4.w >> 28) == (unsigned)qreg ? lg[3] : -INFINITY;
                     }
                     s[kt] = lg;
                     bmax = fmaxf(bmax, fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
@@ -649,9 +625,8 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
                         bf16x8, u32x4{pk[kt][0], pk[kt][1], pk[kt + 1][0], pk[kt + 1][1]});
 #pragma unroll
                     for (int dt = 0; dt < DT; dt++) {
-                        const uint16_t* vrow = Vt + (dt * 16 + col) * L.VSTR + t0 * 16 + grp * 4;
-                        const u32x2 lo = *(const u32x2*)vrow;
-                        const u32x2 hi = *(const u32x2*)(vrow + 16);
+                        const u32x2 lo = vt_frag(t0, dt);
+                        const u32x2 hi = vt_frag(t0 + 1, dt);
                         const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
                         o[dt] = mfma32(a, bop, o[dt]);
                     }
@@ -663,8 +638,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
                     const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{pk[kt][0], pk[kt][1], 0u, 0u});
 #pragma unroll
                     for (int dt = 0; dt < DT; dt++) {
-                        const uint16_t* vrow = Vt + (dt * 16 + col) * L.VSTR + t0 * 16 + grp * 4;
-                        const u32x2 lo = *(const u32x2*)vrow;
+                        const u32x2 lo = vt_frag(t0, dt);
                         const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], 0u, 0u});
                         o[dt] = mfma32(a, bop, o[dt]);
                     }
@@ -770,14 +744,9 @@ __host__ __device__ inline StreamLds stream_lds(const Geometry& g) {
     return S;
 }
 
-constexpr int kRowMask = (1 << 28) - 1; // packed table word: source row + 1 in bits 0..27
 constexpr uint32_t kOutOfRange = 0x80000000u; // buffer offset past every tensor the schedule takes
 constexpr int kBufferWord3 = 0x00020000;     // raw buffer resource, 32-bit data format
 constexpr int kNonTemporal = 2;              // cache policy of read-once / write-once traffic (nt)
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (expcnt and lgkmcnt left unconstrained)
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
 // Waits until at most min(n, 63) vector-memory operations of this wave are
 // outstanding; n must be wave-uniform (a scalar branch picks the immediate).
@@ -831,9 +800,6 @@ __device__ inline Unit decode_unit(const Geometry& g, uint32_t u) {
     U.wc[1] = (int)(r2 - (uint32_t)U.wc[0] * (uint32_t)g.nwin[1]);
     return U;
 }
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // The 1 KB copies (per tensor) of loader wave j: [c0, c1), covering token rows
 // [c0 * RPC, c1 * RPC) with RPC = 64 / (D / 8) rows per copy.
@@ -904,43 +870,45 @@ constexpr int loader_max_copies() {
 // 128-byte token row, the source chunk chosen so that the row lands swizzled.
 // Pad rows copy row 0 (finite values that get weight exactly 0, or outputs
 // that are never stored).  All table reads are issued before any is used.
-template <int D, int MAXC, bool VROWS>
+template <int D, int MAXC, bool EXACT>
 __device__ inline void stream_offsets(const Geometry& g, const StreamLds& L, const unsigned char* smem, LoaderRange R,
                                       int lane, int s, uint32_t (&off)[MAXC]) {
     constexpr int CH = D / 8;
     constexpr int RPC = 64 / CH;
     const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
-    const int m0 = lane / CH; // row within a copy; RPC is a multiple of the swizzle periods
-    // the logical chunk whose slot is this lane's (both swizzles are XORs, so self-inverse)
-    const int ch = VROWS ? v_slot<D>(m0, lane % CH) : k_slot<D>(m0, lane % CH);
+    const int m0 = lane / CH; // row within a copy; RPC is a multiple of the swizzle period
+    // the logical chunk whose slot is this lane's (the swizzle is an XOR, so self-inverse)
+    const int ch = k_slot<D>(m0, lane % CH);
     int r1[MAXC];
 #pragma unroll
-    for (int i = 0; i < MAXC; i++) r1[i] = R.c0 + i < R.c1 ? tw[(R.c0 + i) * RPC + m0] & kRowMask : 0;
+    for (int i = 0; i < MAXC; i++) r1[i] = EXACT || R.c0 + i < R.c1 ? tw[(R.c0 + i) * RPC + m0] & kRowMask : 0;
 #pragma unroll
     for (int i = 0; i < MAXC; i++)
         off[i] = (uint32_t)(r1[i] == 0 ? 0 : r1[i] - 1) * (uint32_t)g.row + ch * 8;
 }
 
-template <int D, int MAXC>
+// EXACT: the wave issues exactly MAXC copies (the copies divide evenly among
+// the loader waves), so no copy is conditional.
+template <int D, int MAXC, bool EXACT>
 __device__ inline void stream_issue(LoaderRange R, int hh, const uint32_t (&off)[MAXC],
                                     const uint16_t* __restrict__ src, unsigned char* dst) {
     const uint16_t* sh = src + hh * D;
 #pragma unroll
     for (int i = 0; i < MAXC; i++)
-        if (R.c0 + i < R.c1)
+        if (EXACT || R.c0 + i < R.c1)
             __builtin_amdgcn_global_load_lds((const void*)(sh + off[i]), (lds_void*)(dst + (R.c0 + i) * 1024), 16, 0,
                                              kNonTemporal);
 }
 
 // K and Q of a unit of head hh (source offsets off from its table) into
 // buffer pair b, and for loader 0 the streamed bias slice into bias slot s.
-template <int D, int MAXC>
+template <int D, int MAXC, bool EXACT>
 __device__ inline void stream_copy_kq(const Geometry& g, const StreamLds& L, unsigned char* smem, int j,
                                       LoaderRange R, int lane, int hh, const uint32_t (&off)[MAXC], int s, int b,
                                       const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                       const float* __restrict__ table) {
-    stream_issue<D, MAXC>(R, hh, off, k, smem + L.k0 + b * L.tb);
-    stream_issue<D, MAXC>(R, hh, off, q, smem + L.q0 + b * L.tb);
+    stream_issue<D, MAXC, EXACT>(R, hh, off, k, smem + L.k0 + b * L.tb);
+    stream_issue<D, MAXC, EXACT>(R, hh, off, q, smem + L.q0 + b * L.tb);
     if (j == 0 && !L.bias_resident) {
         float* bdst = (float*)(smem + L.bias) + s * L.TSP;
         for (int jj = 0; jj * 64 < L.TSP; jj++) {
@@ -1139,7 +1107,7 @@ __device__ inline void stream_pv(const Geometry& g, const StreamLds& L, unsigned
     auto vt_frag = [&](int t0, int dt) __attribute__((always_inline)) {
         const int row = t0 * 16 + grp * 4 + (col >> 2);
         const int d = dt * 16 + (col & 3) * 4;
-        const unsigned char* p = Vb + row * (D * 2) + v_slot<D>(row, d >> 3) * 16 + (d & 7) * 2;
+        const unsigned char* p = Vb + row * (D * 2) + k_slot<D>(row, d >> 3) * 16 + (d & 7) * 2;
         const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)p);
         return __builtin_bit_cast(u32x2, x);
     };
@@ -1245,6 +1213,8 @@ __global__ __launch_bounds__((NWAVES + NL) * 64) void attn_bf16_stream_kernel(
         // source offsets of each batch of copies while the previous batch is
         // awaited, so that after a barrier a loader only issues copies.
         constexpr int MAXC = loader_max_copies<D, KT_FIXED, NL>();
+        constexpr int NCOPY = KT_FIXED * 16 * (D / 8) / 64; // copies per tensor (fixed tile counts)
+        constexpr bool EX = KT_FIXED > 0 && NCOPY % NL == 0;
         const int j = wave - NWAVES;
         const LoaderRange R = loader_range(g, L, j, NL);
         const int nkq = loader_kq_copies(g, L, j, NL), nv = loader_v_copies(g, L, j, NL);
@@ -1252,15 +1222,15 @@ __global__ __launch_bounds__((NWAVES + NL) * 64) void attn_bf16_stream_kernel(
         uint32_t okq[MAXC], ov[MAXC]; // source offsets of the next K/Q and V copies
         const uint32_t u1 = u0 + per, u2 = u1 + per;
         stream_table<D>(g, L, smem, R, lane, u0, 0, staged);
-        stream_offsets<D, MAXC, false>(g, L, smem, R, lane, 0, okq);
-        stream_copy_kq<D, MAXC>(g, L, smem, j, R, lane, head(u0), okq, 0, 0, q, k, table);
-        stream_offsets<D, MAXC, true>(g, L, smem, R, lane, 0, ov);
-        stream_issue<D, MAXC>(R, head(u0), ov, v, smem + L.v0);
+        stream_offsets<D, MAXC, EX>(g, L, smem, R, lane, 0, okq);
+        stream_copy_kq<D, MAXC, EX>(g, L, smem, j, R, lane, head(u0), okq, 0, 0, q, k, table);
+        stream_offsets<D, MAXC, EX>(g, L, smem, R, lane, 0, ov);
+        stream_issue<D, MAXC, EX>(R, head(u0), ov, v, smem + L.v0);
         if (u1 < uend) {
             stream_table<D>(g, L, smem, R, lane, u1, 1, staged);
-            stream_offsets<D, MAXC, false>(g, L, smem, R, lane, 1, okq);
-            stream_copy_kq<D, MAXC>(g, L, smem, j, R, lane, head(u1), okq, 1, 1, q, k, table);
-            stream_offsets<D, MAXC, true>(g, L, smem, R, lane, 1, ov);
+            stream_offsets<D, MAXC, EX>(g, L, smem, R, lane, 1, okq);
+            stream_copy_kq<D, MAXC, EX>(g, L, smem, j, R, lane, head(u1), okq, 1, 1, q, k, table);
+            stream_offsets<D, MAXC, EX>(g, L, smem, R, lane, 1, ov);
         }
         if (u2 < uend) stream_table<D>(g, L, smem, R, lane, u2, 2, staged);
         loader_barrier(); // prologue: window-independent tables and the first token tables
@@ -1271,15 +1241,15 @@ __global__ __launch_bounds__((NWAVES + NL) * 64) void attn_bf16_stream_kernel(
             // A: K, Q of unit u have landed once at most V(u) and K/Q(un) remain
             wait_vmcnt_le(nv + (has_next ? nkq : 0));
             loader_barrier();
-            if (has_next) stream_issue<D, MAXC>(R, head(un), ov, v, smem + L.v0 + ((iter + 1) % kBufs) * L.tb);
-            if (un2 < uend) stream_offsets<D, MAXC, false>(g, L, smem, R, lane, (iter + 2) % kTableSlots, okq);
+            if (has_next) stream_issue<D, MAXC, EX>(R, head(un), ov, v, smem + L.v0 + ((iter + 1) % kBufs) * L.tb);
+            if (un2 < uend) stream_offsets<D, MAXC, EX>(g, L, smem, R, lane, (iter + 2) % kTableSlots, okq);
             // B: V of unit u has landed once at most K/Q(un) and V(un) remain
             wait_vmcnt_le(has_next ? nkq + nv : 0);
             loader_barrier();
             if (un2 < uend) {
-                stream_copy_kq<D, MAXC>(g, L, smem, j, R, lane, head(un2), okq, (iter + 2) % kTableSlots, iter % kBufs,
+                stream_copy_kq<D, MAXC, EX>(g, L, smem, j, R, lane, head(un2), okq, (iter + 2) % kTableSlots, iter % kBufs,
                                         q, k, table);
-                stream_offsets<D, MAXC, true>(g, L, smem, R, lane, (iter + 2) % kTableSlots, ov);
+                stream_offsets<D, MAXC, EX>(g, L, smem, R, lane, (iter + 2) % kTableSlots, ov);
             }
             if (un3 < uend) stream_table<D>(g, L, smem, R, lane, un3, (iter + 3) % kTableSlots, staged);
             if (!has_next) break;
@@ -1326,7 +1296,9 @@ static Bf16Variant bf16_variant_b(int KT) {
     case 4: return {attn_bf16_kernel<D, 4, 1, 4, BV>, 4};
     case 7: return {attn_bf16_kernel<D, 7, 1, 7, BV>, 7};
     case 9: return {attn_bf16_kernel<D, 9, 1, 9, BV>, 9};
-    case 18: return {attn_bf16_kernel<D, 9, 2, 18, BV>, 9};
+    // 18 tiles (e.g. 2 x 12 x 12 windows): 8 waves of up to 3 tiles, so that two
+    // workgroups (80 KB of LDS each, 4 waves per SIMD) share a compute unit
+    case 18: return {attn_bf16_kernel<D, 8, 3, 18, BV>, 8};
     default:
         if (KT <= 8) return {attn_bf16_kernel<D, 8, 1, 0, BV>, 8};
         return {attn_bf16_kernel<D, 8, 4, 0, BV>, 8};
@@ -1334,11 +1306,12 @@ static Bf16Variant bf16_variant_b(int KT) {
 }
 
 // Loader waves of a streaming variant.  Issuing the copies is what limits a
-// loader wave, so the 64-wide variants take six where their registers allow
-// 15 or 16 waves per workgroup (four per SIMD); the others take three.
+// loader wave, so the 64-wide variants take as many as their registers allow
+// (15 or 16 waves per workgroup, four per SIMD) and divide the copies evenly
+// (18 or 14 per tensor); the others take three.
 template <int D, int KT, bool BV>
 constexpr int stream_loaders() {
-    return (D == 64 && (KT == 7 || (KT == 9 && BV))) ? 6 : 3;
+    return D == 64 && KT == 7 ? 7 : (D == 64 && KT == 9 && BV ? 6 : 3);
 }
 
 template <int D, int NWAVES, int KT, bool BV>
