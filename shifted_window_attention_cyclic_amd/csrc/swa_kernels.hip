@@ -1082,21 +1082,18 @@ __device__ inline void stream_qk(const Geometry& g, const StreamLds& L, const un
     }
 }
 
-// Second half: O^T = V^T P^T from V in buffer b, divide by the sum, stage the O
-// tile in the wave's rows of the LDS staging buffer and store whole token rows.
+// Second half: O^T = V^T P^T from V in buffer b, divide by the sum and leave
+// the O tile in this tile's rows of the LDS staging buffer (the loader waves
+// store it).
 template <int D, int KT_FIXED>
-__device__ inline void stream_pv(const Geometry& g, const StreamLds& L, unsigned char* smem,
-                                 __amdgpu_buffer_rsrc_t ors, int qt, int lane, int staged, uint32_t uu, int s, int b,
+__device__ inline void stream_pv(const StreamLds& L, unsigned char* smem, int lane, int b,
                                  const TileState<(KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles)>& ts) {
     constexpr int DT = D / 16;
-    constexpr int CH = D / 8;
     constexpr int KB = KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles;
     const int col = lane & 15, grp = lane >> 4;
-    const int N = g.N;
     const int KT = KT_FIXED > 0 ? KT_FIXED : L.NP / 16;
     const unsigned one2 = 0x3F803F80u; // two bf16 ones
     const bf16x8 ones8 = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
-    const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
     const unsigned char* Vb = smem + L.v0 + b * L.tb;
     uint16_t* Os = (uint16_t*)(smem + L.o0);
     f32x4 o[DT], osum = {0.f, 0.f, 0.f, 0.f};
@@ -1138,7 +1135,7 @@ __device__ inline void stream_pv(const Geometry& g, const StreamLds& L, unsigned
             osum = mfma32(ones8, bop, osum);
         }
     }
-    // O tile into the staging rows of this tile (same swizzle), then out as whole token rows
+    // O tile into the staging rows of this tile (same swizzle)
     const int n = ts.n;
     const float inv = ts.r >= 0 ? __builtin_amdgcn_rcpf(osum[0]) : 0.f;
 #pragma unroll
@@ -1147,19 +1144,40 @@ __device__ inline void stream_pv(const Geometry& g, const StreamLds& L, unsigned
         const int c = dt * 2 + (grp >> 1); // 16-byte chunk of d = 16 dt + 4 grp
         *(u32x2*)(Os + n * D + k_slot<D>(n, c) * 8 + (grp & 1) * 4) = w;
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): the tile is written
-    __builtin_amdgcn_wave_barrier();
+}
+
+// Loader j's stores of a unit's O (table in slot s) from the LDS staging
+// buffer: whole 128-byte token rows of its own row range, to the real token or,
+// in the staged layout, also to pad slots (zeros); other lanes store out of
+// range, which the buffer range check drops.
+template <int D, int MAXC, bool EXACT>
+__device__ inline void stream_store_o(const Geometry& g, const StreamLds& L, const unsigned char* smem,
+                                      __amdgpu_buffer_rsrc_t ors, LoaderRange R, int lane, uint32_t uu, int s,
+                                      int staged) {
+    constexpr int CH = D / 8;
+    constexpr int RPC = 64 / CH;
+    const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
+    const uint16_t* Os = (const uint16_t*)(smem + L.o0);
     const Unit U = decode_unit(g, uu);
-    constexpr int RPI = 64 / CH; // token rows per store instruction
+    const int c = lane % CH;
+    u32x4 val[MAXC];
+    int rm[MAXC];
 #pragma unroll
-    for (int i = 0; i < 16 / RPI; i++) {
-        const int m = qt * 16 + i * RPI + lane / CH, c = lane % CH;
-        const u32x4 val = *(const u32x4*)(Os + m * D + k_slot<D>(m, c) * 8);
-        const int rm = (tw[m] & kRowMask) - 1;
-        // the real token, or in the staged layout also pad slots (zeros)
-        const int orow = rm >= 0 ? rm : (staged && m < N ? (int)(U.wi * (uint32_t)N + m) : -1);
-        const uint32_t ob = orow >= 0 ? ((uint32_t)orow * (uint32_t)g.row + U.h * D + c * 8) * 2 : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b128(val, ors, ob, 0, kNonTemporal);
+    for (int i = 0; i < MAXC; i++) {
+        const int m = (R.c0 + i) * RPC + lane / CH;
+        if (EXACT || R.c0 + i < R.c1) {
+            val[i] = *(const u32x4*)(Os + m * D + k_slot<D>(m, c) * 8);
+            rm[i] = (tw[m] & kRowMask) - 1;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXC; i++) {
+        if (EXACT || R.c0 + i < R.c1) {
+            const int m = (R.c0 + i) * RPC + lane / CH;
+            const int orow = rm[i] >= 0 ? rm[i] : (staged && m < g.N ? (int)(U.wi * (uint32_t)g.N + m) : -1);
+            const uint32_t ob = orow >= 0 ? ((uint32_t)orow * (uint32_t)g.row + U.h * D + c * 8) * 2 : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(val[i], ors, ob, 0, kNonTemporal);
+        }
     }
 }
 
@@ -1215,9 +1233,12 @@ __global__ __launch_bounds__((NWAVES + NL) * 64) void attn_bf16_stream_kernel(
         constexpr int MAXC = loader_max_copies<D, KT_FIXED, NL>();
         constexpr int NCOPY = KT_FIXED * 16 * (D / 8) / 64; // copies per tensor (fixed tile counts)
         constexpr bool EX = KT_FIXED > 0 && NCOPY % NL == 0;
+        const __amdgpu_buffer_rsrc_t ors =
+            __builtin_amdgcn_make_buffer_rsrc((void*)out, 0, (int)stream_tensor_bytes(g, staged), kBufferWord3);
         const int j = wave - NWAVES;
         const LoaderRange R = loader_range(g, L, j, NL);
-        const int nkq = loader_kq_copies(g, L, j, NL), nv = loader_v_copies(g, L, j, NL);
+        // copies with a unit's K and Q, with its V, and O stores (one per 1 KB of rows)
+        const int nkq = loader_kq_copies(g, L, j, NL), nv = loader_v_copies(g, L, j, NL), nst = nv;
         auto head = [&](uint32_t uu) { return (int)(uu - fdiv(g.fd_heads, uu) * (uint32_t)g.heads); };
         uint32_t okq[MAXC], ov[MAXC]; // source offsets of the next K/Q and V copies
         const uint32_t u1 = u0 + per, u2 = u1 + per;
@@ -1234,17 +1255,24 @@ __global__ __launch_bounds__((NWAVES + NL) * 64) void attn_bf16_stream_kernel(
         }
         if (u2 < uend) stream_table<D>(g, L, smem, R, lane, u2, 2, staged);
         loader_barrier(); // prologue: window-independent tables and the first token tables
+        // Issue order (loader j): K0 Q0 V0 K1 Q1 | after A_i: V(i+1), O(i-1) stores |
+        // after B_i: K(i+2) Q(i+2).  Vector memory operations of a wave complete in
+        // order, so each wait counts what was issued after the awaited copies.
         uint32_t u = u0;
         for (int iter = 0;; iter++) {
             const uint32_t un = u + per, un2 = un + per, un3 = un2 + per;
             const bool has_next = un < uend;
-            // A: K, Q of unit u have landed once at most V(u) and K/Q(un) remain
-            wait_vmcnt_le(nv + (has_next ? nkq : 0));
+            // A: K, Q of unit u have landed once at most V(u), O(u-2) stores and
+            // K/Q(un) remain
+            wait_vmcnt_le(nv + (iter >= 2 ? nst : 0) + (has_next ? nkq : 0));
             loader_barrier();
             if (has_next) stream_issue<D, MAXC, EX>(R, head(un), ov, v, smem + L.v0 + ((iter + 1) % kBufs) * L.tb);
+            if (iter >= 1) // O of the previous unit, staged by the compute waves before A
+                stream_store_o<D, MAXC, EX>(g, L, smem, ors, R, lane, u - per, (iter - 1) % kTableSlots, staged);
             if (un2 < uend) stream_offsets<D, MAXC, EX>(g, L, smem, R, lane, (iter + 2) % kTableSlots, okq);
-            // B: V of unit u has landed once at most K/Q(un) and V(un) remain
-            wait_vmcnt_le(has_next ? nkq + nv : 0);
+            // B: V of unit u has landed once at most O(u-2) stores, K/Q(un), V(un)
+            // and O(u-1) stores remain
+            wait_vmcnt_le((iter >= 2 ? nst : 0) + (has_next ? nkq + nv : 0) + (iter >= 1 ? nst : 0));
             loader_barrier();
             if (un2 < uend) {
                 stream_copy_kq<D, MAXC, EX>(g, L, smem, j, R, lane, head(un2), okq, (iter + 2) % kTableSlots, iter % kBufs,
@@ -1255,10 +1283,11 @@ __global__ __launch_bounds__((NWAVES + NL) * 64) void attn_bf16_stream_kernel(
             if (!has_next) break;
             u = un;
         }
+        // O of the last unit, staged before the final barrier
+        loader_barrier();
+        stream_store_o<D, MAXC, EX>(g, L, smem, ors, R, lane, u, (int)((uend - 1 - u0) / per) % kTableSlots, staged);
     } else {
         // ---- compute waves
-        const __amdgpu_buffer_rsrc_t ors =
-            __builtin_amdgcn_make_buffer_rsrc((void*)out, 0, (int)stream_tensor_bytes(g, staged), kBufferWord3);
         const int KT = KT_FIXED > 0 ? KT_FIXED : NP / 16;
         const bool active = wave < KT;
         TileState<(KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles)> ts;
@@ -1271,10 +1300,11 @@ __global__ __launch_bounds__((NWAVES + NL) * 64) void attn_bf16_stream_kernel(
             lds_barrier(); // A
             if (active) stream_qk<D, KT_FIXED, BIAS_VEC>(g, L, smem, wave, lane, u, s, b, bo, ts);
             lds_barrier(); // B
-            if (active) stream_pv<D, KT_FIXED>(g, L, smem, ors, wave, lane, staged, u, s, b, ts);
+            if (active) stream_pv<D, KT_FIXED>(L, smem, lane, b, ts);
             u += per;
             if (u >= uend) break;
         }
+        lds_barrier(); // final: the last O tile is staged
     }
 }
 
