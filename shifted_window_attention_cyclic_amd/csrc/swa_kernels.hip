@@ -988,25 +988,7 @@ __device__ inline void stream_qk(const Geometry& g, const StreamLds& L, const un
     const int qreg = (unsigned)qword >> 28;
     ts.n = n;
     ts.r = (qword & kRowMask) - 1;
-    // every bias this lane adds (addresses need no LDS reads); with 64-wide heads
-    // they are all read before the products, with 32-wide heads tile by tile
-    constexpr bool kBiasEarly = D == 64;
-    float bias[KB][4];
-#pragma unroll
-    for (int kt = 0; kt < KB; kt++) {
-        if (kBiasEarly && (KT_FIXED > 0 || kt < KT)) {
-            if (BIAS_VEC) {
-                const float* bp = (const float*)(bias_bytes + bo.off[kt][0]);
-                bias[kt][3] = bp[0];
-                bias[kt][2] = bp[1];
-                bias[kt][1] = bp[2];
-                bias[kt][0] = bp[3];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; i++) bias[kt][i] = *(const float*)(bias_bytes + bo.off[kt][BIAS_VEC ? 0 : i]);
-            }
-        }
-    }
+    float bias[KB][4]; // read tile by tile, after the products (addresses need no LDS reads)
     bf16x8 qf[KSTEPS]; // B operand: query n, d = 32 ks + 8 grp + 0..7
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ks++)
@@ -1029,18 +1011,15 @@ __device__ inline void stream_qk(const Geometry& g, const StreamLds& L, const un
 #pragma unroll
     for (int kt = 0; kt < KB; kt++) {
         if (KT_FIXED > 0 || kt < KT) {
-            if (!kBiasEarly) {
-                if (BIAS_VEC) {
-                    const float* bp = (const float*)(bias_bytes + bo.off[kt][0]);
-                    bias[kt][3] = bp[0];
-                    bias[kt][2] = bp[1];
-                    bias[kt][1] = bp[2];
-                    bias[kt][0] = bp[3];
-                } else {
+            if (BIAS_VEC) {
+                const float* bp = (const float*)(bias_bytes + bo.off[kt][0]);
+                bias[kt][3] = bp[0];
+                bias[kt][2] = bp[1];
+                bias[kt][1] = bp[2];
+                bias[kt][0] = bp[3];
+            } else {
 #pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        bias[kt][i] = *(const float*)(bias_bytes + bo.off[kt][BIAS_VEC ? 0 : i]);
-                }
+                for (int i = 0; i < 4; i++) bias[kt][i] = *(const float*)(bias_bytes + bo.off[kt][i]);
             }
             // logits, natural units: scale * q.k + bias
             sc[kt] = f32x4{fmaf(sc[kt][0], g.scale, bias[kt][0]), fmaf(sc[kt][1], g.scale, bias[kt][1]),
