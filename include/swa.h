@@ -85,7 +85,7 @@ typedef enum swa_schedule {
 typedef struct swa_config {
     int batch;     /* B >= 1 */
     int heads;     /* N_h >= 1 (TERRA, Table V) */
-    int head_dim;  /* d / N_h: 32 or 64 */
+    int head_dim;  /* d / N_h: 32 or 64; 128 with SWA_BF16 (TERRA, Table V: d / N_h = 128) */
     int grid[3];   /* real extents (T, H, W): time, latitude, longitude (TERRA, Table I) */
     int padded[3]; /* padded extents (T^, H^, W^) >= grid; must equal grid on cyclic axes */
     int window[3]; /* window (w_t, w_y, w_x); 1 <= w <= padded, padded % w == 0 */

@@ -90,8 +90,10 @@ swa_status validate(const swa_config* c, swa::Geometry* g, int* elem_bytes) {
         if (tokens > (int64_t)1 << 40 || windows > (int64_t)1 << 40)
             return fail(SWA_ERR_UNSUPPORTED, "grid too large");
     }
-    if (c->head_dim != 32 && c->head_dim != 64)
-        return fail(SWA_ERR_UNSUPPORTED, "head_dim must be 32 or 64");
+    if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+        return fail(SWA_ERR_UNSUPPORTED, "head_dim must be 32, 64 or 128");
+    if (c->head_dim == 128 && c->dtype != SWA_BF16)
+        return fail(SWA_ERR_UNSUPPORTED, "head_dim 128 needs bf16 (the fp32 kernel takes 32 or 64)");
     if (c->heads > 4096) return fail(SWA_ERR_UNSUPPORTED, "at most 4096 heads");
     if (table >= 1 << 16) return fail(SWA_ERR_UNSUPPORTED, "bias table too large (window too large)");
     const int64_t row = (int64_t)c->heads * c->head_dim;

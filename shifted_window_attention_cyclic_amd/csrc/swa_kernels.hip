@@ -374,12 +374,27 @@ __device__ inline unsigned pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// 16-byte chunk slot of logical chunk c in K row m (rows of D bf16)
+// 16-byte chunk slot of logical chunk c in K row m (rows of D bf16): an XOR
+// with a key that changes every 128 bytes of rows, so that 16 consecutive rows
+// read at one logical chunk spread over the banks
 template <int D>
 __device__ inline int k_slot(int m, int c) {
     constexpr int CH = D / 8;
-    constexpr int ROWS_PER_128B = 128 / (D * 2);
+    constexpr int ROWS_PER_128B = D * 2 >= 128 ? 1 : 128 / (D * 2);
     return c ^ ((m / ROWS_PER_128B) % CH);
+}
+
+// Logical chunk that a 1 KB copy lane lands in its slot of row m (the swizzle
+// is an XOR, so self-inverse).  Each copy moves 64 / (D / 8) rows; when that
+// is a multiple of the swizzle period (D <= 64) the row within the copy is
+// enough, otherwise the key comes from the row itself.
+template <int D>
+__device__ inline int copy_chunk(int m, int lane) {
+    constexpr int CH = D / 8;
+    constexpr int RPC = 64 / CH;
+    constexpr int ROWS_PER_128B = D * 2 >= 128 ? 1 : 128 / (D * 2);
+    constexpr int PERIOD = ROWS_PER_128B * CH;
+    return k_slot<D>(RPC % PERIOD == 0 ? lane / CH : m, lane % CH);
 }
 
 // window-local coordinates of local index n
@@ -466,10 +481,10 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
     {
         const int ncopy = NP * CH / 64; // 1 KB copies per tensor
         const int m0 = lane / CH;
-        const int ch = k_slot<D>(m0, lane % CH); // logical chunk landing in this lane's slot
         for (int c = wave; c < 2 * ncopy; c += NWAVES) {
             const bool is_v = c >= ncopy;
             const int cc = is_v ? c - ncopy : c;
+            const int ch = copy_chunk<D>(cc * RPC + m0, lane); // logical chunk landing in this lane's slot
             const int r1 = tw[cc * RPC + m0] & kRowMask;
             const uint64_t off = (uint64_t)(uint32_t)(r1 == 0 ? 0 : r1 - 1) * (uint32_t)g.row + h * D + ch * 8;
             __builtin_amdgcn_global_load_lds((const void*)((is_v ? v : k) + off),
@@ -707,6 +722,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 constexpr int kBufs = 2;       // buffers each of K, Q and V
 constexpr int kTableSlots = 4; // token tables of units i .. i+3
 constexpr int kStreamMaxTiles = 9;
+constexpr int kStreamMaxTiles128 = 5; // 128-wide heads: seven buffers of 5 tiles fill the LDS
 
 struct StreamLds {
     int NP, TSP;   // padded keys; bias table entries per head slice (multiple of 64)
@@ -876,15 +892,14 @@ __device__ inline void stream_offsets(const Geometry& g, const StreamLds& L, con
     constexpr int CH = D / 8;
     constexpr int RPC = 64 / CH;
     const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
-    const int m0 = lane / CH; // row within a copy; RPC is a multiple of the swizzle period
-    // the logical chunk whose slot is this lane's (the swizzle is an XOR, so self-inverse)
-    const int ch = k_slot<D>(m0, lane % CH);
+    const int m0 = lane / CH; // row within a copy
     int r1[MAXC];
 #pragma unroll
     for (int i = 0; i < MAXC; i++) r1[i] = EXACT || R.c0 + i < R.c1 ? tw[(R.c0 + i) * RPC + m0] & kRowMask : 0;
 #pragma unroll
     for (int i = 0; i < MAXC; i++)
-        off[i] = (uint32_t)(r1[i] == 0 ? 0 : r1[i] - 1) * (uint32_t)g.row + ch * 8;
+        off[i] = (uint32_t)(r1[i] == 0 ? 0 : r1[i] - 1) * (uint32_t)g.row +
+                 copy_chunk<D>((R.c0 + i) * RPC + m0, lane) * 8;
 }
 
 // EXACT: the wave issues exactly MAXC copies (the copies divide evenly among
@@ -1301,26 +1316,32 @@ struct Bf16Variant {
 
 template <int D, bool BV>
 static Bf16Variant bf16_variant_b(int KT) {
-    switch (KT) {
-    case 4: return {attn_bf16_kernel<D, 4, 1, 4, BV>, 4};
-    case 7: return {attn_bf16_kernel<D, 7, 1, 7, BV>, 7};
-    case 9: return {attn_bf16_kernel<D, 9, 1, 9, BV>, 9};
-    // 18 tiles (e.g. 2 x 12 x 12 windows): 8 waves of up to 3 tiles, so that two
-    // workgroups (80 KB of LDS each, 4 waves per SIMD) share a compute unit
-    case 18: return {attn_bf16_kernel<D, 8, 3, 18, BV>, 8};
-    default:
+    if constexpr (D == 128) { // 128-wide heads: the general tile counts only
         if (KT <= 8) return {attn_bf16_kernel<D, 8, 1, 0, BV>, 8};
         return {attn_bf16_kernel<D, 8, 4, 0, BV>, 8};
+    } else {
+        switch (KT) {
+        case 4: return {attn_bf16_kernel<D, 4, 1, 4, BV>, 4};
+        case 7: return {attn_bf16_kernel<D, 7, 1, 7, BV>, 7};
+        case 9: return {attn_bf16_kernel<D, 9, 1, 9, BV>, 9};
+        // 18 tiles (e.g. 2 x 12 x 12 windows): 8 waves of up to 3 tiles, so that two
+        // workgroups (80 KB of LDS each, 4 waves per SIMD) share a compute unit
+        case 18: return {attn_bf16_kernel<D, 8, 3, 18, BV>, 8};
+        default:
+            if (KT <= 8) return {attn_bf16_kernel<D, 8, 1, 0, BV>, 8};
+            return {attn_bf16_kernel<D, 8, 4, 0, BV>, 8};
+        }
     }
 }
 
 // Loader waves of a streaming variant.  Issuing the copies is what limits a
 // loader wave, so the 64-wide variants take as many as their registers allow
 // (15 or 16 waves per workgroup, four per SIMD) and divide the copies evenly
-// (18 or 14 per tensor); the others take three.
+// (18 or 14 per tensor); the 128-wide 4-tile variant takes four (16 copies per
+// tensor); the others take three.
 template <int D, int KT, bool BV>
 constexpr int stream_loaders() {
-    return D == 64 && KT == 7 ? 7 : (D == 64 && KT == 9 && BV ? 6 : 3);
+    return D == 64 && KT == 7 ? 7 : (D == 64 && KT == 9 && BV ? 6 : (D == 128 && KT == 4 ? 4 : 3));
 }
 
 template <int D, int NWAVES, int KT, bool BV>
@@ -1331,11 +1352,16 @@ static Bf16Variant stream_variant() {
 
 template <int D, bool BV>
 static Bf16Variant stream_variant_b(int KT) {
-    switch (KT) {
-    case 4: return stream_variant<D, 4, 4, BV>();
-    case 7: return stream_variant<D, 7, 7, BV>();
-    case 9: return stream_variant<D, 9, 9, BV>();
-    default: return stream_variant<D, kStreamMaxTiles, 0, BV>();
+    if constexpr (D == 128) { // 128-wide heads: LDS holds the buffers of windows of up to 5 tiles
+        if (KT == 4) return stream_variant<D, 4, 4, BV>();
+        return stream_variant<D, kStreamMaxTiles128, 0, BV>();
+    } else {
+        switch (KT) {
+        case 4: return stream_variant<D, 4, 4, BV>();
+        case 7: return stream_variant<D, 7, 7, BV>();
+        case 9: return stream_variant<D, 9, 9, BV>();
+        default: return stream_variant<D, kStreamMaxTiles, 0, BV>();
+        }
     }
 }
 
@@ -1344,9 +1370,11 @@ static Bf16Variant bf16_variant_for(const Geometry& g, bool stream) {
     const bool bv = g.win[2] % 4 == 0;
     if (stream) {
         if (g.head_dim == 32) return bv ? stream_variant_b<32, true>(KT) : stream_variant_b<32, false>(KT);
+        if (g.head_dim == 128) return bv ? stream_variant_b<128, true>(KT) : stream_variant_b<128, false>(KT);
         return bv ? stream_variant_b<64, true>(KT) : stream_variant_b<64, false>(KT);
     }
     if (g.head_dim == 32) return bv ? bf16_variant_b<32, true>(KT) : bf16_variant_b<32, false>(KT);
+    if (g.head_dim == 128) return bv ? bf16_variant_b<128, true>(KT) : bf16_variant_b<128, false>(KT);
     return bv ? bf16_variant_b<64, true>(KT) : bf16_variant_b<64, false>(KT);
 }
 
@@ -1355,7 +1383,7 @@ bool bf16_stream_fits(const Geometry& g) {
     const int64_t wrows = g.windows * g.N;
     const int KT = (g.N + 15) / 16;
     // rows + 1 fit the packed table word; buffer offsets of both layouts stay below 2^31
-    return stream_lds(g).total <= (size_t)kLdsBytes && KT <= kStreamMaxTiles &&
+    return stream_lds(g).total <= (size_t)kLdsBytes && KT <= (g.head_dim == 128 ? kStreamMaxTiles128 : kStreamMaxTiles) &&
            (rows > wrows ? rows : wrows) < kRowMask && stream_tensor_bytes(g, false) < kOutOfRange &&
            stream_tensor_bytes(g, true) < kOutOfRange;
 }
@@ -1404,7 +1432,9 @@ hipError_t prepare_kernels(int max_lds) {
                 stream ? stream_variant_b<32, true>(KT).f : bf16_variant_b<32, true>(KT).f,
                 stream ? stream_variant_b<32, false>(KT).f : bf16_variant_b<32, false>(KT).f,
                 stream ? stream_variant_b<64, true>(KT).f : bf16_variant_b<64, true>(KT).f,
-                stream ? stream_variant_b<64, false>(KT).f : bf16_variant_b<64, false>(KT).f};
+                stream ? stream_variant_b<64, false>(KT).f : bf16_variant_b<64, false>(KT).f,
+                stream ? stream_variant_b<128, true>(KT).f : bf16_variant_b<128, true>(KT).f,
+                stream ? stream_variant_b<128, false>(KT).f : bf16_variant_b<128, false>(KT).f};
             for (bf16_kernel_t f : fs) {
                 hipError_t e =
                     hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);

@@ -1,12 +1,14 @@
 """Problem shapes and seeded synthetic inputs.
 
-This module holds no attention arithmetic: only the five workload shapes and
-the random draws that both the library's tests and the oracle's tests feed
-in.  Shapes follow the grids the pages work on: the 0.25 degree field and the
+This module holds no attention arithmetic: only the workload shapes and the
+random draws that both the library's tests and the oracle's tests feed in.
+Shapes follow the grids the pages work on: the 0.25 degree field and the
 1/12 degree field at patch size 4 (TERRA page, Table V patch size; BEAST's
 0.25 degree atmosphere), with heads and window sizes in the range of TERRA's
-Table V.  All tensors are [B, T, H, W, heads, head_dim], C-contiguous, over
-the REAL extents; axis 0 is time, 1 latitude, 2 longitude.
+Table V.  The sixth workload is the layer shape of Table V's Small model
+(d = 1024 over N_h = 8 heads of 128, w = 8) on the 0.25 degree grid.  All
+tensors are [B, T, H, W, heads, head_dim], C-contiguous, over the REAL
+extents; axis 0 is time, 1 latitude, 2 longitude.
 """
 from dataclasses import dataclass, replace
 from typing import Optional, Tuple
@@ -67,7 +69,7 @@ class Problem:
         return replace(self, **kw)
 
 
-# The five workloads.  Seeds are 1000 + index.
+# The workloads.  Seeds are 1000 + index.
 WORKLOADS = {
     "c1_f32_16x32": Problem("c1_f32_16x32", "f32", 1, 3, 32, (1, 16, 32), (1, 16, 32),
                             (1, 8, 8), (0, 4, 4), seed=1000),
@@ -79,6 +81,10 @@ WORKLOADS = {
                                       (1, 190, 360), (1, 10, 10), (0, 5, 5), seed=1003),
     "c5_bf16_4x180x360_3d": Problem("c5_bf16_4x180x360_3d", "bf16", 1, 12, 64, (4, 180, 360),
                                     (4, 180, 360), (2, 12, 12), (1, 6, 6), seed=1004),
+    # TERRA, Table V, Small model: 8 heads of 128, 8 x 8 windows (N = 64); 180
+    # latitude rows padded to 184 so that the windows tile the grid
+    "c6_bf16_180x360_pad184_d128": Problem("c6_bf16_180x360_pad184_d128", "bf16", 1, 8, 128, (1, 180, 360),
+                                           (1, 184, 360), (1, 8, 8), (0, 4, 4), seed=1005),
 }
 ORDER = list(WORKLOADS)
 

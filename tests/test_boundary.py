@@ -77,7 +77,8 @@ BAD = [
     ("pad_on_cyclic_axis", BASE.with_(extent=(1, 540, 1070), padded=(1, 540, 1080)), binding.SWA_ERR_INVALID_ARGUMENT),
     ("extent0", BASE.with_(extent=(0, 540, 1080)), binding.SWA_ERR_INVALID_ARGUMENT),
     ("head_dim48", BASE.with_(head_dim=48), binding.SWA_ERR_UNSUPPORTED),
-    ("head_dim128", BASE.with_(head_dim=128), binding.SWA_ERR_UNSUPPORTED),
+    ("head_dim256", BASE.with_(head_dim=256), binding.SWA_ERR_UNSUPPORTED),
+    ("head_dim128_f32", WORKLOADS["c1_f32_16x32"].with_(head_dim=128), binding.SWA_ERR_UNSUPPORTED),
     ("window_27x27_bf16", BASE.with_(window=(1, 27, 27)), binding.SWA_ERR_UNSUPPORTED),
     ("bf16_window_over_512", BASE.with_(extent=(1, 540, 1080), window=(1, 20, 27)), binding.SWA_ERR_UNSUPPORTED),
 ]

@@ -35,6 +35,7 @@ SMALL = {
     "c3s": small_variant(WORKLOADS["c3_bf16_540x1080"], 36, 48),
     "c4s": WORKLOADS["c4_bf16_181x360_pad190"].with_(name="c4s", extent=(1, 31, 40), padded=(1, 40, 40)),
     "c5s": small_variant(WORKLOADS["c5_bf16_4x180x360_3d"], 24, 36),
+    "c6s": small_variant(WORKLOADS["c6_bf16_180x360_pad184_d128"], 36, 48),
 }
 
 
@@ -53,6 +54,12 @@ EDGE = {
     "time_pad": _edge("tpad", "bf16", 2, 2, 64, (3, 12, 24), (4, 12, 24), (2, 6, 6), (1, 3, 3)),
     "f32_d64_3d_pad": _edge("f32d64", "f32", 2, 2, 64, (3, 10, 16), (4, 12, 16), (2, 4, 8), (1, 2, 4)),
     "f32_n288": _edge("f32n288", "f32", 1, 2, 32, (2, 12, 12), (2, 12, 12), (2, 12, 12), (1, 6, 6)),
+    # 128-wide heads: 5 tiles with a window width that is no multiple of 4 (general
+    # streaming variant), 9 tiles (per-unit schedule: the streaming ring does not
+    # fit the LDS) and 18 tiles in 3-D
+    "d128_n80_ragged": _edge("d128n80", "bf16", 2, 3, 128, (1, 19, 30), (1, 24, 30), (1, 8, 10), (0, 4, 5)),
+    "d128_n144": _edge("d128n144", "bf16", 1, 2, 128, (1, 24, 36), (1, 24, 36), (1, 12, 12), (0, 6, 6)),
+    "d128_n288_3d": _edge("d128n288", "bf16", 1, 2, 128, (2, 12, 24), (2, 12, 24), (2, 12, 12), (1, 6, 6)),
 }
 
 
@@ -71,7 +78,8 @@ def test_parity_small_full_grid(name, variant, schedule):
     assert torch.isfinite(out.float()).all()
 
 
-FULL = ["c2_bf16_180x360", "c3_bf16_540x1080", "c4_bf16_181x360_pad190", "c5_bf16_4x180x360_3d"]
+FULL = ["c2_bf16_180x360", "c3_bf16_540x1080", "c4_bf16_181x360_pad190", "c5_bf16_4x180x360_3d",
+        "c6_bf16_180x360_pad184_d128"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -276,7 +284,12 @@ def test_auto_schedule_choice():
     """AUTO takes the streaming schedule for windows of up to 9 query tiles that
     fit its LDS ring, and the per-(window, head) schedule otherwise."""
     want = {"c2_bf16_180x360": 1, "c3_bf16_540x1080": 1, "c4_bf16_181x360_pad190": 1,
-            "c5_bf16_4x180x360_3d": 2}
+            "c5_bf16_4x180x360_3d": 2, "c6_bf16_180x360_pad184_d128": 1}
+    small = {"d128_n80_ragged": 1, "d128_n144": 2, "d128_n288_3d": 2}
+    for name, schedule in small.items():
+        att = WindowAttention(EDGE[name])
+        assert att.info.schedule == schedule, name
+        att.close()
     for name, schedule in want.items():
         att = WindowAttention(WORKLOADS[name])
         assert att.info.schedule == schedule, name
