@@ -30,13 +30,15 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 MALL_BYTES = 256 << 20     # Infinity Cache; rotate inputs until the working set is 3x this
 KERNEL_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_kernels.hip",
                   "shifted_window_attention_cyclic_amd/csrc/swa_geometry.h"]
-SCHEDULE_STREAM, SCHEDULE_BLOCK = 1, 2  # swa_info.schedule
+SCHEDULE_STREAM, SCHEDULE_BLOCK, SCHEDULE_KEYBLOCK = 1, 2, 3  # swa_info.schedule
+CPU_SAMPLE_FLOPS = 4e11  # nominal FLOPs of the CPU-baseline sample (about 10 s of fp64 on 16 cores)
 
 
 def kernel_name(p, info) -> str:
     if p.dtype == "f32":
         return "attn_f32_kernel"
-    return "attn_bf16_stream_kernel" if info.schedule == SCHEDULE_STREAM else "attn_bf16_kernel"
+    return {SCHEDULE_STREAM: "attn_bf16_stream_kernel", SCHEDULE_KEYBLOCK: "attn_bf16_kblock_kernel"}.get(
+        info.schedule, "attn_bf16_kernel")
 
 
 def kernel_source_hash() -> str:
@@ -87,7 +89,9 @@ def cpu_baseline(p, x, out_gpu, rows):
     import oracle
 
     T, H, W = p.extent
-    rows = min(rows, H)
+    # whole latitude rows, as many as keep the sample near CPU_SAMPLE_FLOPS
+    per_row = 4.0 * p.window_tokens * p.head_dim * p.heads * p.batch * T * W
+    rows = max(1, min(rows, H, int(CPU_SAMPLE_FLOPS // per_row)))
     idx = np.array([((b * T + t) * H + y) * W + xx for b in range(p.batch) for t in range(T)
                     for y in range(rows) for xx in range(W)], dtype=np.int64)
     host = {n: x[n].float().numpy() for n in ("q", "k", "v", "table")}
@@ -115,7 +119,8 @@ def main():
     ap.add_argument("--workload", default="c3_bf16_540x1080")
     ap.add_argument("--variant", default="fused", choices=["fused", "staged"])
     ap.add_argument("--cpu-rows", type=int, default=1 << 30,
-                    help="latitude rows in the CPU-baseline sample (default: all)")
+                    help="latitude rows in the CPU-baseline sample (default: all that keep it "
+                         "near 4e11 nominal FLOPs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (counter calibration)")
@@ -178,8 +183,16 @@ def main():
     tflops = info.nominal_flops / (ms_per_step * 1e-3) / 1e12
     useful = 4.0 * useful_pairs(p) * p.head_dim * p.heads
     achieved_gbs = info.algorithmic_bytes / (avg_launch_ms * 1e-3) / 1e9
+    kernel_tflops = info.nominal_flops / (avg_launch_ms * 1e-3) / 1e12
     peak_tf = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
     traffic = traffic_from_profiles(p.name) if args.variant == "fused" else None
+    # the roof that binds: HBM below the ridge (peak FLOP/s over peak bytes/s), MFMA above it
+    intensity = info.nominal_flops / info.algorithmic_bytes
+    mfma_bound = intensity > peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
+    roof = ({"bound": "mfma", "achieved": round(kernel_tflops, 1), "peak": peak_tf, "unit": "TFLOP/s",
+             "frac": round(kernel_tflops / peak_tf, 4)} if mfma_bound else
+            {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(achieved_gbs / PEAK_HBM_GBS, 4)})
     result = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -209,12 +222,10 @@ def main():
                    "p90_ms": round(launch_ms[(9 * len(launch_ms)) // 10], 5),
                    "source_sha256_16": kernel_source_hash()},
         "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved_gbs, 1),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
+            **roof,
             "traffic": traffic,
+            "algorithmic_gbs": round(achieved_gbs, 1),
+            "intensity_flop_per_byte": round(intensity, 2),
             "algorithmic_bytes_per_launch": info.algorithmic_bytes,
             "nominal_flops_per_launch": info.nominal_flops,
             "mfma_ceiling_frac_at_hbm_roof": round(

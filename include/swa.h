@@ -36,8 +36,11 @@
  *
  * Ownership.  The caller owns every buffer passed in; they must stay valid
  * until the work queued on the given stream has finished.  A handle owns only
- * its constants and, for the staged variant, a workspace it allocates in
- * swa_create and frees in swa_destroy.  swa_forward never allocates.
+ * its constants and the workspaces it allocates in swa_create and frees in
+ * swa_destroy: four window-major tensors for the staged variant, and for the
+ * key-blocked schedule a head-major copy of the bias table (heads *
+ * table entries floats), which each swa_forward refreshes from bias_table
+ * before the attention kernel reads it.  swa_forward never allocates.
  *
  * Errors.  Every call validates its arguments before touching the GPU and
  * returns SWA_ERR_INVALID_ARGUMENT or SWA_ERR_UNSUPPORTED without side
@@ -46,7 +49,8 @@
  * available from swa_last_error().  No C++ exception crosses this ABI.
  * All device work is asynchronous on the stream passed in (a hipStream_t;
  * NULL is the default stream).  A handle may be used from one thread at a
- * time; the staged variant's workspace is shared by all calls on a handle.
+ * time; the workspaces are shared by all calls on a handle, so calls on one
+ * handle queued on different streams must not overlap.
  */
 #ifndef SWA_H
 #define SWA_H
@@ -77,9 +81,12 @@ typedef enum swa_variant {
 } swa_variant;
 
 typedef enum swa_schedule {
-    SWA_SCHEDULE_AUTO = 0,   /* STREAM when it fits in LDS, else BLOCK */
-    SWA_SCHEDULE_STREAM = 1, /* bf16: persistent blocks streaming K/V into a two-stage LDS ring */
-    SWA_SCHEDULE_BLOCK = 2   /* bf16: one workgroup per (window, head) */
+    SWA_SCHEDULE_AUTO = 0,    /* STREAM when it fits in LDS, else BLOCK, else KEYBLOCK */
+    SWA_SCHEDULE_STREAM = 1,  /* bf16: persistent blocks streaming K/V into a two-stage LDS ring */
+    SWA_SCHEDULE_BLOCK = 2,   /* bf16: one workgroup per (window, head), windows of up to 512 tokens */
+    SWA_SCHEDULE_KEYBLOCK = 3 /* bf16: workgroups of 256 queries of a (window, head) stream K/V in
+                                 blocks of 32 keys (online softmax): windows of any size whose
+                                 bias slice and token tables leave LDS room for the ring */
 } swa_schedule;
 
 typedef struct swa_config {
@@ -105,20 +112,20 @@ typedef struct swa_info {
     int32_t window_tokens;      /* N = w_t * w_y * w_x */
     int64_t tokens;             /* real tokens B * T * H * W */
     int64_t window_major_elems; /* windows * N * heads * head_dim */
-    size_t workspace_bytes;     /* device bytes owned by the handle (staged variant) */
+    size_t workspace_bytes;     /* device bytes owned by the handle (staged variant, key-blocked bias copy) */
     double nominal_flops;       /* 4 * N^2 * head_dim per (window, head), all windows */
     double algorithmic_bytes;   /* q, k, v read and out written once, real tokens, plus the table */
-    int32_t schedule;           /* bf16: the schedule in use (SWA_SCHEDULE_STREAM or _BLOCK); fp32: 0 */
+    int32_t schedule;           /* bf16: the schedule in use (_STREAM, _BLOCK or _KEYBLOCK); fp32: 0 */
     int32_t workgroups;         /* bf16: workgroups per attention launch; fp32: 0 */
 } swa_info;
 
 /*
  * Validates cfg, checks that the current HIP device is a gfx950, and creates
- * a handle.  The staged variant allocates its workspace (four window-major
- * tensors) here.  On failure *out is set to NULL.
+ * a handle.  The workspaces (staged variant; key-blocked schedule) are
+ * allocated here.  On failure *out is set to NULL.
  * Errors: INVALID_ARGUMENT (NULL pointers, malformed tiling, unknown enum),
- * UNSUPPORTED (head_dim or window size outside the kernels' range, or
- * SWA_SCHEDULE_STREAM for a window too large for it),
+ * UNSUPPORTED (head_dim or window size outside the kernels' range, or an
+ * explicit schedule that cannot take the window),
  * HIP (no gfx950 device), OUT_OF_MEMORY (workspace).
  */
 swa_status swa_create(const swa_config* cfg, swa_handle** out);

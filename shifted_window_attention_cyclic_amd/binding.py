@@ -15,8 +15,9 @@ from .build import LIBRARY
 SWA_OK, SWA_ERR_INVALID_ARGUMENT, SWA_ERR_UNSUPPORTED, SWA_ERR_OUT_OF_MEMORY, SWA_ERR_HIP = range(5)
 SWA_F32, SWA_BF16 = 0, 1
 SWA_VARIANT_FUSED, SWA_VARIANT_STAGED = 0, 1
-SWA_SCHEDULE_AUTO, SWA_SCHEDULE_STREAM, SWA_SCHEDULE_BLOCK = 0, 1, 2
-SCHEDULES = {"auto": SWA_SCHEDULE_AUTO, "stream": SWA_SCHEDULE_STREAM, "block": SWA_SCHEDULE_BLOCK}
+SWA_SCHEDULE_AUTO, SWA_SCHEDULE_STREAM, SWA_SCHEDULE_BLOCK, SWA_SCHEDULE_KEYBLOCK = 0, 1, 2, 3
+SCHEDULES = {"auto": SWA_SCHEDULE_AUTO, "stream": SWA_SCHEDULE_STREAM, "block": SWA_SCHEDULE_BLOCK,
+             "keyblock": SWA_SCHEDULE_KEYBLOCK}
 
 EXPORTS = ("swa_create", "swa_forward", "swa_destroy", "swa_get_info", "swa_status_string",
            "swa_last_error", "swa_gather", "swa_scatter", "swa_debug_visibility")

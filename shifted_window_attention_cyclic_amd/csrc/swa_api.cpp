@@ -19,10 +19,11 @@ struct swa_handle {
     swa::Geometry g;
     int elem_bytes;
     int device;
-    bool stream;        // bf16: streaming schedule
+    int schedule;       // bf16: SWA_SCHEDULE_STREAM, _BLOCK or _KEYBLOCK; fp32: 0
     int blocks;         // bf16: workgroups per attention launch
     size_t wm_bytes;    // bytes of one window-major tensor
     void* workspace;    // staged variant: q, k, v, o window-major tensors
+    float* bias_hm;     // key-blocked schedule: head-major copy of the bias table
 };
 
 namespace {
@@ -44,7 +45,8 @@ swa_status validate(const swa_config* c, swa::Geometry* g, int* elem_bytes) {
     if (c->dtype != SWA_F32 && c->dtype != SWA_BF16) return fail(SWA_ERR_INVALID_ARGUMENT, "unknown dtype");
     if (c->variant != SWA_VARIANT_FUSED && c->variant != SWA_VARIANT_STAGED)
         return fail(SWA_ERR_INVALID_ARGUMENT, "unknown variant");
-    if (c->schedule != SWA_SCHEDULE_AUTO && c->schedule != SWA_SCHEDULE_STREAM && c->schedule != SWA_SCHEDULE_BLOCK)
+    if (c->schedule != SWA_SCHEDULE_AUTO && c->schedule != SWA_SCHEDULE_STREAM && c->schedule != SWA_SCHEDULE_BLOCK &&
+        c->schedule != SWA_SCHEDULE_KEYBLOCK)
         return fail(SWA_ERR_INVALID_ARGUMENT, "unknown schedule");
     if (c->head_dim < 1) return fail(SWA_ERR_INVALID_ARGUMENT, "head_dim must be >= 1");
     if (!(isfinite(c->scale)) || c->scale < 0.f)
@@ -132,9 +134,12 @@ swa_status validate(const swa_config* c, swa::Geometry* g, int* elem_bytes) {
     G.fd_win2 = swa::make_fastdiv((uint32_t)c->window[2]);
     *elem_bytes = c->dtype == SWA_F32 ? 4 : 2;
 
-    const size_t lds = swa::attention_lds_bytes(G, c->dtype == SWA_BF16);
-    if (c->dtype == SWA_BF16 && N > 512) return fail(SWA_ERR_UNSUPPORTED, "bf16 kernels take windows of at most 512 tokens");
-    if (lds > 160 * 1024) return fail(SWA_ERR_UNSUPPORTED, "window too large for the LDS of one workgroup");
+    if (c->dtype == SWA_BF16) {
+        if (!swa::bf16_stream_fits(G) && !swa::bf16_block_fits(G) && !swa::bf16_kblock_fits(G))
+            return fail(SWA_ERR_UNSUPPORTED, "window too large for the LDS of every bf16 schedule");
+    } else if (swa::attention_lds_bytes(G, false) > 160 * 1024) {
+        return fail(SWA_ERR_UNSUPPORTED, "window too large for the LDS of one workgroup");
+    }
     return SWA_OK;
 }
 
@@ -197,20 +202,27 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
         return fail(SWA_ERR_UNSUPPORTED, buf);
     }
     if ((e = swa::prepare_kernels(max_lds)) != hipSuccess) return fail_hip(e, "hipFuncSetAttribute");
-    bool stream = false;
-    int blocks = 0;
+    int schedule = 0, blocks = 0;
     if (cfg->dtype == SWA_BF16) {
-        const bool fits = swa::bf16_stream_fits(g);
-        if (cfg->schedule == SWA_SCHEDULE_STREAM && !fits)
-            return fail(SWA_ERR_UNSUPPORTED, "window too large for the streaming schedule");
-        stream = cfg->schedule == SWA_SCHEDULE_STREAM || (cfg->schedule == SWA_SCHEDULE_AUTO && fits);
-        if ((e = swa::bf16_plan(g, stream, &blocks)) != hipSuccess) return fail_hip(e, "occupancy query");
-        if (blocks < 1 && stream && cfg->schedule == SWA_SCHEDULE_AUTO) {
-            // the streaming workgroup cannot be resident: take the per-unit schedule
-            stream = false;
-            if ((e = swa::bf16_plan(g, stream, &blocks)) != hipSuccess) return fail_hip(e, "occupancy query");
+        // AUTO: the streaming schedule, else the per-unit one, else the key-blocked one,
+        // each only when its workgroup fits and can be resident
+        const bool fit[4] = {false, swa::bf16_stream_fits(g), swa::bf16_block_fits(g), swa::bf16_kblock_fits(g)};
+        const int order[3] = {SWA_SCHEDULE_STREAM, SWA_SCHEDULE_BLOCK, SWA_SCHEDULE_KEYBLOCK};
+        for (int sc : order) {
+            if (cfg->schedule != SWA_SCHEDULE_AUTO && cfg->schedule != sc) continue;
+            if (!fit[sc]) {
+                if (cfg->schedule == sc) return fail(SWA_ERR_UNSUPPORTED, "the requested schedule cannot take this window");
+                continue;
+            }
+            e = sc == SWA_SCHEDULE_KEYBLOCK ? swa::kblock_plan(g, &blocks)
+                                            : swa::bf16_plan(g, sc == SWA_SCHEDULE_STREAM, &blocks);
+            if (e != hipSuccess) return fail_hip(e, "occupancy query");
+            if (blocks >= 1) {
+                schedule = sc;
+                break;
+            }
         }
-        if (blocks < 1) return fail(SWA_ERR_UNSUPPORTED, "attention kernel does not fit on a compute unit");
+        if (schedule == 0) return fail(SWA_ERR_UNSUPPORTED, "attention kernel does not fit on a compute unit");
     }
 
     swa_handle* h = new (std::nothrow) swa_handle();
@@ -219,16 +231,26 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
     h->g = g;
     h->elem_bytes = eb;
     h->device = dev;
-    h->stream = stream;
+    h->schedule = schedule;
     h->blocks = blocks;
     h->wm_bytes = (size_t)g.windows * g.N * g.row * eb;
     h->workspace = nullptr;
+    h->bias_hm = nullptr;
     if (cfg->variant == SWA_VARIANT_STAGED) {
         e = hipMalloc(&h->workspace, 4 * h->wm_bytes);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             delete h;
             return fail(SWA_ERR_OUT_OF_MEMORY, "staged workspace");
+        }
+    }
+    if (schedule == SWA_SCHEDULE_KEYBLOCK) {
+        e = hipMalloc((void**)&h->bias_hm, swa::bf16_kblock_workspace_bytes(g));
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            if (h->workspace) (void)hipFree(h->workspace);
+            delete h;
+            return fail(SWA_ERR_OUT_OF_MEMORY, "bias table copy");
         }
     }
     *out = h;
@@ -238,9 +260,10 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
 swa_status swa_destroy(swa_handle* h) {
     if (!h) return SWA_OK;
     swa_status st = SWA_OK;
-    if (h->workspace) {
+    if (h->workspace || h->bias_hm) {
         hipError_t e = hipDeviceSynchronize();
-        if (e == hipSuccess) e = hipFree(h->workspace);
+        if (e == hipSuccess && h->workspace) e = hipFree(h->workspace);
+        if (e == hipSuccess && h->bias_hm) e = hipFree(h->bias_hm);
         if (e != hipSuccess) st = fail_hip(e, "releasing the workspace");
     }
     delete h;
@@ -254,11 +277,12 @@ swa_status swa_get_info(const swa_handle* h, swa_info* info) {
     info->window_tokens = g.N;
     info->tokens = (int64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
     info->window_major_elems = g.windows * g.N * (int64_t)g.row;
-    info->workspace_bytes = h->workspace ? 4 * h->wm_bytes : 0;
+    info->workspace_bytes = (h->workspace ? 4 * h->wm_bytes : 0) +
+                            (h->bias_hm ? swa::bf16_kblock_workspace_bytes(g) : 0);
     info->nominal_flops = 4.0 * g.N * (double)g.N * g.head_dim * (double)g.windows * g.heads;
     info->algorithmic_bytes = 4.0 * (double)info->tokens * g.row * h->elem_bytes + 4.0 * g.table_size * g.heads;
     const bool bf16 = h->cfg.dtype == SWA_BF16;
-    info->schedule = bf16 ? (h->stream ? SWA_SCHEDULE_STREAM : SWA_SCHEDULE_BLOCK) : 0;
+    info->schedule = bf16 ? h->schedule : 0;
     info->workgroups = bf16 ? h->blocks : 0;
     return SWA_OK;
 }
@@ -280,11 +304,19 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
     const swa::Geometry& g = h->g;
     const bool bf16 = h->cfg.dtype == SWA_BF16;
     hipError_t e;
+    auto attention = [&](bool staged, const void* aq, const void* ak, const void* av, void* ao) {
+        if (!bf16)
+            return swa::launch_attention_f32(g, staged, (const float*)aq, (const float*)ak, (const float*)av,
+                                             bias_table, (float*)ao, s);
+        if (h->schedule == SWA_SCHEDULE_KEYBLOCK)
+            return swa::launch_attention_kblock(g, staged, (const uint16_t*)aq, (const uint16_t*)ak,
+                                                (const uint16_t*)av, bias_table, h->bias_hm, (uint16_t*)ao, s);
+        return swa::launch_attention_bf16(g, h->schedule == SWA_SCHEDULE_STREAM, h->blocks, staged,
+                                          (const uint16_t*)aq, (const uint16_t*)ak, (const uint16_t*)av, bias_table,
+                                          (uint16_t*)ao, s);
+    };
     if (h->cfg.variant == SWA_VARIANT_FUSED) {
-        e = bf16 ? swa::launch_attention_bf16(g, h->stream, h->blocks, false, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                              bias_table, (uint16_t*)out, s)
-                 : swa::launch_attention_f32(g, false, (const float*)q, (const float*)k, (const float*)v,
-                                             bias_table, (float*)out, s);
+        e = attention(false, q, k, v, out);
         return e == hipSuccess ? SWA_OK : fail_hip(e, "attention launch");
     }
     char* ws = (char*)h->workspace;
@@ -295,11 +327,7 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
     if ((e = swa::launch_gather(g, h->elem_bytes, q, wq, s)) != hipSuccess) return fail_hip(e, "gather launch");
     if ((e = swa::launch_gather(g, h->elem_bytes, k, wk, s)) != hipSuccess) return fail_hip(e, "gather launch");
     if ((e = swa::launch_gather(g, h->elem_bytes, v, wv, s)) != hipSuccess) return fail_hip(e, "gather launch");
-    e = bf16 ? swa::launch_attention_bf16(g, h->stream, h->blocks, true, (const uint16_t*)wq, (const uint16_t*)wk, (const uint16_t*)wv,
-                                          bias_table, (uint16_t*)wo, s)
-             : swa::launch_attention_f32(g, true, (const float*)wq, (const float*)wk, (const float*)wv, bias_table,
-                                         (float*)wo, s);
-    if (e != hipSuccess) return fail_hip(e, "attention launch");
+    if ((e = attention(true, wq, wk, wv, wo)) != hipSuccess) return fail_hip(e, "attention launch");
     if ((e = swa::launch_scatter(g, h->elem_bytes, wo, out, s)) != hipSuccess) return fail_hip(e, "scatter launch");
     return SWA_OK;
 }

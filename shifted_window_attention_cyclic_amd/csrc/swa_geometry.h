@@ -146,12 +146,24 @@ hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, 
 hipError_t launch_attention_bf16(const Geometry& g, bool stream, int blocks, bool staged, const uint16_t* q,
                                  const uint16_t* k, const uint16_t* v, const float* table,
                                  uint16_t* out, hipStream_t s);
-// LDS bytes the attention kernels need for g.
+// LDS bytes the attention kernels need for g (bf16: the smallest among the
+// schedules that take the window; (size_t)-1 when none does).
 size_t attention_lds_bytes(const Geometry& g, bool bf16);
 // Whether the streaming bf16 schedule (persistent blocks, two LDS stages) fits.
 bool bf16_stream_fits(const Geometry& g);
+// Whether the per-unit bf16 schedule (a window's K and V in one workgroup's LDS) fits.
+bool bf16_block_fits(const Geometry& g);
 // Workgroups one bf16 attention launch uses (0: the kernel does not fit).
 hipError_t bf16_plan(const Geometry& g, bool stream, int* blocks);
+// Key-blocked bf16 schedule (windows of any size): whether its LDS ring fits,
+// the head-major bias copy it needs (bytes), its workgroup count (0: does not
+// fit) and its launch (which first refreshes the bias copy from table).
+bool bf16_kblock_fits(const Geometry& g);
+size_t bf16_kblock_workspace_bytes(const Geometry& g);
+hipError_t kblock_plan(const Geometry& g, int* blocks);
+hipError_t launch_attention_kblock(const Geometry& g, bool staged, const uint16_t* q, const uint16_t* k,
+                                   const uint16_t* v, const float* table, float* bias_hm, uint16_t* out,
+                                   hipStream_t s);
 // Lets every attention kernel take up to max_lds bytes of dynamic LDS.
 hipError_t prepare_kernels(int max_lds);
 

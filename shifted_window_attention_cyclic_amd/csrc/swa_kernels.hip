@@ -1302,13 +1302,409 @@ __global__ __launch_bounds__((NWAVES + NL) * 64) void attn_bf16_stream_kernel(
     }
 }
 
+// bf16 attention kernels share one signature: (geometry, staged, q, k, v, table, out)
+typedef void (*bf16_kernel_t)(Geometry, int, const uint16_t*, const uint16_t*, const uint16_t*,
+                              const float*, uint16_t*);
+
+// --------------------------------------------------------------------------
+// bf16 attention, key-blocked schedule: windows whose K and V do not fit in
+// one workgroup's LDS, e.g. the 32 x 32 windows (N = 1024) of TERRA's Large
+// model (TERRA page, Table V).  There the path turns MFMA-bound: the
+// intensity is N / 2 FLOP per byte, 512 against a ridge near 315.
+//
+// A workgroup takes kKbQueries queries of one (window, head).  Each of its
+// eight compute waves holds two 16-query tiles of Q in registers, so every K
+// and V fragment it reads from LDS feeds two MFMAs.  Two loader waves stream
+// K and V in blocks of 32 keys through a ring of LDS stages with
+// global_load_lds (the swizzled [key][d] layout of the other bf16 kernels)
+// and the compute waves run an online softmax over the blocks: running max
+// per query; O and the row sum rescaled when some query's max grows (a
+// wave-uniform test, so that the common case skips it).  One barrier per
+// block: at barrier j block j has landed and block j - 1 is no longer read,
+// so the loaders refill its stage with block j + stages - 1; a wave's vector
+// memory operations complete in order, so the loaders' waits are exact
+// counts.  The head's bias slice is read from a head-major copy of the table
+// (one contiguous read instead of one line per entry).  At the end the
+// compute waves stage their O rows in the ring and store whole token rows.
+// --------------------------------------------------------------------------
+constexpr int kKbWaveQueries = 32;
+constexpr int kKbComputeWaves = 8;
+constexpr int kKbLoaders = 2;
+constexpr int kKbQueries = kKbWaveQueries * kKbComputeWaves; // per workgroup
+constexpr int kKbKeys = 32;                                   // keys per block
+constexpr int kKbMaxStages = 8;
+constexpr int kKbMinStages = 3;
+
+struct KbLds {
+    int NK, NT, stages; // keys rounded up to whole blocks; table words; ring stages
+    size_t stage_bytes, ring_bytes, bias, tw, kb4, total;
+};
+
+__host__ __device__ inline KbLds kb_lds(const Geometry& g) {
+    KbLds L;
+    L.NK = (g.N + kKbKeys - 1) / kKbKeys * kKbKeys;
+    const int NQ = (g.N + kKbQueries - 1) / kKbQueries * kKbQueries;
+    L.NT = L.NK > NQ ? L.NK : NQ;
+    L.stage_bytes = (size_t)2 * kKbKeys * g.head_dim * 2; // K, then V
+    const size_t bias_bytes = ((size_t)g.table_size * 4 + 15) / 16 * 16;
+    const size_t fixed = bias_bytes + (size_t)L.NT * 4 + (size_t)L.NK * 4;
+    const size_t staging = (size_t)kKbQueries * g.head_dim * 2; // O rows, at the end
+    int st = kKbMaxStages;
+    while (st > 1 && fixed + (size_t)st * L.stage_bytes > (size_t)kLdsBytes) st--;
+    L.stages = st;
+    L.ring_bytes = (size_t)st * L.stage_bytes > staging ? (size_t)st * L.stage_bytes : staging;
+    L.bias = L.ring_bytes;
+    L.tw = L.bias + bias_bytes;
+    L.kb4 = L.tw + (size_t)L.NT * 4;
+    L.total = L.kb4 + (size_t)L.NK * 4;
+    return L;
+}
+
+__global__ __launch_bounds__(256) void bias_head_major_kernel(int table_size, int heads,
+                                                              const float* __restrict__ table,
+                                                              float* __restrict__ dst) {
+    const int64_t n = (int64_t)table_size * heads;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = e / heads;
+        const int hh = (int)(e - i * heads);
+        dst[(int64_t)hh * table_size + i] = table[e];
+    }
+}
+
+template <int D, bool BIAS_VEC>
+__global__ __launch_bounds__((kKbComputeWaves + kKbLoaders) * 64) void attn_bf16_kblock_kernel(
+    Geometry g, int staged, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ bias_hm, uint16_t* __restrict__ out) {
+    constexpr int THREADS = (kKbComputeWaves + kKbLoaders) * 64;
+    constexpr int KSTEPS = D / 32, DT = D / 16, CH = D / 8, RPC = 64 / CH;
+    constexpr int KCOPIES = kKbKeys * CH / 64;        // 1 KB copies per tensor per block
+    constexpr int LCOPIES = 2 * KCOPIES / kKbLoaders; // per loader wave per block
+    static_assert((2 * KCOPIES) % kKbLoaders == 0, "the copies of a block divide among the loaders");
+    extern __shared__ __align__(16) unsigned char smem[];
+    const KbLds L = kb_lds(g);
+    float* bias = (float*)(smem + L.bias);
+    int* tw = (int*)(smem + L.tw);
+    int* kb4 = (int*)(smem + L.kb4);
+    const int N = g.N;
+    const int NB = L.NK / kKbKeys, S = L.stages;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+    const int nqb = (N + kKbQueries - 1) / kKbQueries;
+
+    // block -> (window, head, query block): the query blocks and heads of a
+    // window run side by side on one XCD and share its L2 copy of K and V
+    const int64_t work = xcd_work_index(blockIdx.x, g.windows * g.heads * nqb);
+    const int64_t wh = work / nqb;
+    const int qblk = (int)(work - wh * nqb);
+    const uint32_t wi = (uint32_t)(wh / g.heads);
+    const int h = (int)(wh - (int64_t)wi * g.heads);
+    const int b = (int)fdiv(g.fd_nW, wi);
+    int wc[3];
+    {
+        const uint32_t r = wi - (uint32_t)b * (uint32_t)g.nW;
+        const uint32_t r2 = fdiv(g.fd_nwin2, r);
+        wc[2] = (int)(r - r2 * (uint32_t)g.nwin[2]);
+        wc[0] = (int)fdiv(g.fd_nwin1, r2);
+        wc[1] = (int)(r2 - (uint32_t)wc[0] * (uint32_t)g.nwin[1]);
+    }
+    const bool masked_window = window_maybe_masked(g, wc);
+
+    // ---- token table (packed as in the other bf16 kernels), key bias offsets
+    // and this head's bias slice
+    for (int n = tid; n < L.NT; n += THREADS) {
+        if (n < N) {
+            int l[3];
+            local_coords(g, n, l[0], l[1], l[2]);
+            int region = 0, tok = b;
+            bool is_pad = false;
+#pragma unroll
+            for (int a = 0; a < 3; a++) {
+                const int cr = wc[a] * g.win[a] + l[a];
+                int c = cr + g.shift[a];
+                if (c >= g.pad[a]) c -= g.pad[a];
+                is_pad |= c >= g.ext[a];
+                if (!g.cyc[a] && cr >= g.pad[a] - g.shift[a]) region |= 1 << a;
+                tok = tok * g.ext[a] + c;
+            }
+            const int row = is_pad ? -1 : (staged ? (int)(wi * (uint32_t)N + n) : tok);
+            tw[n] = (row + 1) | ((region | (is_pad ? 8 : 0)) << 28);
+            if (n < L.NK) kb4[n] = ((l[0] * g.tdy + l[1]) * g.tdx + l[2]) * 4;
+        } else {
+            tw[n] = 15 << 28;
+            if (n < L.NK) kb4[n] = BIAS_VEC ? 12 : 0; // keeps qb - kb (- 3) inside the table
+        }
+    }
+    {
+        const float* bsrc = bias_hm + (size_t)h * g.table_size;
+        for (int i = tid; i < g.table_size; i += THREADS) bias[i] = bsrc[i];
+    }
+    __syncthreads();
+
+    if (wave >= kKbComputeWaves) {
+        // ---- loader waves: copies j * LCOPIES .. of every block (K copies, then V)
+        const int j = wave - kKbComputeWaves;
+        auto issue = [&](int blk) __attribute__((always_inline)) {
+            unsigned char* st = smem + (size_t)(blk % S) * L.stage_bytes;
+#pragma unroll
+            for (int i = 0; i < LCOPIES; i++) {
+                const int c = j * LCOPIES + i;
+                const bool is_v = c >= KCOPIES;
+                const int cc = is_v ? c - KCOPIES : c;
+                const int m = cc * RPC + lane / CH; // key row in the block
+                const int r1 = tw[blk * kKbKeys + m] & kRowMask;
+                const uint64_t off = (uint64_t)(uint32_t)(r1 == 0 ? 0 : r1 - 1) * (uint32_t)g.row + h * D +
+                                     copy_chunk<D>(m, lane) * 8;
+                __builtin_amdgcn_global_load_lds((const void*)((is_v ? v : k) + off),
+                                                 (lds_void*)(st + (is_v ? kKbKeys * D * 2 : 0) + cc * 1024), 16, 0,
+                                                 0);
+            }
+        };
+        const int pre = NB < S - 1 ? NB : S - 1;
+        for (int blk = 0; blk < pre; blk++) issue(blk);
+        for (int blk = 0; blk < NB; blk++) {
+            // block blk has landed once at most the blocks issued after it remain
+            const int after = NB - 1 - blk < S - 2 ? NB - 1 - blk : S - 2;
+            wait_vmcnt_le(after * LCOPIES);
+            loader_barrier();
+            if (blk + S - 1 < NB) issue(blk + S - 1);
+        }
+        loader_barrier(); // final: the ring is free for the O rows
+        return;
+    }
+
+    // ---- compute waves: queries qbase .. qbase + 31 in two tiles
+    const int qbase = qblk * kKbQueries + wave * kKbWaveQueries;
+    const bool active = qbase < N;
+    const unsigned one2 = 0x3F803F80u; // two bf16 ones
+    const bf16x8 ones8 = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
+    int qreg[2], qr[2], qb4[2];
+    bf16x8 qf[2][KSTEPS]; // B operand: query n, d = 32 ks + 8 grp + 0..7
+    f32x4 o[2][DT], osum[2];
+    float mrun[2];
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+        const int n = qbase + t * 16 + col;
+        const int word = tw[n];
+        qreg[t] = (unsigned)word >> 28;
+        qr[t] = (word & kRowMask) - 1;
+        if (n < N) {
+            int lt, ly, lx;
+            local_coords(g, n, lt, ly, lx);
+            qb4[t] = (((lt * g.tdy + ly) * g.tdx + lx) + g.c0) * 4;
+        } else {
+            qb4[t] = (g.table_size - 1) * 4; // largest qb keeps qb - kb inside the table
+        }
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ks++) {
+            u32x4 val = {0, 0, 0, 0};
+            if (active && qr[t] >= 0)
+                val = *(const u32x4*)(q + (uint64_t)(uint32_t)qr[t] * (uint32_t)g.row + h * D + ks * 32 + grp * 8);
+            qf[t][ks] = __builtin_bit_cast(bf16x8, val);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        osum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mrun[t] = -INFINITY;
+    }
+
+    for (int blk = 0; blk < NB; blk++) {
+        lds_barrier();
+        if (!active) continue;
+        const unsigned char* st = smem + (size_t)(blk % S) * L.stage_bytes;
+        const uint16_t* Ks = (const uint16_t*)st;
+        const unsigned char* Vb = st + kKbKeys * D * 2;
+        const int key_base = blk * kKbKeys;
+        // S^T = K Q^T for both query tiles, each K fragment read once
+        f32x4 sc[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++) {
+            const int krow = kt * 16 + col;
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ks++) {
+                const bf16x8 a =
+                    __builtin_bit_cast(bf16x8, *(const u32x4*)(Ks + krow * D + k_slot<D>(krow, ks * 4 + grp) * 8));
+                a0 = mfma32(a, qf[0][ks], a0);
+                a1 = mfma32(a, qf[1][ks], a1);
+            }
+            sc[0][kt] = a0;
+            sc[1][kt] = a1;
+        }
+        // logits, natural units: scale * q.k + bias; then the mask where keys can be hidden
+        const bool need_mask = masked_window || key_base + kKbKeys > N;
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++) {
+            const int kq = key_base + kt * 16 + grp * 4;
+            if (BIAS_VEC) {
+                const int kb0 = kb4[kq]; // keys kq + i share a window row: biases at qb - kb0 - i
+#pragma unroll
+                for (int t = 0; t < 2; t++) {
+                    const float* bp = (const float*)((const unsigned char*)bias + qb4[t] - kb0 - 12);
+                    sc[t][kt] = f32x4{fmaf(sc[t][kt][0], g.scale, bp[3]), fmaf(sc[t][kt][1], g.scale, bp[2]),
+                                      fmaf(sc[t][kt][2], g.scale, bp[1]), fmaf(sc[t][kt][3], g.scale, bp[0])};
+                }
+            } else {
+                const int4 k4 = *(const int4*)(kb4 + kq);
+#pragma unroll
+                for (int t = 0; t < 2; t++) {
+                    const unsigned char* qb = (const unsigned char*)bias + qb4[t];
+                    sc[t][kt] = f32x4{fmaf(sc[t][kt][0], g.scale, *(const float*)(qb - k4.x)),
+                                      fmaf(sc[t][kt][1], g.scale, *(const float*)(qb - k4.y)),
+                                      fmaf(sc[t][kt][2], g.scale, *(const float*)(qb - k4.z)),
+                                      fmaf(sc[t][kt][3], g.scale, *(const float*)(qb - k4.w))};
+                }
+            }
+            if (need_mask) {
+                const int4 kr4 = *(const int4*)(tw + kq);
+#pragma unroll
+                for (int t = 0; t < 2; t++) {
+                    const unsigned qg = (unsigned)qreg[t];
+                    sc[t][kt][0] = ((unsigned)kr4.x >> 28) == qg ? sc[t][kt][0] : -INFINITY;
+                    sc[t][kt][1] = ((unsigned)kr4.y >> 28) == qg ? sc[t][kt][1] : -INFINITY;
+                    sc[t][kt][2] = ((unsigned)kr4.z >> 28) == qg ? sc[t][kt][2] : -INFINITY;
+                    sc[t][kt][3] = ((unsigned)kr4.w >> 28) == qg ? sc[t][kt][3] : -INFINITY;
+                }
+            }
+        }
+        // online softmax per query tile; P packed to bf16 (keys 0..31 of the block)
+        bf16x8 bop[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            float bmax = fmaxf(fmaxf(fmaxf(sc[t][0][0], sc[t][0][1]), fmaxf(sc[t][0][2], sc[t][0][3])),
+                               fmaxf(fmaxf(sc[t][1][0], sc[t][1][1]), fmaxf(sc[t][1][2], sc[t][1][3])));
+            bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+            bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+            const float mnew = fmaxf(mrun[t], bmax);
+            const float mc = (mnew == -INFINITY ? 0.f : mnew) * kLog2e;
+            if (__builtin_amdgcn_ballot_w64(mnew > mrun[t]) != 0) {
+                // some query of the tile has a larger max: rescale what earlier blocks gave
+                const float alpha = __builtin_amdgcn_exp2f(mrun[t] * kLog2e - mc);
+                osum[t] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; dt++) o[t][dt] *= alpha;
+            }
+            mrun[t] = mnew;
+            unsigned pk[4];
+#pragma unroll
+            for (int kt = 0; kt < 2; kt++) {
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[t][kt][i], kLog2e, -mc));
+                pk[2 * kt] = pack_bf16x2(p[0], p[1]);
+                pk[2 * kt + 1] = pack_bf16x2(p[2], p[3]);
+            }
+            bop[t] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+        }
+        // O^T += V^T P^T, each V^T fragment read once for both tiles; the row sums with A = 1
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            u32x2 half[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; kt++) {
+                const int row = kt * 16 + grp * 4 + (col >> 2);
+                const int d = dt * 16 + (col & 3) * 4;
+                const unsigned char* p = Vb + row * (D * 2) + k_slot<D>(row, d >> 3) * 16 + (d & 7) * 2;
+                half[kt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)p));
+            }
+            const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
+            o[0][dt] = mfma32(a, bop[0], o[0][dt]);
+            o[1][dt] = mfma32(a, bop[1], o[1][dt]);
+        }
+        osum[0] = mfma32(ones8, bop[0], osum[0]);
+        osum[1] = mfma32(ones8, bop[1], osum[1]);
+    }
+    lds_barrier(); // final: every wave is done with the ring
+    if (!active) return;
+
+    // ---- O: divide by the sum, stage this wave's 32 rows in the ring, store whole rows
+    uint16_t* Os = (uint16_t*)(smem + (size_t)wave * kKbWaveQueries * D * 2);
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+        const float inv = qr[t] >= 0 ? __builtin_amdgcn_rcpf(osum[t][0]) : 0.f;
+        const int m = t * 16 + col;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            const u32x2 w = {pack_bf16x2(o[t][dt][0] * inv, o[t][dt][1] * inv),
+                             pack_bf16x2(o[t][dt][2] * inv, o[t][dt][3] * inv)};
+            const int c = dt * 2 + (grp >> 1); // 16-byte chunk of d = 16 dt + 4 grp
+            *(u32x2*)(Os + m * D + k_slot<D>(m, c) * 8 + (grp & 1) * 4) = w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kKbWaveQueries / RPC; i++) {
+        const int m = i * RPC + lane / CH, c = lane % CH;
+        const u32x4 val = *(const u32x4*)(Os + m * D + k_slot<D>(m, c) * 8);
+        const int n = qbase + m;
+        const int r = (tw[n] & kRowMask) - 1;
+        // staged: pad slots of the window-major output get zeros (their sums are 0)
+        const int64_t orow = r >= 0 ? (int64_t)r : (staged && n < N ? (int64_t)wi * N + n : -1);
+        if (orow >= 0)
+            __builtin_nontemporal_store(val, (u32x4*)(out + orow * g.row + h * D + c * 8));
+    }
+}
+
+bool bf16_kblock_fits(const Geometry& g) {
+    const KbLds L = kb_lds(g);
+    const int64_t rows = (int64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
+    const int64_t wrows = g.windows * g.N;
+    return L.total <= (size_t)kLdsBytes && L.stages >= kKbMinStages && (rows > wrows ? rows : wrows) < kRowMask &&
+           g.windows * g.heads * ((g.N + kKbQueries - 1) / kKbQueries) < ((int64_t)1 << 31);
+}
+
+size_t bf16_kblock_workspace_bytes(const Geometry& g) { return (size_t)g.table_size * g.heads * sizeof(float); }
+
+template <int D>
+static bf16_kernel_t kblock_variant(bool bv) {
+    return bv ? attn_bf16_kblock_kernel<D, true> : attn_bf16_kblock_kernel<D, false>;
+}
+
+static bf16_kernel_t kblock_variant_for(const Geometry& g) {
+    const bool bv = g.win[2] % 4 == 0;
+    if (g.head_dim == 32) return kblock_variant<32>(bv);
+    if (g.head_dim == 128) return kblock_variant<128>(bv);
+    return kblock_variant<64>(bv);
+}
+
+static int64_t kblock_workgroups(const Geometry& g) {
+    return g.windows * g.heads * ((g.N + kKbQueries - 1) / kKbQueries);
+}
+
+hipError_t kblock_plan(const Geometry& g, int* blocks) {
+    int per_cu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, (const void*)kblock_variant_for(g), (kKbComputeWaves + kKbLoaders) * 64, kb_lds(g).total);
+    if (e != hipSuccess) return e;
+    *blocks = per_cu < 1 ? 0 : (int)kblock_workgroups(g);
+    return hipSuccess;
+}
+
+hipError_t launch_attention_kblock(const Geometry& g, bool staged, const uint16_t* q, const uint16_t* k,
+                                   const uint16_t* v, const float* table, float* bias_hm, uint16_t* out,
+                                   hipStream_t s) {
+    const int64_t n = (int64_t)g.table_size * g.heads;
+    const int64_t tb = (n + 255) / 256;
+    hipLaunchKernelGGL(bias_head_major_kernel, dim3((unsigned)(tb < 1024 ? tb : 1024)), dim3(256), 0, s,
+                       g.table_size, g.heads, table, bias_hm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kblock_variant_for(g), dim3((unsigned)kblock_workgroups(g)),
+                       dim3((kKbComputeWaves + kKbLoaders) * 64), kb_lds(g).total, s, g, (int)staged, q, k, v,
+                       (const float*)bias_hm, out);
+    return hipGetLastError();
+}
+
 size_t attention_lds_bytes(const Geometry& g, bool bf16) {
-    return bf16 ? bf16_lds(g).total : f32_lds_bytes(g);
+    if (!bf16) return f32_lds_bytes(g);
+    // the smallest footprint among the bf16 schedules that can take the window
+    size_t best = (size_t)-1;
+    if (bf16_stream_fits(g)) best = stream_lds(g).total;
+    if (bf16_block_fits(g) && bf16_lds(g).total < best) best = bf16_lds(g).total;
+    if (bf16_kblock_fits(g) && kb_lds(g).total < best) best = kb_lds(g).total;
+    return best;
 }
 
 // Kernel variant for a geometry: specialised tile counts, else the general one.
-typedef void (*bf16_kernel_t)(Geometry, int, const uint16_t*, const uint16_t*, const uint16_t*,
-                              const float*, uint16_t*);
 struct Bf16Variant {
     bf16_kernel_t f;
     int waves; // waves per workgroup
@@ -1378,6 +1774,11 @@ static Bf16Variant bf16_variant_for(const Geometry& g, bool stream) {
     return bv ? bf16_variant_b<64, true>(KT) : bf16_variant_b<64, false>(KT);
 }
 
+bool bf16_block_fits(const Geometry& g) {
+    // the general per-unit variant takes up to 8 waves x 4 tiles = 512 tokens
+    return g.N <= 512 && bf16_lds(g).total <= (size_t)kLdsBytes;
+}
+
 bool bf16_stream_fits(const Geometry& g) {
     const int64_t rows = (int64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
     const int64_t wrows = g.windows * g.N;
@@ -1440,6 +1841,12 @@ hipError_t prepare_kernels(int max_lds) {
                     hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
                 if (e != hipSuccess) return e;
             }
+        }
+    }
+    for (bool bv : {true, false}) {
+        for (bf16_kernel_t f : {kblock_variant<32>(bv), kblock_variant<64>(bv), kblock_variant<128>(bv)}) {
+            hipError_t e = hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+            if (e != hipSuccess) return e;
         }
     }
     return hipSuccess;

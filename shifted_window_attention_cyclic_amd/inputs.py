@@ -5,10 +5,14 @@ random draws that both the library's tests and the oracle's tests feed in.
 Shapes follow the grids the pages work on: the 0.25 degree field and the
 1/12 degree field at patch size 4 (TERRA page, Table V patch size; BEAST's
 0.25 degree atmosphere), with heads and window sizes in the range of TERRA's
-Table V.  The sixth workload is the layer shape of Table V's Small model
-(d = 1024 over N_h = 8 heads of 128, w = 8) on the 0.25 degree grid.  All
-tensors are [B, T, H, W, heads, head_dim], C-contiguous, over the REAL
-extents; axis 0 is time, 1 latitude, 2 longitude.
+Table V.  The sixth and seventh workloads are the layer shapes of Table V's
+Small model (d = 1024 over N_h = 8 heads of 128, w = 8) and Large model
+(d = 8192 over N_h = 64 heads of 128, w = 32).  32-wide windows tile neither
+360 nor 1080 longitude points, so the Large shape takes the 0.25 degree
+grid's 180 latitude rows (padded to 192) and 384 longitude points, the next
+multiple of 32.  All tensors are [B, T, H, W, heads, head_dim],
+C-contiguous, over the REAL extents; axis 0 is time, 1 latitude, 2
+longitude.
 """
 from dataclasses import dataclass, replace
 from typing import Optional, Tuple
@@ -85,6 +89,10 @@ WORKLOADS = {
     # latitude rows padded to 184 so that the windows tile the grid
     "c6_bf16_180x360_pad184_d128": Problem("c6_bf16_180x360_pad184_d128", "bf16", 1, 8, 128, (1, 180, 360),
                                            (1, 184, 360), (1, 8, 8), (0, 4, 4), seed=1005),
+    # TERRA, Table V, Large model: 64 heads of 128, 32 x 32 windows (N = 1024)
+    "c7_bf16_180x384_pad192_d128_w32": Problem("c7_bf16_180x384_pad192_d128_w32", "bf16", 1, 64, 128,
+                                               (1, 180, 384), (1, 192, 384), (1, 32, 32), (0, 16, 16),
+                                               seed=1006),
 }
 ORDER = list(WORKLOADS)
 

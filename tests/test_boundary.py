@@ -79,8 +79,11 @@ BAD = [
     ("head_dim48", BASE.with_(head_dim=48), binding.SWA_ERR_UNSUPPORTED),
     ("head_dim256", BASE.with_(head_dim=256), binding.SWA_ERR_UNSUPPORTED),
     ("head_dim128_f32", WORKLOADS["c1_f32_16x32"].with_(head_dim=128), binding.SWA_ERR_UNSUPPORTED),
-    ("window_27x27_bf16", BASE.with_(window=(1, 27, 27)), binding.SWA_ERR_UNSUPPORTED),
-    ("bf16_window_over_512", BASE.with_(extent=(1, 540, 1080), window=(1, 20, 27)), binding.SWA_ERR_UNSUPPORTED),
+    # N = 10800: its bias slice (179 x 239 floats) alone leaves no LDS for any schedule
+    ("bf16_window_90x120", BASE.with_(window=(1, 90, 120), shift=(0, 45, 60)), binding.SWA_ERR_UNSUPPORTED),
+    ("f32_window_27x27", WORKLOADS["c1_f32_16x32"].with_(extent=(1, 27, 27), padded=(1, 27, 27),
+                                                          window=(1, 27, 27), shift=(0, 13, 13)),
+     binding.SWA_ERR_UNSUPPORTED),
 ]
 
 

@@ -63,10 +63,25 @@ EDGE = {
 }
 
 
-@pytest.mark.parametrize("name", list(SMALL) + list(EDGE))
-@pytest.mark.parametrize("variant,schedule", [("fused", "auto"), ("staged", "auto"), ("fused", "block")])
+# windows of more than 512 tokens: only the key-blocked schedule takes them
+LARGE = {
+    # TERRA Table V's Large-model window (32 x 32, 128-wide heads), latitude padded 40 -> 64
+    "n1024_d128_pad": _edge("n1024", "bf16", 1, 2, 128, (1, 40, 64), (1, 64, 64), (1, 32, 32), (0, 16, 16)),
+    "n1024_d64": _edge("n1024d64", "bf16", 1, 3, 64, (1, 64, 64), (1, 64, 64), (1, 32, 32), (0, 16, 16)),
+    # 540 keys (a ragged last key block), 3 query blocks, window width 27 (no 4-key bias runs)
+    "n540_ragged": _edge("n540", "bf16", 1, 2, 64, (1, 36, 54), (1, 40, 54), (1, 20, 27), (0, 10, 13)),
+    # 3-D, time padded 5 -> 6 and masked, 32-wide heads
+    "n768_3d_d32": _edge("n768", "bf16", 1, 3, 32, (5, 16, 32), (6, 16, 32), (3, 16, 16), (1, 8, 8)),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL) + list(EDGE) + list(LARGE))
+@pytest.mark.parametrize("variant,schedule", [("fused", "auto"), ("staged", "auto"), ("fused", "block"),
+                                              ("fused", "keyblock")])
 def test_parity_small_full_grid(name, variant, schedule):
-    p = SMALL.get(name) or EDGE[name]
+    p = SMALL.get(name) or EDGE.get(name) or LARGE[name]
+    if schedule == "block" and p.window_tokens > 512:
+        pytest.skip("the per-unit schedule takes windows of at most 512 tokens")
     say(f"[parity] {name} {variant} {schedule} dtype={p.dtype} B={p.batch} grid={p.extent} pad={p.padded} "
         f"win={p.window} shift={p.shift} heads={p.heads}x{p.head_dim} seed={p.seed}")
     x, d = device_inputs(p)
@@ -79,7 +94,7 @@ def test_parity_small_full_grid(name, variant, schedule):
 
 
 FULL = ["c2_bf16_180x360", "c3_bf16_540x1080", "c4_bf16_181x360_pad190", "c5_bf16_4x180x360_3d",
-        "c6_bf16_180x360_pad184_d128"]
+        "c6_bf16_180x360_pad184_d128", "c7_bf16_180x384_pad192_d128_w32"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -100,9 +115,18 @@ def test_parity_full_size_sampled(name):
     # the staged variant runs the same attention arithmetic on window-major copies
     out2 = run(p, d, "staged")
     assert torch.equal(out, out2)
-    # the per-window-block schedule computes the same sums in the same order
-    out3 = run(p, d, "fused", "block")
-    assert torch.equal(out, out3)
+    del out2
+    if p.window_tokens <= 512:
+        # the per-window-block schedule computes the same sums in the same order
+        out3 = run(p, d, "fused", "block")
+        assert torch.equal(out, out3)
+        del out3
+        # the key-blocked schedule sums in blocks of 32 keys: within tolerance of the oracle
+        out4 = run(p, d, "fused", "keyblock")
+        got4 = host_f32(out4).reshape(p.tokens, p.heads, p.head_dim)[idx]
+        err4 = rel_err(got4, ref)
+        say(f"  key-blocked schedule: rel err {err4:.3e}")
+        assert err4 <= TOL[p.dtype]
 
 
 def test_fp32_full_workload_matches_oracle_everywhere():
@@ -282,12 +306,13 @@ def test_larger_logits_still_match():
 @pytest.mark.gpu
 def test_auto_schedule_choice():
     """AUTO takes the streaming schedule for windows of up to 9 query tiles that
-    fit its LDS ring, and the per-(window, head) schedule otherwise."""
+    fit its LDS ring, else the per-(window, head) schedule for windows of up to
+    512 tokens that fit its LDS, else the key-blocked one."""
     want = {"c2_bf16_180x360": 1, "c3_bf16_540x1080": 1, "c4_bf16_181x360_pad190": 1,
-            "c5_bf16_4x180x360_3d": 2, "c6_bf16_180x360_pad184_d128": 1}
-    small = {"d128_n80_ragged": 1, "d128_n144": 2, "d128_n288_3d": 2}
+            "c5_bf16_4x180x360_3d": 2, "c6_bf16_180x360_pad184_d128": 1, "c7_bf16_180x384_pad192_d128_w32": 3}
+    small = {"d128_n80_ragged": 1, "d128_n144": 2, "d128_n288_3d": 2, "n1024_d128_pad": 3, "n540_ragged": 3}
     for name, schedule in small.items():
-        att = WindowAttention(EDGE[name])
+        att = WindowAttention(EDGE.get(name) or LARGE[name])
         assert att.info.schedule == schedule, name
         att.close()
     for name, schedule in want.items():
