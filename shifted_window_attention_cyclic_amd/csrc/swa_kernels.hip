@@ -1317,14 +1317,22 @@ typedef void (*bf16_kernel_t)(Geometry, int, const uint16_t*, const uint16_t*, c
 // and V fragment it reads from LDS feeds two MFMAs.  Two loader waves stream
 // K and V in blocks of 32 keys through a ring of LDS stages with
 // global_load_lds (the swizzled [key][d] layout of the other bf16 kernels)
-// and the compute waves run an online softmax over the blocks: running max
-// per query; O and the row sum rescaled when some query's max grows (a
-// wave-uniform test, so that the common case skips it).  One barrier per
+// and the compute waves run an online softmax over the blocks.  The logits
+// come straight out of the MFMA: its accumulator starts at bias / scale, so
+// S^T holds q.k + bias / scale and the exponent is one FMA with scale *
+// log2(e).  The exponent's reference M per query moves lazily: a block
+// whose logits all stay within 2^8 of exp2(M) (a per-lane test and one
+// ballot) is exponentiated against M as it stands (P <= 256, exact in the
+// final ratio, and fp32 sums cannot overflow); otherwise the wave takes the
+// exact block max across lanes, M moves to it and O and the row sum are
+// rescaled.  Softmax is invariant to the reference, so the result is the
+// same function; only rounding differs.  One barrier per
 // block: at barrier j block j has landed and block j - 1 is no longer read,
 // so the loaders refill its stage with block j + stages - 1; a wave's vector
 // memory operations complete in order, so the loaders' waits are exact
 // counts.  The head's bias slice is read from a head-major copy of the table
-// (one contiguous read instead of one line per entry).  At the end the
+// holding bias / scale (one contiguous read instead of one line per entry,
+// refreshed by a small kernel before each launch).  At the end the
 // compute waves stage their O rows in the ring and store whole token rows.
 // --------------------------------------------------------------------------
 constexpr int kKbWaveQueries = 32;
@@ -1334,6 +1342,7 @@ constexpr int kKbQueries = kKbWaveQueries * kKbComputeWaves; // per workgroup
 constexpr int kKbKeys = 32;                                   // keys per block
 constexpr int kKbMaxStages = 8;
 constexpr int kKbMinStages = 3;
+constexpr float kKbSlack = 8.f; // log2 of the largest P before the reference max moves
 
 struct KbLds {
     int NK, NT, stages; // keys rounded up to whole blocks; table words; ring stages
@@ -1360,14 +1369,15 @@ __host__ __device__ inline KbLds kb_lds(const Geometry& g) {
     return L;
 }
 
-__global__ __launch_bounds__(256) void bias_head_major_kernel(int table_size, int heads,
+// dst[h][i] = table[i][h] / scale
+__global__ __launch_bounds__(256) void bias_head_major_kernel(int table_size, int heads, float scale,
                                                               const float* __restrict__ table,
                                                               float* __restrict__ dst) {
     const int64_t n = (int64_t)table_size * heads;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
         const int64_t i = e / heads;
         const int hh = (int)(e - i * heads);
-        dst[(int64_t)hh * table_size + i] = table[e];
+        dst[(int64_t)hh * table_size + i] = table[e] / scale;
     }
 }
 
@@ -1481,7 +1491,8 @@ __global__ __launch_bounds__((kKbComputeWaves + kKbLoaders) * 64) void attn_bf16
     int qreg[2], qr[2], qb4[2];
     bf16x8 qf[2][KSTEPS]; // B operand: query n, d = 32 ks + 8 grp + 0..7
     f32x4 o[2][DT], osum[2];
-    float mrun[2];
+    float mref[2];                       // exponent reference per query, log2 units
+    const float c2 = g.scale * kLog2e;   // logits (q.k + bias / scale) to log2 units
 #pragma unroll
     for (int t = 0; t < 2; t++) {
         const int n = qbase + t * 16 + col;
@@ -1505,7 +1516,7 @@ __global__ __launch_bounds__((kKbComputeWaves + kKbLoaders) * 64) void attn_bf16
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         osum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        mrun[t] = -INFINITY;
+        mref[t] = -INFINITY;
     }
 
     for (int blk = 0; blk < NB; blk++) {
@@ -1515,48 +1526,45 @@ __global__ __launch_bounds__((kKbComputeWaves + kKbLoaders) * 64) void attn_bf16
         const uint16_t* Ks = (const uint16_t*)st;
         const unsigned char* Vb = st + kKbKeys * D * 2;
         const int key_base = blk * kKbKeys;
-        // S^T = K Q^T for both query tiles, each K fragment read once
+        // S^T = K Q^T + bias / scale for both query tiles (the accumulators start at
+        // the biases), each K fragment read once
         f32x4 sc[2][2];
 #pragma unroll
         for (int kt = 0; kt < 2; kt++) {
-            const int krow = kt * 16 + col;
-            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ks++) {
-                const bf16x8 a =
-                    __builtin_bit_cast(bf16x8, *(const u32x4*)(Ks + krow * D + k_slot<D>(krow, ks * 4 + grp) * 8));
-                a0 = mfma32(a, qf[0][ks], a0);
-                a1 = mfma32(a, qf[1][ks], a1);
-            }
-            sc[0][kt] = a0;
-            sc[1][kt] = a1;
-        }
-        // logits, natural units: scale * q.k + bias; then the mask where keys can be hidden
-        const bool need_mask = masked_window || key_base + kKbKeys > N;
-#pragma unroll
-        for (int kt = 0; kt < 2; kt++) {
             const int kq = key_base + kt * 16 + grp * 4;
+            f32x4 acc[2];
             if (BIAS_VEC) {
                 const int kb0 = kb4[kq]; // keys kq + i share a window row: biases at qb - kb0 - i
 #pragma unroll
                 for (int t = 0; t < 2; t++) {
                     const float* bp = (const float*)((const unsigned char*)bias + qb4[t] - kb0 - 12);
-                    sc[t][kt] = f32x4{fmaf(sc[t][kt][0], g.scale, bp[3]), fmaf(sc[t][kt][1], g.scale, bp[2]),
-                                      fmaf(sc[t][kt][2], g.scale, bp[1]), fmaf(sc[t][kt][3], g.scale, bp[0])};
+                    acc[t] = f32x4{bp[3], bp[2], bp[1], bp[0]};
                 }
             } else {
                 const int4 k4 = *(const int4*)(kb4 + kq);
 #pragma unroll
                 for (int t = 0; t < 2; t++) {
                     const unsigned char* qb = (const unsigned char*)bias + qb4[t];
-                    sc[t][kt] = f32x4{fmaf(sc[t][kt][0], g.scale, *(const float*)(qb - k4.x)),
-                                      fmaf(sc[t][kt][1], g.scale, *(const float*)(qb - k4.y)),
-                                      fmaf(sc[t][kt][2], g.scale, *(const float*)(qb - k4.z)),
-                                      fmaf(sc[t][kt][3], g.scale, *(const float*)(qb - k4.w))};
+                    acc[t] = f32x4{*(const float*)(qb - k4.x), *(const float*)(qb - k4.y),
+                                   *(const float*)(qb - k4.z), *(const float*)(qb - k4.w)};
                 }
             }
-            if (need_mask) {
-                const int4 kr4 = *(const int4*)(tw + kq);
+            const int krow = kt * 16 + col;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ks++) {
+                const bf16x8 a =
+                    __builtin_bit_cast(bf16x8, *(const u32x4*)(Ks + krow * D + k_slot<D>(krow, ks * 4 + grp) * 8));
+                acc[0] = mfma32(a, qf[0][ks], acc[0]);
+                acc[1] = mfma32(a, qf[1][ks], acc[1]);
+            }
+            sc[0][kt] = acc[0];
+            sc[1][kt] = acc[1];
+        }
+        // the mask, where keys can be hidden
+        if (masked_window || key_base + kKbKeys > N) {
+#pragma unroll
+            for (int kt = 0; kt < 2; kt++) {
+                const int4 kr4 = *(const int4*)(tw + key_base + kt * 16 + grp * 4);
 #pragma unroll
                 for (int t = 0; t < 2; t++) {
                     const unsigned qg = (unsigned)qreg[t];
@@ -1567,30 +1575,39 @@ __global__ __launch_bounds__((kKbComputeWaves + kKbLoaders) * 64) void attn_bf16
                 }
             }
         }
-        // online softmax per query tile; P packed to bf16 (keys 0..31 of the block)
-        bf16x8 bop[2];
+        // exponent reference: moves only when a logit passes it by more than the slack
+        float lmax[2];
+        bool grow = false;
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-            float bmax = fmaxf(fmaxf(fmaxf(sc[t][0][0], sc[t][0][1]), fmaxf(sc[t][0][2], sc[t][0][3])),
-                               fmaxf(fmaxf(sc[t][1][0], sc[t][1][1]), fmaxf(sc[t][1][2], sc[t][1][3])));
-            bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-            bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-            const float mnew = fmaxf(mrun[t], bmax);
-            const float mc = (mnew == -INFINITY ? 0.f : mnew) * kLog2e;
-            if (__builtin_amdgcn_ballot_w64(mnew > mrun[t]) != 0) {
-                // some query of the tile has a larger max: rescale what earlier blocks gave
-                const float alpha = __builtin_amdgcn_exp2f(mrun[t] * kLog2e - mc);
+            lmax[t] = fmaxf(fmaxf(fmaxf(sc[t][0][0], sc[t][0][1]), fmaxf(sc[t][0][2], sc[t][0][3])),
+                            fmaxf(fmaxf(sc[t][1][0], sc[t][1][1]), fmaxf(sc[t][1][2], sc[t][1][3]))) * c2;
+            grow |= lmax[t] > mref[t] + kKbSlack;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                float bm = fmaxf(lmax[t], __shfl_xor(lmax[t], 16));
+                bm = fmaxf(bm, __shfl_xor(bm, 32));
+                const float mn = fmaxf(mref[t], bm);
+                const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref[t] - mn);
                 osum[t] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < DT; dt++) o[t][dt] *= alpha;
+                mref[t] = mn;
             }
-            mrun[t] = mnew;
+        }
+        // P = exp2(c2 * logit - M), packed to bf16 (keys 0..31 of the block)
+        bf16x8 bop[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const float mc = mref[t] == -INFINITY ? 0.f : mref[t];
             unsigned pk[4];
 #pragma unroll
             for (int kt = 0; kt < 2; kt++) {
                 float p[4];
 #pragma unroll
-                for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[t][kt][i], kLog2e, -mc));
+                for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[t][kt][i], c2, -mc));
                 pk[2 * kt] = pack_bf16x2(p[0], p[1]);
                 pk[2 * kt + 1] = pack_bf16x2(p[2], p[3]);
             }
@@ -1685,7 +1702,7 @@ hipError_t launch_attention_kblock(const Geometry& g, bool staged, const uint16_
     const int64_t n = (int64_t)g.table_size * g.heads;
     const int64_t tb = (n + 255) / 256;
     hipLaunchKernelGGL(bias_head_major_kernel, dim3((unsigned)(tb < 1024 ? tb : 1024)), dim3(256), 0, s,
-                       g.table_size, g.heads, table, bias_hm);
+                       g.table_size, g.heads, g.scale, table, bias_hm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kblock_variant_for(g), dim3((unsigned)kblock_workgroups(g)),
