@@ -10,13 +10,17 @@ Two formulations, written separately and required to agree:
     directly from per-axis segments; usable at full size on selected queries;
   * ``literal_forward`` (numpy): pad, roll, partition, masked window
     attention, reverse; for small grids.
+
+``literal_backward`` (numpy) gives the gradients of the literal form, window
+by window, for all windows or a chosen subset.
 """
 from .direct import check, default_scale, direct_forward, local_coord, visible
+from .backward import literal_backward, token_windows
 from .literal import (literal_bias, literal_forward, literal_unwindows, literal_visibility,
                       literal_windows, pad_flags)
 
 __all__ = [
     "check", "default_scale", "direct_forward", "local_coord", "visible",
     "literal_bias", "literal_forward", "literal_unwindows", "literal_visibility",
-    "literal_windows", "pad_flags",
+    "literal_windows", "pad_flags", "literal_backward", "token_windows",
 ]
