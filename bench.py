@@ -29,6 +29,7 @@ PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 MALL_BYTES = 256 << 20     # Infinity Cache; rotate inputs until the working set is 3x this
 KERNEL_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_kernels.hip",
+                  "shifted_window_attention_cyclic_amd/csrc/swa_device.h",
                   "shifted_window_attention_cyclic_amd/csrc/swa_geometry.h"]
 SCHEDULE_STREAM, SCHEDULE_BLOCK, SCHEDULE_KEYBLOCK = 1, 2, 3  # swa_info.schedule
 CPU_SAMPLE_FLOPS = 4e11  # nominal FLOPs of the CPU-baseline sample (about 10 s of fp64 on 16 cores)

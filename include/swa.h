@@ -117,6 +117,9 @@ typedef struct swa_info {
     double algorithmic_bytes;   /* q, k, v read and out written once, real tokens, plus the table */
     int32_t schedule;           /* bf16: the schedule in use (_STREAM, _BLOCK or _KEYBLOCK); fp32: 0 */
     int32_t workgroups;         /* bf16: workgroups per attention launch; fp32: 0 */
+    size_t backward_workspace_bytes; /* workspace swa_backward needs; 0: the backward pass does not take
+                                        this window (bf16: more than 144 tokens or past LDS; fp32: past
+                                        LDS or head_dim above 64) */
 } swa_info;
 
 /*
@@ -140,6 +143,29 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out);
  */
 swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* v,
                        const float* bias_table, void* out, void* stream);
+
+/*
+ * Gradients of the forward pass (the pages' models are trained: TERRA page,
+ * abstract and Table V).  Given dout = dL/d(out) in the layout of out, writes
+ * dq, dk, dv = dL/dq, dL/dk, dL/dv (layout and dtype of q, k, v; every real
+ * token) and dtable = dL/d(bias_table) (fp32, the table's layout); all four
+ * are overwritten.  The pad tokens of a window have no output, so they add
+ * nothing.  workspace: device buffer of info.backward_workspace_bytes bytes,
+ * 16-byte aligned, owned by the caller (per-(window, head) shares of the
+ * table gradient and their partial sums; its contents on entry do not
+ * matter).  The pass reads and writes the spatial layout whatever the
+ * variant and allocates nothing.  dq, dk and dv are bitwise reproducible;
+ * dtable sums the (window, head) shares in a fixed order, but inside one
+ * share the additions run in whatever order the share's waves reach them,
+ * so it is reproducible to fp32 rounding.  Asynchronous on `stream`, like
+ * swa_forward.
+ * Errors: INVALID_ARGUMENT (NULL handle or pointer, misalignment, a buffer
+ * written that overlaps another argument), UNSUPPORTED (the window is beyond
+ * the backward kernels: backward_workspace_bytes is 0), HIP (launch failure).
+ */
+swa_status swa_backward(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
+                        const void* dout, void* dq, void* dk, void* dv, float* dtable, void* workspace,
+                        void* stream);
 
 /* Frees the handle and its workspace (synchronising the device first when a
  * workspace exists).  NULL is a no-op returning SWA_OK. */

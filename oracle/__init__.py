@@ -15,12 +15,12 @@ Two formulations, written separately and required to agree:
 by window, for all windows or a chosen subset.
 """
 from .direct import check, default_scale, direct_forward, local_coord, visible
-from .backward import literal_backward, token_windows
+from .backward import literal_backward, token_windows, window_tokens
 from .literal import (literal_bias, literal_forward, literal_unwindows, literal_visibility,
                       literal_windows, pad_flags)
 
 __all__ = [
     "check", "default_scale", "direct_forward", "local_coord", "visible",
     "literal_bias", "literal_forward", "literal_unwindows", "literal_visibility",
-    "literal_windows", "pad_flags", "literal_backward", "token_windows",
+    "literal_windows", "pad_flags", "literal_backward", "token_windows", "window_tokens",
 ]

@@ -19,7 +19,7 @@ SWA_SCHEDULE_AUTO, SWA_SCHEDULE_STREAM, SWA_SCHEDULE_BLOCK, SWA_SCHEDULE_KEYBLOC
 SCHEDULES = {"auto": SWA_SCHEDULE_AUTO, "stream": SWA_SCHEDULE_STREAM, "block": SWA_SCHEDULE_BLOCK,
              "keyblock": SWA_SCHEDULE_KEYBLOCK}
 
-EXPORTS = ("swa_create", "swa_forward", "swa_destroy", "swa_get_info", "swa_status_string",
+EXPORTS = ("swa_create", "swa_forward", "swa_backward", "swa_destroy", "swa_get_info", "swa_status_string",
            "swa_last_error", "swa_gather", "swa_scatter", "swa_debug_visibility")
 
 
@@ -39,6 +39,7 @@ class swa_info(ctypes.Structure):
         ("window_major_elems", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
         ("nominal_flops", ctypes.c_double), ("algorithmic_bytes", ctypes.c_double),
         ("schedule", ctypes.c_int32), ("workgroups", ctypes.c_int32),
+        ("backward_workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -64,6 +65,8 @@ def load_library(path: str = LIBRARY):
     lib.swa_create.restype = st
     lib.swa_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.swa_forward.restype = st
+    lib.swa_backward.argtypes = [vp] * 12
+    lib.swa_backward.restype = st
     lib.swa_destroy.argtypes = [vp]
     lib.swa_destroy.restype = st
     lib.swa_get_info.argtypes = [vp, ctypes.POINTER(swa_info)]
@@ -152,6 +155,15 @@ def swa_forward(handle, q, k, v, table, out, stream=None) -> None:
                                       _stream(stream)))
 
 
+def swa_backward(handle, q, k, v, table, dout, dq, dk, dv, dtable, workspace, stream=None) -> None:
+    dt = q.dtype
+    _check(load_library().swa_backward(handle, _dev(q, "q"), _dev(k, "k", dt), _dev(v, "v", dt),
+                                       _dev(table, "table", torch.float32), _dev(dout, "dout", dt),
+                                       _dev(dq, "dq", dt), _dev(dk, "dk", dt), _dev(dv, "dv", dt),
+                                       _dev(dtable, "dtable", torch.float32), _dev(workspace, "workspace"),
+                                       _stream(stream)))
+
+
 def swa_gather(handle, src, dst_window_major, stream=None) -> None:
     _check(load_library().swa_gather(handle, _dev(src, "src"), _dev(dst_window_major, "dst", src.dtype),
                                      _stream(stream)))
@@ -200,6 +212,21 @@ class WindowAttention:
         self._shape(out, self.io_shape, "out")
         swa_forward(self.handle, q, k, v, table, out, stream)
         return out
+
+    def backward(self, q, k, v, table, dout, stream=None):
+        """Gradients (dq, dk, dv, dtable) of sum(dout * forward(q, k, v, table))."""
+        for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+            self._shape(t, self.io_shape, name)
+        w = self.problem.window
+        self._shape(table, (2 * w[0] - 1, 2 * w[1] - 1, 2 * w[2] - 1, self.problem.heads), "table")
+        nws = self.info.backward_workspace_bytes
+        if nws == 0:
+            raise SwaError(SWA_ERR_UNSUPPORTED, "the backward kernels do not take this window")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dtable = torch.empty_like(table)
+        ws = torch.empty((nws + 15) // 16 * 4, dtype=torch.float32, device=q.device)
+        swa_backward(self.handle, q, k, v, table, dout, dq, dk, dv, dtable, ws, stream)
+        return dq, dk, dv, dtable
 
     def gather(self, src, dst=None, stream=None):
         self._shape(src, self.io_shape, "src")

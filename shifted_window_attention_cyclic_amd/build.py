@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libswa.so")
-SOURCES = [os.path.join(CSRC, "swa_kernels.hip"), os.path.join(CSRC, "swa_api.cpp")]
+SOURCES = [os.path.join(CSRC, "swa_kernels.hip"), os.path.join(CSRC, "swa_backward.hip"),
+           os.path.join(CSRC, "swa_api.cpp")]
 ARCH = "gfx950"
 
 

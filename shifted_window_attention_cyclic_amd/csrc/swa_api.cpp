@@ -202,6 +202,7 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
         return fail(SWA_ERR_UNSUPPORTED, buf);
     }
     if ((e = swa::prepare_kernels(max_lds)) != hipSuccess) return fail_hip(e, "hipFuncSetAttribute");
+    if ((e = swa::prepare_backward_kernels(max_lds)) != hipSuccess) return fail_hip(e, "hipFuncSetAttribute");
     int schedule = 0, blocks = 0;
     if (cfg->dtype == SWA_BF16) {
         // AUTO: the streaming schedule, else the per-unit one, else the key-blocked one,
@@ -284,6 +285,7 @@ swa_status swa_get_info(const swa_handle* h, swa_info* info) {
     const bool bf16 = h->cfg.dtype == SWA_BF16;
     info->schedule = bf16 ? h->schedule : 0;
     info->workgroups = bf16 ? h->blocks : 0;
+    info->backward_workspace_bytes = swa::backward_fits(g, bf16) ? swa::backward_workspace_bytes(g) : 0;
     return SWA_OK;
 }
 
@@ -330,6 +332,34 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
     if ((e = attention(true, wq, wk, wv, wo)) != hipSuccess) return fail_hip(e, "attention launch");
     if ((e = swa::launch_scatter(g, h->elem_bytes, wo, out, s)) != hipSuccess) return fail_hip(e, "scatter launch");
     return SWA_OK;
+}
+
+swa_status swa_backward(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
+                        const void* dout, void* dq, void* dk, void* dv, float* dtable, void* workspace,
+                        void* stream) {
+    if (!h || !q || !k || !v || !bias_table || !dout || !dq || !dk || !dv || !dtable || !workspace)
+        return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    const void* tensors[] = {q, k, v, dout, dq, dk, dv, workspace};
+    for (const void* p : tensors)
+        if (!aligned(p, 16)) return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned pointer (tensors and workspace need 16 bytes)");
+    if (!aligned(bias_table, 4) || !aligned(dtable, 4)) return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned table");
+    const swa::Geometry& g = h->g;
+    const bool bf16 = h->cfg.dtype == SWA_BF16;
+    if (!swa::backward_fits(g, bf16))
+        return fail(SWA_ERR_UNSUPPORTED, "the backward kernels do not take this window");
+    const size_t n = io_bytes(h);
+    const size_t nt = (size_t)g.table_size * g.heads * sizeof(float);
+    const size_t nw = swa::backward_workspace_bytes(g);
+    // every buffer written must be disjoint from every other argument
+    const void* all[] = {q, k, v, dout, bias_table, dq, dk, dv, dtable, workspace};
+    const size_t len[] = {n, n, n, n, nt, n, n, n, nt, nw};
+    for (int i = 5; i < 10; i++)
+        for (int j = 0; j < 10; j++)
+            if (j != i && overlap(all[i], len[i], all[j], len[j]))
+                return fail(SWA_ERR_INVALID_ARGUMENT, "a gradient or the workspace overlaps another argument");
+    hipError_t e = swa::launch_backward(g, bf16, q, k, v, bias_table, dout, dq, dk, dv, dtable, workspace,
+                                        (hipStream_t)stream);
+    return e == hipSuccess ? SWA_OK : fail_hip(e, "backward launch");
 }
 
 swa_status swa_gather(swa_handle* h, const void* src, void* dst_window_major, void* stream) {

@@ -167,4 +167,15 @@ hipError_t launch_attention_kblock(const Geometry& g, bool staged, const uint16_
 // Lets every attention kernel take up to max_lds bytes of dynamic LDS.
 hipError_t prepare_kernels(int max_lds);
 
+// Backward pass (swa_backward.hip): whether a kernel takes the window, the
+// workspace it needs (bytes: per-unit shares of the table gradient and their
+// per-chunk sums), kernel set-up, and the launch (attention gradients, then the
+// two table-gradient sums).
+bool backward_fits(const Geometry& g, bool bf16);
+size_t backward_workspace_bytes(const Geometry& g);
+hipError_t prepare_backward_kernels(int max_lds);
+hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
+                           const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
+                           void* workspace, hipStream_t s);
+
 } // namespace swa

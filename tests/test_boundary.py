@@ -50,6 +50,7 @@ def test_null_handles(lib):
     assert lib.swa_scatter(None, None, None, None) == binding.SWA_ERR_INVALID_ARGUMENT
     assert lib.swa_debug_visibility(None, 0, None, None) == binding.SWA_ERR_INVALID_ARGUMENT
     assert lib.swa_get_info(None, None) == binding.SWA_ERR_INVALID_ARGUMENT
+    assert lib.swa_backward(*([None] * 12)) == binding.SWA_ERR_INVALID_ARGUMENT
     h = ctypes.c_void_p(1234)
     assert lib.swa_create(None, ctypes.byref(h)) == binding.SWA_ERR_INVALID_ARGUMENT
     assert h.value is None  # *out cleared on failure

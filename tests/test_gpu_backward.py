@@ -1,0 +1,117 @@
+"""GPU parity of the backward pass (swa_backward) against the fp64 oracle.
+
+Gradients dq, dk, dv and the bias-table gradient are compared element by
+element with the oracle's per-window backward, with the forward's metric:
+max|G_gpu - G_ref| / max|G_ref| <= 1e-2 for bf16 and <= 1e-5 for fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import TOL, host_f32, rel_err
+from shifted_window_attention_cyclic_amd import SwaError, WindowAttention
+from shifted_window_attention_cyclic_amd.inputs import WORKLOADS, make_inputs, small_variant
+from test_gpu_parity import EDGE, SMALL
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _dout(p, seed=11):
+    g = torch.Generator().manual_seed(seed)
+    dt = torch.float32 if p.dtype == "f32" else torch.bfloat16
+    return torch.randn((p.batch,) + tuple(p.extent) + (p.heads, p.head_dim), generator=g).to(dt)
+
+
+def _run(p, x, dout):
+    att = WindowAttention(p)
+    d = {n: t.cuda() for n, t in x.items()}
+    grads = att.backward(d["q"], d["k"], d["v"], d["table"], dout.cuda())
+    torch.cuda.synchronize()
+    att.close()
+    return grads
+
+
+def _takes_backward(p):
+    att = WindowAttention(p)
+    ok = att.info.backward_workspace_bytes > 0
+    att.close()
+    return ok
+
+
+CASES = {**SMALL, **EDGE}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_small_grid(name):
+    p = CASES[name]
+    if not _takes_backward(p):
+        pytest.skip("the backward kernels do not take this window")
+    say(f"[backward] {name} dtype={p.dtype} grid={p.extent} pad={p.padded} win={p.window} "
+        f"shift={p.shift} heads={p.heads}x{p.head_dim}")
+    x = make_inputs(p)
+    dout = _dout(p)
+    got = _run(p, x, dout)
+    ref = oracle.literal_backward(p, host_f32(x["q"]), host_f32(x["k"]), host_f32(x["v"]),
+                                  host_f32(x["table"]), host_f32(dout))
+    for gname, g_gpu, g_ref in zip(("dq", "dk", "dv", "dtable"), got, ref):
+        err = rel_err(host_f32(g_gpu), g_ref)
+        say(f"  {gname}: rel err {err:.3e}")
+        assert err <= TOL[p.dtype], gname
+        assert torch.isfinite(g_gpu.float()).all(), gname
+
+
+def test_backward_full_size_sampled_windows():
+    """540x1080 at full size: the gradients of every token of a sample of
+    windows (first and last window rows and columns, the latitude wrap, and
+    random ones) against the oracle; the table gradient sums to zero per head."""
+    p = WORKLOADS["c3_bf16_540x1080"]
+    x = make_inputs(p)
+    dout = _dout(p)
+    dq, dk, dv, dtable = _run(p, x, dout)
+    nwy, nwx = p.padded[1] // p.window[1], p.padded[2] // p.window[2]
+    rng = np.random.default_rng(0)
+    rows = sorted({0, 1, nwy - 2, nwy - 1} | set(rng.integers(0, nwy, 4).tolist()))
+    cols = sorted({0, 1, nwx - 1} | set(rng.integers(0, nwx, 3).tolist()))
+    wins = [r * nwx + c for r in rows for c in cols]
+    say(f"[backward full] {len(wins)} windows")
+    ref = oracle.literal_backward(p, host_f32(x["q"]), host_f32(x["k"]), host_f32(x["v"]),
+                                  host_f32(x["table"]), host_f32(dout), windows=wins)
+    mine = np.isin(oracle.token_windows(p), wins)[None]  # [1, T, H, W]
+    for gname, g_gpu, g_ref in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+        err = rel_err(host_f32(g_gpu)[mine], g_ref[mine])
+        say(f"  {gname}: rel err {err:.3e} over {int(mine.sum())} tokens")
+        assert err <= TOL["bf16"], gname
+    dt = host_f32(dtable)
+    sums = np.abs(dt.reshape(-1, p.heads).sum(axis=0)).max()
+    say(f"  dtable: max |sum over entries| {sums:.3e}, max |entry| {np.abs(dt).max():.3e}")
+    assert sums <= 1e-3 * np.abs(dt).max()
+    for g in (dq, dk, dv, dtable):
+        assert torch.isfinite(g.float()).all()
+
+
+def test_backward_reproducibility():
+    """dq, dk, dv bitwise; the table gradient to fp32 rounding (its per-unit
+    shares are summed with LDS atomics)."""
+    p = WORKLOADS["c4_bf16_181x360_pad190"]
+    x = make_inputs(p)
+    dout = _dout(p)
+    a = _run(p, x, dout)
+    b = _run(p, x, dout)
+    for ga, gb in zip(a[:3], b[:3]):
+        assert torch.equal(ga, gb)
+    assert rel_err(host_f32(a[3]), host_f32(b[3]).astype(np.float64)) <= 1e-6
+
+
+def test_backward_rejects_windows_it_does_not_take():
+    p = small_variant(WORKLOADS["c5_bf16_4x180x360_3d"], 24, 36)  # 288-token windows
+    att = WindowAttention(p)
+    assert att.info.backward_workspace_bytes == 0
+    x = {n: t.cuda() for n, t in make_inputs(p).items()}
+    with pytest.raises(SwaError):
+        att.backward(x["q"], x["k"], x["v"], x["table"], torch.zeros_like(x["q"]))
+    att.close()
