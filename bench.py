@@ -4,6 +4,8 @@
 
 A step is one swa_forward call over the whole workload (gather, window
 attention with bias and mask, softmax, PV and scatter), inputs already in HBM.
+With --pass backward a step is one swa_backward call (dq, dk, dv and the
+bias-table gradient of the same workload).
 Default workload: bf16, B=1, 540x1080 grid (1/12 degree field at patch 4),
 8 heads x 64, window 12x12, shift 6.  Prints one JSON line.
 
@@ -24,6 +26,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "shifted-window attention fwd TFLOP/s + tokens/s, % of bf16 MFMA peak"
+METRIC_BWD = "shifted-window attention bwd TFLOP/s + tokens/s, % of bf16 MFMA peak"
+BWD_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_backward.hip",
+               "shifted_window_attention_cyclic_amd/csrc/swa_device.h",
+               "shifted_window_attention_cyclic_amd/csrc/swa_geometry.h"]
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
@@ -42,25 +48,25 @@ def kernel_name(p, info) -> str:
         info.schedule, "attn_bf16_kernel")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str):
+def traffic_from_profiles(workload: str, backward: bool = False):
     """HBM bytes per launch measured by rocprofv3 counters, if the summary in
     profiles/ was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"traffic_{'bwd_' if backward else ''}{workload}.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"^traffic_json:\s*(\{.*\})\s*$", open(path).read(), flags=re.M)
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(BWD_SOURCES if backward else None):
         return None
     return rec.get("bytes_per_launch")
 
@@ -112,6 +118,30 @@ def cpu_baseline(p, x, out_gpu, rows):
     }
 
 
+def cpu_baseline_backward(p, x, dout, grads_gpu, windows):
+    import numpy as np
+
+    import oracle
+
+    host = {n: x[n].float().numpy() for n in ("q", "k", "v", "table")}
+    t0 = time.perf_counter()
+    ref = oracle.literal_backward(p, host["q"], host["k"], host["v"], host["table"], dout.float().numpy(),
+                                  windows=windows)
+    dt = time.perf_counter() - t0
+    mine = np.isin(oracle.token_windows(p), [w % (p.windows // p.batch) for w in windows])
+    err = 0.0
+    for g, r in zip(grads_gpu[:3], ref[:3]):
+        got = g.float().cpu().numpy()[0][mine]
+        err = max(err, float(np.abs(got - r[0][mine]).max() / np.abs(r[0][mine]).max()))
+    flops = 10.0 * p.window_tokens ** 2 * p.head_dim * p.heads * len(windows)
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+        "sample": (f"fp64 per-window oracle backward (numpy) over {len(windows)} of {p.windows} windows "
+                   f"of batch item 0, all {p.heads} heads"),
+        "seconds": dt, "gpu_rel_max_abs_err_on_sample": err,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +155,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"],
+                    help="time swa_forward (default) or swa_backward")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -136,7 +168,7 @@ def main():
 
     import torch
 
-    from shifted_window_attention_cyclic_amd import WindowAttention, swa_forward
+    from shifted_window_attention_cyclic_amd import WindowAttention, swa_backward, swa_forward
     from shifted_window_attention_cyclic_amd.inputs import WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
@@ -154,9 +186,25 @@ def main():
         d["out"] = torch.empty_like(d["q"])
         sets.append(d)
 
+    backward = args.which == "backward"
+    if backward:
+        if info.backward_workspace_bytes == 0:
+            sys.exit("the backward kernels do not take this workload's window")
+        g = torch.Generator().manual_seed(p.seed + 17)
+        dout_host = torch.randn(tuple(x["q"].shape), generator=g).to(x["q"].dtype)
+        ws = torch.empty((info.backward_workspace_bytes + 15) // 16 * 4, dtype=torch.float32, device="cuda")
+        for s in sets:
+            s["dout"] = dout_host.cuda()
+            s["dq"], s["dk"], s["dv"] = (torch.empty_like(s["q"]) for _ in range(3))
+            s["dtable"] = torch.empty_like(s["table"])
+
     def step(i):
         s = sets[i % nsets]
-        swa_forward(att.handle, s["q"], s["k"], s["v"], s["table"], s["out"])
+        if backward:
+            swa_backward(att.handle, s["q"], s["k"], s["v"], s["table"], s["dout"], s["dq"], s["dk"], s["dv"],
+                         s["dtable"], ws)
+        else:
+            swa_forward(att.handle, s["q"], s["k"], s["v"], s["table"], s["out"])
 
     for i in range(args.warmup):
         step(i)
@@ -181,21 +229,29 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    tflops = info.nominal_flops / (ms_per_step * 1e-3) / 1e12
-    useful = 4.0 * useful_pairs(p) * p.head_dim * p.heads
-    achieved_gbs = info.algorithmic_bytes / (avg_launch_ms * 1e-3) / 1e9
-    kernel_tflops = info.nominal_flops / (avg_launch_ms * 1e-3) / 1e12
+    # forward: 4 N^2 d per unit (Q K^T, P V); backward: 10 N^2 d (Q K^T again, dO V^T,
+    # dS K, dS^T Q, P^T dO).  Bytes: forward q, k, v read and out written; backward
+    # q, k, v, dout read and dq, dk, dv written; the table once each way.
+    flop_mul = 2.5 if backward else 1.0
+    nominal_flops = info.nominal_flops * flop_mul
+    table_bytes = 4.0 * math.prod(p.table_shape)
+    tensor_bytes = (info.algorithmic_bytes - table_bytes) / 4
+    alg_bytes = (7 * tensor_bytes + 2 * table_bytes) if backward else info.algorithmic_bytes
+    tflops = nominal_flops / (ms_per_step * 1e-3) / 1e12
+    useful = 4.0 * useful_pairs(p) * p.head_dim * p.heads * flop_mul
+    achieved_gbs = alg_bytes / (avg_launch_ms * 1e-3) / 1e9
+    kernel_tflops = nominal_flops / (avg_launch_ms * 1e-3) / 1e12
     peak_tf = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = traffic_from_profiles(p.name) if args.variant == "fused" else None
+    traffic = traffic_from_profiles(p.name, backward) if args.variant == "fused" else None
     # the roof that binds: HBM below the ridge (peak FLOP/s over peak bytes/s), MFMA above it
-    intensity = info.nominal_flops / info.algorithmic_bytes
+    intensity = nominal_flops / alg_bytes
     mfma_bound = intensity > peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
     roof = ({"bound": "mfma", "achieved": round(kernel_tflops, 1), "peak": peak_tf, "unit": "TFLOP/s",
              "frac": round(kernel_tflops / peak_tf, 4)} if mfma_bound else
             {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
              "frac": round(achieved_gbs / PEAK_HBM_GBS, 4)})
     result = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if backward else METRIC,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -210,33 +266,44 @@ def main():
         "config": {
             "workload": p.name, "batch": p.batch, "grid_thw": list(p.extent),
             "padded_thw": list(p.padded), "window": list(p.window), "shift": list(p.shift),
-            "heads": p.heads, "head_dim": p.head_dim, "variant": args.variant,
+            "heads": p.heads, "head_dim": p.head_dim, "variant": args.variant, "pass": args.which,
             "input_sets_rotated": nsets,
         },
         "tokens_per_s": round(info.tokens / (ms_per_step * 1e-3), 1),
         "mfma_peak_frac": round(tflops / peak_tf, 5),
         "useful_tflops": round(useful / (ms_per_step * 1e-3) / 1e12, 3),
-        "kernel": {"name": kernel_name(p, info) if args.variant == "fused" else "gather+attn+scatter",
+        "kernel": {"name": (("attn_f32_bwd_kernel" if p.dtype == "f32" else "attn_bf16_bwd_kernel") if backward
+                            else kernel_name(p, info) if args.variant == "fused" else "gather+attn+scatter"),
                    "workgroups": info.workgroups,
                    "avg_launch_ms": round(avg_launch_ms, 5),
                    "p10_ms": round(launch_ms[len(launch_ms) // 10], 5),
                    "p90_ms": round(launch_ms[(9 * len(launch_ms)) // 10], 5),
-                   "source_sha256_16": kernel_source_hash()},
+                   "source_sha256_16": kernel_source_hash(BWD_SOURCES if backward else None)},
         "roofline": {
             **roof,
             "traffic": traffic,
             "algorithmic_gbs": round(achieved_gbs, 1),
             "intensity_flop_per_byte": round(intensity, 2),
-            "algorithmic_bytes_per_launch": info.algorithmic_bytes,
-            "nominal_flops_per_launch": info.nominal_flops,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "nominal_flops_per_launch": nominal_flops,
             "mfma_ceiling_frac_at_hbm_roof": round(
-                min(1.0, info.nominal_flops / info.algorithmic_bytes * PEAK_HBM_GBS * 1e9
-                    / (peak_tf * 1e12)), 4),
+                min(1.0, nominal_flops / alg_bytes * PEAK_HBM_GBS * 1e9 / (peak_tf * 1e12)), 4),
         },
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(p, x, sets[0]["out"], args.cpu_rows)
+        if backward:
+            s0 = sets[0]
+            step(0)
+            torch.cuda.synchronize()
+            per_b = p.windows // p.batch
+            count = max(1, min(per_b, int(CPU_SAMPLE_FLOPS / 40 // (10.0 * p.window_tokens ** 2 * p.head_dim
+                                                                     * p.heads))))
+            wins = [int(w) for w in range(0, per_b, max(1, per_b // count))][:count]
+            result["cpu_baseline"] = cpu_baseline_backward(p, x, s0["dout"].cpu(),
+                                                           (s0["dq"], s0["dk"], s0["dv"]), wins)
+        else:
+            result["cpu_baseline"] = cpu_baseline(p, x, sets[0]["out"], args.cpu_rows)
     att.close()
     print(json.dumps(result), flush=True)
 

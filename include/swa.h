@@ -154,11 +154,9 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
  * 16-byte aligned, owned by the caller (per-(window, head) shares of the
  * table gradient and their partial sums; its contents on entry do not
  * matter).  The pass reads and writes the spatial layout whatever the
- * variant and allocates nothing.  dq, dk and dv are bitwise reproducible;
- * dtable sums the (window, head) shares in a fixed order, but inside one
- * share the additions run in whatever order the share's waves reach them,
- * so it is reproducible to fp32 rounding.  Asynchronous on `stream`, like
- * swa_forward.
+ * variant and allocates nothing.  Every sum runs in a fixed order, so the
+ * results are bitwise reproducible.  The table gradient sums bf16-rounded
+ * dS terms in fp32.  Asynchronous on `stream`, like swa_forward.
  * Errors: INVALID_ARGUMENT (NULL handle or pointer, misalignment, a buffer
  * written that overlaps another argument), UNSUPPORTED (the window is beyond
  * the backward kernels: backward_workspace_bytes is 0), HIP (launch failure).

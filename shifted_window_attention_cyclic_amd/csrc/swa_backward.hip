@@ -11,18 +11,22 @@
 // Every real token lies in exactly one window of the shifted partition, so
 // its dQ, dK and dV come from one unit each and need no accumulation across
 // workgroups.  The table gradient does: each unit writes its share (one
-// slice of the table, summed in LDS with atomic adds, so in the order its
-// waves reach them) to a workspace, and two small kernels add the shares up
-// in a fixed order.
+// slice of the table) to a workspace, and two small kernels add the shares
+// up in a fixed order.  A unit's share is gathered, not scattered: each
+// thread takes a table entry, i.e. a relative offset (query minus key), and
+// sums dS over the key positions whose query at that offset lies in the
+// window, in a fixed order, from the bf16 dS that pass 2 reads anyway.  The
+// whole backward pass is therefore bitwise reproducible.
 //
 // Kernels:
 //   attn_bf16_bwd_kernel  one workgroup per unit, windows of up to 9 query
 //                         tiles.  Pass 1, a query tile per wave: recompute the
-//                         logits and P on MFMA, dP^T = V dO^T, dS, the table
-//                         gradient (LDS atomics), dQ^T = K^T dS^T; P and dS go
-//                         to LDS as [query][key] bf16.  Pass 2, a key tile per
-//                         wave: dV^T = dO^T P and dK^T = Q^T dS, with the
-//                         operands fetched by transposing LDS reads.
+//                         logits and P on MFMA, dP^T = V dO^T, dS and
+//                         dQ^T = K^T dS^T; P and dS go to LDS as [query][key]
+//                         bf16.  Pass 2, a key tile per wave: dV^T = dO^T P and
+//                         dK^T = Q^T dS, with the operands fetched by
+//                         transposing LDS reads.  Then the unit's share of the
+//                         table gradient, an entry per thread.
 //   attn_f32_bwd_kernel   the fp32 counterpart: one thread per query, then one
 //                         per key.
 //   dtable_chunk_kernel,
@@ -44,7 +48,7 @@ constexpr int kDtableChunks = 64;   // first-stage sums of the table gradient
 // ---- LDS of the bf16 backward workgroup
 struct BwdLds {
     int NP;
-    size_t qs, ks, vs, dos, pm, dsm, bias, dtab, tw, kb, total;
+    size_t qs, ks, vs, dos, pm, dsm, bias, tw, kb, total;
 };
 
 __host__ __device__ inline BwdLds bwd_lds(const Geometry& g) {
@@ -59,8 +63,7 @@ __host__ __device__ inline BwdLds bwd_lds(const Geometry& g) {
     L.pm = L.dos + t;                                          // P, [query][key] bf16
     L.dsm = L.pm + (size_t)L.NP * L.NP * 2;                    // dS, [query][key] bf16
     L.bias = L.dsm + (size_t)L.NP * L.NP * 2;
-    L.dtab = L.bias + tab;
-    L.tw = L.dtab + tab;
+    L.tw = L.bias + tab;
     L.kb = L.tw + (size_t)L.NP * 4;
     L.total = L.kb + ((size_t)L.NP * 2 + 15) / 16 * 16;
     return L;
@@ -85,7 +88,6 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
     const BwdLds L = bwd_lds(g);
     const int N = g.N, NP = L.NP, KT = NP / 16;
     float* bias = (float*)(smem + L.bias);
-    float* dtab = (float*)(smem + L.dtab);
     int* tw = (int*)(smem + L.tw);
     uint16_t* kb = (uint16_t*)(smem + L.kb);
     const int tid = threadIdx.x, lane = tid & 63;
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
     const bool masked_window = window_maybe_masked(g, wc);
 
     // ---- token table (packed word: source row + 1 | mask field << 28), key
-    // bias offsets, this head's bias slice, the table gradient slice at zero
+    // bias offsets, this head's bias slice
     for (int n = tid; n < NP; n += THREADS) {
         if (n < N) {
             int l[3];
@@ -131,10 +133,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
             kb[n] = BIAS_VEC ? 3 : 0; // keeps qb - kb (- 3) inside the table
         }
     }
-    for (int i = tid; i < g.table_size; i += THREADS) {
-        bias[i] = table[(size_t)i * g.heads + h];
-        dtab[i] = 0.f;
-    }
+    for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)i * g.heads + h];
     __syncthreads();
 
     // ---- Q, K, V, dO of the window into LDS ([token][d], swizzled; pad rows copy
@@ -268,7 +267,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
         }
         dsum += __shfl_xor(dsum, 16);
         dsum += __shfl_xor(dsum, 32);
-        // dS = P * (dP - D); the table gradient; P and dS to LDS ([query][key] bf16)
+        // dS = P * (dP - D); P and dS to LDS ([query][key] bf16)
         unsigned pk[KB][2];
         uint16_t* Pm = (uint16_t*)(smem + L.pm);
         uint16_t* dSm = (uint16_t*)(smem + L.dsm);
@@ -277,10 +276,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
             if (kt < KT) {
                 f32x4 ds;
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    ds[i] = s[kt][i] * (dp[kt][i] - dsum);
-                    if (ds[i] != 0.f) atomicAdd(&dtab[bidx[kt][i]], ds[i]);
-                }
+                for (int i = 0; i < 4; i++) ds[i] = s[kt][i] * (dp[kt][i] - dsum);
                 pk[kt][0] = pack_bf16x2(ds[0], ds[1]);
                 pk[kt][1] = pack_bf16x2(ds[2], ds[3]);
                 const int key0 = kt * 16 + grp * 4;
@@ -357,9 +353,60 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
         }
     }
 
-    // ---- this unit's share of the table gradient
+    // ---- this unit's share of the table gradient.  Entry e is the offset
+    // (query minus key) d = coords(e) - (w - 1): the sum of dS[key + d][key]
+    // over the keys whose query at that offset lies in the window (pairs that
+    // are masked or involve pad hold dS = 0).  Two balanced stages when the
+    // partial sums fit in the P region (free once pass 2 is done): per
+    // (query row, key row, x offset) along x, then per entry over the rows.
     float* dst = dtab_units + (size_t)work * g.table_size;
-    for (int i = tid; i < g.table_size; i += THREADS) dst[i] = dtab[i];
+    const uint16_t* dSm = (const uint16_t*)(smem + L.dsm);
+    auto ds_at = [&](int n, int m) __attribute__((always_inline)) {
+        return __builtin_bit_cast(float, (unsigned)dSm[(size_t)n * NP + m] << 16);
+    };
+    const int wx = g.win[2], R = g.win[0] * g.win[1]; // tokens per window row; rows (t, y) per window
+    const int items = R * R * g.tdx;
+    __syncthreads(); // pass 2 is done with P
+    if ((size_t)items * 4 <= (size_t)NP * NP * 2) {
+        float* part = (float*)(smem + L.pm);
+        for (int it = tid; it < items; it += THREADS) {
+            const int ex = it % g.tdx, rr = it / g.tdx;
+            const int rk = rr % R, rq = rr / R;
+            const int dx = ex - (wx - 1);
+            const int n0 = rq * wx + dx, m0 = rk * wx;
+            float acc = 0.f;
+            for (int kx = dx < 0 ? -dx : 0; kx < wx - (dx > 0 ? dx : 0); kx++) acc += ds_at(n0 + kx, m0 + kx);
+            part[it] = acc;
+        }
+        __syncthreads();
+        for (int e = tid; e < g.table_size; e += THREADS) {
+            const int et = e / (g.tdy * g.tdx), r0 = e - et * (g.tdy * g.tdx);
+            const int ey = r0 / g.tdx, ex = r0 - ey * g.tdx;
+            const int dt = et - (g.win[0] - 1), dy = ey - (g.win[1] - 1);
+            float acc = 0.f;
+            for (int kt = dt < 0 ? -dt : 0; kt < g.win[0] - (dt > 0 ? dt : 0); kt++)
+                for (int ky = dy < 0 ? -dy : 0; ky < g.win[1] - (dy > 0 ? dy : 0); ky++) {
+                    const int rq = (kt + dt) * g.win[1] + ky + dy, rk = kt * g.win[1] + ky;
+                    acc += part[(rq * R + rk) * g.tdx + ex];
+                }
+            dst[e] = acc;
+        }
+    } else {
+        for (int e = tid; e < g.table_size; e += THREADS) {
+            const int et = e / (g.tdy * g.tdx), r0 = e - et * (g.tdy * g.tdx);
+            const int ey = r0 / g.tdx, ex = r0 - ey * g.tdx;
+            const int dt = et - (g.win[0] - 1), dy = ey - (g.win[1] - 1), dx = ex - (wx - 1);
+            float acc = 0.f;
+            for (int kt = dt < 0 ? -dt : 0; kt < g.win[0] - (dt > 0 ? dt : 0); kt++)
+                for (int ky = dy < 0 ? -dy : 0; ky < g.win[1] - (dy > 0 ? dy : 0); ky++) {
+                    const int m0 = (kt * g.win[1] + ky) * wx;
+                    const int n0 = ((kt + dt) * g.win[1] + ky + dy) * wx + dx;
+                    for (int kx = dx < 0 ? -dx : 0; kx < wx - (dx > 0 ? dx : 0); kx++)
+                        acc += ds_at(n0 + kx, m0 + kx);
+                }
+            dst[e] = acc;
+        }
+    }
 }
 
 // ---- fp32 backward: one block per unit, a thread per query, then per key
@@ -367,7 +414,7 @@ constexpr int kF32BwdThreads = 256;
 
 __host__ __device__ inline size_t f32_bwd_lds_bytes(const Geometry& g) {
     return (size_t)g.N * g.head_dim * 4 * sizeof(float) + (size_t)g.N * g.N * 2 * sizeof(float) +
-           (size_t)g.table_size * 2 * sizeof(float) + (size_t)g.N * 3 * sizeof(int);
+           (size_t)g.table_size * sizeof(float) + (size_t)g.N * 3 * sizeof(int);
 }
 
 template <int D>
@@ -384,8 +431,7 @@ __global__ __launch_bounds__(kF32BwdThreads) void attn_f32_bwd_kernel(
     float* Pm = dOs + N * D;
     float* dSm = Pm + N * N;
     float* bias = dSm + N * N;
-    float* dtab = bias + g.table_size;
-    int* kword = (int*)(dtab + g.table_size);
+    int* kword = (int*)(bias + g.table_size);
     int* qword = kword + N;
     int* rowi = qword + N;
 
@@ -395,10 +441,7 @@ __global__ __launch_bounds__(kF32BwdThreads) void attn_f32_bwd_kernel(
     const int h = (int)(work - wi * g.heads);
 
     fill_token_tables(g, wi, false, N, kword, qword, rowi);
-    for (int i = threadIdx.x; i < g.table_size; i += blockDim.x) {
-        bias[i] = table[(int64_t)i * g.heads + h];
-        dtab[i] = 0.f;
-    }
+    for (int i = threadIdx.x; i < g.table_size; i += blockDim.x) bias[i] = table[(int64_t)i * g.heads + h];
     __syncthreads();
     for (int i = threadIdx.x; i < N * D; i += blockDim.x) {
         const int m = i / D, e = i % D;
@@ -460,10 +503,8 @@ __global__ __launch_bounds__(kF32BwdThreads) void attn_f32_bwd_kernel(
         for (int m = 0; m < N; m++) {
             const float ds = prow[m] * (srow[m] - dd);
             srow[m] = ds;
-            if (ds != 0.f) {
-                atomicAdd(&dtab[(qw & 0xFFFF) - (kword[m] & 0xFFFF)], ds);
+            if (ds != 0.f)
                 for (int e = 0; e < D; e++) acc[e] = fmaf(ds, Ks[m * D + e], acc[e]);
-            }
         }
         float* o = dq + (int64_t)rowi[n] * g.row + (int64_t)h * D;
         for (int e = 0; e < D; e++) o[e] = acc[e] * g.scale;
@@ -487,9 +528,22 @@ __global__ __launch_bounds__(kF32BwdThreads) void attn_f32_bwd_kernel(
             dk[off + e] = ak[e] * g.scale;
         }
     }
-    __syncthreads();
+    // this unit's share of the table gradient, an entry per thread (see the bf16 kernel)
     float* dst = dtab_units + (size_t)work * g.table_size;
-    for (int i = threadIdx.x; i < g.table_size; i += blockDim.x) dst[i] = dtab[i];
+    for (int e = threadIdx.x; e < g.table_size; e += blockDim.x) {
+        const int et = e / (g.tdy * g.tdx), r0 = e - et * (g.tdy * g.tdx);
+        const int ey = r0 / g.tdx, ex = r0 - ey * g.tdx;
+        const int dt = et - (g.win[0] - 1), dy = ey - (g.win[1] - 1), dx = ex - (g.win[2] - 1);
+        float acc = 0.f;
+        for (int kt = dt < 0 ? -dt : 0; kt < g.win[0] - (dt > 0 ? dt : 0); kt++)
+            for (int ky = dy < 0 ? -dy : 0; ky < g.win[1] - (dy > 0 ? dy : 0); ky++) {
+                const int m0 = (kt * g.win[1] + ky) * g.win[2];
+                const int n0 = ((kt + dt) * g.win[1] + ky + dy) * g.win[2] + dx;
+                for (int kx = dx < 0 ? -dx : 0; kx < g.win[2] - (dx > 0 ? dx : 0); kx++)
+                    acc += dSm[(n0 + kx) * N + m0 + kx];
+            }
+        dst[e] = acc;
+    }
 }
 
 // ---- the table gradient: dtable[e][h] = sum over windows (and batch) of the
