@@ -12,10 +12,13 @@ Two formulations, written separately and required to agree:
     attention, reverse; for small grids.
 
 ``literal_backward`` (numpy) gives the gradients of the literal form, window
-by window, for all windows or a chosen subset.
+by window, for all windows or a chosen subset.  ``layer_forward`` (numpy) adds
+the query/key/value and output projections of a Swin block around the
+direct form.
 """
 from .direct import check, default_scale, direct_forward, local_coord, visible
 from .backward import literal_backward, token_windows, window_tokens
+from .layer import layer_forward
 from .literal import (literal_bias, literal_forward, literal_unwindows, literal_visibility,
                       literal_windows, pad_flags)
 
@@ -23,4 +26,5 @@ __all__ = [
     "check", "default_scale", "direct_forward", "local_coord", "visible",
     "literal_bias", "literal_forward", "literal_unwindows", "literal_visibility",
     "literal_windows", "pad_flags", "literal_backward", "token_windows", "window_tokens",
+    "layer_forward",
 ]

@@ -123,3 +123,23 @@ def small_variant(p: Problem, lat: int, lon: int, t: Optional[int] = None) -> Pr
     pad_h = p.padded[1] - p.extent[1]
     return p.with_(name=p.name + f"_small{T}x{lat}x{lon}", extent=(T, lat, lon),
                    padded=(T, lat + pad_h, lon))
+
+
+def make_layer_inputs(p: Problem, seed: Optional[int] = None):
+    """Seeded draws for the projection layer, in a fixed order: the token
+    embeddings X ~ N(0, 1) [B, T, H, W, C] (C = heads * head_dim), the
+    weights W_qkv [3C, C] and W_o [C, C] ~ N(0, 1/C) (so that Q, K, V come
+    out near unit variance), the biases b_qkv [3C] and b_o [C] ~ N(0, 0.02^2)
+    and the attention's bias table ~ N(0, table_std^2).  X and the weights
+    are rounded to the problem's dtype; biases and table stay fp32."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(p.seed if seed is None else seed)
+    dt = torch_dtype(p)
+    C = p.heads * p.head_dim
+    out = {"x": torch.randn((p.batch,) + tuple(p.extent) + (C,), generator=g).to(dt)}
+    out["w_qkv"] = (torch.randn((3 * C, C), generator=g) / C ** 0.5).to(dt)
+    out["b_qkv"] = torch.randn(3 * C, generator=g) * 0.02
+    out["w_o"] = (torch.randn((C, C), generator=g) / C ** 0.5).to(dt)
+    out["b_o"] = torch.randn(C, generator=g) * 0.02
+    out["table"] = torch.randn(p.table_shape, generator=g, dtype=torch.float32) * p.table_std
+    return out
