@@ -5,7 +5,9 @@
 A step is one swa_forward call over the whole workload (gather, window
 attention with bias and mask, softmax, PV and scatter), inputs already in HBM.
 With --pass backward a step is one swa_backward call (dq, dk, dv and the
-bias-table gradient of the same workload).
+bias-table gradient of the same workload).  With --pass layer a step is one
+swa_layer_forward call: the query/key/value projection of the token
+embeddings, the window attention and the output projection.
 Default workload: bf16, B=1, 540x1080 grid (1/12 degree field at patch 4),
 8 heads x 64, window 12x12, shift 6.  Prints one JSON line.
 
@@ -30,6 +32,11 @@ METRIC_BWD = "shifted-window attention bwd TFLOP/s + tokens/s, % of bf16 MFMA pe
 BWD_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_backward.hip",
                "shifted_window_attention_cyclic_amd/csrc/swa_device.h",
                "shifted_window_attention_cyclic_amd/csrc/swa_geometry.h"]
+METRIC_LAYER = ("shifted-window attention layer fwd (QKV projection + attention + output projection) "
+                "TFLOP/s, % of bf16 MFMA peak")
+PROJ_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_projection.hip",
+                "shifted_window_attention_cyclic_amd/csrc/swa_device.h",
+                "shifted_window_attention_cyclic_amd/csrc/swa_geometry.h"]
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
@@ -56,17 +63,18 @@ def kernel_source_hash(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str, backward: bool = False):
+def traffic_from_profiles(workload: str, backward: bool = False, tag: str = None, sources=None):
     """HBM bytes per launch measured by rocprofv3 counters, if the summary in
     profiles/ was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{'bwd_' if backward else ''}{workload}.md")
+    tag = tag if tag is not None else ("bwd_" if backward else "")
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}{workload}.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"^traffic_json:\s*(\{.*\})\s*$", open(path).read(), flags=re.M)
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash(BWD_SOURCES if backward else None):
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(sources or (BWD_SOURCES if backward else None)):
         return None
     return rec.get("bytes_per_launch")
 
@@ -155,8 +163,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"],
-                    help="time swa_forward (default) or swa_backward")
+    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward", "layer"],
+                    help="time swa_forward (default), swa_backward or swa_layer_forward")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -173,6 +181,8 @@ def main():
 
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
+    if args.which == "layer":
+        return run_layer(args)
     p = WORKLOADS[args.workload]
     x = make_inputs(p)
     att = WindowAttention(p, args.variant)
@@ -304,6 +314,185 @@ def main():
                                                            (s0["dq"], s0["dk"], s0["dv"]), wins)
         else:
             result["cpu_baseline"] = cpu_baseline(p, x, sets[0]["out"], args.cpu_rows)
+    att.close()
+    print(json.dumps(result), flush=True)
+
+
+def timed(fn, steps):
+    """Average milliseconds of fn() over `steps` calls, from HIP events recorded
+    on torch's current stream (the stream the binding launches on)."""
+    import torch
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    return sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+
+
+def cpu_baseline_layer(p, x, y_gpu, rows):
+    import numpy as np
+
+    import oracle
+
+    T, H, W = p.extent
+    C = p.heads * p.head_dim
+    per_query = 8.0 * C * C + 4.0 * p.window_tokens * C
+    per_row = per_query * p.batch * T * W
+    rows = max(1, min(rows, H, int(CPU_SAMPLE_FLOPS // 4 // per_row)))
+    idx = np.array([((b * T + t) * H + y) * W + xx for b in range(p.batch) for t in range(T)
+                    for y in range(rows) for xx in range(W)], dtype=np.int64)
+    host = {n: t.float().numpy() for n, t in x.items()}
+    # numpy's BLAS and the C oracle's OpenMP both take OMP_NUM_THREADS threads
+    cores = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+    t0 = time.perf_counter()
+    ref = oracle.layer_forward(p, host["x"], host["w_qkv"], host["b_qkv"], host["table"], host["w_o"], host["b_o"],
+                               query_index=idx)
+    dt = time.perf_counter() - t0
+    got = y_gpu.float().cpu().numpy().reshape(p.tokens, C)[idx]
+    err = float(np.abs(got - ref).max() / np.abs(ref).max())
+    return {
+        "value": per_query * len(idx) / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": (f"fp64 oracle layer (numpy projections of the windows the sample sees, C direct-form attention) "
+                   f"for latitude rows 0..{rows - 1} of every time step and batch item ({len(idx)} of "
+                   f"{p.tokens} tokens)"),
+        "seconds": dt, "tokens_per_s": len(idx) / dt, "gpu_rel_max_abs_err_on_sample": err,
+    }
+
+
+def run_layer(args):
+    import torch
+
+    from shifted_window_attention_cyclic_amd import WindowAttention, swa_forward, swa_layer_forward, swa_projection
+    from shifted_window_attention_cyclic_amd.inputs import WORKLOADS, make_layer_inputs
+
+    p = WORKLOADS[args.workload]
+    att = WindowAttention(p, args.variant)
+    info = att.info
+    C = att.channels
+    M = info.tokens
+    eb = p.elem_bytes
+    x = make_layer_inputs(p)
+    set_bytes = 2.0 * M * C * eb
+    nsets = max(1, min(8, math.ceil(3 * MALL_BYTES / set_bytes)))
+    sets = []
+    for i in range(nsets):
+        xi = x if i == 0 else make_layer_inputs(p, seed=p.seed + 7919 * i)
+        d = {n: t.cuda() for n, t in xi.items()}
+        d["y"] = torch.empty_like(d["x"])
+        sets.append(d)
+    ws = att.layer_workspace()
+    q, k, v, o = (ws[i * M * C:(i + 1) * M * C] for i in range(4))
+
+    def step(i):
+        s = sets[i % nsets]
+        swa_layer_forward(att.handle, s["x"], s["w_qkv"], s["b_qkv"], s["table"], s["w_o"], s["b_o"], s["y"], ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # the three kernels of a step, each timed alone through its own entry point
+    # on the same inputs and stream
+    def proj_qkv(i):
+        s = sets[i % nsets]
+        swa_projection(s["x"].view(M, C), s["w_qkv"], s["b_qkv"], [q, k, v], split=C)
+
+    def attention(i):
+        swa_forward(att.handle, q.view(att.io_shape), k.view(att.io_shape), v.view(att.io_shape),
+                    sets[i % nsets]["table"], o.view(att.io_shape))
+
+    def proj_out(i):
+        s = sets[i % nsets]
+        swa_projection(o.view(M, C), s["w_o"], s["b_o"], [s["y"].view(-1)])
+
+    proj_flops_qkv = 2.0 * M * C * 3 * C
+    proj_flops_out = 2.0 * M * C * C
+    proj_name = "proj_bf16_kernel" if p.dtype == "bf16" else "proj_f32_kernel"
+    # name: (call, kernel, flops, algorithmic bytes, kernel sources); projection
+    # bytes: x and the weights read, the outputs written, the fp32 bias read
+    kernels = {
+        "proj_qkv": (proj_qkv, proj_name, proj_flops_qkv, (M * C + 3 * C * C + 3 * M * C) * eb + 12.0 * C,
+                     PROJ_SOURCES),
+        "attention": (attention, kernel_name(p, info), info.nominal_flops, info.algorithmic_bytes, KERNEL_SOURCES),
+        "proj_out": (proj_out, proj_name, proj_flops_out, (2 * M * C + C * C) * eb + 4.0 * C, PROJ_SOURCES),
+    }
+    per_kernel = {}
+    for name, (fn, kname, flops, nbytes, _) in kernels.items():
+        for i in range(args.warmup):
+            fn(i)
+        ms = timed(fn, args.steps)
+        per_kernel[name] = {"kernel": kname, "avg_ms": round(sum(ms) / len(ms), 5),
+                            "p10_ms": round(ms[len(ms) // 10], 5), "p90_ms": round(ms[(9 * len(ms)) // 10], 5),
+                            "flops": flops, "algorithmic_bytes": nbytes}
+    dom = max(per_kernel, key=lambda n: per_kernel[n]["avg_ms"])
+    kd = per_kernel[dom]
+    peak_tf = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
+    intensity = kd["flops"] / kd["algorithmic_bytes"]
+    tf = kd["flops"] / (kd["avg_ms"] * 1e-3) / 1e12
+    gbs = kd["algorithmic_bytes"] / (kd["avg_ms"] * 1e-3) / 1e9
+    mfma_bound = intensity > peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
+    roof = ({"bound": "mfma", "achieved": round(tf, 1), "peak": peak_tf, "unit": "TFLOP/s",
+             "frac": round(tf / peak_tf, 4)} if mfma_bound else
+            {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    dom_sources = kernels[dom][4]
+    traffic = (traffic_from_profiles(p.name, tag=f"layer_{dom}_", sources=dom_sources)
+               if args.variant == "fused" else None)
+    tflops = info.layer_flops / (ms_per_step * 1e-3) / 1e12
+    result = {
+        "metric": METRIC_LAYER,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": ("synthetic (seeded N(0,1) token embeddings, N(0,1/C) weights, N(0,0.02^2) biases and bias "
+                 "table)"),
+        "config": {
+            "workload": p.name, "batch": p.batch, "grid_thw": list(p.extent), "padded_thw": list(p.padded),
+            "window": list(p.window), "shift": list(p.shift), "heads": p.heads, "head_dim": p.head_dim,
+            "channels": C, "variant": args.variant, "pass": "layer", "input_sets_rotated": nsets,
+        },
+        "tokens_per_s": round(M / (ms_per_step * 1e-3), 1),
+        "mfma_peak_frac": round(tflops / peak_tf, 5),
+        "layer_flops_per_step": info.layer_flops,
+        "kernels": per_kernel,
+        "kernel": {"name": kd["kernel"], "step": dom, "avg_launch_ms": kd["avg_ms"], "p10_ms": kd["p10_ms"],
+                   "p90_ms": kd["p90_ms"], "source_sha256_16": kernel_source_hash(dom_sources)},
+        "roofline": {
+            **roof,
+            "traffic": traffic,
+            "algorithmic_gbs": round(gbs, 1),
+            "intensity_flop_per_byte": round(intensity, 2),
+            "algorithmic_bytes_per_launch": kd["algorithmic_bytes"],
+            "nominal_flops_per_launch": kd["flops"],
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        step(0)
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = cpu_baseline_layer(p, x, sets[0]["y"], args.cpu_rows)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     att.close()
     print(json.dumps(result), flush=True)
 

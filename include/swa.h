@@ -120,6 +120,10 @@ typedef struct swa_info {
     size_t backward_workspace_bytes; /* workspace swa_backward needs; 0: the backward pass does not take
                                         this window (bf16: more than 144 tokens or past LDS; fp32: past
                                         LDS or head_dim above 64) */
+    size_t layer_workspace_bytes;    /* workspace swa_layer_forward needs: q, k, v and the attention
+                                        output, tokens * heads * head_dim elements each */
+    double layer_flops;              /* swa_layer_forward: 2 * tokens * C * 4C for the two projections
+                                        (C = heads * head_dim) plus nominal_flops */
 } swa_info;
 
 /*
@@ -164,6 +168,55 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
 swa_status swa_backward(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
                         const void* dout, void* dq, void* dk, void* dv, float* dtable, void* workspace,
                         void* stream);
+
+/*
+ * The window attention inside its Swin block's projections (TERRA page,
+ * abstract: the models are stacks of Swin blocks; Table V: embedding width
+ * d = N_h * head_dim).  With C = heads * head_dim:
+ *   qkv = x w_qkv^T + b_qkv;  q, k, v = qkv[.., 0:C], qkv[.., C:2C], qkv[.., 2C:3C]
+ *   o   = the forward pass above on q, k, v and bias_table
+ *   y   = o w_o^T + b_o
+ * Channels are head-major (head h owns channels h*head_dim .. +head_dim-1),
+ * so q, k, v and o have exactly the [B][T][H][W][heads][head_dim] layout of
+ * swa_forward.  x, y: [B][T][H][W][C] in the handle's dtype.  w_qkv: [3C][C]
+ * and w_o: [C][C], the handle's dtype, row-major (a linear layer's
+ * [out_features][in_features]).  b_qkv: [3C] and b_o: [C], fp32.  bf16: the
+ * products run on bf16 matrix cores with fp32 accumulation; the bias is added
+ * in fp32 and q, k, v, o, y are rounded to bf16 once.  x, y, the weights and
+ * the workspace are device pointers, 16-byte aligned; biases and table
+ * 4-byte aligned.  workspace: info.layer_workspace_bytes bytes, caller-owned,
+ * receiving q, k, v and o in that order (each tokens * C elements); its
+ * contents on entry do not matter, and on return it holds those four
+ * tensors.  y must not overlap any other argument, nor the workspace any
+ * input.  Asynchronous on `stream`; allocates nothing.
+ * Errors: INVALID_ARGUMENT (NULL handle or pointer, misalignment, overlap),
+ * HIP (launch failure).
+ */
+swa_status swa_layer_forward(swa_handle* h, const void* x, const void* w_qkv, const float* b_qkv,
+                             const float* bias_table, const void* w_o, const float* b_o, void* y,
+                             void* workspace, void* stream);
+
+/*
+ * The projection step of swa_layer_forward alone, on any token count:
+ *   out[m][n] = sum_k x[m][k] * w[n][k] + bias[n],  m < rows, n < out_features, k < in_features
+ * with column n written to d0, d1 or d2 (n / split) at [m][n % split]: the
+ * query/key/value projection passes split = C and three tensors, the output
+ * projection split = out_features and one tensor (d1, d2 unused, may be
+ * NULL).  x [rows][in_features], w [out_features][in_features] and the
+ * outputs have element type `dtype` (bf16: bf16 matrix cores, fp32
+ * accumulation and bias, one rounding); bias is fp32.  x, w, d0..d2: device
+ * pointers, 16-byte aligned; bias 4-byte aligned; the outputs must not
+ * overlap the inputs.  Shapes: in_features a positive multiple of 32,
+ * out_features and split positive multiples of 4 with
+ * out_features <= 3 * split, 0 <= rows < 2^31 (rows = 0 does nothing and
+ * returns SWA_OK).  Needs a current gfx950 device.  Asynchronous on
+ * `stream`; allocates nothing.
+ * Errors: INVALID_ARGUMENT (NULL pointer, misalignment, overlap, unknown
+ * dtype, negative rows), UNSUPPORTED (shape), HIP (launch failure).
+ */
+swa_status swa_projection(swa_dtype dtype, const void* x, const void* w, const float* bias, int64_t rows,
+                          int32_t out_features, int32_t in_features, int32_t split, void* d0, void* d1,
+                          void* d2, void* stream);
 
 /* Frees the handle and its workspace (synchronising the device first when a
  * workspace exists).  NULL is a no-op returning SWA_OK. */

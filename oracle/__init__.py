@@ -18,7 +18,7 @@ direct form.
 """
 from .direct import check, default_scale, direct_forward, local_coord, visible
 from .backward import literal_backward, token_windows, window_tokens
-from .layer import layer_forward
+from .layer import layer_forward, linear
 from .literal import (literal_bias, literal_forward, literal_unwindows, literal_visibility,
                       literal_windows, pad_flags)
 
@@ -26,5 +26,5 @@ __all__ = [
     "check", "default_scale", "direct_forward", "local_coord", "visible",
     "literal_bias", "literal_forward", "literal_unwindows", "literal_visibility",
     "literal_windows", "pad_flags", "literal_backward", "token_windows", "window_tokens",
-    "layer_forward",
+    "layer_forward", "linear",
 ]

@@ -25,6 +25,11 @@ from .backward import token_windows
 from .direct import direct_forward
 
 
+def linear(x, w, b):
+    """x w^T + b in fp64: x [.., in], w [out, in] (a linear layer's layout), b [out]."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T + np.asarray(b, dtype=np.float64)
+
+
 def _needed_tokens(prob, query_index):
     """Flat token indices whose keys and values the queries can see: every
     token of the windows that hold them."""
@@ -46,18 +51,15 @@ def layer_forward(prob, x, w_qkv, b_qkv, table, w_o, b_o, query_index=None):
     C = heads * d
     M = B * T * H * W
     x = np.asarray(x).reshape(M, C)
-    w_qkv = np.asarray(w_qkv, dtype=np.float64).reshape(3 * C, C)
-    b_qkv = np.asarray(b_qkv, dtype=np.float64).reshape(3 * C)
     rows = np.arange(M) if query_index is None else _needed_tokens(prob, query_index)
-    qkv = x[rows].astype(np.float64) @ w_qkv.T + b_qkv  # [len(rows), 3C]
+    qkv = linear(x[rows], np.reshape(w_qkv, (3 * C, C)), np.reshape(b_qkv, 3 * C))  # [len(rows), 3C]
     shape = (B, T, H, W, heads, d)
     q, k, v = (np.zeros((M, C), dtype=np.float32) for _ in range(3))
     for i, dst in enumerate((q, k, v)):
         dst[rows] = qkv[:, i * C:(i + 1) * C]
     o, _ = direct_forward(prob, q.reshape(shape), k.reshape(shape), v.reshape(shape), table,
                           query_index=query_index)
-    o = o.reshape(o.shape[:-2] + (C,))
-    return o @ np.asarray(w_o, dtype=np.float64).reshape(C, C).T + np.asarray(b_o, dtype=np.float64)
+    return linear(o.reshape(o.shape[:-2] + (C,)), np.reshape(w_o, (C, C)), b_o)
 
 
-__all__ = ["layer_forward"]
+__all__ = ["layer_forward", "linear"]

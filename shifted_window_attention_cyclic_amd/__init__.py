@@ -6,10 +6,11 @@ ctypes binding with the same entry-point names.
 """
 from .binding import (EXPORTS, SwaError, WindowAttention, load_library, make_config,
                       swa_backward, swa_create, swa_debug_visibility, swa_destroy, swa_forward, swa_gather,
-                      swa_get_info, swa_scatter, swa_status_string)
+                      swa_get_info, swa_layer_forward, swa_projection, swa_scatter,
+                      swa_status_string)
 
 __all__ = [
     "EXPORTS", "SwaError", "WindowAttention", "load_library", "make_config", "swa_backward", "swa_create",
     "swa_debug_visibility", "swa_destroy", "swa_forward", "swa_gather", "swa_get_info",
-    "swa_scatter", "swa_status_string",
+    "swa_layer_forward", "swa_projection", "swa_scatter", "swa_status_string",
 ]

@@ -19,7 +19,8 @@ SWA_SCHEDULE_AUTO, SWA_SCHEDULE_STREAM, SWA_SCHEDULE_BLOCK, SWA_SCHEDULE_KEYBLOC
 SCHEDULES = {"auto": SWA_SCHEDULE_AUTO, "stream": SWA_SCHEDULE_STREAM, "block": SWA_SCHEDULE_BLOCK,
              "keyblock": SWA_SCHEDULE_KEYBLOCK}
 
-EXPORTS = ("swa_create", "swa_forward", "swa_backward", "swa_destroy", "swa_get_info", "swa_status_string",
+EXPORTS = ("swa_create", "swa_forward", "swa_backward", "swa_layer_forward", "swa_projection", "swa_destroy",
+           "swa_get_info", "swa_status_string",
            "swa_last_error", "swa_gather", "swa_scatter", "swa_debug_visibility")
 
 
@@ -39,7 +40,8 @@ class swa_info(ctypes.Structure):
         ("window_major_elems", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
         ("nominal_flops", ctypes.c_double), ("algorithmic_bytes", ctypes.c_double),
         ("schedule", ctypes.c_int32), ("workgroups", ctypes.c_int32),
-        ("backward_workspace_bytes", ctypes.c_size_t),
+        ("backward_workspace_bytes", ctypes.c_size_t), ("layer_workspace_bytes", ctypes.c_size_t),
+        ("layer_flops", ctypes.c_double),
     ]
 
 
@@ -67,6 +69,11 @@ def load_library(path: str = LIBRARY):
     lib.swa_forward.restype = st
     lib.swa_backward.argtypes = [vp] * 12
     lib.swa_backward.restype = st
+    lib.swa_layer_forward.argtypes = [vp] * 10
+    lib.swa_layer_forward.restype = st
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.swa_projection.argtypes = [st, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp]
+    lib.swa_projection.restype = st
     lib.swa_destroy.argtypes = [vp]
     lib.swa_destroy.restype = st
     lib.swa_get_info.argtypes = [vp, ctypes.POINTER(swa_info)]
@@ -164,6 +171,38 @@ def swa_backward(handle, q, k, v, table, dout, dq, dk, dv, dtable, workspace, st
                                        _stream(stream)))
 
 
+def swa_layer_forward(handle, x, w_qkv, b_qkv, table, w_o, b_o, y, workspace, stream=None) -> None:
+    dt = x.dtype
+    f32 = torch.float32
+    _check(load_library().swa_layer_forward(handle, _dev(x, "x"), _dev(w_qkv, "w_qkv", dt), _dev(b_qkv, "b_qkv", f32),
+                                            _dev(table, "table", f32), _dev(w_o, "w_o", dt), _dev(b_o, "b_o", f32),
+                                            _dev(y, "y", dt), _dev(workspace, "workspace"), _stream(stream)))
+
+
+def swa_projection(x, w, bias, outputs, split=None, stream=None) -> None:
+    """outputs[n // split][m, n % split] = (x @ w.T + bias)[m, n]; x [rows, in],
+    w [out, in], bias [out] fp32, outputs: 1 to 3 tensors of rows * split
+    elements (split defaults to out)."""
+    dt = x.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    rows, fin = x.shape
+    fout = w.shape[0]
+    if tuple(w.shape) != (fout, fin) or tuple(bias.shape) != (fout,):
+        raise ValueError("w must be [out, in] and bias [out]")
+    split = fout if split is None else int(split)
+    need = (fout + split - 1) // split
+    if len(outputs) != need:
+        raise ValueError(f"{need} output tensors expected")
+    for i, o in enumerate(outputs):
+        if o.numel() != rows * split:
+            raise ValueError(f"output {i} must hold rows * split elements")
+    ptrs = [_dev(o, f"out{i}", dt) for i, o in enumerate(outputs)] + [None] * (3 - need)
+    _check(load_library().swa_projection(SWA_F32 if dt == torch.float32 else SWA_BF16, _dev(x, "x"),
+                                         _dev(w, "w", dt), _dev(bias, "bias", torch.float32), rows, fout, fin,
+                                         split, *ptrs, _stream(stream)))
+
+
 def swa_gather(handle, src, dst_window_major, stream=None) -> None:
     _check(load_library().swa_gather(handle, _dev(src, "src"), _dev(dst_window_major, "dst", src.dtype),
                                      _stream(stream)))
@@ -227,6 +266,35 @@ class WindowAttention:
         ws = torch.empty((nws + 15) // 16 * 4, dtype=torch.float32, device=q.device)
         swa_backward(self.handle, q, k, v, table, dout, dq, dk, dv, dtable, ws, stream)
         return dq, dk, dv, dtable
+
+    @property
+    def channels(self):
+        return self.problem.heads * self.problem.head_dim
+
+    def layer_workspace(self, device="cuda"):
+        """A workspace for layer_forward (q, k, v and o of the layer, in that order)."""
+        n = self.info.layer_workspace_bytes
+        return torch.empty(n // (2 if self.dtype == torch.bfloat16 else 4), dtype=self.dtype, device=device)
+
+    def layer_forward(self, x, w_qkv, b_qkv, table, w_o, b_o, y=None, workspace=None, stream=None):
+        """y = attention(x w_qkv^T + b_qkv split into q, k, v) w_o^T + b_o."""
+        p, C = self.problem, self.channels
+        self._shape(x, (p.batch,) + tuple(p.extent) + (C,), "x")
+        self._shape(w_qkv, (3 * C, C), "w_qkv")
+        self._shape(b_qkv, (3 * C,), "b_qkv")
+        self._shape(w_o, (C, C), "w_o")
+        self._shape(b_o, (C,), "b_o")
+        w = p.window
+        self._shape(table, (2 * w[0] - 1, 2 * w[1] - 1, 2 * w[2] - 1, p.heads), "table")
+        if y is None:
+            y = torch.empty_like(x)
+        self._shape(y, x.shape, "y")
+        if workspace is None:
+            workspace = self.layer_workspace(x.device)
+        if workspace.numel() * workspace.element_size() < self.info.layer_workspace_bytes:
+            raise ValueError("workspace too small")
+        swa_layer_forward(self.handle, x, w_qkv, b_qkv, table, w_o, b_o, y, workspace, stream)
+        return y
 
     def gather(self, src, dst=None, stream=None):
         self._shape(src, self.io_shape, "src")

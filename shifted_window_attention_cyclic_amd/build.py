@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libswa.so")
 SOURCES = [os.path.join(CSRC, "swa_kernels.hip"), os.path.join(CSRC, "swa_backward.hip"),
-           os.path.join(CSRC, "swa_api.cpp")]
+           os.path.join(CSRC, "swa_projection.hip"), os.path.join(CSRC, "swa_api.cpp")]
 ARCH = "gfx950"
 
 

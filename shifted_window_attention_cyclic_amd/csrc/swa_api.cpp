@@ -143,6 +143,10 @@ swa_status validate(const swa_config* c, swa::Geometry* g, int* elem_bytes) {
     return SWA_OK;
 }
 
+size_t io_bytes(const swa_handle* h) {
+    return (size_t)h->g.batch * h->g.ext[0] * h->g.ext[1] * h->g.ext[2] * h->g.row * h->elem_bytes;
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -286,11 +290,9 @@ swa_status swa_get_info(const swa_handle* h, swa_info* info) {
     info->schedule = bf16 ? h->schedule : 0;
     info->workgroups = bf16 ? h->blocks : 0;
     info->backward_workspace_bytes = swa::backward_fits(g, bf16) ? swa::backward_workspace_bytes(g) : 0;
+    info->layer_workspace_bytes = 4 * io_bytes(h);
+    info->layer_flops = 8.0 * (double)info->tokens * g.row * (double)g.row + info->nominal_flops;
     return SWA_OK;
-}
-
-static size_t io_bytes(const swa_handle* h) {
-    return (size_t)h->g.batch * h->g.ext[0] * h->g.ext[1] * h->g.ext[2] * h->g.row * h->elem_bytes;
 }
 
 swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* v,
@@ -360,6 +362,76 @@ swa_status swa_backward(swa_handle* h, const void* q, const void* k, const void*
     hipError_t e = swa::launch_backward(g, bf16, q, k, v, bias_table, dout, dq, dk, dv, dtable, workspace,
                                         (hipStream_t)stream);
     return e == hipSuccess ? SWA_OK : fail_hip(e, "backward launch");
+}
+
+swa_status swa_layer_forward(swa_handle* h, const void* x, const void* w_qkv, const float* b_qkv,
+                             const float* bias_table, const void* w_o, const float* b_o, void* y,
+                             void* workspace, void* stream) {
+    if (!h || !x || !w_qkv || !b_qkv || !bias_table || !w_o || !b_o || !y || !workspace)
+        return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    const void* wide[] = {x, w_qkv, w_o, y, workspace};
+    for (const void* p : wide)
+        if (!aligned(p, 16)) return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned pointer (x, y, weights and workspace need 16 bytes)");
+    if (!aligned(b_qkv, 4) || !aligned(b_o, 4) || !aligned(bias_table, 4))
+        return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned bias or table");
+    const swa::Geometry& g = h->g;
+    const int C = g.row;
+    const int64_t M = (int64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
+    if (!swa::projection_fits(M, 3 * C, C, C)) return fail(SWA_ERR_UNSUPPORTED, "projection shape");
+    const size_t n = io_bytes(h);
+    const size_t eb = h->elem_bytes;
+    const size_t nt = (size_t)g.table_size * g.heads * sizeof(float);
+    // y is disjoint from every other argument; the workspace from every input
+    const void* all[] = {x, w_qkv, b_qkv, bias_table, w_o, b_o, y, workspace};
+    const size_t len[] = {n, 3 * (size_t)C * C * eb, 3 * (size_t)C * 4, nt, (size_t)C * C * eb, (size_t)C * 4, n,
+                          4 * n};
+    for (int i = 6; i < 8; i++)
+        for (int j = 0; j < 8; j++)
+            if (j != i && overlap(all[i], len[i], all[j], len[j]))
+                return fail(SWA_ERR_INVALID_ARGUMENT, "y or the workspace overlaps another argument");
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    void* q = ws;
+    void* k = ws + n;
+    void* v = ws + 2 * n;
+    void* o = ws + 3 * n;
+    const bool bf16 = h->cfg.dtype == SWA_BF16;
+    hipError_t e = swa::launch_projection(bf16, x, w_qkv, b_qkv, M, 3 * C, C, C, q, k, v, s);
+    if (e != hipSuccess) return fail_hip(e, "projection launch");
+    swa_status st = swa_forward(h, q, k, v, bias_table, o, stream);
+    if (st != SWA_OK) return st;
+    e = swa::launch_projection(bf16, o, w_o, b_o, M, C, C, C, y, y, y, s);
+    return e == hipSuccess ? SWA_OK : fail_hip(e, "projection launch");
+}
+
+swa_status swa_projection(swa_dtype dtype, const void* x, const void* w, const float* bias, int64_t rows,
+                          int32_t out_features, int32_t in_features, int32_t split, void* d0, void* d1,
+                          void* d2, void* stream) {
+    if (dtype != SWA_F32 && dtype != SWA_BF16) return fail(SWA_ERR_INVALID_ARGUMENT, "unknown dtype");
+    const int nt = split > 0 ? (out_features + split - 1) / split : 0;
+    if (!x || !w || !bias || !d0 || (nt > 1 && !d1) || (nt > 2 && !d2))
+        return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (rows < 0) return fail(SWA_ERR_INVALID_ARGUMENT, "negative row count");
+    if (!swa::projection_fits(rows > 0 ? rows : 1, out_features, in_features, split))
+        return fail(SWA_ERR_UNSUPPORTED, "projection shape (in_features a multiple of 32, out_features and split "
+                                         "multiples of 4, out_features <= 3 * split, rows below 2^31)");
+    if (rows == 0) return SWA_OK;
+    void* dst[3] = {d0, nt > 1 ? d1 : d0, nt > 2 ? d2 : d0};
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(bias, 4))
+        return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned pointer (x, w and outputs need 16 bytes)");
+    const size_t eb = dtype == SWA_F32 ? 4 : 2;
+    const size_t nx = (size_t)rows * in_features * eb, nw = (size_t)out_features * in_features * eb;
+    const size_t nb = (size_t)out_features * 4;
+    for (int t = 0; t < nt; t++) {
+        const int cols = out_features - t * split < split ? out_features - t * split : split;
+        const size_t nd = ((size_t)(rows - 1) * split + cols) * eb;
+        if (!aligned(dst[t], 16)) return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned output");
+        if (overlap(dst[t], nd, x, nx) || overlap(dst[t], nd, w, nw) || overlap(dst[t], nd, bias, nb))
+            return fail(SWA_ERR_INVALID_ARGUMENT, "an output overlaps an input");
+    }
+    hipError_t e = swa::launch_projection(dtype == SWA_BF16, x, w, bias, rows, out_features, in_features, split,
+                                          dst[0], dst[1], dst[2], (hipStream_t)stream);
+    return e == hipSuccess ? SWA_OK : fail_hip(e, "projection launch");
 }
 
 swa_status swa_gather(swa_handle* h, const void* src, void* dst_window_major, void* stream) {

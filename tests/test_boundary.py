@@ -20,6 +20,16 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(swa_\w+)\s*\(", text)))
 
 
+def declared_arity():
+    """Parameter count of every function the header declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(swa_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
 @pytest.fixture(scope="module")
 def lib():
     return binding.load_library()
@@ -30,6 +40,13 @@ def test_header_declares_the_entry_points():
     for n in ("swa_create", "swa_forward", "swa_destroy"):
         assert n in names
     assert set(names) == set(binding.EXPORTS)
+
+
+def test_binding_signatures_match_the_header(lib):
+    arity = declared_arity()
+    assert set(arity) == set(declared_functions())
+    for name, n in arity.items():
+        assert len(getattr(lib, name).argtypes) == n, name
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -51,6 +68,21 @@ def test_null_handles(lib):
     assert lib.swa_debug_visibility(None, 0, None, None) == binding.SWA_ERR_INVALID_ARGUMENT
     assert lib.swa_get_info(None, None) == binding.SWA_ERR_INVALID_ARGUMENT
     assert lib.swa_backward(*([None] * 12)) == binding.SWA_ERR_INVALID_ARGUMENT
+    assert lib.swa_layer_forward(*([None] * 10)) == binding.SWA_ERR_INVALID_ARGUMENT
+    # NULL pointers, an unknown dtype and a bad shape are refused before any device call
+    assert lib.swa_projection(binding.SWA_BF16, None, None, None, 1, 4, 32, 4, None, None, None,
+                              None) == binding.SWA_ERR_INVALID_ARGUMENT
+    assert lib.swa_projection(7, None, None, None, 1, 4, 32, 4, None, None, None,
+                              None) == binding.SWA_ERR_INVALID_ARGUMENT
+    buf = ctypes.create_string_buffer(4096 + 16)
+    a = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16
+    for rows, fout, fin, split in ((1, 4, 48, 4), (1, 6, 32, 6), (1, 16, 32, 4), (1 << 31, 4, 32, 4)):
+        assert lib.swa_projection(binding.SWA_BF16, a, a, a, rows, fout, fin, split, a, a, a,
+                                  None) == binding.SWA_ERR_UNSUPPORTED
+    assert lib.swa_projection(binding.SWA_BF16, a, a, a, -1, 4, 32, 4, a, a, a,
+                              None) == binding.SWA_ERR_INVALID_ARGUMENT
+    # no rows: nothing to do, and no device needed
+    assert lib.swa_projection(binding.SWA_F32, a, a, a, 0, 12, 32, 4, a, a, a, None) == binding.SWA_OK
     h = ctypes.c_void_p(1234)
     assert lib.swa_create(None, ctypes.byref(h)) == binding.SWA_ERR_INVALID_ARGUMENT
     assert h.value is None  # *out cleared on failure

@@ -1,0 +1,200 @@
+"""GPU parity of the projection layer (swa_layer_forward) against the fp64
+oracle (oracle.layer_forward): y element by element, and the q, k, v the
+query/key/value projection leaves in the workspace, with the attention's
+metric max|G_gpu - G_ref| / max|G_ref| <= 1e-2 for bf16 and <= 1e-5 for fp32.
+Grids are chosen so that the 256-token and 256-feature tiles of the
+projection kernel end ragged (partial last tiles in both directions)."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import TOL, host_f32, rel_err, sample_tokens
+from shifted_window_attention_cyclic_amd import SwaError, WindowAttention, load_library, swa_projection
+from shifted_window_attention_cyclic_amd.inputs import WORKLOADS, Problem, make_layer_inputs
+from test_gpu_parity import EDGE, SMALL
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+CASES = {
+    **SMALL,
+    "n35_ragged_tiles": EDGE["n35_ragged_tiles"],
+    "global_window_shift0": EDGE["global_window_shift0"],
+    "all_axes_masked": EDGE["all_axes_masked"],
+    # fewer tokens (48) and features (3C = 192) than one tile
+    "one_partial_tile": Problem("tiny", "bf16", 1, 2, 32, (1, 6, 8), (1, 6, 8), (1, 6, 8), (0, 0, 0), seed=21),
+    "f32_ragged_pad": Problem("f32pad", "f32", 2, 2, 32, (1, 13, 24), (1, 16, 24), (1, 8, 8), (0, 4, 4), seed=22),
+}
+
+
+def _host(x):
+    return {n: host_f32(t) for n, t in x.items()}
+
+
+def _run(p, x, variant="fused"):
+    att = WindowAttention(p, variant)
+    d = {n: t.cuda() for n, t in x.items()}
+    ws = att.layer_workspace()
+    y = att.layer_forward(d["x"], d["w_qkv"], d["b_qkv"], d["table"], d["w_o"], d["b_o"], workspace=ws)
+    torch.cuda.synchronize()
+    return att, d, y, ws
+
+
+def _split(att, ws):
+    n = att.info.tokens * att.channels
+    return [ws[i * n:(i + 1) * n].reshape(att.io_shape) for i in range(4)]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_small_grid(name):
+    p = CASES[name]
+    say(f"[layer] {name} dtype={p.dtype} B={p.batch} grid={p.extent} pad={p.padded} win={p.window} "
+        f"shift={p.shift} heads={p.heads}x{p.head_dim}")
+    x = make_layer_inputs(p)
+    att, d, y, ws = _run(p, x)
+    h = _host(x)
+    ref = oracle.layer_forward(p, h["x"], h["w_qkv"], h["b_qkv"], h["table"], h["w_o"], h["b_o"])
+    err = rel_err(host_f32(y), ref)
+    say(f"  y: rel err {err:.3e}")
+    assert err <= TOL[p.dtype]
+    # the projection's own output: q, k, v in the workspace
+    C = p.heads * p.head_dim
+    qkv = oracle.linear(h["x"].reshape(-1, C), h["w_qkv"], h["b_qkv"])
+    q, k, v, o = _split(att, ws)
+    for i, (nm, t) in enumerate((("q", q), ("k", k), ("v", v))):
+        e = rel_err(host_f32(t).reshape(-1, C), qkv[:, i * C:(i + 1) * C])
+        say(f"  {nm}: rel err {e:.3e}")
+        assert e <= TOL[p.dtype]
+    # o is the attention forward pass of those q, k, v, bit for bit
+    assert torch.equal(o, att.forward(q, k, v, d["table"]))
+    att.close()
+
+
+def test_layer_full_size_180x360():
+    """180x360 at full size: every token against the oracle."""
+    p = WORKLOADS["c2_bf16_180x360"]
+    x = make_layer_inputs(p)
+    att, _, y, _ = _run(p, x)
+    h = _host(x)
+    ref = oracle.layer_forward(p, h["x"], h["w_qkv"], h["b_qkv"], h["table"], h["w_o"], h["b_o"])
+    err = rel_err(host_f32(y), ref)
+    say(f"[layer full 180x360] rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    att.close()
+
+
+@pytest.mark.parametrize("name", ["c3_bf16_540x1080", "c4_bf16_181x360_pad190"])
+def test_layer_full_size_sampled(name):
+    """Full size in the benchmark's launch configuration: sampled tokens
+    (window edges, shift boundaries, pad neighbours and random ones) against
+    the oracle, which projects only the windows those tokens see."""
+    p = WORKLOADS[name]
+    x = make_layer_inputs(p)
+    att, _, y, _ = _run(p, x)
+    idx = sample_tokens(p, count=128)
+    h = _host(x)
+    ref = oracle.layer_forward(p, h["x"], h["w_qkv"], h["b_qkv"], h["table"], h["w_o"], h["b_o"],
+                               query_index=idx)
+    got = host_f32(y).reshape(-1, p.heads * p.head_dim)[idx]
+    err = rel_err(got, ref)
+    say(f"[layer full {name}] {idx.size} tokens, rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert torch.isfinite(y.float()).all()
+    att.close()
+
+
+def test_layer_staged_variant_matches_fused():
+    p = SMALL["c4s"]
+    x = make_layer_inputs(p)
+    a1, _, y1, _ = _run(p, x, "fused")
+    a2, _, y2, _ = _run(p, x, "staged")
+    assert torch.equal(y1, y2)
+    a1.close()
+    a2.close()
+
+
+def test_layer_rejects_overlap_and_misalignment():
+    p = SMALL["c2s"]
+    x = make_layer_inputs(p)
+    att = WindowAttention(p)
+    d = {n: t.cuda() for n, t in x.items()}
+    ws = att.layer_workspace()
+    lib = load_library()
+    vp = ctypes.c_void_p
+    args = [att.handle, vp(d["x"].data_ptr()), vp(d["w_qkv"].data_ptr()), vp(d["b_qkv"].data_ptr()),
+            vp(d["table"].data_ptr()), vp(d["w_o"].data_ptr()), vp(d["b_o"].data_ptr()), None,
+            vp(ws.data_ptr()), None]
+    y_on_x = list(args)
+    y_on_x[7] = vp(d["x"].data_ptr())
+    assert lib.swa_layer_forward(*y_on_x) == 1  # INVALID_ARGUMENT
+    y_free = torch.empty_like(d["x"])
+    ws_on_w = list(args)
+    ws_on_w[7] = vp(y_free.data_ptr())
+    ws_on_w[8] = vp(d["w_qkv"].data_ptr())
+    assert lib.swa_layer_forward(*ws_on_w) == 1
+    y_big = torch.empty(d["x"].numel() + 8, dtype=d["x"].dtype, device="cuda")
+    odd = list(args)
+    odd[7] = vp(y_big.data_ptr() + 2)
+    assert lib.swa_layer_forward(*odd) == 1
+    with pytest.raises(ValueError):
+        att.layer_forward(d["x"], d["w_qkv"][:-1], d["b_qkv"], d["table"], d["w_o"], d["b_o"])
+    torch.cuda.synchronize()
+    att.close()
+    att2 = WindowAttention(p)
+    shifted = torch.empty(4 * x["x"].numel() + 8, dtype=d["x"].dtype, device="cuda")[1:]  # 2 bytes off
+    with pytest.raises(SwaError):
+        att2.layer_forward(d["x"], d["w_qkv"], d["b_qkv"], d["table"], d["w_o"], d["b_o"], workspace=shifted)
+    torch.cuda.synchronize()
+    att2.close()
+
+
+PROJ = [  # (dtype, rows, out_features, in_features, split)
+    ("bf16", 1, 4, 32, 4),            # one token, one 4-feature group
+    ("bf16", 300, 288, 96, 96),       # ragged in tokens and features, three outputs
+    ("bf16", 257, 576, 192, 192),     # 3C of 6 heads x 32
+    ("bf16", 1000, 512, 512, 512),    # one output, four token tiles (last one ragged)
+    ("bf16", 513, 1536, 512, 512),    # 3C of 8 heads x 64
+    ("f32", 70, 288, 96, 96),
+    ("f32", 129, 64, 64, 64),
+]
+
+
+@pytest.mark.parametrize("case", PROJ, ids=[f"{c[0]}_{c[1]}x{c[3]}to{c[2]}" for c in PROJ])
+def test_projection_alone(case):
+    dtype, rows, fout, fin, split = case
+    say(f"[projection] {case}")
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    g = torch.Generator().manual_seed(rows * 7 + fout)
+    x = torch.randn((rows, fin), generator=g).to(dt)
+    w = (torch.randn((fout, fin), generator=g) / fin ** 0.5).to(dt)
+    b = torch.randn(fout, generator=g)
+    nout = (fout + split - 1) // split
+    outs = [torch.full((rows * split,), float("nan"), dtype=dt, device="cuda") for _ in range(nout)]
+    swa_projection(x.cuda(), w.cuda(), b.cuda(), outs, split=split)
+    torch.cuda.synchronize()
+    ref = oracle.linear(host_f32(x), host_f32(w), host_f32(b))
+    got = np.concatenate([host_f32(o).reshape(rows, split) for o in outs], axis=1)
+    assert np.isnan(got[:, fout:]).all()  # columns past out_features are not written
+    err = rel_err(got[:, :fout], ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+def test_projection_no_rows_is_a_no_op():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(64, device="cuda")
+    out = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    lib = load_library()
+    vp = ctypes.c_void_p
+    # torch gives empty tensors no storage; any aligned device pointer stands in
+    assert lib.swa_projection(1, vp(w.data_ptr()), vp(w.data_ptr()), vp(b.data_ptr()), 0, 64, 64, 64,
+                              vp(b.data_ptr()), None, None, None) == 0
+    del x, out
