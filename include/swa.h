@@ -190,7 +190,8 @@ swa_status swa_backward(swa_handle* h, const void* q, const void* k, const void*
  * tensors.  y must not overlap any other argument, nor the workspace any
  * input.  Asynchronous on `stream`; allocates nothing.
  * Errors: INVALID_ARGUMENT (NULL handle or pointer, misalignment, overlap),
- * HIP (launch failure).
+ * UNSUPPORTED (C above 10912: 3C output features exceed the projection's
+ * 32768), HIP (launch failure).
  */
 swa_status swa_layer_forward(swa_handle* h, const void* x, const void* w_qkv, const float* b_qkv,
                              const float* bias_table, const void* w_o, const float* b_o, void* y,
@@ -206,10 +207,10 @@ swa_status swa_layer_forward(swa_handle* h, const void* x, const void* w_qkv, co
  * outputs have element type `dtype` (bf16: bf16 matrix cores, fp32
  * accumulation and bias, one rounding); bias is fp32.  x, w, d0..d2: device
  * pointers, 16-byte aligned; bias 4-byte aligned; the outputs must not
- * overlap the inputs.  Shapes: in_features a positive multiple of 32,
- * out_features and split positive multiples of 4 with
- * out_features <= 3 * split, 0 <= rows < 2^31 (rows = 0 does nothing and
- * returns SWA_OK).  Needs a current gfx950 device.  Asynchronous on
+ * overlap the inputs.  Shapes: in_features a positive multiple of 32 up to
+ * 65536, out_features and split positive multiples of 8 with
+ * out_features <= 3 * split and out_features <= 32768, 0 <= rows < 2^31
+ * (rows = 0 does nothing and returns SWA_OK).  Needs a current gfx950 device.  Asynchronous on
  * `stream`; allocates nothing.
  * Errors: INVALID_ARGUMENT (NULL pointer, misalignment, overlap, unknown
  * dtype, negative rows), UNSUPPORTED (shape), HIP (launch failure).

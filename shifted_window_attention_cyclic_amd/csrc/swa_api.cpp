@@ -413,8 +413,9 @@ swa_status swa_projection(swa_dtype dtype, const void* x, const void* w, const f
         return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
     if (rows < 0) return fail(SWA_ERR_INVALID_ARGUMENT, "negative row count");
     if (!swa::projection_fits(rows > 0 ? rows : 1, out_features, in_features, split))
-        return fail(SWA_ERR_UNSUPPORTED, "projection shape (in_features a multiple of 32, out_features and split "
-                                         "multiples of 4, out_features <= 3 * split, rows below 2^31)");
+        return fail(SWA_ERR_UNSUPPORTED, "projection shape (in_features a multiple of 32 up to 65536, out_features "
+                                         "and split multiples of 8, out_features <= 3 * split and <= 32768, rows "
+                                         "below 2^31)");
     if (rows == 0) return SWA_OK;
     void* dst[3] = {d0, nt > 1 ? d1 : d0, nt > 2 ? d2 : d0};
     if (!aligned(x, 16) || !aligned(w, 16) || !aligned(bias, 4))

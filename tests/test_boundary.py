@@ -70,19 +70,20 @@ def test_null_handles(lib):
     assert lib.swa_backward(*([None] * 12)) == binding.SWA_ERR_INVALID_ARGUMENT
     assert lib.swa_layer_forward(*([None] * 10)) == binding.SWA_ERR_INVALID_ARGUMENT
     # NULL pointers, an unknown dtype and a bad shape are refused before any device call
-    assert lib.swa_projection(binding.SWA_BF16, None, None, None, 1, 4, 32, 4, None, None, None,
+    assert lib.swa_projection(binding.SWA_BF16, None, None, None, 1, 8, 32, 8, None, None, None,
                               None) == binding.SWA_ERR_INVALID_ARGUMENT
-    assert lib.swa_projection(7, None, None, None, 1, 4, 32, 4, None, None, None,
+    assert lib.swa_projection(7, None, None, None, 1, 8, 32, 8, None, None, None,
                               None) == binding.SWA_ERR_INVALID_ARGUMENT
     buf = ctypes.create_string_buffer(4096 + 16)
     a = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16
-    for rows, fout, fin, split in ((1, 4, 48, 4), (1, 6, 32, 6), (1, 16, 32, 4), (1 << 31, 4, 32, 4)):
+    for rows, fout, fin, split in ((1, 8, 48, 8), (1, 12, 32, 12), (1, 4, 32, 4), (1, 32, 32, 8),
+                                   (1 << 31, 8, 32, 8), (1, 1 << 16, 32, 1 << 15), (1, 8, 1 << 17, 8)):
         assert lib.swa_projection(binding.SWA_BF16, a, a, a, rows, fout, fin, split, a, a, a,
                                   None) == binding.SWA_ERR_UNSUPPORTED
-    assert lib.swa_projection(binding.SWA_BF16, a, a, a, -1, 4, 32, 4, a, a, a,
+    assert lib.swa_projection(binding.SWA_BF16, a, a, a, -1, 8, 32, 8, a, a, a,
                               None) == binding.SWA_ERR_INVALID_ARGUMENT
     # no rows: nothing to do, and no device needed
-    assert lib.swa_projection(binding.SWA_F32, a, a, a, 0, 12, 32, 4, a, a, a, None) == binding.SWA_OK
+    assert lib.swa_projection(binding.SWA_F32, a, a, a, 0, 24, 32, 8, a, a, a, None) == binding.SWA_OK
     h = ctypes.c_void_p(1234)
     assert lib.swa_create(None, ctypes.byref(h)) == binding.SWA_ERR_INVALID_ARGUMENT
     assert h.value is None  # *out cleared on failure

@@ -156,7 +156,8 @@ def test_layer_rejects_overlap_and_misalignment():
 
 
 PROJ = [  # (dtype, rows, out_features, in_features, split)
-    ("bf16", 1, 4, 32, 4),            # one token, one 4-feature group
+    ("bf16", 1, 8, 32, 8),            # one token, one 8-feature group
+    ("bf16", 37, 24, 32, 8),          # three outputs of 8 features, one partial tile
     ("bf16", 300, 288, 96, 96),       # ragged in tokens and features, three outputs
     ("bf16", 257, 576, 192, 192),     # 3C of 6 heads x 32
     ("bf16", 1000, 512, 512, 512),    # one output, four token tiles (last one ragged)
