@@ -35,6 +35,7 @@ BWD_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_backward.hip",
 METRIC_LAYER = ("shifted-window attention layer fwd (QKV projection + attention + output projection) "
                 "TFLOP/s, % of bf16 MFMA peak")
 PROJ_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_projection.hip",
+                "shifted_window_attention_cyclic_amd/csrc/swa_projection.h",
                 "shifted_window_attention_cyclic_amd/csrc/swa_device.h",
                 "shifted_window_attention_cyclic_amd/csrc/swa_geometry.h"]
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA

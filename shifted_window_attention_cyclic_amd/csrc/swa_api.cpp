@@ -13,6 +13,7 @@
 #include <string>
 
 #include "swa_geometry.h"
+#include "swa_projection.h"
 
 struct swa_handle {
     swa_config cfg;

@@ -29,6 +29,7 @@
 //
 // fp32: a plain 64 x 64 VALU tile with fp32 accumulation.
 #include "swa_device.h"
+#include "swa_projection.h"
 
 namespace swa {
 namespace {
