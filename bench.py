@@ -344,8 +344,8 @@ def cpu_baseline_layer(p, x, y_gpu, rows):
     per_query = 8.0 * C * C + 4.0 * p.window_tokens * C
     per_row = per_query * p.batch * T * W
     # the projections run as numpy matrix products, several times faster than the C
-    # attention per FLOP, so the sample is sized to 4x the attention sample's FLOPs
-    rows = max(1, min(rows, H, int(4 * CPU_SAMPLE_FLOPS // per_row)))
+    # attention per FLOP, so the sample is sized to 8x the attention sample's FLOPs
+    rows = max(1, min(rows, H, int(8 * CPU_SAMPLE_FLOPS // per_row)))
     idx = np.array([((b * T + t) * H + y) * W + xx for b in range(p.batch) for t in range(T)
                     for y in range(rows) for xx in range(W)], dtype=np.int64)
     host = {n: t.float().numpy() for n, t in x.items()}

@@ -16,12 +16,12 @@
 // persistent: it walks its tiles' 32-deep reduction stages as one stream, so
 // the next tile's first stages load while the current tile finishes.  Four
 // loader waves copy each stage (256 x 32 weights and 256 x 32 tokens) straight
-// into a four-stage LDS ring with global_load_lds, three stages ahead, with the
+// into a three-stage LDS ring with global_load_lds, two stages ahead, with the
 // tile's biases alongside; eight compute waves (128 features x 64 tokens each)
 // only read LDS, issue MFMAs and store.  The product is formed transposed
 // (features x tokens): a lane ends with four consecutive features of one
 // token.  A finished tile goes out through a small per-wave LDS staging area,
-// eight tokens at a time, so that every store moves 16 bytes per lane and a
+// sixteen tokens at a time, so that every store moves 16 bytes per lane and a
 // wave's stores cover whole token rows (8-byte stores scattered over 16 rows
 // cost the memory pipeline several times more per byte).  Tiles are dealt so
 // that each XCD walks the feature tiles of a run of token tiles: a token tile
@@ -37,7 +37,7 @@ namespace {
 constexpr int kPT = 256;     // tokens per tile
 constexpr int kPF = 256;     // output features per tile
 constexpr int kPK = 32;      // reduction depth per stage
-constexpr int kPStages = 4;  // LDS ring; stages are copied kPStages - 1 ahead
+constexpr int kPStages = 3;  // LDS ring; stages are copied kPStages - 1 ahead
 constexpr int kPCompute = 8; // compute waves
 constexpr int kPLoaders = 4; // loader waves
 constexpr int kPThreads = (kPCompute + kPLoaders) * 64;
@@ -47,7 +47,7 @@ constexpr int kPBias0 = kPStages * kPStageBytes; // tile biases: tile ti in slot
 constexpr int kPBiasSlots = 4;
 constexpr int kPStg0 = kPBias0 + kPBiasSlots * kPF * 4;
 constexpr int kPStgRow = 128 * 2 + 32; // staging row: a wave's 128 features, padded against bank conflicts
-constexpr int kPStgBytes = 8 * kPStgRow; // per compute wave: eight tokens
+constexpr int kPStgBytes = 16 * kPStgRow; // per compute wave: sixteen tokens (one 16 x 16 block row)
 constexpr int kPLdsBytes = kPStg0 + kPCompute * kPStgBytes;
 constexpr int kPCopies = kPHalf / 1024 / kPLoaders; // 1 KB copies per loader wave and operand per stage
 static_assert(kPT == kPF, "weights and tokens share the stage layout");
@@ -123,9 +123,10 @@ __global__ __launch_bounds__(kPThreads) void proj_bf16_kernel(const uint16_t* __
             }
         };
         for (int s = 0; s < kPStages - 1; s++) issue(s);
-        // vector-memory operations of a wave complete in order: with stages
-        // s .. s + 2 issued, at most two stages outstanding means stage s landed
-        // (a bias copy only adds to its stage's count, so the wait stays sufficient)
+        // vector-memory operations of a wave complete in order: with the stages
+        // s .. s + kPStages - 2 issued, at most kPStages - 2 stages outstanding
+        // means stage s landed (a bias copy only adds to its stage's count, so the
+        // wait stays sufficient)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((kPStages - 2) * kVmIssuedPerStage));
         proj_loader_barrier();
         for (int s = 0; s < steps; s++) {
@@ -160,9 +161,9 @@ __global__ __launch_bounds__(kPThreads) void proj_bf16_kernel(const uint16_t* __
         const int ti = s / KT;
         if (s - ti * KT == KT - 1) {
             // lane (col, grp) holds features 4*grp.. of each 16-feature block a for
-            // token col of each 16-token block b.  Eight tokens at a time go through
-            // the wave's staging rows; each lane then stores 16 bytes (8 features)
-            // of one token row, 16 lanes covering the row's 128 features.  The
+            // token col of each 16-token block b.  A block row of 16 tokens at a time
+            // goes through the wave's staging rows; each lane then stores 16 bytes
+            // (8 features) of one token row, 16 lanes covering the row's 128 features.  The
             // biases come from LDS: a global load here would make the wave wait for
             // every store it has in flight (the memory counter is in order).
             const int item = base + ti * stride;
@@ -174,24 +175,22 @@ __global__ __launch_bounds__(kPThreads) void proj_bf16_kernel(const uint16_t* __
             uint16_t* dq = (tq == 0 ? d0 : (tq == 1 ? d1 : d2)) + (fq - tq * split);
             const bool fok = fq < N;
             for (int b = 0; b < 4; b++) {
-                for (int h = 0; h < 2; h++) {
-                    if ((col >> 3) == h) {
-                        uint8_t* row = stg + (col - 8 * h) * kPStgRow;
-                        for (int a = 0; a < 8; a++) {
-                            const f32x4 bv = *(const f32x4*)&tb[wf + a * 16 + 4 * grp];
-                            const f32x4 v = acc[a][b];
-                            *(u32x2*)(row + (a * 16 + 4 * grp) * 2) =
-                                u32x2{pack_bf16x2(v[0] + bv[0], v[1] + bv[1]), pack_bf16x2(v[2] + bv[2], v[3] + bv[3])};
-                        }
-                    }
-                    // LDS operations of a wave run in order: these reads see the writes
-                    // above, and the next round's writes follow them
-                    for (int j = 0; j < 2; j++) {
-                        const int r = 4 * j + grp;
-                        const u32x4 val = *(const u32x4*)(stg + r * kPStgRow + col * 16);
-                        const int m = t0 + wt + b * 16 + 8 * h + r;
-                        if (fok && m < M) *(u32x4*)(dq + (int64_t)m * split) = val;
-                    }
+                uint8_t* row = stg + col * kPStgRow;
+                for (int a = 0; a < 8; a++) {
+                    const f32x4 bv = *(const f32x4*)&tb[wf + a * 16 + 4 * grp];
+                    const f32x4 v = acc[a][b];
+                    *(u32x2*)(row + (a * 16 + 4 * grp) * 2) =
+                        u32x2{pack_bf16x2(v[0] + bv[0], v[1] + bv[1]), pack_bf16x2(v[2] + bv[2], v[3] + bv[3])};
+                }
+                // LDS operations of a wave run in order: these reads see the writes
+                // above, and the next block's writes follow them
+                for (int j = 0; j < 4; j++) {
+                    const int r = 4 * j + grp;
+                    const u32x4 val = *(const u32x4*)(stg + r * kPStgRow + col * 16);
+                    const int m = t0 + wt + b * 16 + r;
+                    // non-temporal: the outputs are not read again here, and
+                    // keeping them out of L2 keeps the token tiles and weights in it
+                    if (fok && m < M) __builtin_nontemporal_store(val, (u32x4*)(dq + (int64_t)m * split));
                 }
             }
             for (int a = 0; a < 8; a++)
