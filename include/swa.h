@@ -118,8 +118,8 @@ typedef struct swa_info {
     int32_t schedule;           /* bf16: the schedule in use (_STREAM, _BLOCK or _KEYBLOCK); fp32: 0 */
     int32_t workgroups;         /* bf16: workgroups per attention launch; fp32: 0 */
     size_t backward_workspace_bytes; /* workspace swa_backward needs; 0: the backward pass does not take
-                                        this window (bf16: more than 144 tokens or past LDS; fp32: past
-                                        LDS or head_dim above 64) */
+                                        this window (bf16: a bias table slice and token tables past LDS;
+                                        fp32: past LDS or head_dim above 64) */
     size_t layer_workspace_bytes;    /* workspace swa_layer_forward needs: q, k, v and the attention
                                         output, tokens * heads * head_dim elements each */
     double layer_flops;              /* swa_layer_forward: 2 * tokens * C * 4C for the two projections
@@ -158,9 +158,13 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
  * 16-byte aligned, owned by the caller (per-(window, head) shares of the
  * table gradient and their partial sums; its contents on entry do not
  * matter).  The pass reads and writes the spatial layout whatever the
- * variant and allocates nothing.  Every sum runs in a fixed order, so the
- * results are bitwise reproducible.  The table gradient sums bf16-rounded
- * dS terms in fp32.  Asynchronous on `stream`, like swa_forward.
+ * variant and allocates nothing.  bf16 windows of up to 144 tokens (and
+ * fp32): every sum runs in a fixed order, so the results are bitwise
+ * reproducible, and the table gradient sums bf16-rounded dS terms in fp32.
+ * Larger bf16 windows (the key-blocked kernels): dq, dk, dv are still
+ * reproducible; the table gradient sums fp32 dS terms with LDS atomics, in
+ * an order that may differ between runs.  Asynchronous on `stream`, like
+ * swa_forward.
  * Errors: INVALID_ARGUMENT (NULL handle or pointer, misalignment, a buffer
  * written that overlaps another argument), UNSUPPORTED (the window is beyond
  * the backward kernels: backward_workspace_bytes is 0), HIP (launch failure).

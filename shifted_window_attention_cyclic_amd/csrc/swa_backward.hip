@@ -16,7 +16,7 @@
 // thread takes a table entry, i.e. a relative offset (query minus key), and
 // sums dS over the key positions whose query at that offset lies in the
 // window, in a fixed order, from the bf16 dS that pass 2 reads anyway.  The
-// whole backward pass is therefore bitwise reproducible.
+// single-workgroup backward pass is therefore bitwise reproducible.
 //
 // Kernels:
 //   attn_bf16_bwd_kernel  one workgroup per unit, windows of up to 9 query
@@ -29,6 +29,9 @@
 //                         table gradient, an entry per thread.
 //   attn_f32_bwd_kernel   the fp32 counterpart: one thread per query, then one
 //                         per key.
+//   attn_bf16_bwd_q_kernel, attn_bf16_bwd_kv_kernel
+//                         bf16 windows the single-workgroup kernel does not
+//                         take (see below).
 //   dtable_chunk_kernel,
 //   dtable_sum_kernel     the table gradient: per-chunk sums over windows,
 //                         then the sum of the chunks.
@@ -409,6 +412,483 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
     }
 }
 
+// ---- bf16 backward for windows beyond the single-workgroup kernel (more than
+// 9 query tiles, e.g. 2x12x12 or 32x32): nothing of size N x N is kept.  Two
+// kernels, both streaming 32-token blocks of the other side through LDS:
+//   attn_bf16_bwd_q_kernel   a block of 64 queries (a wave per 16) of a unit.
+//     Three passes over the key blocks: the softmax statistics (running max
+//     and sum, as log2 of the normaliser), D = rowsum(P * dP), then dS and
+//     dQ^T = K^T dS^T.  The statistics and D go to the workspace.
+//   attn_bf16_bwd_kv_kernel  one workgroup per unit, a wave per 16-key tile
+//     (K and V of the tile held as MFMA operands in registers).  Per block of
+//     32 queries: S = Q K^T and dP = dO V^T, P from the stored statistics,
+//     dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS; dS is added
+//     into the unit's table-gradient share in LDS with atomics (so this share,
+//     unlike the small-window kernel's, is summed in a run-dependent order).
+constexpr int kBwdBlk = 32;     // tokens per streamed block
+
+// Waits until at most n (0..8, wave-uniform) vector-memory operations of this
+// wave are outstanding.
+__device__ inline void bwd_wait_vm(int n) {
+    switch (n) {
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    }
+}
+
+// 1 KB copies per [32][D] block, and how many of them wave w of nwaves issues
+template <int D>
+constexpr int block_copies() { return kBwdBlk / (64 / (D / 8)); }
+template <int D>
+__device__ inline int block_copies_of(int w, int nwaves) {
+    return w < block_copies<D>() ? (block_copies<D>() - 1 - w) / nwaves + 1 : 0;
+}
+constexpr int kBwdQWaves = 4;   // query kernel: 64 queries per workgroup
+constexpr int kBwdKWaves = 8;   // key kernel: 8 key tiles at a time
+
+struct BwdBigLds {
+    int NPX;                     // tokens rounded up to a whole block
+    size_t tw, kb, qb, bias, dtab, stat, buf, buf_bytes, total_q, total_k;
+};
+
+__host__ __device__ inline BwdBigLds bwd_big_lds(const Geometry& g) {
+    BwdBigLds L;
+    L.NPX = (g.N + kBwdBlk - 1) / kBwdBlk * kBwdBlk;
+    const size_t tab = ((size_t)g.table_size * 4 + 15) / 16 * 16;
+    L.tw = 0;                                               // int per token
+    L.kb = L.tw + (size_t)L.NPX * 4;                        // int per token: key bias offset
+    L.qb = L.kb + (size_t)L.NPX * 4;                        // int per token: query bias offset
+    L.bias = L.qb + (size_t)L.NPX * 4;                      // the head's table slice
+    L.dtab = L.bias + tab;                                  // key kernel: the unit's share
+    L.stat = L.dtab + tab;                                  // key kernel: lse2, D per query
+    L.buf = L.stat + (size_t)L.NPX * 8;
+    L.buf_bytes = (size_t)kBwdBlk * g.head_dim * 2;         // one [32][D] bf16 block
+    L.total_q = L.dtab + 4 * L.buf_bytes;                   // query kernel: K, V double-buffered from dtab on
+    L.total_k = L.buf + 4 * L.buf_bytes;                    // key kernel: Q, dO double-buffered
+    return L;
+}
+
+// token table of a unit for the big-window kernels: tw (row + 1 | mask field
+// << 28, as the single-workgroup kernel), key and query bias offsets
+__device__ inline void big_token_table(const Geometry& g, const int wc[3], int b, int NPX, int* tw, int* kbo,
+                                       int* qbo, int nthreads) {
+    for (int n = threadIdx.x; n < NPX; n += nthreads) {
+        if (n < g.N) {
+            int l[3];
+            local_coords(g, n, l[0], l[1], l[2]);
+            int region = 0, tok = b;
+            bool is_pad = false;
+#pragma unroll
+            for (int a = 0; a < 3; a++) {
+                const int cr = wc[a] * g.win[a] + l[a];
+                int c = cr + g.shift[a];
+                if (c >= g.pad[a]) c -= g.pad[a];
+                is_pad |= c >= g.ext[a];
+                if (!g.cyc[a] && cr >= g.pad[a] - g.shift[a]) region |= 1 << a;
+                tok = tok * g.ext[a] + c;
+            }
+            tw[n] = ((is_pad ? -1 : tok) + 1) | ((region | (is_pad ? 8 : 0)) << 28);
+            kbo[n] = (l[0] * g.tdy + l[1]) * g.tdx + l[2];
+            qbo[n] = kbo[n] + g.c0;
+        } else {
+            tw[n] = 15 << 28; // a field no query has: never visible
+            kbo[n] = 0;
+            qbo[n] = g.table_size - 1; // qb - kb stays inside the table
+        }
+    }
+}
+
+__device__ inline void unit_coords(const Geometry& g, uint32_t unit, int& h, int& b, int wc[3], uint32_t& wi) {
+    wi = fdiv(g.fd_heads, unit);
+    h = (int)(unit - wi * (uint32_t)g.heads);
+    b = (int)fdiv(g.fd_nW, wi);
+    const uint32_t r = wi - (uint32_t)b * (uint32_t)g.nW;
+    const uint32_t r2 = fdiv(g.fd_nwin2, r);
+    wc[2] = (int)(r - r2 * (uint32_t)g.nwin[2]);
+    wc[0] = (int)fdiv(g.fd_nwin1, r2);
+    wc[1] = (int)(r2 - (uint32_t)wc[0] * (uint32_t)g.nwin[1]);
+}
+
+// copies one [32][D] block of a tensor (rows from the token table; pad and
+// past-N rows read row 0) into LDS, swizzled; the calling waves split the
+// 1 KB copies.  Returns the copies this wave issued.
+template <int D>
+__device__ inline int copy_block(const Geometry& g, const uint16_t* src, int h, const int* tw, int t0,
+                                 unsigned char* dst, int wave, int nwaves) {
+    constexpr int CH = D / 8, RPC = 64 / CH, NC = kBwdBlk / RPC;
+    const int lane = threadIdx.x & 63, m0 = lane / CH;
+    int issued = 0;
+    for (int c = wave; c < NC; c += nwaves) {
+        const int r1 = tw[t0 + c * RPC + m0] & kRowMask;
+        const uint64_t off = (uint64_t)(uint32_t)(r1 == 0 ? 0 : r1 - 1) * (uint32_t)g.row + h * D +
+                             copy_chunk<D>(c * RPC + m0, lane) * 8;
+        __builtin_amdgcn_global_load_lds((const void*)(src + off), (lds_void*)(dst + c * 1024), 16, 0, 0);
+        issued++;
+    }
+    return issued;
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdQWaves * 64) void attn_bf16_bwd_q_kernel(
+    Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
+    float* __restrict__ stats) {
+    constexpr int THREADS = kBwdQWaves * 64;
+    constexpr int KSTEPS = D / 32, DT = D / 16;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const BwdBigLds L = bwd_big_lds(g);
+    const int N = g.N, NPX = L.NPX, NB = NPX / kBwdBlk;
+    int* tw = (int*)(smem + L.tw);
+    int* kbo = (int*)(smem + L.kb);
+    int* qbo = (int*)(smem + L.qb);
+    float* bias = (float*)(smem + L.bias);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+
+    const int QB = (N + 63) / 64;
+    const uint32_t total = (uint32_t)(g.windows * g.heads) * (uint32_t)QB;
+    const uint32_t work = (uint32_t)xcd_work_index(blockIdx.x, total);
+    const uint32_t unit = work / (uint32_t)QB;
+    const int qblk = (int)(work - unit * (uint32_t)QB);
+    int h, b, wc[3];
+    uint32_t wi;
+    unit_coords(g, unit, h, b, wc, wi);
+    const bool masked_window = window_maybe_masked(g, wc);
+
+    big_token_table(g, wc, b, NPX, tw, kbo, qbo, THREADS);
+    for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)i * g.heads + h];
+    __syncthreads();
+
+    // this lane's query and its B operands (query n, d = 32 ks + 8 grp + 0..7)
+    const int n = qblk * 64 + wave * 16 + col;
+    const bool in_window = n < N;
+    const int qword = in_window ? tw[n] : (15 << 28);
+    const unsigned qreg = (unsigned)qword >> 28;
+    const int r = (qword & kRowMask) - 1;
+    const float qvalid = r >= 0 ? 1.f : 0.f; // pad queries have no output, so no gradient
+    const int qb = in_window ? qbo[n] : g.table_size - 1;
+    bf16x8 qf[KSTEPS], df[KSTEPS];
+    {
+        const uint64_t base = (uint64_t)(uint32_t)(r < 0 ? 0 : r) * (uint32_t)g.row + h * D + grp * 8;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ks++) {
+            qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q + base + ks * 32));
+            df[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(dout + base + ks * 32));
+        }
+    }
+
+    // K and V blocks through a double buffer: block j in buffer j % 2; a wave
+    // issues `own` copies per block
+    const int own = 2 * block_copies_of<D>(wave, kBwdQWaves);
+    auto kbuf = [&](int j) { return smem + L.dtab + (size_t)(j & 1) * 2 * L.buf_bytes; };
+    auto issue = [&](int j) {
+        copy_block<D>(g, k, h, tw, j * kBwdBlk, kbuf(j), wave, kBwdQWaves);
+        copy_block<D>(g, v, h, tw, j * kBwdBlk, kbuf(j) + L.buf_bytes, wave, kBwdQWaves);
+    };
+    // S^T and dP^T of one block for this lane's query: tiles t = 0, 1 (keys 16 t + 4 grp + 0..3)
+    auto block_products = [&](int j, f32x4 (&s)[2], f32x4 (&dp)[2], bool with_dp) __attribute__((always_inline)) {
+        const uint16_t* Ks = (const uint16_t*)kbuf(j);
+        const uint16_t* Vs = (const uint16_t*)(kbuf(j) + L.buf_bytes);
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const int krow = t * 16 + col;
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ks++) {
+                const int slot = k_slot<D>(krow, ks * 4 + grp) * 8;
+                a0 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(Ks + krow * D + slot)), qf[ks], a0);
+                if (with_dp)
+                    a1 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(Vs + krow * D + slot)), df[ks], a1);
+            }
+            s[t] = a0;
+            dp[t] = a1;
+        }
+        // logits in log2 units: (scale * s + bias) * log2(e), -inf where masked
+        const int key0 = j * kBwdBlk;
+        const bool check = masked_window || key0 + kBwdBlk > N;
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const int kk = key0 + t * 16 + grp * 4;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                float lg = fmaf(s[t][i], g.scale, bias[qb - kbo[kk + i]]) * kLog2e;
+                if (check && ((unsigned)tw[kk + i] >> 28) != qreg) lg = -INFINITY;
+                s[t][i] = lg;
+            }
+        }
+    };
+
+    // ---- pass 1: softmax statistics (max m and sum l over this lane's keys, then across the 4 lanes)
+    float m_run = -INFINITY, l_run = 0.f;
+    issue(0);
+    for (int j = 0; j < NB; j++) {
+        if (j + 1 < NB) issue(j + 1);
+        bwd_wait_vm(j + 1 < NB ? own : 0); // block j landed (copies complete in order)
+        __syncthreads();
+        f32x4 s[2], dp[2];
+        block_products(j, s, dp, false);
+        float bm = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) bm = fmaxf(bm, s[t][i]);
+        const float mn = fmaxf(m_run, bm);
+        if (mn != -INFINITY) {
+            float add = 0.f;
+#pragma unroll
+            for (int t = 0; t < 2; t++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) add += __builtin_amdgcn_exp2f(s[t][i] - mn);
+            l_run = l_run * __builtin_amdgcn_exp2f(m_run - mn) + add;
+            m_run = mn;
+        }
+        __syncthreads(); // the buffer of block j is rewritten by issue(j + 2)
+    }
+    float m_all = fmaxf(m_run, __shfl_xor(m_run, 16));
+    m_all = fmaxf(m_all, __shfl_xor(m_all, 32));
+    float l_all = m_run == -INFINITY ? 0.f : l_run * __builtin_amdgcn_exp2f(m_run - m_all);
+    l_all += __shfl_xor(l_all, 16);
+    l_all += __shfl_xor(l_all, 32);
+    // P = qvalid * exp2(logit - lse2); a query with no visible key (pad) gets P = 0
+    const float lse2 = l_all > 0.f ? m_all + log2f(l_all) : 0.f;
+    const float pscale = l_all > 0.f ? qvalid : 0.f;
+
+    // ---- pass 2: D = rowsum(P * dP)
+    float dsum = 0.f;
+    issue(0);
+    for (int j = 0; j < NB; j++) {
+        if (j + 1 < NB) issue(j + 1);
+        bwd_wait_vm(j + 1 < NB ? own : 0);
+        __syncthreads();
+        f32x4 s[2], dp[2];
+        block_products(j, s, dp, true);
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) dsum = fmaf(pscale * __builtin_amdgcn_exp2f(s[t][i] - lse2), dp[t][i], dsum);
+        __syncthreads();
+    }
+    dsum += __shfl_xor(dsum, 16);
+    dsum += __shfl_xor(dsum, 32);
+    // statistics per query: lse2 (log2 of the softmax normaliser) and D; a pad
+    // query gets lse2 = +inf, so that every P it would take is 0
+    if (grp == 0 && in_window) {
+        float* st = stats + (size_t)unit * 2 * NPX;
+        st[n] = pscale == 0.f ? INFINITY : lse2;
+        st[NPX + n] = pscale == 0.f ? 0.f : dsum;
+    }
+
+    // ---- pass 3: dS and dQ^T = K^T dS^T (the forward's O^T = V^T P^T with K for V, dS for P)
+    f32x4 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    issue(0);
+    for (int j = 0; j < NB; j++) {
+        if (j + 1 < NB) issue(j + 1);
+        bwd_wait_vm(j + 1 < NB ? own : 0);
+        __syncthreads();
+        f32x4 s[2], dp[2];
+        block_products(j, s, dp, true);
+        unsigned pk[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            f32x4 ds;
+#pragma unroll
+            for (int i = 0; i < 4; i++) ds[i] = pscale * __builtin_amdgcn_exp2f(s[t][i] - lse2) * (dp[t][i] - dsum);
+            pk[t][0] = pack_bf16x2(ds[0], ds[1]);
+            pk[t][1] = pack_bf16x2(ds[2], ds[3]);
+        }
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]});
+        const unsigned char* Kb = kbuf(j);
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            // transposed 4 x 16 reads of K: keys 16 t + 4 grp + 0..3, d = 16 dt + col
+            u32x2 part[2];
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int row = t * 16 + grp * 4 + (col >> 2);
+                const int d = dt * 16 + (col & 3) * 4;
+                part[t] = tr_read(Kb + row * (D * 2) + k_slot<D>(row, d >> 3) * 16 + (d & 7) * 2);
+            }
+            acc[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}), bop,
+                             acc[dt]);
+        }
+        __syncthreads();
+    }
+    if (r >= 0) {
+        uint16_t* op = dq + (uint64_t)(uint32_t)r * (uint32_t)g.row + h * D + grp * 4;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+            *(u32x2*)(op + dt * 16) = u32x2{pack_bf16x2(acc[dt][0] * g.scale, acc[dt][1] * g.scale),
+                                            pack_bf16x2(acc[dt][2] * g.scale, acc[dt][3] * g.scale)};
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdKWaves * 64) void attn_bf16_bwd_kv_kernel(
+    Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, const float* __restrict__ stats, float* __restrict__ dtab_units) {
+    constexpr int THREADS = kBwdKWaves * 64;
+    constexpr int KSTEPS = D / 32, DT = D / 16;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const BwdBigLds L = bwd_big_lds(g);
+    const int N = g.N, NPX = L.NPX, NB = NPX / kBwdBlk;
+    int* tw = (int*)(smem + L.tw);
+    int* kbo = (int*)(smem + L.kb);
+    int* qbo = (int*)(smem + L.qb);
+    float* bias = (float*)(smem + L.bias);
+    float* dtab = (float*)(smem + L.dtab);
+    float* lse = (float*)(smem + L.stat);
+    float* dd = lse + NPX;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+
+    const uint32_t units = (uint32_t)(g.windows * g.heads);
+    const uint32_t unit = (uint32_t)xcd_work_index(blockIdx.x, units);
+    int h, b, wc[3];
+    uint32_t wi;
+    unit_coords(g, unit, h, b, wc, wi);
+    const bool masked_window = window_maybe_masked(g, wc);
+
+    big_token_table(g, wc, b, NPX, tw, kbo, qbo, THREADS);
+    for (int i = tid; i < g.table_size; i += THREADS) {
+        bias[i] = table[(size_t)i * g.heads + h];
+        dtab[i] = 0.f;
+    }
+    {
+        const float* st = stats + (size_t)unit * 2 * NPX;
+        for (int i = tid; i < NPX; i += THREADS) {
+            lse[i] = i < N ? st[i] : INFINITY; // slots past N: P = 0
+            dd[i] = i < N ? st[NPX + i] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // Q and dO blocks through a double buffer: block j in buffer j % 2
+    const int own = 2 * block_copies_of<D>(wave, kBwdKWaves);
+    auto qbuf = [&](int j) { return smem + L.buf + (size_t)(j & 1) * 2 * L.buf_bytes; };
+    auto issue = [&](int j) {
+        copy_block<D>(g, q, h, tw, j * kBwdBlk, qbuf(j), wave, kBwdKWaves);
+        copy_block<D>(g, dout, h, tw, j * kBwdBlk, qbuf(j) + L.buf_bytes, wave, kBwdKWaves);
+    };
+    // transposed 4 x 16 read of a [32][D] block: rows t0 + 4 grp + 0..3, d = 16 dt + col
+    auto tr_blk = [&](const unsigned char* base, int t0, int dt) __attribute__((always_inline)) {
+        const int row = t0 + grp * 4 + (col >> 2);
+        const int d = dt * 16 + (col & 3) * 4;
+        return tr_read(base + row * (D * 2) + k_slot<D>(row, d >> 3) * 16 + (d & 7) * 2);
+    };
+
+    const int KT = NPX / 16; // key tiles; waves take them kBwdKWaves at a time
+    for (int kt0 = 0; kt0 < KT; kt0 += kBwdKWaves) {
+        const int kt = kt0 + wave;
+        const bool active = kt < KT;
+        const int m = (active ? kt : 0) * 16 + col;
+        const int kword = active ? tw[m] : (15 << 28);
+        const unsigned kreg = (unsigned)kword >> 28;
+        const int kr = (kword & kRowMask) - 1;
+        const int kbm = active ? kbo[m] : 0;
+        const bool key_in = active && m < N; // slots past N see no query: masked in every block
+        // B operands: key m, d = 32 ks + 8 grp + 0..7 (pad keys read row 0; they are masked)
+        bf16x8 kf[KSTEPS], vf[KSTEPS];
+        {
+            const uint64_t base = (uint64_t)(uint32_t)(kr < 0 ? 0 : kr) * (uint32_t)g.row + h * D + grp * 8;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ks++) {
+                kf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(k + base + ks * 32));
+                vf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(v + base + ks * 32));
+            }
+        }
+        f32x4 av[DT], ak[DT]; // dV^T and dK^T: lane (key m, d = 16 dt + 4 grp + 0..3)
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            av[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            ak[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        issue(0);
+        for (int j = 0; j < NB; j++) {
+            if (j + 1 < NB) issue(j + 1);
+            bwd_wait_vm(j + 1 < NB ? own : 0); // block j landed (copies complete in order)
+            __syncthreads();
+            if (active) {
+                const unsigned char* Qb = qbuf(j);
+                const unsigned char* Ob = qbuf(j) + L.buf_bytes;
+                const uint16_t* Qs = (const uint16_t*)Qb;
+                const uint16_t* dOs = (const uint16_t*)Ob;
+                // S = Q K^T and dP = dO V^T: lane (key m, queries 16 t + 4 grp + 0..3 of the block)
+                f32x4 sv[2], dpv[2];
+#pragma unroll
+                for (int t = 0; t < 2; t++) {
+                    const int qrow = t * 16 + col;
+                    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KSTEPS; ks++) {
+                        const int slot = k_slot<D>(qrow, ks * 4 + grp) * 8;
+                        a0 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(Qs + qrow * D + slot)), kf[ks], a0);
+                        a1 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(dOs + qrow * D + slot)), vf[ks], a1);
+                    }
+                    sv[t] = a0;
+                    dpv[t] = a1;
+                }
+                const bool check = masked_window || (j + 1) * kBwdBlk > N;
+                unsigned pp[2][2], ps[2][2];
+                // the lane's key is fixed: one past N is masked whatever the query block
+#pragma unroll
+                for (int t = 0; t < 2; t++) {
+                    f32x4 p, ds;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int n = j * kBwdBlk + t * 16 + grp * 4 + i;
+                        const int e = qbo[n] - kbm;
+                        float lg = fmaf(sv[t][i], g.scale, bias[e]) * kLog2e;
+                        if (!key_in || (check && ((unsigned)tw[n] >> 28) != kreg)) lg = -INFINITY;
+                        p[i] = __builtin_amdgcn_exp2f(lg - lse[n]);
+                        ds[i] = p[i] * (dpv[t][i] - dd[n]);
+                        if (p[i] != 0.f) atomicAdd(&dtab[e], ds[i]);
+                    }
+                    pp[t][0] = pack_bf16x2(p[0], p[1]);
+                    pp[t][1] = pack_bf16x2(p[2], p[3]);
+                    ps[t][0] = pack_bf16x2(ds[0], ds[1]);
+                    ps[t][1] = pack_bf16x2(ds[2], ds[3]);
+                }
+                const bf16x8 bp = __builtin_bit_cast(bf16x8, u32x4{pp[0][0], pp[0][1], pp[1][0], pp[1][1]});
+                const bf16x8 bs = __builtin_bit_cast(bf16x8, u32x4{ps[0][0], ps[0][1], ps[1][0], ps[1][1]});
+                // dV^T += dO^T P and dK^T += Q^T dS, contracting over the block's 32 queries
+#pragma unroll
+                for (int dt = 0; dt < DT; dt++) {
+                    const u32x2 o0 = tr_blk(Ob, 0, dt), o1 = tr_blk(Ob, 16, dt);
+                    const u32x2 q0 = tr_blk(Qb, 0, dt), q1 = tr_blk(Qb, 16, dt);
+                    av[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{o0[0], o0[1], o1[0], o1[1]}), bp, av[dt]);
+                    ak[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), bs, ak[dt]);
+                }
+            }
+            __syncthreads(); // the buffer of block j is rewritten by issue(j + 2)
+        }
+        if (active && kr >= 0) {
+            const uint64_t base = (uint64_t)(uint32_t)kr * (uint32_t)g.row + h * D + grp * 4;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                *(u32x2*)(dv + base + dt * 16) =
+                    u32x2{pack_bf16x2(av[dt][0], av[dt][1]), pack_bf16x2(av[dt][2], av[dt][3])};
+                *(u32x2*)(dk + base + dt * 16) = u32x2{pack_bf16x2(ak[dt][0] * g.scale, ak[dt][1] * g.scale),
+                                                       pack_bf16x2(ak[dt][2] * g.scale, ak[dt][3] * g.scale)};
+            }
+        }
+    }
+    __syncthreads();
+    float* dst = dtab_units + (size_t)unit * g.table_size;
+    for (int e = tid; e < g.table_size; e += THREADS) dst[e] = dtab[e];
+}
+
 // ---- fp32 backward: one block per unit, a thread per query, then per key
 constexpr int kF32BwdThreads = 256;
 
@@ -571,16 +1051,28 @@ __global__ __launch_bounds__(256) void dtable_sum_kernel(int heads, int ts, cons
 }
 
 // ---- host side
+// the single-workgroup bf16 kernel, or else the two big-window kernels
+static bool bwd_small_fits(const Geometry& g) {
+    return (g.N + 15) / 16 <= kBwdMaxTiles && bwd_lds(g).total <= (size_t)kLdsBytes;
+}
+
+static bool bwd_big_fits(const Geometry& g) {
+    const BwdBigLds L = bwd_big_lds(g);
+    return L.total_q <= (size_t)kLdsBytes && L.total_k <= (size_t)kLdsBytes;
+}
+
 bool backward_fits(const Geometry& g, bool bf16) {
     if (!bf16) return g.head_dim <= 64 && f32_bwd_lds_bytes(g) <= (size_t)kLdsBytes;
     const int64_t rows = (int64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
-    return (g.N + 15) / 16 <= kBwdMaxTiles && bwd_lds(g).total <= (size_t)kLdsBytes && rows < kRowMask;
+    return rows < kRowMask && (bwd_small_fits(g) || bwd_big_fits(g));
 }
 
 size_t backward_workspace_bytes(const Geometry& g) {
     const size_t units = (size_t)(g.windows * g.heads) * g.table_size;
     const size_t chunks = (size_t)kDtableChunks * g.heads * g.table_size;
-    return (units + chunks) * sizeof(float);
+    // big windows: per query, lse2 and D
+    const size_t stats = bwd_small_fits(g) ? 0 : (size_t)(g.windows * g.heads) * 2 * bwd_big_lds(g).NPX;
+    return (units + chunks + stats) * sizeof(float);
 }
 
 typedef void (*bwd_bf16_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
@@ -597,7 +1089,10 @@ hipError_t prepare_backward_kernels(int max_lds) {
     const void* fs[] = {(const void*)attn_bf16_bwd_kernel<32, true>,  (const void*)attn_bf16_bwd_kernel<32, false>,
                         (const void*)attn_bf16_bwd_kernel<64, true>,  (const void*)attn_bf16_bwd_kernel<64, false>,
                         (const void*)attn_bf16_bwd_kernel<128, true>, (const void*)attn_bf16_bwd_kernel<128, false>,
-                        (const void*)attn_f32_bwd_kernel<32>,         (const void*)attn_f32_bwd_kernel<64>};
+                        (const void*)attn_f32_bwd_kernel<32>,         (const void*)attn_f32_bwd_kernel<64>,
+                        (const void*)attn_bf16_bwd_q_kernel<32>,      (const void*)attn_bf16_bwd_q_kernel<64>,
+                        (const void*)attn_bf16_bwd_q_kernel<128>,     (const void*)attn_bf16_bwd_kv_kernel<32>,
+                        (const void*)attn_bf16_bwd_kv_kernel<64>,     (const void*)attn_bf16_bwd_kv_kernel<128>};
     for (const void* f : fs) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
         if (e != hipSuccess) return e;
@@ -611,7 +1106,26 @@ hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const vo
     const dim3 grid((unsigned)(g.windows * g.heads));
     float* units = (float*)workspace;
     float* chunks = units + (size_t)(g.windows * g.heads) * g.table_size;
-    if (bf16) {
+    float* stats = chunks + (size_t)kDtableChunks * g.heads * g.table_size;
+    if (bf16 && !bwd_small_fits(g)) {
+        const BwdBigLds L = bwd_big_lds(g);
+        const dim3 qgrid((unsigned)(g.windows * g.heads * ((g.N + 63) / 64)));
+        typedef void (*qk_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
+                             const uint16_t*, uint16_t*, float*);
+        typedef void (*kv_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
+                             const uint16_t*, uint16_t*, uint16_t*, const float*, float*);
+        const qk_t fq = g.head_dim == 32 ? attn_bf16_bwd_q_kernel<32>
+                        : g.head_dim == 64 ? attn_bf16_bwd_q_kernel<64> : attn_bf16_bwd_q_kernel<128>;
+        const kv_t fk = g.head_dim == 32 ? attn_bf16_bwd_kv_kernel<32>
+                        : g.head_dim == 64 ? attn_bf16_bwd_kv_kernel<64> : attn_bf16_bwd_kv_kernel<128>;
+        hipLaunchKernelGGL(fq, qgrid, dim3(kBwdQWaves * 64), L.total_q, s, g, (const uint16_t*)q, (const uint16_t*)k,
+                           (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dq, stats);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(fk, grid, dim3(kBwdKWaves * 64), L.total_k, s, g, (const uint16_t*)q, (const uint16_t*)k,
+                           (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dk, (uint16_t*)dv,
+                           (const float*)stats, units);
+    } else if (bf16) {
         hipLaunchKernelGGL(bwd_bf16_variant(g), grid, dim3(kBwdWaves * 64), bwd_lds(g).total, s, g,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, table, (const uint16_t*)dout,
                            (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, units);

@@ -11,8 +11,8 @@ import torch
 import oracle
 from helpers import TOL, host_f32, rel_err
 from shifted_window_attention_cyclic_amd import SwaError, WindowAttention
-from shifted_window_attention_cyclic_amd.inputs import WORKLOADS, make_inputs, small_variant
-from test_gpu_parity import EDGE, SMALL
+from shifted_window_attention_cyclic_amd.inputs import WORKLOADS, Problem, make_inputs
+from test_gpu_parity import EDGE, LARGE, SMALL
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +43,7 @@ def _takes_backward(p):
     return ok
 
 
-CASES = {**SMALL, **EDGE}
+CASES = {**SMALL, **EDGE, **LARGE}
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -116,8 +116,31 @@ def test_backward_is_bitwise_reproducible():
         assert torch.equal(ga, gb)
 
 
+@pytest.mark.parametrize("name", ["c5_bf16_4x180x360_3d", "c7_bf16_180x384_pad192_d128_w32"])
+def test_backward_big_windows_full_size_sampled(name):
+    """The big-window kernels at full size (2x12x12 and 32x32 windows): every
+    token's gradients in a few sampled windows (first, last, latitude wrap)."""
+    p = WORKLOADS[name]
+    x = make_inputs(p)
+    dout = _dout(p)
+    dq, dk, dv, dtable = _run(p, x, dout)
+    nw = p.windows // p.batch
+    wins = sorted({0, nw // 2 + 1, nw - 1})
+    say(f"[backward big {name}] windows {wins}")
+    ref = oracle.literal_backward(p, host_f32(x["q"]), host_f32(x["k"]), host_f32(x["v"]),
+                                  host_f32(x["table"]), host_f32(dout), windows=wins)
+    mine = np.isin(oracle.token_windows(p), wins)[None]
+    for gname, g_gpu, g_ref in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+        err = rel_err(host_f32(g_gpu)[mine], g_ref[mine])
+        say(f"  {gname}: rel err {err:.3e} over {int(mine.sum())} tokens")
+        assert err <= TOL["bf16"], gname
+    for g in (dq, dk, dv, dtable):
+        assert torch.isfinite(g.float()).all()
+
+
 def test_backward_rejects_windows_it_does_not_take():
-    p = small_variant(WORKLOADS["c5_bf16_4x180x360_3d"], 24, 36)  # 288-token windows
+    # fp32 keeps whole windows in LDS: 16 x 16 windows do not fit
+    p = Problem("f32big", "f32", 1, 2, 32, (1, 32, 32), (1, 32, 32), (1, 16, 16), (0, 8, 8), seed=3)
     att = WindowAttention(p)
     assert att.info.backward_workspace_bytes == 0
     x = {n: t.cuda() for n, t in make_inputs(p).items()}
