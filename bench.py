@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "shifted-window attention fwd TFLOP/s + tokens/s, % of bf16 MFMA peak"
 METRIC_BWD = "shifted-window attention bwd TFLOP/s + tokens/s, % of bf16 MFMA peak"
 BWD_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_backward.hip",
+               "shifted_window_attention_cyclic_amd/csrc/swa_backward.h",
                "shifted_window_attention_cyclic_amd/csrc/swa_device.h",
                "shifted_window_attention_cyclic_amd/csrc/swa_geometry.h"]
 METRIC_LAYER = ("shifted-window attention layer fwd (QKV projection + attention + output projection) "
@@ -283,7 +284,9 @@ def main():
         "tokens_per_s": round(info.tokens / (ms_per_step * 1e-3), 1),
         "mfma_peak_frac": round(tflops / peak_tf, 5),
         "useful_tflops": round(useful / (ms_per_step * 1e-3) / 1e12, 3),
-        "kernel": {"name": (("attn_f32_bwd_kernel" if p.dtype == "f32" else "attn_bf16_bwd_kernel") if backward
+        "kernel": {"name": (("attn_f32_bwd_kernel" if p.dtype == "f32" else
+                             "attn_bf16_bwd_kernel" if info.backward_schedule == 1 else
+                             "attn_bf16_bwd_q_kernel+attn_bf16_bwd_kv_kernel") if backward
                             else kernel_name(p, info) if args.variant == "fused" else "gather+attn+scatter"),
                    "workgroups": info.workgroups,
                    "avg_launch_ms": round(avg_launch_ms, 5),

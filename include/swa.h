@@ -124,6 +124,9 @@ typedef struct swa_info {
                                         output, tokens * heads * head_dim elements each */
     double layer_flops;              /* swa_layer_forward: 2 * tokens * C * 4C for the two projections
                                         (C = heads * head_dim) plus nominal_flops */
+    int32_t backward_schedule;       /* 0: no backward pass; 1: one workgroup per (window, head), the
+                                        whole window in LDS (fp32 always); 2: bf16 key-blocked kernels
+                                        for windows beyond that (32-token blocks streamed) */
 } swa_info;
 
 /*
@@ -158,12 +161,13 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
  * 16-byte aligned, owned by the caller (per-(window, head) shares of the
  * table gradient and their partial sums; its contents on entry do not
  * matter).  The pass reads and writes the spatial layout whatever the
- * variant and allocates nothing.  bf16 windows of up to 144 tokens (and
- * fp32): every sum runs in a fixed order, so the results are bitwise
- * reproducible, and the table gradient sums bf16-rounded dS terms in fp32.
- * Larger bf16 windows (the key-blocked kernels): dq, dk, dv are still
- * reproducible; the table gradient sums fp32 dS terms with LDS atomics, in
- * an order that may differ between runs.  Asynchronous on `stream`, like
+ * variant and allocates nothing.  backward_schedule 1 (bf16 windows whose
+ * Q, K, V, dO and two N x N matrices fit one workgroup's LDS: up to 144
+ * tokens with head_dim <= 64, fewer at 128; and fp32): every sum runs in a
+ * fixed order, so the results are bitwise reproducible, and the table
+ * gradient sums bf16-rounded dS terms in fp32.  backward_schedule 2 (larger
+ * bf16 windows): dq, dk, dv are still reproducible; the table gradient sums
+ * fp32 dS terms with LDS atomics, in an order that may differ between runs.  Asynchronous on `stream`, like
  * swa_forward.
  * Errors: INVALID_ARGUMENT (NULL handle or pointer, misalignment, a buffer
  * written that overlaps another argument), UNSUPPORTED (the window is beyond

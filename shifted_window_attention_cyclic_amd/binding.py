@@ -41,7 +41,7 @@ class swa_info(ctypes.Structure):
         ("nominal_flops", ctypes.c_double), ("algorithmic_bytes", ctypes.c_double),
         ("schedule", ctypes.c_int32), ("workgroups", ctypes.c_int32),
         ("backward_workspace_bytes", ctypes.c_size_t), ("layer_workspace_bytes", ctypes.c_size_t),
-        ("layer_flops", ctypes.c_double),
+        ("layer_flops", ctypes.c_double), ("backward_schedule", ctypes.c_int32),
     ]
 
 

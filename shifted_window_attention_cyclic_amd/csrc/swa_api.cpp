@@ -14,6 +14,7 @@
 
 #include "swa_geometry.h"
 #include "swa_projection.h"
+#include "swa_backward.h"
 
 struct swa_handle {
     swa_config cfg;
@@ -291,6 +292,7 @@ swa_status swa_get_info(const swa_handle* h, swa_info* info) {
     info->schedule = bf16 ? h->schedule : 0;
     info->workgroups = bf16 ? h->blocks : 0;
     info->backward_workspace_bytes = swa::backward_fits(g, bf16) ? swa::backward_workspace_bytes(g) : 0;
+    info->backward_schedule = swa::backward_schedule(g, bf16);
     info->layer_workspace_bytes = 4 * io_bytes(h);
     info->layer_flops = 8.0 * (double)info->tokens * g.row * (double)g.row + info->nominal_flops;
     return SWA_OK;

@@ -39,6 +39,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "swa_backward.h"
 #include "swa_device.h"
 #include "swa_geometry.h"
 
@@ -1065,6 +1066,11 @@ bool backward_fits(const Geometry& g, bool bf16) {
     if (!bf16) return g.head_dim <= 64 && f32_bwd_lds_bytes(g) <= (size_t)kLdsBytes;
     const int64_t rows = (int64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
     return rows < kRowMask && (bwd_small_fits(g) || bwd_big_fits(g));
+}
+
+int backward_schedule(const Geometry& g, bool bf16) {
+    if (!backward_fits(g, bf16)) return 0;
+    return !bf16 || bwd_small_fits(g) ? 1 : 2;
 }
 
 size_t backward_workspace_bytes(const Geometry& g) {

@@ -138,11 +138,22 @@ def test_backward_big_windows_full_size_sampled(name):
         assert torch.isfinite(g.float()).all()
 
 
+@pytest.mark.parametrize("name,schedule", [("c3_bf16_540x1080", 1), ("c6_bf16_180x360_pad184_d128", 1),
+                                           ("c5_bf16_4x180x360_3d", 2), ("c7_bf16_180x384_pad192_d128_w32", 2),
+                                           ("c1_f32_16x32", 1)])
+def test_backward_schedule_reported(name, schedule):
+    att = WindowAttention(WORKLOADS[name])
+    assert att.info.backward_schedule == schedule
+    assert att.info.backward_workspace_bytes > 0
+    att.close()
+
+
 def test_backward_rejects_windows_it_does_not_take():
     # fp32 keeps whole windows in LDS: 16 x 16 windows do not fit
     p = Problem("f32big", "f32", 1, 2, 32, (1, 32, 32), (1, 32, 32), (1, 16, 16), (0, 8, 8), seed=3)
     att = WindowAttention(p)
     assert att.info.backward_workspace_bytes == 0
+    assert att.info.backward_schedule == 0
     x = {n: t.cuda() for n, t in make_inputs(p).items()}
     with pytest.raises(SwaError):
         att.backward(x["q"], x["k"], x["v"], x["table"], torch.zeros_like(x["q"]))
