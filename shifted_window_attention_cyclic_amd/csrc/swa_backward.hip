@@ -451,12 +451,11 @@ template <int D>
 __device__ inline int block_copies_of(int w, int nwaves) {
     return w < block_copies<D>() ? (block_copies<D>() - 1 - w) / nwaves + 1 : 0;
 }
-constexpr int kBwdQWaves = 4;   // query kernel: 64 queries per workgroup
 constexpr int kBwdKWaves = 8;   // key kernel: 8 key tiles at a time
 
 struct BwdBigLds {
     int NPX;                     // tokens rounded up to a whole block
-    size_t tw, kb, qb, bias, dtab, stat, buf, buf_bytes, total_q, total_k;
+    size_t tw, kb, qb, bias, dtab, stat, diag, buf, buf_bytes, total_q, total_k;
 };
 
 __host__ __device__ inline BwdBigLds bwd_big_lds(const Geometry& g) {
@@ -469,7 +468,8 @@ __host__ __device__ inline BwdBigLds bwd_big_lds(const Geometry& g) {
     L.bias = L.qb + (size_t)L.NPX * 4;                      // the head's table slice
     L.dtab = L.bias + tab;                                  // key kernel: the unit's share
     L.stat = L.dtab + tab;                                  // key kernel: lse2, D per query
-    L.buf = L.stat + (size_t)L.NPX * 8;
+    L.diag = L.stat + (size_t)L.NPX * 8;                    // key kernel: per-wave 31 x 16 diagonal scratch
+    L.buf = L.diag + (size_t)kBwdKWaves * 31 * 16 * 4;
     L.buf_bytes = (size_t)kBwdBlk * g.head_dim * 2;         // one [32][D] bf16 block
     L.total_q = L.dtab + 4 * L.buf_bytes;                   // query kernel: K, V double-buffered from dtab on
     L.total_k = L.buf + 4 * L.buf_bytes;                    // key kernel: Q, dO double-buffered
@@ -536,12 +536,12 @@ __device__ inline int copy_block(const Geometry& g, const uint16_t* src, int h, 
     return issued;
 }
 
-template <int D>
-__global__ __launch_bounds__(kBwdQWaves * 64) void attn_bf16_bwd_q_kernel(
+template <int D, int QW>
+__global__ __launch_bounds__(QW * 64) void attn_bf16_bwd_q_kernel(
     Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
     float* __restrict__ stats) {
-    constexpr int THREADS = kBwdQWaves * 64;
+    constexpr int THREADS = QW * 64;
     constexpr int KSTEPS = D / 32, DT = D / 16;
     extern __shared__ __align__(16) unsigned char smem[];
     const BwdBigLds L = bwd_big_lds(g);
@@ -554,7 +554,7 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void attn_bf16_bwd_q_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;
 
-    const int QB = (N + 63) / 64;
+    const int QB = (N + QW * 16 - 1) / (QW * 16);
     const uint32_t total = (uint32_t)(g.windows * g.heads) * (uint32_t)QB;
     const uint32_t work = (uint32_t)xcd_work_index(blockIdx.x, total);
     const uint32_t unit = work / (uint32_t)QB;
@@ -569,7 +569,7 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void attn_bf16_bwd_q_kernel(
     __syncthreads();
 
     // this lane's query and its B operands (query n, d = 32 ks + 8 grp + 0..7)
-    const int n = qblk * 64 + wave * 16 + col;
+    const int n = qblk * QW * 16 + wave * 16 + col;
     const bool in_window = n < N;
     const int qword = in_window ? tw[n] : (15 << 28);
     const unsigned qreg = (unsigned)qword >> 28;
@@ -588,11 +588,11 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void attn_bf16_bwd_q_kernel(
 
     // K and V blocks through a double buffer: block j in buffer j % 2; a wave
     // issues `own` copies per block
-    const int own = 2 * block_copies_of<D>(wave, kBwdQWaves);
+    const int own = 2 * block_copies_of<D>(wave, QW);
     auto kbuf = [&](int j) { return smem + L.dtab + (size_t)(j & 1) * 2 * L.buf_bytes; };
     auto issue = [&](int j) {
-        copy_block<D>(g, k, h, tw, j * kBwdBlk, kbuf(j), wave, kBwdQWaves);
-        copy_block<D>(g, v, h, tw, j * kBwdBlk, kbuf(j) + L.buf_bytes, wave, kBwdQWaves);
+        copy_block<D>(g, k, h, tw, j * kBwdBlk, kbuf(j), wave, QW);
+        copy_block<D>(g, v, h, tw, j * kBwdBlk, kbuf(j) + L.buf_bytes, wave, QW);
     };
     // S^T and dP^T of one block for this lane's query: tiles t = 0, 1 (keys 16 t + 4 grp + 0..3)
     auto block_products = [&](int j, f32x4 (&s)[2], f32x4 (&dp)[2], bool with_dp) __attribute__((always_inline)) {
@@ -760,6 +760,7 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void attn_bf16_bwd_kv_kernel(
     uint32_t wi;
     unit_coords(g, unit, h, b, wc, wi);
     const bool masked_window = window_maybe_masked(g, wc);
+    const bool diag = g.win[2] % 16 == 0; // 16-token tiles never straddle a window row
 
     big_token_table(g, wc, b, NPX, tw, kbo, qbo, THREADS);
     for (int i = tid; i < g.table_size; i += THREADS) {
@@ -799,6 +800,7 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void attn_bf16_bwd_kv_kernel(
         const int kr = (kword & kRowMask) - 1;
         const int kbm = active ? kbo[m] : 0;
         const bool key_in = active && m < N; // slots past N see no query: masked in every block
+        // (N is a whole number of 16-key tiles when diag is set, so key_in is wave-uniform then)
         // B operands: key m, d = 32 ks + 8 grp + 0..7 (pad keys read row 0; they are masked)
         bf16x8 kf[KSTEPS], vf[KSTEPS];
         {
@@ -842,6 +844,7 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void attn_bf16_bwd_kv_kernel(
                 }
                 const bool check = masked_window || (j + 1) * kBwdBlk > N;
                 unsigned pp[2][2], ps[2][2];
+                f32x4 dsv[2];
                 // the lane's key is fixed: one past N is masked whatever the query block
 #pragma unroll
                 for (int t = 0; t < 2; t++) {
@@ -854,12 +857,38 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void attn_bf16_bwd_kv_kernel(
                         if (!key_in || (check && ((unsigned)tw[n] >> 28) != kreg)) lg = -INFINITY;
                         p[i] = __builtin_amdgcn_exp2f(lg - lse[n]);
                         ds[i] = p[i] * (dpv[t][i] - dd[n]);
-                        if (p[i] != 0.f) atomicAdd(&dtab[e], ds[i]);
+                        if (!diag && p[i] != 0.f) atomicAdd(&dtab[e], ds[i]);
                     }
+                    dsv[t] = ds;
                     pp[t][0] = pack_bf16x2(p[0], p[1]);
                     pp[t][1] = pack_bf16x2(p[2], p[3]);
                     ps[t][0] = pack_bf16x2(ds[0], ds[1]);
                     ps[t][1] = pack_bf16x2(ds[2], ds[3]);
+                }
+                if (diag) {
+                    // 16 x 16 tiles lie in one window row each (the width is a multiple
+                    // of 16), so pair (query 4 grp + i, key col) of tile t reads entry
+                    // E0 + 4 grp + i - col: each of the 31 diagonals is one entry.
+                    // Lane (col, grp) parks its 4 terms at [diagonal][4 grp + i] (one
+                    // writer per slot); lane d then sums diagonal d - 15 and adds it.
+                    float* sc = (float*)(smem + L.diag) + wave * 31 * 16;
+#pragma unroll
+                    for (int t = 0; t < 2; t++) {
+                        const int n0 = j * kBwdBlk + t * 16;
+                        if (key_in && n0 < N) { // wave-uniform: all or none of the tile's queries
+#pragma unroll
+                            for (int i = 0; i < 4; i++) sc[(4 * grp + i - col + 15) * 16 + 4 * grp + i] = dsv[t][i];
+                            __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's writes landed
+                            if (lane < 31) {
+                                const int dgl = lane - 15;
+                                float sum = 0.f;
+                                for (int sl = dgl > 0 ? dgl : 0; sl < (dgl > 0 ? 16 : 16 + dgl); sl++)
+                                    sum += sc[lane * 16 + sl];
+                                atomicAdd(&dtab[qbo[n0] - kbo[kt * 16] + dgl], sum);
+                            }
+                            __builtin_amdgcn_s_waitcnt(0xC07F); // the reads are done before the next writes
+                        }
+                    }
                 }
                 const bf16x8 bp = __builtin_bit_cast(bf16x8, u32x4{pp[0][0], pp[0][1], pp[1][0], pp[1][1]});
                 const bf16x8 bs = __builtin_bit_cast(bf16x8, u32x4{ps[0][0], ps[0][1], ps[1][0], ps[1][1]});
@@ -1096,8 +1125,10 @@ hipError_t prepare_backward_kernels(int max_lds) {
                         (const void*)attn_bf16_bwd_kernel<64, true>,  (const void*)attn_bf16_bwd_kernel<64, false>,
                         (const void*)attn_bf16_bwd_kernel<128, true>, (const void*)attn_bf16_bwd_kernel<128, false>,
                         (const void*)attn_f32_bwd_kernel<32>,         (const void*)attn_f32_bwd_kernel<64>,
-                        (const void*)attn_bf16_bwd_q_kernel<32>,      (const void*)attn_bf16_bwd_q_kernel<64>,
-                        (const void*)attn_bf16_bwd_q_kernel<128>,     (const void*)attn_bf16_bwd_kv_kernel<32>,
+                        (const void*)attn_bf16_bwd_q_kernel<32, 4>,   (const void*)attn_bf16_bwd_q_kernel<64, 4>,
+                        (const void*)attn_bf16_bwd_q_kernel<128, 4>,  (const void*)attn_bf16_bwd_q_kernel<32, 8>,
+                        (const void*)attn_bf16_bwd_q_kernel<64, 8>,   (const void*)attn_bf16_bwd_q_kernel<128, 8>,
+                        (const void*)attn_bf16_bwd_kv_kernel<32>,
                         (const void*)attn_bf16_bwd_kv_kernel<64>,     (const void*)attn_bf16_bwd_kv_kernel<128>};
     for (const void* f : fs) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
@@ -1115,16 +1146,21 @@ hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const vo
     float* stats = chunks + (size_t)kDtableChunks * g.heads * g.table_size;
     if (bf16 && !bwd_small_fits(g)) {
         const BwdBigLds L = bwd_big_lds(g);
-        const dim3 qgrid((unsigned)(g.windows * g.heads * ((g.N + 63) / 64)));
+        const int QW = g.N >= 512 ? 8 : 4; // wider query blocks re-stream K and V fewer times
+        const dim3 qgrid((unsigned)(g.windows * g.heads * ((g.N + QW * 16 - 1) / (QW * 16))));
         typedef void (*qk_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
                              const uint16_t*, uint16_t*, float*);
         typedef void (*kv_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
                              const uint16_t*, uint16_t*, uint16_t*, const float*, float*);
-        const qk_t fq = g.head_dim == 32 ? attn_bf16_bwd_q_kernel<32>
-                        : g.head_dim == 64 ? attn_bf16_bwd_q_kernel<64> : attn_bf16_bwd_q_kernel<128>;
+        const qk_t fq = QW == 8 ? (g.head_dim == 32   ? attn_bf16_bwd_q_kernel<32, 8>
+                                   : g.head_dim == 64 ? attn_bf16_bwd_q_kernel<64, 8>
+                                                      : attn_bf16_bwd_q_kernel<128, 8>)
+                                : (g.head_dim == 32   ? attn_bf16_bwd_q_kernel<32, 4>
+                                   : g.head_dim == 64 ? attn_bf16_bwd_q_kernel<64, 4>
+                                                      : attn_bf16_bwd_q_kernel<128, 4>);
         const kv_t fk = g.head_dim == 32 ? attn_bf16_bwd_kv_kernel<32>
                         : g.head_dim == 64 ? attn_bf16_bwd_kv_kernel<64> : attn_bf16_bwd_kv_kernel<128>;
-        hipLaunchKernelGGL(fq, qgrid, dim3(kBwdQWaves * 64), L.total_q, s, g, (const uint16_t*)q, (const uint16_t*)k,
+        hipLaunchKernelGGL(fq, qgrid, dim3(QW * 64), L.total_q, s, g, (const uint16_t*)q, (const uint16_t*)k,
                            (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dq, stats);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
