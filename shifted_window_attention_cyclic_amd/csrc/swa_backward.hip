@@ -760,7 +760,6 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void attn_bf16_bwd_kv_kernel(
     uint32_t wi;
     unit_coords(g, unit, h, b, wc, wi);
     const bool masked_window = window_maybe_masked(g, wc);
-    const bool diag = g.win[2] % 16 == 0; // 16-token tiles never straddle a window row
 
     big_token_table(g, wc, b, NPX, tw, kbo, qbo, THREADS);
     for (int i = tid; i < g.table_size; i += THREADS) {
@@ -800,7 +799,6 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void attn_bf16_bwd_kv_kernel(
         const int kr = (kword & kRowMask) - 1;
         const int kbm = active ? kbo[m] : 0;
         const bool key_in = active && m < N; // slots past N see no query: masked in every block
-        // (N is a whole number of 16-key tiles when diag is set, so key_in is wave-uniform then)
         // B operands: key m, d = 32 ks + 8 grp + 0..7 (pad keys read row 0; they are masked)
         bf16x8 kf[KSTEPS], vf[KSTEPS];
         {
@@ -857,7 +855,6 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void attn_bf16_bwd_kv_kernel(
                         if (!key_in || (check && ((unsigned)tw[n] >> 28) != kreg)) lg = -INFINITY;
                         p[i] = __builtin_amdgcn_exp2f(lg - lse[n]);
                         ds[i] = p[i] * (dpv[t][i] - dd[n]);
-                        if (!diag && p[i] != 0.f) atomicAdd(&dtab[e], ds[i]);
                     }
                     dsv[t] = ds;
                     pp[t][0] = pack_bf16x2(p[0], p[1]);
@@ -865,26 +862,45 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void attn_bf16_bwd_kv_kernel(
                     ps[t][0] = pack_bf16x2(ds[0], ds[1]);
                     ps[t][1] = pack_bf16x2(ds[2], ds[3]);
                 }
-                if (diag) {
-                    // 16 x 16 tiles lie in one window row each (the width is a multiple
-                    // of 16), so pair (query 4 grp + i, key col) of tile t reads entry
-                    // E0 + 4 grp + i - col: each of the 31 diagonals is one entry.
-                    // Lane (col, grp) parks its 4 terms at [diagonal][4 grp + i] (one
-                    // writer per slot); lane d then sums diagonal d - 15 and adds it.
+                {
+                    // The tile's dS into the unit's table share.  Pair (query 4 grp + i,
+                    // key col) of a 16 x 16 tile lies on diagonal 4 grp + i - col, and
+                    // along a diagonal the table entry changes only where the query or
+                    // the key crosses a window row.  Lane (col, grp) parks its 4 terms
+                    // at [diagonal][4 grp + i] (one writer per slot); lane d then walks
+                    // diagonal d - 15 and adds each run of equal entries with one
+                    // atomic: once per diagonal when the window width is a multiple
+                    // of 16, a few times otherwise, instead of once per term.
                     float* sc = (float*)(smem + L.diag) + wave * 31 * 16;
+                    const int m0 = kt * 16;
+                    const bool rowtile = g.win[2] % 16 == 0; // 16-token tiles never straddle a window row
 #pragma unroll
                     for (int t = 0; t < 2; t++) {
                         const int n0 = j * kBwdBlk + t * 16;
-                        if (key_in && n0 < N) { // wave-uniform: all or none of the tile's queries
+                        if (active && m0 < N && n0 < N) { // wave-uniform; terms past N are 0
 #pragma unroll
                             for (int i = 0; i < 4; i++) sc[(4 * grp + i - col + 15) * 16 + 4 * grp + i] = dsv[t][i];
                             __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's writes landed
-                            if (lane < 31) {
+                            if (lane < 31 && rowtile) {
+                                // one window row each: a single entry per diagonal
                                 const int dgl = lane - 15;
-                                float sum = 0.f;
-                                for (int sl = dgl > 0 ? dgl : 0; sl < (dgl > 0 ? 16 : 16 + dgl); sl++)
-                                    sum += sc[lane * 16 + sl];
-                                atomicAdd(&dtab[qbo[n0] - kbo[kt * 16] + dgl], sum);
+                                float run = 0.f;
+                                for (int a = dgl > 0 ? dgl : 0; a < (dgl > 0 ? 16 : 16 + dgl); a++) run += sc[lane * 16 + a];
+                                atomicAdd(&dtab[qbo[n0] - kbo[m0] + dgl], run);
+                            } else if (lane < 31) {
+                                const int dgl = lane - 15;
+                                float run = 0.f;
+                                int ecur = -1;
+                                for (int a = dgl > 0 ? dgl : 0; a < (dgl > 0 ? 16 : 16 + dgl); a++) {
+                                    const int e = qbo[n0 + a] - kbo[m0 + a - dgl];
+                                    if (e != ecur) {
+                                        if (ecur >= 0) atomicAdd(&dtab[ecur], run);
+                                        ecur = e;
+                                        run = 0.f;
+                                    }
+                                    run += sc[lane * 16 + a];
+                                }
+                                if (ecur >= 0) atomicAdd(&dtab[ecur], run);
                             }
                             __builtin_amdgcn_s_waitcnt(0xC07F); // the reads are done before the next writes
                         }
