@@ -24,8 +24,12 @@
 // sixteen tokens at a time, so that every store moves 16 bytes per lane and a
 // wave's stores cover whole token rows (8-byte stores scattered over 16 rows
 // cost the memory pipeline several times more per byte).  Tiles are dealt so
-// that each XCD walks the feature tiles of a run of token tiles: a token tile
-// is read from HBM once into that XCD's L2 and the weights stay resident there.
+// that each XCD walks a contiguous run of work items.  When the weights fit
+// L2 the feature tile runs fastest: a token tile is read from HBM once into
+// that XCD's L2 and the weights stay resident there.  Larger weights (C = 8192:
+// 400 MB) are walked in groups of 8 token tiles, so that the blocks running
+// together share each weight slice 8 ways instead of re-reading it per token
+// tile.
 //
 // fp32: a plain 64 x 64 VALU tile with fp32 accumulation.
 #include "swa_device.h"
@@ -74,11 +78,23 @@ __global__ __launch_bounds__(kPThreads) void proj_bf16_kernel(const uint16_t* __
                                                               const float* __restrict__ bias, int M, int N,
                                                               int K, int split, uint16_t* __restrict__ d0,
                                                               uint16_t* __restrict__ d1,
-                                                              uint16_t* __restrict__ d2) {
+                                                              uint16_t* __restrict__ d2, int GM) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ntf = (N + kPF - 1) / kPF;
+    const int ntt = (M + kPT - 1) / kPT;
+    // work item -> (token tile, feature tile), in groups of GM token tiles that
+    // walk all feature tiles with the token tile fastest: the tiles a wave of
+    // blocks runs together share weight slices GM ways and token slices
+    // (blocks / GM) ways.  GM = 1: the feature tile fastest (weights that fit L2).
+    auto tile_of = [&](int item, int& f0_, int& t0_) __attribute__((always_inline)) {
+        const int gsz = GM * ntf;
+        const int gi = item / gsz, j = item - gi * gsz;
+        const int rows = ntt - gi * GM < GM ? ntt - gi * GM : GM;
+        t0_ = (gi * GM + j % rows) * kPT;
+        f0_ = (j / rows) * kPF;
+    };
     const int tiles = ((M + kPT - 1) / kPT) * ntf;
     const int G = gridDim.x;
     const int mine = (tiles - 1 - (int)blockIdx.x) / G + 1; // the grid has at most `tiles` blocks
@@ -100,7 +116,8 @@ __global__ __launch_bounds__(kPThreads) void proj_bf16_kernel(const uint16_t* __
             s = past ? steps - 1 : s; // past the end: a harmless copy into a slot nobody reads
             const int ti = s / KT, kt = s - ti * KT;
             const int item = base + ti * stride;
-            const int f0 = (item % ntf) * kPF, t0 = (item / ntf) * kPT;
+            int f0, t0;
+            tile_of(item, f0, t0);
             if (kt == 0 && !past) {
                 // the tile's biases go with its first stage, into bias slot ti % 4: read
                 // at its last step, not overwritten before tile ti + 4 starts loading
@@ -167,7 +184,8 @@ __global__ __launch_bounds__(kPThreads) void proj_bf16_kernel(const uint16_t* __
             // biases come from LDS: a global load here would make the wave wait for
             // every store it has in flight (the memory counter is in order).
             const int item = base + ti * stride;
-            const int f0 = (item % ntf) * kPF, t0 = (item / ntf) * kPT;
+            int f0, t0;
+            tile_of(item, f0, t0);
             const float* tb = (const float*)(lds + kPBias0 + (ti % kPBiasSlots) * kPF * 4);
             uint8_t* stg = lds + kPStg0 + wave * kPStgBytes;
             const int fq = f0 + wf + 8 * col; // the 8 features this lane stores
@@ -289,9 +307,11 @@ hipError_t launch_projection(bool bf16, const void* x, const void* w, const floa
         int grid = 0;
         hipError_t e = projection_grid(tiles, &grid);
         if (e != hipSuccess) return e;
+        // weights beyond a couple of MB do not stay in an XCD's L2: group the tiles
+        const int GM = (int64_t)N * K * 2 > ((int64_t)2 << 20) ? 8 : 1;
         hipLaunchKernelGGL(proj_bf16_kernel, dim3(grid), dim3(kPThreads), kPLdsBytes, s, (const uint16_t*)x,
                            (const uint16_t*)w, bias, (int)M, N, K, split, (uint16_t*)d0, (uint16_t*)d1,
-                           (uint16_t*)d2);
+                           (uint16_t*)d2, GM);
     } else {
         const int64_t tiles = ((M + kFT - 1) / kFT) * ((N + kFT - 1) / kFT);
         hipLaunchKernelGGL(proj_f32_kernel, dim3((unsigned)tiles), dim3(256), 0, s, (const float*)x,

@@ -90,7 +90,8 @@ def test_layer_full_size_180x360():
     att.close()
 
 
-@pytest.mark.parametrize("name", ["c3_bf16_540x1080", "c4_bf16_181x360_pad190"])
+@pytest.mark.parametrize("name", ["c3_bf16_540x1080", "c4_bf16_181x360_pad190", "c5_bf16_4x180x360_3d",
+                                  "c6_bf16_180x360_pad184_d128"])
 def test_layer_full_size_sampled(name):
     """Full size in the benchmark's launch configuration: sampled tokens
     (window edges, shift boundaries, pad neighbours and random ones) against
