@@ -43,7 +43,10 @@ def _takes_backward(p):
     return ok
 
 
-CASES = {**SMALL, **EDGE, **LARGE}
+CASES = {**SMALL, **EDGE, **LARGE,
+         # the big-window kernels with two batch items and a padded, masked latitude
+         "b2_n288_3d_pad": Problem("b2n288", "bf16", 2, 3, 64, (2, 20, 24), (2, 24, 24), (2, 12, 12), (1, 6, 6),
+                                   seed=31)}
 
 
 @pytest.mark.parametrize("name", list(CASES))
