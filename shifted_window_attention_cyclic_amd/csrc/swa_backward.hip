@@ -415,18 +415,27 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
 
 // ---- bf16 backward for windows beyond the single-workgroup kernel (more than
 // 9 query tiles, e.g. 2x12x12 or 32x32): nothing of size N x N is kept.  Two
-// kernels, both streaming 32-token blocks of the other side through LDS:
-//   attn_bf16_bwd_q_kernel   a block of 64 queries (a wave per 16) of a unit.
-//     Three passes over the key blocks: the softmax statistics (running max
-//     and sum, as log2 of the normaliser), D = rowsum(P * dP), then dS and
-//     dQ^T = K^T dS^T.  The statistics and D go to the workspace.
+// kernels, both streaming 32-token blocks of the other side through an LDS
+// ring filled by loader waves of their own:
+//   attn_bf16_bwd_q_kernel   a block of 64 or 128 queries (a wave per 16) of
+//     a unit.  Two passes over the key blocks: first the softmax statistics
+//     and D = rowsum(P * dP) together (running max, normaliser and D, the
+//     last two rescaled whenever the max grows), then dS and
+//     dQ^T = K^T dS^T.  The statistics (as log2 of the normaliser) and D go
+//     to the workspace.
 //   attn_bf16_bwd_kv_kernel  one workgroup per unit, a wave per 16-key tile
 //     (K and V of the tile held as MFMA operands in registers).  Per block of
 //     32 queries: S = Q K^T and dP = dO V^T, P from the stored statistics,
 //     dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS; dS is added
 //     into the unit's table-gradient share in LDS with atomics (so this share,
 //     unlike the small-window kernel's, is summed in a run-dependent order).
+// Only the loader waves issue LDS copies.  A wave that both copies and reads
+// LDS gets a vmcnt(0) from the compiler before its barriers, transposing
+// reads and LDS atomics (it cannot tell the copies in flight from the data
+// read), which leaves no copy in flight while the wave computes.
 constexpr int kBwdBlk = 32;     // tokens per streamed block
+constexpr int kBwdStages = 3;   // ring slots: the block in use and two in flight
+constexpr int kBwdLoaders = 2;  // loader waves per workgroup
 
 // Waits until at most n (0..8, wave-uniform) vector-memory operations of this
 // wave are outstanding.
@@ -444,6 +453,44 @@ __device__ inline void bwd_wait_vm(int n) {
     }
 }
 
+// Block barrier of the compute waves, which issue no LDS copies: the fence
+// orders LDS accesses only.
+__device__ inline void bwd_compute_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Block barrier of the loader waves.  Their only LDS writes are copies they
+// have waited for with vmcnt; a release fence would make the compiler wait
+// for every copy in flight.  The empty asm statements keep the compiler from
+// moving LDS accesses across the barrier.
+__device__ inline void bwd_loader_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The loader waves' side of a stream of T blocks through the ring.  Block s
+// goes to slot s % kBwdStages, issued kBwdStages - 1 blocks ahead of its use;
+// before barrier s a loader waits only for its copies of block s (the later
+// ones may stay in flight, since a wave's copies complete in order).  The
+// compute waves take block s between barriers s and s + 1, so the slot that
+// block s + kBwdStages - 1 overwrites after barrier s is free.
+// issue(s, slot) issues this wave's `own` copies of block s.
+template <typename Issue>
+__device__ inline void bwd_stream(int T, int own, Issue&& issue) {
+    for (int s = 0; s < kBwdStages - 1 && s < T; s++) issue(s, s);
+    for (int s = 0; s < T; s++) {
+        const int ahead = T - 1 - s < kBwdStages - 2 ? T - 1 - s : kBwdStages - 2;
+        bwd_wait_vm(ahead * own);
+        bwd_loader_barrier();
+        const int nxt = s + kBwdStages - 1;
+        if (nxt < T) issue(nxt, nxt % kBwdStages);
+    }
+}
+
 // 1 KB copies per [32][D] block, and how many of them wave w of nwaves issues
 template <int D>
 constexpr int block_copies() { return kBwdBlk / (64 / (D / 8)); }
@@ -451,7 +498,10 @@ template <int D>
 __device__ inline int block_copies_of(int w, int nwaves) {
     return w < block_copies<D>() ? (block_copies<D>() - 1 - w) / nwaves + 1 : 0;
 }
-constexpr int kBwdKWaves = 8;   // key kernel: 8 key tiles at a time
+constexpr int kBwdKWaves = 8;   // key kernel: at most 8 key tiles at a time
+// the loaders' waits stay within bwd_wait_vm's range
+static_assert((kBwdStages - 2) * 2 * ((block_copies<128>() + kBwdLoaders - 1) / kBwdLoaders) <= 8,
+              "copies in flight per loader wave");
 
 struct BwdBigLds {
     int NPX;                     // tokens rounded up to a whole block
@@ -468,11 +518,11 @@ __host__ __device__ inline BwdBigLds bwd_big_lds(const Geometry& g) {
     L.bias = L.qb + (size_t)L.NPX * 4;                      // the head's table slice
     L.dtab = L.bias + tab;                                  // key kernel: the unit's share
     L.stat = L.dtab + tab;                                  // key kernel: lse2, D per query
-    L.diag = L.stat + (size_t)L.NPX * 8;                    // key kernel: per-wave 31 x 16 diagonal scratch
-    L.buf = L.diag + (size_t)kBwdKWaves * 31 * 16 * 4;
+    L.diag = L.stat + (size_t)L.NPX * 8;                    // key kernel: per-wave 2 x 31 x 16 diagonal scratch
+    L.buf = L.diag + (size_t)kBwdKWaves * 2 * 31 * 16 * 4;
     L.buf_bytes = (size_t)kBwdBlk * g.head_dim * 2;         // one [32][D] bf16 block
-    L.total_q = L.dtab + 4 * L.buf_bytes;                   // query kernel: K, V double-buffered from dtab on
-    L.total_k = L.buf + 4 * L.buf_bytes;                    // key kernel: Q, dO double-buffered
+    L.total_q = L.dtab + 2 * kBwdStages * L.buf_bytes;      // query kernel: the K, V ring from dtab on
+    L.total_k = L.buf + 2 * kBwdStages * L.buf_bytes;       // key kernel: the Q, dO ring
     return L;
 }
 
@@ -537,11 +587,11 @@ __device__ inline int copy_block(const Geometry& g, const uint16_t* src, int h, 
 }
 
 template <int D, int QW>
-__global__ __launch_bounds__(QW * 64) void attn_bf16_bwd_q_kernel(
+__global__ __launch_bounds__((QW + kBwdLoaders) * 64) void attn_bf16_bwd_q_kernel(
     Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
     float* __restrict__ stats) {
-    constexpr int THREADS = QW * 64;
+    constexpr int THREADS = (QW + kBwdLoaders) * 64;
     constexpr int KSTEPS = D / 32, DT = D / 16;
     extern __shared__ __align__(16) unsigned char smem[];
     const BwdBigLds L = bwd_big_lds(g);
@@ -550,6 +600,7 @@ __global__ __launch_bounds__(QW * 64) void attn_bf16_bwd_q_kernel(
     int* kbo = (int*)(smem + L.kb);
     int* qbo = (int*)(smem + L.qb);
     float* bias = (float*)(smem + L.bias);
+    unsigned char* ring = smem + L.dtab; // kBwdStages slots of a K block and a V block
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;
@@ -567,6 +618,17 @@ __global__ __launch_bounds__(QW * 64) void attn_bf16_bwd_q_kernel(
     big_token_table(g, wc, b, NPX, tw, kbo, qbo, THREADS);
     for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)i * g.heads + h];
     __syncthreads();
+
+    if (wave >= QW) { // loader waves: K and V blocks, once per pass
+        const int li = wave - QW;
+        bwd_stream(2 * NB, 2 * block_copies_of<D>(li, kBwdLoaders), [&](int s, int slot) {
+            const int j = s < NB ? s : s - NB;
+            unsigned char* dst = ring + (size_t)slot * 2 * L.buf_bytes;
+            copy_block<D>(g, k, h, tw, j * kBwdBlk, dst, li, kBwdLoaders);
+            copy_block<D>(g, v, h, tw, j * kBwdBlk, dst + L.buf_bytes, li, kBwdLoaders);
+        });
+        return;
+    }
 
     // this lane's query and its B operands (query n, d = 32 ks + 8 grp + 0..7)
     const int n = qblk * QW * 16 + wave * 16 + col;
@@ -586,56 +648,59 @@ __global__ __launch_bounds__(QW * 64) void attn_bf16_bwd_q_kernel(
         }
     }
 
-    // K and V blocks through a double buffer: block j in buffer j % 2; a wave
-    // issues `own` copies per block
-    const int own = 2 * block_copies_of<D>(wave, QW);
-    auto kbuf = [&](int j) { return smem + L.dtab + (size_t)(j & 1) * 2 * L.buf_bytes; };
-    auto issue = [&](int j) {
-        copy_block<D>(g, k, h, tw, j * kBwdBlk, kbuf(j), wave, QW);
-        copy_block<D>(g, v, h, tw, j * kBwdBlk, kbuf(j) + L.buf_bytes, wave, QW);
-    };
-    // S^T and dP^T of one block for this lane's query: tiles t = 0, 1 (keys 16 t + 4 grp + 0..3)
-    auto block_products = [&](int j, f32x4 (&s)[2], f32x4 (&dp)[2], bool with_dp) __attribute__((always_inline)) {
-        const uint16_t* Ks = (const uint16_t*)kbuf(j);
-        const uint16_t* Vs = (const uint16_t*)(kbuf(j) + L.buf_bytes);
+    // S^T and dP^T of key block j (in ring slot `slot`) for this lane's query:
+    // tiles t = 0, 1 (keys 16 t + 4 grp + 0..3); S as logits in log2 units
+    auto block_products = [&](int slot, int j, f32x4 (&s)[2], f32x4 (&dp)[2]) __attribute__((always_inline)) {
+        const uint16_t* Ks = (const uint16_t*)(ring + (size_t)slot * 2 * L.buf_bytes);
+        const uint16_t* Vs = (const uint16_t*)(ring + (size_t)slot * 2 * L.buf_bytes + L.buf_bytes);
 #pragma unroll
         for (int t = 0; t < 2; t++) {
             const int krow = t * 16 + col;
             f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ks++) {
-                const int slot = k_slot<D>(krow, ks * 4 + grp) * 8;
-                a0 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(Ks + krow * D + slot)), qf[ks], a0);
-                if (with_dp)
-                    a1 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(Vs + krow * D + slot)), df[ks], a1);
+                const int kslot = k_slot<D>(krow, ks * 4 + grp) * 8;
+                a0 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(Ks + krow * D + kslot)), qf[ks], a0);
+                a1 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(Vs + krow * D + kslot)), df[ks], a1);
             }
             s[t] = a0;
             dp[t] = a1;
         }
-        // logits in log2 units: (scale * s + bias) * log2(e), -inf where masked
+        // logits in log2 units: (scale * s + bias) * log2(e), -inf where masked.
+        // The lane's 4 keys are consecutive: their words come in one 16-byte
+        // read each, and every bias read is issued before any is used.
         const int key0 = j * kBwdBlk;
         const bool check = masked_window || key0 + kBwdBlk > N;
+        u32x4 kb4[2], tw4[2];
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-            const int kk = key0 + t * 16 + grp * 4;
+            kb4[t] = *(const u32x4*)(kbo + key0 + t * 16 + grp * 4);
+            tw4[t] = *(const u32x4*)(tw + key0 + t * 16 + grp * 4);
+        }
+        float bv[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) bv[t][i] = bias[qb - (int)kb4[t][i]];
+#pragma unroll
+        for (int t = 0; t < 2; t++)
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                float lg = fmaf(s[t][i], g.scale, bias[qb - kbo[kk + i]]) * kLog2e;
-                if (check && ((unsigned)tw[kk + i] >> 28) != qreg) lg = -INFINITY;
-                s[t][i] = lg;
+                const float lg = fmaf(s[t][i], g.scale, bv[t][i]) * kLog2e;
+                s[t][i] = check && (tw4[t][i] >> 28) != qreg ? -INFINITY : lg;
             }
-        }
     };
 
-    // ---- pass 1: softmax statistics (max m and sum l over this lane's keys, then across the 4 lanes)
-    float m_run = -INFINITY, l_run = 0.f;
-    issue(0);
+    // ---- pass 1: the softmax statistics and D = rowsum(P * dP) at once.  Per
+    // lane, over its keys: the running max m, l = sum 2^(logit - m) and
+    // dsum = sum 2^(logit - m) dP, both rescaled when m grows; then across the
+    // query's 4 lanes.  D = dsum / l.
+    float m_run = -INFINITY, l_run = 0.f, d_run = 0.f;
+    int slot = 0;
     for (int j = 0; j < NB; j++) {
-        if (j + 1 < NB) issue(j + 1);
-        bwd_wait_vm(j + 1 < NB ? own : 0); // block j landed (copies complete in order)
-        __syncthreads();
+        bwd_compute_barrier(); // block j is in its slot
         f32x4 s[2], dp[2];
-        block_products(j, s, dp, false);
+        block_products(slot, j, s, dp);
         float bm = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 2; t++)
@@ -643,61 +708,50 @@ __global__ __launch_bounds__(QW * 64) void attn_bf16_bwd_q_kernel(
             for (int i = 0; i < 4; i++) bm = fmaxf(bm, s[t][i]);
         const float mn = fmaxf(m_run, bm);
         if (mn != -INFINITY) {
-            float add = 0.f;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mn); // 0 while m_run is -inf
+            float la = 0.f, da = 0.f;
 #pragma unroll
             for (int t = 0; t < 2; t++)
 #pragma unroll
-                for (int i = 0; i < 4; i++) add += __builtin_amdgcn_exp2f(s[t][i] - mn);
-            l_run = l_run * __builtin_amdgcn_exp2f(m_run - mn) + add;
+                for (int i = 0; i < 4; i++) {
+                    const float e = __builtin_amdgcn_exp2f(s[t][i] - mn);
+                    la += e;
+                    da = fmaf(e, dp[t][i], da);
+                }
+            l_run = fmaf(l_run, alpha, la);
+            d_run = fmaf(d_run, alpha, da);
             m_run = mn;
         }
-        __syncthreads(); // the buffer of block j is rewritten by issue(j + 2)
+        slot = slot + 1 == kBwdStages ? 0 : slot + 1;
     }
     float m_all = fmaxf(m_run, __shfl_xor(m_run, 16));
     m_all = fmaxf(m_all, __shfl_xor(m_all, 32));
-    float l_all = m_run == -INFINITY ? 0.f : l_run * __builtin_amdgcn_exp2f(m_run - m_all);
+    const float wgt = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_all);
+    float l_all = l_run * wgt, d_all = d_run * wgt;
     l_all += __shfl_xor(l_all, 16);
     l_all += __shfl_xor(l_all, 32);
+    d_all += __shfl_xor(d_all, 16);
+    d_all += __shfl_xor(d_all, 32);
     // P = qvalid * exp2(logit - lse2); a query with no visible key (pad) gets P = 0
     const float lse2 = l_all > 0.f ? m_all + log2f(l_all) : 0.f;
     const float pscale = l_all > 0.f ? qvalid : 0.f;
-
-    // ---- pass 2: D = rowsum(P * dP)
-    float dsum = 0.f;
-    issue(0);
-    for (int j = 0; j < NB; j++) {
-        if (j + 1 < NB) issue(j + 1);
-        bwd_wait_vm(j + 1 < NB ? own : 0);
-        __syncthreads();
-        f32x4 s[2], dp[2];
-        block_products(j, s, dp, true);
-#pragma unroll
-        for (int t = 0; t < 2; t++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) dsum = fmaf(pscale * __builtin_amdgcn_exp2f(s[t][i] - lse2), dp[t][i], dsum);
-        __syncthreads();
-    }
-    dsum += __shfl_xor(dsum, 16);
-    dsum += __shfl_xor(dsum, 32);
+    const float dsum = pscale == 0.f ? 0.f : d_all / l_all;
     // statistics per query: lse2 (log2 of the softmax normaliser) and D; a pad
     // query gets lse2 = +inf, so that every P it would take is 0
     if (grp == 0 && in_window) {
         float* st = stats + (size_t)unit * 2 * NPX;
         st[n] = pscale == 0.f ? INFINITY : lse2;
-        st[NPX + n] = pscale == 0.f ? 0.f : dsum;
+        st[NPX + n] = dsum;
     }
 
-    // ---- pass 3: dS and dQ^T = K^T dS^T (the forward's O^T = V^T P^T with K for V, dS for P)
+    // ---- pass 2: dS and dQ^T = K^T dS^T (the forward's O^T = V^T P^T with K for V, dS for P)
     f32x4 acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    issue(0);
     for (int j = 0; j < NB; j++) {
-        if (j + 1 < NB) issue(j + 1);
-        bwd_wait_vm(j + 1 < NB ? own : 0);
-        __syncthreads();
+        bwd_compute_barrier();
         f32x4 s[2], dp[2];
-        block_products(j, s, dp, true);
+        block_products(slot, j, s, dp);
         unsigned pk[2][2];
 #pragma unroll
         for (int t = 0; t < 2; t++) {
@@ -708,7 +762,7 @@ __global__ __launch_bounds__(QW * 64) void attn_bf16_bwd_q_kernel(
             pk[t][1] = pack_bf16x2(ds[2], ds[3]);
         }
         const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]});
-        const unsigned char* Kb = kbuf(j);
+        const unsigned char* Kb = ring + (size_t)slot * 2 * L.buf_bytes;
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
             // transposed 4 x 16 reads of K: keys 16 t + 4 grp + 0..3, d = 16 dt + col
@@ -722,7 +776,7 @@ __global__ __launch_bounds__(QW * 64) void attn_bf16_bwd_q_kernel(
             acc[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}), bop,
                              acc[dt]);
         }
-        __syncthreads();
+        slot = slot + 1 == kBwdStages ? 0 : slot + 1;
     }
     if (r >= 0) {
         uint16_t* op = dq + (uint64_t)(uint32_t)r * (uint32_t)g.row + h * D + grp * 4;
@@ -733,13 +787,19 @@ __global__ __launch_bounds__(QW * 64) void attn_bf16_bwd_q_kernel(
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(kBwdKWaves * 64) void attn_bf16_bwd_kv_kernel(
+// KW compute waves, a 16-key tile each: 8 for 128-wide heads (one workgroup
+// per CU, bounded by LDS), 6 otherwise, so that two workgroups of 8 waves fit
+// a CU's registers.
+template <int D, int KW>
+__global__ __launch_bounds__((KW + kBwdLoaders) * 64)
+__attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kernel(
     Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, const float* __restrict__ stats, float* __restrict__ dtab_units) {
-    constexpr int THREADS = kBwdKWaves * 64;
+    static_assert(KW <= kBwdKWaves, "diagonal scratch per compute wave");
+    constexpr int THREADS = (KW + kBwdLoaders) * 64;
     constexpr int KSTEPS = D / 32, DT = D / 16;
+    constexpr int DIAG = 31 * 16; // one tile's diagonals x slots
     extern __shared__ __align__(16) unsigned char smem[];
     const BwdBigLds L = bwd_big_lds(g);
     const int N = g.N, NPX = L.NPX, NB = NPX / kBwdBlk;
@@ -750,6 +810,7 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void attn_bf16_bwd_kv_kernel(
     float* dtab = (float*)(smem + L.dtab);
     float* lse = (float*)(smem + L.stat);
     float* dd = lse + NPX;
+    float* diag = (float*)(smem + L.diag);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;
@@ -773,164 +834,189 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void attn_bf16_bwd_kv_kernel(
             dd[i] = i < N ? st[NPX + i] : 0.f;
         }
     }
+    // the diagonal scratch starts at zero: slots off a tile's diagonals are never written
+    for (int i = tid; i < KW * 2 * DIAG; i += THREADS) diag[i] = 0.f;
     __syncthreads();
 
-    // Q and dO blocks through a double buffer: block j in buffer j % 2
-    const int own = 2 * block_copies_of<D>(wave, kBwdKWaves);
-    auto qbuf = [&](int j) { return smem + L.buf + (size_t)(j & 1) * 2 * L.buf_bytes; };
-    auto issue = [&](int j) {
-        copy_block<D>(g, q, h, tw, j * kBwdBlk, qbuf(j), wave, kBwdKWaves);
-        copy_block<D>(g, dout, h, tw, j * kBwdBlk, qbuf(j) + L.buf_bytes, wave, kBwdKWaves);
-    };
-    // transposed 4 x 16 read of a [32][D] block: rows t0 + 4 grp + 0..3, d = 16 dt + col
-    auto tr_blk = [&](const unsigned char* base, int t0, int dt) __attribute__((always_inline)) {
-        const int row = t0 + grp * 4 + (col >> 2);
-        const int d = dt * 16 + (col & 3) * 4;
-        return tr_read(base + row * (D * 2) + k_slot<D>(row, d >> 3) * 16 + (d & 7) * 2);
-    };
+    unsigned char* ring = smem + L.buf; // kBwdStages slots of a Q block and a dO block
+    const int KT = NPX / 16;            // key tiles; the compute waves take them KW at a time
+    const int G = (KT + KW - 1) / KW;
+    if (wave >= KW) { // loader waves: every Q and dO block, once per group of key tiles
+        const int li = wave - KW;
+        bwd_stream(G * NB, 2 * block_copies_of<D>(li, kBwdLoaders), [&](int s, int slot) {
+            const int j = s - (s / NB) * NB;
+            unsigned char* dst = ring + (size_t)slot * 2 * L.buf_bytes;
+            copy_block<D>(g, q, h, tw, j * kBwdBlk, dst, li, kBwdLoaders);
+            copy_block<D>(g, dout, h, tw, j * kBwdBlk, dst + L.buf_bytes, li, kBwdLoaders);
+        });
+        bwd_loader_barrier(); // final: the table share is complete
+    } else {
+        // transposed 4 x 16 read of a [32][D] block: rows t0 + 4 grp + 0..3, d = 16 dt + col
+        auto tr_blk = [&](const unsigned char* base, int t0, int dt) __attribute__((always_inline)) {
+            const int row = t0 + grp * 4 + (col >> 2);
+            const int d = dt * 16 + (col & 3) * 4;
+            return tr_read(base + row * (D * 2) + k_slot<D>(row, d >> 3) * 16 + (d & 7) * 2);
+        };
+        float* sc = diag + wave * 2 * DIAG;     // [tile][diagonal][slot]
+        const bool rowtile = g.win[2] % 16 == 0; // 16-token tiles never straddle a window row
+        const int dl = lane & 31, tt = lane >> 5; // the diagonal and the tile this lane sums
 
-    const int KT = NPX / 16; // key tiles; waves take them kBwdKWaves at a time
-    for (int kt0 = 0; kt0 < KT; kt0 += kBwdKWaves) {
-        const int kt = kt0 + wave;
-        const bool active = kt < KT;
-        const int m = (active ? kt : 0) * 16 + col;
-        const int kword = active ? tw[m] : (15 << 28);
-        const unsigned kreg = (unsigned)kword >> 28;
-        const int kr = (kword & kRowMask) - 1;
-        const int kbm = active ? kbo[m] : 0;
-        const bool key_in = active && m < N; // slots past N see no query: masked in every block
-        // B operands: key m, d = 32 ks + 8 grp + 0..7 (pad keys read row 0; they are masked)
-        bf16x8 kf[KSTEPS], vf[KSTEPS];
-        {
-            const uint64_t base = (uint64_t)(uint32_t)(kr < 0 ? 0 : kr) * (uint32_t)g.row + h * D + grp * 8;
+        int slot = 0;
+        for (int kt0 = 0; kt0 < KT; kt0 += KW) {
+            const int kt = kt0 + wave;
+            const bool active = kt < KT;
+            const int m0 = (active ? kt : 0) * 16;
+            const int m = m0 + col;
+            const int kword = active ? tw[m] : (15 << 28);
+            const unsigned kreg = (unsigned)kword >> 28;
+            const int kr = (kword & kRowMask) - 1;
+            const int kbm = active ? kbo[m] : 0;
+            const bool key_in = active && m < N; // slots past N see no query: masked in every block
+            // B operands: key m, d = 32 ks + 8 grp + 0..7 (pad keys read row 0; they are masked)
+            bf16x8 kf[KSTEPS], vf[KSTEPS];
+            {
+                const uint64_t base = (uint64_t)(uint32_t)(kr < 0 ? 0 : kr) * (uint32_t)g.row + h * D + grp * 8;
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ks++) {
-                kf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(k + base + ks * 32));
-                vf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(v + base + ks * 32));
+                for (int ks = 0; ks < KSTEPS; ks++) {
+                    kf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(k + base + ks * 32));
+                    vf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(v + base + ks * 32));
+                }
             }
-        }
-        f32x4 av[DT], ak[DT]; // dV^T and dK^T: lane (key m, d = 16 dt + 4 grp + 0..3)
+            f32x4 av[DT], ak[DT]; // dV^T and dK^T: lane (key m, d = 16 dt + 4 grp + 0..3)
 #pragma unroll
-        for (int dt = 0; dt < DT; dt++) {
-            av[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            ak[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        issue(0);
-        for (int j = 0; j < NB; j++) {
-            if (j + 1 < NB) issue(j + 1);
-            bwd_wait_vm(j + 1 < NB ? own : 0); // block j landed (copies complete in order)
-            __syncthreads();
-            if (active) {
-                const unsigned char* Qb = qbuf(j);
-                const unsigned char* Ob = qbuf(j) + L.buf_bytes;
-                const uint16_t* Qs = (const uint16_t*)Qb;
-                const uint16_t* dOs = (const uint16_t*)Ob;
-                // S = Q K^T and dP = dO V^T: lane (key m, queries 16 t + 4 grp + 0..3 of the block)
-                f32x4 sv[2], dpv[2];
-#pragma unroll
-                for (int t = 0; t < 2; t++) {
-                    const int qrow = t * 16 + col;
-                    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KSTEPS; ks++) {
-                        const int slot = k_slot<D>(qrow, ks * 4 + grp) * 8;
-                        a0 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(Qs + qrow * D + slot)), kf[ks], a0);
-                        a1 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(dOs + qrow * D + slot)), vf[ks], a1);
-                    }
-                    sv[t] = a0;
-                    dpv[t] = a1;
-                }
-                const bool check = masked_window || (j + 1) * kBwdBlk > N;
-                unsigned pp[2][2], ps[2][2];
-                f32x4 dsv[2];
-                // the lane's key is fixed: one past N is masked whatever the query block
-#pragma unroll
-                for (int t = 0; t < 2; t++) {
-                    f32x4 p, ds;
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const int n = j * kBwdBlk + t * 16 + grp * 4 + i;
-                        const int e = qbo[n] - kbm;
-                        float lg = fmaf(sv[t][i], g.scale, bias[e]) * kLog2e;
-                        if (!key_in || (check && ((unsigned)tw[n] >> 28) != kreg)) lg = -INFINITY;
-                        p[i] = __builtin_amdgcn_exp2f(lg - lse[n]);
-                        ds[i] = p[i] * (dpv[t][i] - dd[n]);
-                    }
-                    dsv[t] = ds;
-                    pp[t][0] = pack_bf16x2(p[0], p[1]);
-                    pp[t][1] = pack_bf16x2(p[2], p[3]);
-                    ps[t][0] = pack_bf16x2(ds[0], ds[1]);
-                    ps[t][1] = pack_bf16x2(ds[2], ds[3]);
-                }
-                {
-                    // The tile's dS into the unit's table share.  Pair (query 4 grp + i,
-                    // key col) of a 16 x 16 tile lies on diagonal 4 grp + i - col, and
-                    // along a diagonal the table entry changes only where the query or
-                    // the key crosses a window row.  Lane (col, grp) parks its 4 terms
-                    // at [diagonal][4 grp + i] (one writer per slot); lane d then walks
-                    // diagonal d - 15 and adds each run of equal entries with one
-                    // atomic: once per diagonal when the window width is a multiple
-                    // of 16, a few times otherwise, instead of once per term.
-                    float* sc = (float*)(smem + L.diag) + wave * 31 * 16;
-                    const int m0 = kt * 16;
-                    const bool rowtile = g.win[2] % 16 == 0; // 16-token tiles never straddle a window row
+            for (int dt = 0; dt < DT; dt++) {
+                av[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                ak[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            for (int j = 0; j < NB; j++) {
+                bwd_compute_barrier(); // query block j is in its slot
+                if (active) {
+                    const unsigned char* Qb = ring + (size_t)slot * 2 * L.buf_bytes;
+                    const unsigned char* Ob = Qb + L.buf_bytes;
+                    const uint16_t* Qs = (const uint16_t*)Qb;
+                    const uint16_t* dOs = (const uint16_t*)Ob;
+                    const int nb = j * kBwdBlk;
+                    // S = Q K^T and dP = dO V^T: lane (key m, queries 16 t + 4 grp + 0..3 of the block)
+                    f32x4 sv[2], dpv[2];
 #pragma unroll
                     for (int t = 0; t < 2; t++) {
-                        const int n0 = j * kBwdBlk + t * 16;
-                        if (active && m0 < N && n0 < N) { // wave-uniform; terms past N are 0
+                        const int qrow = t * 16 + col;
+                        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                            for (int i = 0; i < 4; i++) sc[(4 * grp + i - col + 15) * 16 + 4 * grp + i] = dsv[t][i];
-                            __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's writes landed
-                            if (lane < 31 && rowtile) {
-                                // one window row each: a single entry per diagonal
-                                const int dgl = lane - 15;
-                                float run = 0.f;
-                                for (int a = dgl > 0 ? dgl : 0; a < (dgl > 0 ? 16 : 16 + dgl); a++) run += sc[lane * 16 + a];
-                                atomicAdd(&dtab[qbo[n0] - kbo[m0] + dgl], run);
-                            } else if (lane < 31) {
-                                const int dgl = lane - 15;
+                        for (int ks = 0; ks < KSTEPS; ks++) {
+                            const int ksl = k_slot<D>(qrow, ks * 4 + grp) * 8;
+                            a0 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(Qs + qrow * D + ksl)), kf[ks], a0);
+                            a1 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(dOs + qrow * D + ksl)), vf[ks], a1);
+                        }
+                        sv[t] = a0;
+                        dpv[t] = a1;
+                    }
+                    const bool check = masked_window || nb + kBwdBlk > N;
+                    unsigned pp[2][2], ps[2][2];
+                    // the lane's key is fixed: one past N is masked whatever the query block
+#pragma unroll
+                    for (int t = 0; t < 2; t++) {
+                        // the words of the lane's 4 queries (consecutive: one 16-byte read
+                        // each), then every bias read before any is used
+                        const int n4 = nb + t * 16 + grp * 4;
+                        const u32x4 qb4 = *(const u32x4*)(qbo + n4);
+                        const f32x4 ls4 = *(const f32x4*)(lse + n4);
+                        float lg[4];
+#pragma unroll
+                        for (int i = 0; i < 4; i++) lg[i] = bias[(int)qb4[i] - kbm];
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            lg[i] = key_in ? fmaf(sv[t][i], g.scale, lg[i]) * kLog2e : -INFINITY;
+                        if (check) { // wave-uniform: queries of another region, pad or past N
+                            const u32x4 tw4 = *(const u32x4*)(tw + n4);
+#pragma unroll
+                            for (int i = 0; i < 4; i++)
+                                if ((tw4[i] >> 28) != kreg) lg[i] = -INFINITY;
+                        }
+                        const f32x4 dd4 = *(const f32x4*)(dd + n4);
+                        f32x4 p, ds;
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            p[i] = __builtin_amdgcn_exp2f(lg[i] - ls4[i]);
+                            ds[i] = p[i] * (dpv[t][i] - dd4[i]);
+                        }
+                        pp[t][0] = pack_bf16x2(p[0], p[1]);
+                        pp[t][1] = pack_bf16x2(p[2], p[3]);
+                        ps[t][0] = pack_bf16x2(ds[0], ds[1]);
+                        ps[t][1] = pack_bf16x2(ds[2], ds[3]);
+                        // pair (query 4 grp + i, key col) of tile t lies on diagonal
+                        // 4 grp + i - col; park the term at [t][diagonal + 15][4 grp + i]
+#pragma unroll
+                        for (int i = 0; i < 4; i++) sc[t * DIAG + (4 * grp + i - col + 15) * 16 + 4 * grp + i] = ds[i];
+                    }
+                    // The block's dS into the unit's table share.  Along a diagonal of a
+                    // 16 x 16 tile the table entry changes only where the query or the
+                    // key crosses a window row, so lane (tt, dl) sums diagonal dl - 15 of
+                    // tile tt (slots off the diagonal hold 0) and adds each run of equal
+                    // entries with one atomic: a single run when the window width is a
+                    // multiple of 16, a few otherwise.
+                    if (m0 < N) { // wave-uniform; terms past N are 0
+                        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's terms landed
+                        const int n0 = nb + tt * 16, dgl = dl - 15;
+                        if (dl < 31 && n0 < N) {
+                            const f32x4* row = (const f32x4*)(sc + tt * DIAG + dl * 16);
+                            if (rowtile) {
+                                const f32x4 r0 = row[0], r1 = row[1], r2 = row[2], r3 = row[3];
+                                const f32x4 r = (r0 + r1) + (r2 + r3);
+                                atomicAdd(&dtab[qbo[n0] - kbo[m0] + dgl], (r[0] + r[1]) + (r[2] + r[3]));
+                            } else {
+                                // slot a pairs query n0 + a with key m0 + a - dgl; 8 slots at a time
                                 float run = 0.f;
                                 int ecur = -1;
-                                for (int a = dgl > 0 ? dgl : 0; a < (dgl > 0 ? 16 : 16 + dgl); a++) {
-                                    const int e = qbo[n0 + a] - kbo[m0 + a - dgl];
-                                    if (e != ecur) {
-                                        if (ecur >= 0) atomicAdd(&dtab[ecur], run);
-                                        ecur = e;
-                                        run = 0.f;
+#pragma unroll
+                                for (int half = 0; half < 2; half++) {
+                                    const f32x4 ra = row[2 * half], rb = row[2 * half + 1];
+                                    const float x[8] = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
+#pragma unroll
+                                    for (int c = 0; c < 8; c++) {
+                                        const int a = 8 * half + c;
+                                        if (a - dgl >= 0 && a - dgl < 16) {
+                                            const int ea = qbo[n0 + a] - kbo[m0 + a - dgl];
+                                            if (ea != ecur) {
+                                                if (ecur >= 0) atomicAdd(&dtab[ecur], run);
+                                                ecur = ea;
+                                                run = 0.f;
+                                            }
+                                            run += x[c];
+                                        }
                                     }
-                                    run += sc[lane * 16 + a];
                                 }
                                 if (ecur >= 0) atomicAdd(&dtab[ecur], run);
                             }
-                            __builtin_amdgcn_s_waitcnt(0xC07F); // the reads are done before the next writes
                         }
+                        __builtin_amdgcn_s_waitcnt(0xC07F); // the reads are done before the next block's terms
+                    }
+                    const bf16x8 bp = __builtin_bit_cast(bf16x8, u32x4{pp[0][0], pp[0][1], pp[1][0], pp[1][1]});
+                    const bf16x8 bs = __builtin_bit_cast(bf16x8, u32x4{ps[0][0], ps[0][1], ps[1][0], ps[1][1]});
+                    // dV^T += dO^T P and dK^T += Q^T dS, contracting over the block's 32 queries
+#pragma unroll
+                    for (int dt = 0; dt < DT; dt++) {
+                        const u32x2 o0 = tr_blk(Ob, 0, dt), o1 = tr_blk(Ob, 16, dt);
+                        const u32x2 q0 = tr_blk(Qb, 0, dt), q1 = tr_blk(Qb, 16, dt);
+                        av[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{o0[0], o0[1], o1[0], o1[1]}), bp, av[dt]);
+                        ak[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), bs, ak[dt]);
                     }
                 }
-                const bf16x8 bp = __builtin_bit_cast(bf16x8, u32x4{pp[0][0], pp[0][1], pp[1][0], pp[1][1]});
-                const bf16x8 bs = __builtin_bit_cast(bf16x8, u32x4{ps[0][0], ps[0][1], ps[1][0], ps[1][1]});
-                // dV^T += dO^T P and dK^T += Q^T dS, contracting over the block's 32 queries
+                slot = slot + 1 == kBwdStages ? 0 : slot + 1;
+            }
+            if (active && kr >= 0) {
+                const uint64_t base = (uint64_t)(uint32_t)kr * (uint32_t)g.row + h * D + grp * 4;
 #pragma unroll
                 for (int dt = 0; dt < DT; dt++) {
-                    const u32x2 o0 = tr_blk(Ob, 0, dt), o1 = tr_blk(Ob, 16, dt);
-                    const u32x2 q0 = tr_blk(Qb, 0, dt), q1 = tr_blk(Qb, 16, dt);
-                    av[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{o0[0], o0[1], o1[0], o1[1]}), bp, av[dt]);
-                    ak[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), bs, ak[dt]);
+                    *(u32x2*)(dv + base + dt * 16) =
+                        u32x2{pack_bf16x2(av[dt][0], av[dt][1]), pack_bf16x2(av[dt][2], av[dt][3])};
+                    *(u32x2*)(dk + base + dt * 16) = u32x2{pack_bf16x2(ak[dt][0] * g.scale, ak[dt][1] * g.scale),
+                                                           pack_bf16x2(ak[dt][2] * g.scale, ak[dt][3] * g.scale)};
                 }
             }
-            __syncthreads(); // the buffer of block j is rewritten by issue(j + 2)
         }
-        if (active && kr >= 0) {
-            const uint64_t base = (uint64_t)(uint32_t)kr * (uint32_t)g.row + h * D + grp * 4;
-#pragma unroll
-            for (int dt = 0; dt < DT; dt++) {
-                *(u32x2*)(dv + base + dt * 16) =
-                    u32x2{pack_bf16x2(av[dt][0], av[dt][1]), pack_bf16x2(av[dt][2], av[dt][3])};
-                *(u32x2*)(dk + base + dt * 16) = u32x2{pack_bf16x2(ak[dt][0] * g.scale, ak[dt][1] * g.scale),
-                                                       pack_bf16x2(ak[dt][2] * g.scale, ak[dt][3] * g.scale)};
-            }
-        }
+        bwd_compute_barrier(); // final: every atomic of the table share has landed
     }
-    __syncthreads();
     float* dst = dtab_units + (size_t)unit * g.table_size;
     for (int e = tid; e < g.table_size; e += THREADS) dst[e] = dtab[e];
 }
@@ -1144,8 +1230,8 @@ hipError_t prepare_backward_kernels(int max_lds) {
                         (const void*)attn_bf16_bwd_q_kernel<32, 4>,   (const void*)attn_bf16_bwd_q_kernel<64, 4>,
                         (const void*)attn_bf16_bwd_q_kernel<128, 4>,  (const void*)attn_bf16_bwd_q_kernel<32, 8>,
                         (const void*)attn_bf16_bwd_q_kernel<64, 8>,   (const void*)attn_bf16_bwd_q_kernel<128, 8>,
-                        (const void*)attn_bf16_bwd_kv_kernel<32>,
-                        (const void*)attn_bf16_bwd_kv_kernel<64>,     (const void*)attn_bf16_bwd_kv_kernel<128>};
+                        (const void*)attn_bf16_bwd_kv_kernel<32, 6>,
+                        (const void*)attn_bf16_bwd_kv_kernel<64, 6>,  (const void*)attn_bf16_bwd_kv_kernel<128, 8>};
     for (const void* f : fs) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
         if (e != hipSuccess) return e;
@@ -1174,13 +1260,14 @@ hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const vo
                                 : (g.head_dim == 32   ? attn_bf16_bwd_q_kernel<32, 4>
                                    : g.head_dim == 64 ? attn_bf16_bwd_q_kernel<64, 4>
                                                       : attn_bf16_bwd_q_kernel<128, 4>);
-        const kv_t fk = g.head_dim == 32 ? attn_bf16_bwd_kv_kernel<32>
-                        : g.head_dim == 64 ? attn_bf16_bwd_kv_kernel<64> : attn_bf16_bwd_kv_kernel<128>;
-        hipLaunchKernelGGL(fq, qgrid, dim3(QW * 64), L.total_q, s, g, (const uint16_t*)q, (const uint16_t*)k,
+        const int KW = g.head_dim == 128 ? 8 : 6;
+        const kv_t fk = g.head_dim == 32 ? attn_bf16_bwd_kv_kernel<32, 6>
+                        : g.head_dim == 64 ? attn_bf16_bwd_kv_kernel<64, 6> : attn_bf16_bwd_kv_kernel<128, 8>;
+        hipLaunchKernelGGL(fq, qgrid, dim3((QW + kBwdLoaders) * 64), L.total_q, s, g, (const uint16_t*)q, (const uint16_t*)k,
                            (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dq, stats);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(fk, grid, dim3(kBwdKWaves * 64), L.total_k, s, g, (const uint16_t*)q, (const uint16_t*)k,
+        hipLaunchKernelGGL(fk, grid, dim3((KW + kBwdLoaders) * 64), L.total_k, s, g, (const uint16_t*)q, (const uint16_t*)k,
                            (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dk, (uint16_t*)dv,
                            (const float*)stats, units);
     } else if (bf16) {
