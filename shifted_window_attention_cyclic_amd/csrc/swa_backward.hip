@@ -499,6 +499,12 @@ __device__ inline int block_copies_of(int w, int nwaves) {
     return w < block_copies<D>() ? (block_copies<D>() - 1 - w) / nwaves + 1 : 0;
 }
 constexpr int kBwdKWaves = 8;   // key kernel: at most 8 key tiles at a time
+constexpr int kBwdDiag = 16 * 48; // key kernel: floats of one tile's diagonal scratch
+
+// compute waves of the key kernel: 8 for 128-wide heads (one workgroup per
+// CU, bounded by LDS), 6 otherwise, so that two workgroups of 8 waves fit a
+// CU's registers
+__host__ __device__ constexpr int bwd_kv_waves(int head_dim) { return head_dim == 128 ? 8 : 6; }
 // the loaders' waits stay within bwd_wait_vm's range
 static_assert((kBwdStages - 2) * 2 * ((block_copies<128>() + kBwdLoaders - 1) / kBwdLoaders) <= 8,
               "copies in flight per loader wave");
@@ -508,7 +514,7 @@ struct BwdBigLds {
     size_t tw, kb, qb, bias, dtab, stat, diag, buf, buf_bytes, total_q, total_k;
 };
 
-__host__ __device__ inline BwdBigLds bwd_big_lds(const Geometry& g) {
+__host__ __device__ inline BwdBigLds bwd_big_lds(const Geometry& g, int kw) {
     BwdBigLds L;
     L.NPX = (g.N + kBwdBlk - 1) / kBwdBlk * kBwdBlk;
     const size_t tab = ((size_t)g.table_size * 4 + 15) / 16 * 16;
@@ -518,8 +524,8 @@ __host__ __device__ inline BwdBigLds bwd_big_lds(const Geometry& g) {
     L.bias = L.qb + (size_t)L.NPX * 4;                      // the head's table slice
     L.dtab = L.bias + tab;                                  // key kernel: the unit's share
     L.stat = L.dtab + tab;                                  // key kernel: lse2, D per query
-    L.diag = L.stat + (size_t)L.NPX * 8;                    // key kernel: per-wave 2 x 31 x 16 diagonal scratch
-    L.buf = L.diag + (size_t)kBwdKWaves * 2 * 31 * 16 * 4;
+    L.diag = L.stat + (size_t)L.NPX * 8;                    // key kernel: per compute wave 2 x 16 x 48 diagonal scratch
+    L.buf = L.diag + (size_t)kw * 2 * kBwdDiag * 4;
     L.buf_bytes = (size_t)kBwdBlk * g.head_dim * 2;         // one [32][D] bf16 block
     L.total_q = L.dtab + 2 * kBwdStages * L.buf_bytes;      // query kernel: the K, V ring from dtab on
     L.total_k = L.buf + 2 * kBwdStages * L.buf_bytes;       // key kernel: the Q, dO ring
@@ -594,7 +600,7 @@ __global__ __launch_bounds__((QW + kBwdLoaders) * 64) void attn_bf16_bwd_q_kerne
     constexpr int THREADS = (QW + kBwdLoaders) * 64;
     constexpr int KSTEPS = D / 32, DT = D / 16;
     extern __shared__ __align__(16) unsigned char smem[];
-    const BwdBigLds L = bwd_big_lds(g);
+    const BwdBigLds L = bwd_big_lds(g, bwd_kv_waves(g.head_dim));
     const int N = g.N, NPX = L.NPX, NB = NPX / kBwdBlk;
     int* tw = (int*)(smem + L.tw);
     int* kbo = (int*)(smem + L.kb);
@@ -787,9 +793,7 @@ __global__ __launch_bounds__((QW + kBwdLoaders) * 64) void attn_bf16_bwd_q_kerne
     }
 }
 
-// KW compute waves, a 16-key tile each: 8 for 128-wide heads (one workgroup
-// per CU, bounded by LDS), 6 otherwise, so that two workgroups of 8 waves fit
-// a CU's registers.
+// KW = bwd_kv_waves(D) compute waves, a 16-key tile each.
 template <int D, int KW>
 __global__ __launch_bounds__((KW + kBwdLoaders) * 64)
 __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kernel(
@@ -799,9 +803,9 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
     static_assert(KW <= kBwdKWaves, "diagonal scratch per compute wave");
     constexpr int THREADS = (KW + kBwdLoaders) * 64;
     constexpr int KSTEPS = D / 32, DT = D / 16;
-    constexpr int DIAG = 31 * 16; // one tile's diagonals x slots
+    constexpr int DIAG = kBwdDiag; // one tile's scratch: [slot][diagonal + slot]
     extern __shared__ __align__(16) unsigned char smem[];
-    const BwdBigLds L = bwd_big_lds(g);
+    const BwdBigLds L = bwd_big_lds(g, KW);
     const int N = g.N, NPX = L.NPX, NB = NPX / kBwdBlk;
     int* tw = (int*)(smem + L.tw);
     int* kbo = (int*)(smem + L.kb);
@@ -857,7 +861,7 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
             const int d = dt * 16 + (col & 3) * 4;
             return tr_read(base + row * (D * 2) + k_slot<D>(row, d >> 3) * 16 + (d & 7) * 2);
         };
-        float* sc = diag + wave * 2 * DIAG;     // [tile][diagonal][slot]
+        float* sc = diag + wave * 2 * DIAG;     // [tile][slot][diagonal + slot]
         const bool rowtile = g.win[2] % 16 == 0; // 16-token tiles never straddle a window row
         const int dl = lane & 31, tt = lane >> 5; // the diagonal and the tile this lane sums
 
@@ -944,10 +948,12 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
                         pp[t][1] = pack_bf16x2(p[2], p[3]);
                         ps[t][0] = pack_bf16x2(ds[0], ds[1]);
                         ps[t][1] = pack_bf16x2(ds[2], ds[3]);
-                        // pair (query 4 grp + i, key col) of tile t lies on diagonal
-                        // 4 grp + i - col; park the term at [t][diagonal + 15][4 grp + i]
+                        // pair (query a = 4 grp + i, key col) of tile t lies on diagonal
+                        // d = a - col + 15 (0..30); its term goes to [t][a][d + a], rows
+                        // of 48: word 50 a - col + 15, which spreads a write's 64 lanes
+                        // evenly over the 32 banks
 #pragma unroll
-                        for (int i = 0; i < 4; i++) sc[t * DIAG + (4 * grp + i - col + 15) * 16 + 4 * grp + i] = ds[i];
+                        for (int i = 0; i < 4; i++) sc[t * DIAG + 50 * (4 * grp + i) - col + 15] = ds[i];
                     }
                     // The block's dS into the unit's table share.  Along a diagonal of a
                     // 16 x 16 tile the table entry changes only where the query or the
@@ -959,19 +965,24 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
                         __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's terms landed
                         const int n0 = nb + tt * 16, dgl = dl - 15;
                         if (dl < 31 && n0 < N) {
-                            const f32x4* row = (const f32x4*)(sc + tt * DIAG + dl * 16);
+                            // slot a of this diagonal pairs query n0 + a with key m0 + a - dgl
+                            const float* sd = sc + tt * DIAG;
                             if (rowtile) {
-                                const f32x4 r0 = row[0], r1 = row[1], r2 = row[2], r3 = row[3];
-                                const f32x4 r = (r0 + r1) + (r2 + r3);
-                                atomicAdd(&dtab[qbo[n0] - kbo[m0] + dgl], (r[0] + r[1]) + (r[2] + r[3]));
+                                float x[16];
+#pragma unroll
+                                for (int a = 0; a < 16; a++) x[a] = sd[49 * a + dl];
+                                float run = 0.f;
+#pragma unroll
+                                for (int a = 0; a < 16; a++) run += x[a];
+                                atomicAdd(&dtab[qbo[n0] - kbo[m0] + dgl], run);
                             } else {
-                                // slot a pairs query n0 + a with key m0 + a - dgl; 8 slots at a time
                                 float run = 0.f;
                                 int ecur = -1;
 #pragma unroll
                                 for (int half = 0; half < 2; half++) {
-                                    const f32x4 ra = row[2 * half], rb = row[2 * half + 1];
-                                    const float x[8] = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
+                                    float x[8];
+#pragma unroll
+                                    for (int c = 0; c < 8; c++) x[c] = sd[49 * (8 * half + c) + dl];
 #pragma unroll
                                     for (int c = 0; c < 8; c++) {
                                         const int a = 8 * half + c;
@@ -1189,7 +1200,7 @@ static bool bwd_small_fits(const Geometry& g) {
 }
 
 static bool bwd_big_fits(const Geometry& g) {
-    const BwdBigLds L = bwd_big_lds(g);
+    const BwdBigLds L = bwd_big_lds(g, bwd_kv_waves(g.head_dim));
     return L.total_q <= (size_t)kLdsBytes && L.total_k <= (size_t)kLdsBytes;
 }
 
@@ -1208,7 +1219,8 @@ size_t backward_workspace_bytes(const Geometry& g) {
     const size_t units = (size_t)(g.windows * g.heads) * g.table_size;
     const size_t chunks = (size_t)kDtableChunks * g.heads * g.table_size;
     // big windows: per query, lse2 and D
-    const size_t stats = bwd_small_fits(g) ? 0 : (size_t)(g.windows * g.heads) * 2 * bwd_big_lds(g).NPX;
+    const size_t stats =
+        bwd_small_fits(g) ? 0 : (size_t)(g.windows * g.heads) * 2 * bwd_big_lds(g, bwd_kv_waves(g.head_dim)).NPX;
     return (units + chunks + stats) * sizeof(float);
 }
 
@@ -1229,7 +1241,7 @@ hipError_t prepare_backward_kernels(int max_lds) {
                         (const void*)attn_f32_bwd_kernel<32>,         (const void*)attn_f32_bwd_kernel<64>,
                         (const void*)attn_bf16_bwd_q_kernel<32, 4>,   (const void*)attn_bf16_bwd_q_kernel<64, 4>,
                         (const void*)attn_bf16_bwd_q_kernel<128, 4>,  (const void*)attn_bf16_bwd_q_kernel<32, 8>,
-                        (const void*)attn_bf16_bwd_q_kernel<64, 8>,   (const void*)attn_bf16_bwd_q_kernel<128, 8>,
+                        (const void*)attn_bf16_bwd_q_kernel<64, 8>,   (const void*)attn_bf16_bwd_q_kernel<128, 6>,
                         (const void*)attn_bf16_bwd_kv_kernel<32, 6>,
                         (const void*)attn_bf16_bwd_kv_kernel<64, 6>,  (const void*)attn_bf16_bwd_kv_kernel<128, 8>};
     for (const void* f : fs) {
@@ -1247,20 +1259,21 @@ hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const vo
     float* chunks = units + (size_t)(g.windows * g.heads) * g.table_size;
     float* stats = chunks + (size_t)kDtableChunks * g.heads * g.table_size;
     if (bf16 && !bwd_small_fits(g)) {
-        const BwdBigLds L = bwd_big_lds(g);
-        const int QW = g.N >= 512 ? 8 : 4; // wider query blocks re-stream K and V fewer times
+        const BwdBigLds L = bwd_big_lds(g, bwd_kv_waves(g.head_dim));
+        // wider query blocks re-stream K and V fewer times; 128-wide heads take 6
+        // waves, so that two workgroups of 8 fit a CU's registers
+        const int QW = g.N < 512 ? 4 : g.head_dim == 128 ? 6 : 8;
         const dim3 qgrid((unsigned)(g.windows * g.heads * ((g.N + QW * 16 - 1) / (QW * 16))));
         typedef void (*qk_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
                              const uint16_t*, uint16_t*, float*);
         typedef void (*kv_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
                              const uint16_t*, uint16_t*, uint16_t*, const float*, float*);
-        const qk_t fq = QW == 8 ? (g.head_dim == 32   ? attn_bf16_bwd_q_kernel<32, 8>
-                                   : g.head_dim == 64 ? attn_bf16_bwd_q_kernel<64, 8>
-                                                      : attn_bf16_bwd_q_kernel<128, 8>)
-                                : (g.head_dim == 32   ? attn_bf16_bwd_q_kernel<32, 4>
-                                   : g.head_dim == 64 ? attn_bf16_bwd_q_kernel<64, 4>
-                                                      : attn_bf16_bwd_q_kernel<128, 4>);
-        const int KW = g.head_dim == 128 ? 8 : 6;
+        const qk_t fq = QW == 6   ? attn_bf16_bwd_q_kernel<128, 6>
+                        : QW == 8 ? (g.head_dim == 32 ? attn_bf16_bwd_q_kernel<32, 8> : attn_bf16_bwd_q_kernel<64, 8>)
+                                  : (g.head_dim == 32   ? attn_bf16_bwd_q_kernel<32, 4>
+                                     : g.head_dim == 64 ? attn_bf16_bwd_q_kernel<64, 4>
+                                                        : attn_bf16_bwd_q_kernel<128, 4>);
+        const int KW = bwd_kv_waves(g.head_dim);
         const kv_t fk = g.head_dim == 32 ? attn_bf16_bwd_kv_kernel<32, 6>
                         : g.head_dim == 64 ? attn_bf16_bwd_kv_kernel<64, 6> : attn_bf16_bwd_kv_kernel<128, 8>;
         hipLaunchKernelGGL(fq, qgrid, dim3((QW + kBwdLoaders) * 64), L.total_q, s, g, (const uint16_t*)q, (const uint16_t*)k,
