@@ -159,16 +159,17 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
  * are overwritten.  The pad tokens of a window have no output, so they add
  * nothing.  workspace: device buffer of info.backward_workspace_bytes bytes,
  * 16-byte aligned, owned by the caller (per-(window, head) shares of the
- * table gradient and their partial sums; its contents on entry do not
- * matter).  The pass reads and writes the spatial layout whatever the
+ * table gradient and their partial sums; with backward_schedule 2 also each
+ * query's softmax normaliser and D = rowsum(P * dP); its contents on entry
+ * do not matter).  The pass reads and writes the spatial layout whatever the
  * variant and allocates nothing.  backward_schedule 1 (bf16 windows whose
  * Q, K, V, dO and two N x N matrices fit one workgroup's LDS: up to 144
  * tokens with head_dim <= 64, fewer at 128; and fp32): every sum runs in a
  * fixed order, so the results are bitwise reproducible, and the table
  * gradient sums bf16-rounded dS terms in fp32.  backward_schedule 2 (larger
  * bf16 windows): dq, dk, dv are still reproducible; the table gradient sums
- * fp32 dS terms with LDS atomics, in an order that may differ between runs.  Asynchronous on `stream`, like
- * swa_forward.
+ * fp32 dS terms with LDS atomics, in an order that may differ between runs.
+ * Asynchronous on `stream`, like swa_forward.
  * Errors: INVALID_ARGUMENT (NULL handle or pointer, misalignment, a buffer
  * written that overlaps another argument), UNSUPPORTED (the window is beyond
  * the backward kernels: backward_workspace_bytes is 0), HIP (launch failure).
