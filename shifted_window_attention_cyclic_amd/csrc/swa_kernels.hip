@@ -407,6 +407,27 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
     const unsigned one2 = 0x3F803F80u; // two bf16 ones
     const bf16x8 ones8 = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
     const unsigned char* bias_bytes = (const unsigned char*)bias;
+    // Mask fields present in each key block, 16 bits per block.  A query sees a
+    // key only when their fields are equal, so a key block that shares no field
+    // with a query tile adds nothing to its output (P = 0) and leaves its
+    // running max alone: it is skipped.  In a window split across a
+    // non-cyclic boundary along time, a time slice of 12 x 12 tokens is exactly
+    // one block of 9 tiles, so half of such a window's blocks drop out.
+    constexpr int NKB = (KT_MAX + KB - 1) / KB;
+    static_assert(NKB <= 4, "four 16-bit field sets in a 64-bit word");
+    uint64_t ksets = ~(uint64_t)0;
+    if (masked_window && NKB > 1) {
+        ksets = 0;
+#pragma unroll
+        for (int bi = 0; bi < NKB; bi++) {
+            unsigned m = 0;
+            for (int kn = bi * KB * 16 + lane; kn < (bi + 1) * KB * 16 && kn < NP; kn += 64)
+                m |= 1u << ((unsigned)tw[kn] >> 28);
+#pragma unroll
+            for (int sh = 32; sh >= 1; sh >>= 1) m |= __shfl_xor(m, sh);
+            ksets |= (uint64_t)__builtin_amdgcn_readfirstlane(m) << (16 * bi);
+        }
+    }
     // V^T fragment of key tile t: lane (col, grp) gets keys 16t + 4grp + 0..3 at
     // d = 16 dt + col; lane s of the group points at row 16t + 4grp + s/4, d 16dt + 4(s%4)
     auto vt_frag = [&](int t0, int dt) __attribute__((always_inline)) {
@@ -433,6 +454,11 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
             qb4 = (g.table_size - 1) * 4; // largest qb keeps qb - kb inside the table
         }
         const unsigned char* qbias = bias_bytes + qb4;
+        // mask fields of the tile's 16 queries (one per lane column)
+        unsigned qset = 1u << qreg;
+#pragma unroll
+        for (int sh = 8; sh >= 1; sh >>= 1) qset |= __shfl_xor(qset, sh);
+        qset = __builtin_amdgcn_readfirstlane(qset);
         f32x4 o[DT], osum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -440,6 +466,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 
 #pragma unroll KB_UNROLL
         for (int kb0 = 0; kb0 < (KT_FIXED > 0 ? KT_FIXED : KT); kb0 += KB) {
+            if ((qset & (unsigned)(ksets >> (16 * (kb0 / KB)))) == 0) continue; // every pair masked
             f32x4 s[KB];
 #pragma unroll
             for (int kt = 0; kt < KB; kt++) {
