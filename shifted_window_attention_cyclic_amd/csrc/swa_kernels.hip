@@ -1093,8 +1093,13 @@ __host__ __device__ inline uint64_t stream_tensor_bytes(const Geometry& g, bool 
     return rows * (uint64_t)g.row * 2;
 }
 
+// With 32-wide heads a workgroup's LDS is about half a CU's, so the 9-tile
+// variant is held to 80 VGPRs: two workgroups of 12 waves then share a CU, and
+// one computes while the other waits at its barriers.
 template <int D, int NWAVES, int NL, int KT_FIXED, bool BIAS_VEC>
-__global__ __launch_bounds__((NWAVES + NL) * 64) void attn_bf16_stream_kernel(
+__global__ __launch_bounds__((NWAVES + NL) * 64)
+__attribute__((amdgpu_waves_per_eu(D == 32 && BIAS_VEC && KT_FIXED == 9 && NWAVES + NL == 12 ? 6 : 1))) void
+attn_bf16_stream_kernel(
     Geometry g, int staged, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ table, uint16_t* __restrict__ out) {
     constexpr int THREADS = (NWAVES + NL) * 64;
