@@ -1433,10 +1433,27 @@ __global__ __launch_bounds__((kKbComputeWaves + kKbLoaders) * 64) void attn_bf16
         osum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         mref[t] = -INFINITY;
     }
+    // A block that shares no mask field with any of the wave's 32 queries adds
+    // P = 0 and leaves the exponent reference alone, so the wave skips it; a
+    // wave of pad queries only (no output) skips every block.  A 32-key block
+    // is one row of a 32-wide window, so where a window is split by the
+    // non-cyclic boundary, each side's waves skip the other side's rows.
+    unsigned qset = (1u << qreg[0]) | (1u << qreg[1]);
+#pragma unroll
+    for (int sh = 8; sh >= 1; sh >>= 1) qset |= __shfl_xor(qset, sh);
+    qset = __builtin_amdgcn_readfirstlane(qset);
+    const bool any_real = __builtin_amdgcn_ballot_w64(qr[0] >= 0 || qr[1] >= 0) != 0;
 
     for (int blk = 0; blk < NB; blk++) {
         lds_barrier();
-        if (!active) continue;
+        if (!active || !any_real) continue;
+        if (masked_window) { // the fields present among the block's 32 keys
+            const u32x4 f = *(const u32x4*)(tw + blk * kKbKeys + (lane & 7) * 4);
+            unsigned m = (1u << (f[0] >> 28)) | (1u << (f[1] >> 28)) | (1u << (f[2] >> 28)) | (1u << (f[3] >> 28));
+#pragma unroll
+            for (int sh = 4; sh >= 1; sh >>= 1) m |= __shfl_xor(m, sh);
+            if ((__builtin_amdgcn_readfirstlane(m) & qset) == 0) continue;
+        }
         const unsigned char* st = smem + (size_t)(blk % S) * L.stage_bytes;
         const uint16_t* Ks = (const uint16_t*)st;
         const unsigned char* Vb = st + kKbKeys * D * 2;
