@@ -9,10 +9,23 @@
 //   scatter_kernel     window-major layout -> spatial layout (reverse)
 //   visibility_kernel  the attention mask of one window, as the kernels use it
 //   attn_f32_kernel    fp32 window attention (VALU), one block per (window, head)
-//   attn_bf16_kernel   bf16 window attention on MFMA with fp32 accumulation and
-//                      softmax; reads Q/K/V straight from the spatial layout and
-//                      writes O back to it (fused), or works on window-major
-//                      buffers (staged)
+//   attn_bf16_stream_kernel
+//                      bf16 window attention on MFMA with fp32 accumulation,
+//                      windows of up to 9 query tiles: persistent workgroups,
+//                      loader waves streaming each unit's K, Q, V through LDS
+//                      while compute waves work on the one before
+//   attn_bf16_kernel   the same arithmetic with one workgroup per (window,
+//                      head): windows of up to 32 tiles, online softmax over
+//                      9-tile key blocks, blocks masked for a whole query tile
+//                      skipped
+//   attn_bf16_kblock_kernel
+//                      windows of any size: 256 queries per workgroup, K and V
+//                      streamed in 32-key blocks, blocks masked for all of a
+//                      wave's queries skipped
+//   bias_head_major_kernel
+//                      the head-major bias copy the key-blocked kernel reads
+// Every bf16 kernel reads Q/K/V straight from the spatial layout and writes O
+// back to it (fused), or works on window-major buffers (staged).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
