@@ -1234,6 +1234,24 @@ static bwd_bf16_t bwd_bf16_variant(const Geometry& g) {
     return bv ? attn_bf16_bwd_kernel<64, true> : attn_bf16_bwd_kernel<64, false>;
 }
 
+// Compute waves of the query kernel (16 queries each).  Heads of up to 64:
+// whichever of 4, 6 and 8 waves leaves the fewest idle query slots in the
+// last block, ties to more waves (fewer re-reads of K and V).  128-wide heads:
+// 6 for windows of 512 tokens or more, so that two workgroups of 8 waves fit a
+// CU's registers, 4 below.
+static int bwd_q_waves(const Geometry& g) {
+    if (g.head_dim == 128) return g.N < 512 ? 4 : 6;
+    int best = 4, idle = 1 << 30;
+    for (int qw : {4, 6, 8}) {
+        const int slots = (g.N + qw * 16 - 1) / (qw * 16) * (qw * 16);
+        if (slots - g.N <= idle) {
+            idle = slots - g.N;
+            best = qw;
+        }
+    }
+    return best;
+}
+
 hipError_t prepare_backward_kernels(int max_lds) {
     const void* fs[] = {(const void*)attn_bf16_bwd_kernel<32, true>,  (const void*)attn_bf16_bwd_kernel<32, false>,
                         (const void*)attn_bf16_bwd_kernel<64, true>,  (const void*)attn_bf16_bwd_kernel<64, false>,
@@ -1242,6 +1260,7 @@ hipError_t prepare_backward_kernels(int max_lds) {
                         (const void*)attn_bf16_bwd_q_kernel<32, 4>,   (const void*)attn_bf16_bwd_q_kernel<64, 4>,
                         (const void*)attn_bf16_bwd_q_kernel<128, 4>,  (const void*)attn_bf16_bwd_q_kernel<32, 8>,
                         (const void*)attn_bf16_bwd_q_kernel<64, 8>,   (const void*)attn_bf16_bwd_q_kernel<128, 6>,
+                        (const void*)attn_bf16_bwd_q_kernel<32, 6>,   (const void*)attn_bf16_bwd_q_kernel<64, 6>,
                         (const void*)attn_bf16_bwd_kv_kernel<32, 6>,
                         (const void*)attn_bf16_bwd_kv_kernel<64, 6>,  (const void*)attn_bf16_bwd_kv_kernel<128, 8>};
     for (const void* f : fs) {
@@ -1260,19 +1279,20 @@ hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const vo
     float* stats = chunks + (size_t)kDtableChunks * g.heads * g.table_size;
     if (bf16 && !bwd_small_fits(g)) {
         const BwdBigLds L = bwd_big_lds(g, bwd_kv_waves(g.head_dim));
-        // wider query blocks re-stream K and V fewer times; 128-wide heads take 6
-        // waves, so that two workgroups of 8 fit a CU's registers
-        const int QW = g.N < 512 ? 4 : g.head_dim == 128 ? 6 : 8;
+        const int QW = bwd_q_waves(g);
         const dim3 qgrid((unsigned)(g.windows * g.heads * ((g.N + QW * 16 - 1) / (QW * 16))));
         typedef void (*qk_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
                              const uint16_t*, uint16_t*, float*);
         typedef void (*kv_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
                              const uint16_t*, uint16_t*, uint16_t*, const float*, float*);
-        const qk_t fq = QW == 6   ? attn_bf16_bwd_q_kernel<128, 6>
-                        : QW == 8 ? (g.head_dim == 32 ? attn_bf16_bwd_q_kernel<32, 8> : attn_bf16_bwd_q_kernel<64, 8>)
-                                  : (g.head_dim == 32   ? attn_bf16_bwd_q_kernel<32, 4>
-                                     : g.head_dim == 64 ? attn_bf16_bwd_q_kernel<64, 4>
-                                                        : attn_bf16_bwd_q_kernel<128, 4>);
+        const qk_t fq = g.head_dim == 128 ? (QW == 6 ? attn_bf16_bwd_q_kernel<128, 6> : attn_bf16_bwd_q_kernel<128, 4>)
+                        : g.head_dim == 64
+                            ? (QW == 8   ? attn_bf16_bwd_q_kernel<64, 8>
+                               : QW == 6 ? attn_bf16_bwd_q_kernel<64, 6>
+                                         : attn_bf16_bwd_q_kernel<64, 4>)
+                            : (QW == 8   ? attn_bf16_bwd_q_kernel<32, 8>
+                               : QW == 6 ? attn_bf16_bwd_q_kernel<32, 6>
+                                         : attn_bf16_bwd_q_kernel<32, 4>);
         const int KW = bwd_kv_waves(g.head_dim);
         const kv_t fk = g.head_dim == 32 ? attn_bf16_bwd_kv_kernel<32, 6>
                         : g.head_dim == 64 ? attn_bf16_bwd_kv_kernel<64, 6> : attn_bf16_bwd_kv_kernel<128, 8>;
