@@ -320,3 +320,17 @@ def test_auto_schedule_choice():
         assert att.info.schedule == schedule, name
         assert att.info.workgroups >= 8, name
         att.close()
+
+
+def test_streaming_workgroups_per_cu():
+    """The persistent streaming schedule launches one workgroup per CU, and two
+    for the 32-wide 9-tile variant, whose LDS is half a CU's and whose registers
+    are held to what two 12-wave workgroups allow: a change that raises its
+    register count past that halves its occupancy, and this fails."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    per_cu = {"c2_bf16_180x360": 2, "c3_bf16_540x1080": 1, "c4_bf16_181x360_pad190": 1,
+              "c6_bf16_180x360_pad184_d128": 1}
+    for name, n in per_cu.items():
+        att = WindowAttention(WORKLOADS[name])
+        assert att.info.workgroups == n * cus // 8 * 8, (name, att.info.workgroups, cus)
+        att.close()
