@@ -46,7 +46,11 @@ def _takes_backward(p):
 CASES = {**SMALL, **EDGE, **LARGE,
          # the big-window kernels with two batch items and a padded, masked latitude
          "b2_n288_3d_pad": Problem("b2n288", "bf16", 2, 3, 64, (2, 20, 24), (2, 24, 24), (2, 12, 12), (1, 6, 6),
-                                   seed=31)}
+                                   seed=31),
+         # 16 x 20 windows (320 tokens, 5 blocks of 4 query waves with no idle slot;
+         # a width of 20 splits diagonal runs at window rows), latitude padded 30 -> 32
+         "n320_w20_pad": Problem("n320", "bf16", 1, 2, 64, (1, 30, 40), (1, 32, 40), (1, 16, 20), (0, 8, 10),
+                                 seed=32)}
 
 
 @pytest.mark.parametrize("name", list(CASES))
