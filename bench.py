@@ -152,11 +152,41 @@ def cpu_baseline_backward(p, x, dout, grads_gpu, windows):
     }
 
 
+def warm_up(step, steps, min_ms):
+    """Untimed warm-up: `steps` calls, then batches of 10 more until `min_ms`
+    of wall time (GPU work included) have passed.  Returns (calls, ms)."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(steps):
+        step(n)
+        n += 1
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(10):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n, (time.perf_counter() - t0) * 1e3
+
+
+def launch_stats(launch_ms):
+    """Mean, median, p10 and p90 of sorted per-launch times (ms)."""
+    n = len(launch_ms)
+    med = launch_ms[n // 2] if n % 2 else 0.5 * (launch_ms[n // 2 - 1] + launch_ms[n // 2])
+    return {"avg_launch_ms": round(sum(launch_ms) / n, 5), "median_ms": round(med, 5),
+            "p10_ms": round(launch_ms[n // 10], 5), "p90_ms": round(launch_ms[(9 * n) // 10], 5)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-ms", type=float, default=200.0,
+                    help="after the --warmup steps, keep warming up (untimed) until this much wall time has "
+                         "passed, so that clocks have settled before the timed steps")
     ap.add_argument("--workload", default="c3_bf16_540x1080")
     ap.add_argument("--variant", default="fused", choices=["fused", "staged"])
     ap.add_argument("--cpu-rows", type=int, default=1 << 30,
@@ -218,9 +248,7 @@ def main():
         else:
             swa_forward(att.handle, s["q"], s["k"], s["v"], s["table"], s["out"])
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_steps, warm_ms = warm_up(step, args.warmup, args.warmup_ms)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -289,10 +317,10 @@ def main():
                              "attn_bf16_bwd_q_kernel+attn_bf16_bwd_kv_kernel") if backward
                             else kernel_name(p, info) if args.variant == "fused" else "gather+attn+scatter"),
                    "workgroups": info.workgroups,
-                   "avg_launch_ms": round(avg_launch_ms, 5),
-                   "p10_ms": round(launch_ms[len(launch_ms) // 10], 5),
-                   "p90_ms": round(launch_ms[(9 * len(launch_ms)) // 10], 5),
+                   **launch_stats(launch_ms),
                    "source_sha256_16": kernel_source_hash(BWD_SOURCES if backward else None)},
+        "warmup_calls": warm_steps,
+        "warmup_ms": round(warm_ms, 1),
         "roofline": {
             **roof,
             "traffic": traffic,
@@ -397,9 +425,7 @@ def run_layer(args):
         s = sets[i % nsets]
         swa_layer_forward(att.handle, s["x"], s["w_qkv"], s["b_qkv"], s["table"], s["w_o"], s["b_o"], s["y"], ws)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_steps, warm_ms = warm_up(step, args.warmup, args.warmup_ms)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
@@ -433,11 +459,11 @@ def run_layer(args):
     }
     per_kernel = {}
     for name, (fn, kname, flops, nbytes, _) in kernels.items():
-        for i in range(args.warmup):
-            fn(i)
+        warm_up(fn, args.warmup, args.warmup_ms / 3)
         ms = timed(fn, args.steps)
-        per_kernel[name] = {"kernel": kname, "avg_ms": round(sum(ms) / len(ms), 5),
-                            "p10_ms": round(ms[len(ms) // 10], 5), "p90_ms": round(ms[(9 * len(ms)) // 10], 5),
+        st = launch_stats(ms)
+        per_kernel[name] = {"kernel": kname, "avg_ms": st["avg_launch_ms"], "median_ms": st["median_ms"],
+                            "p10_ms": st["p10_ms"], "p90_ms": st["p90_ms"],
                             "flops": flops, "algorithmic_bytes": nbytes}
     dom = max(per_kernel, key=lambda n: per_kernel[n]["avg_ms"])
     kd = per_kernel[dom]
@@ -477,8 +503,10 @@ def run_layer(args):
         "mfma_peak_frac": round(tflops / peak_tf, 5),
         "layer_flops_per_step": info.layer_flops,
         "kernels": per_kernel,
-        "kernel": {"name": kd["kernel"], "step": dom, "avg_launch_ms": kd["avg_ms"], "p10_ms": kd["p10_ms"],
-                   "p90_ms": kd["p90_ms"], "source_sha256_16": kernel_source_hash(dom_sources)},
+        "kernel": {"name": kd["kernel"], "step": dom, "avg_launch_ms": kd["avg_ms"], "median_ms": kd["median_ms"],
+                   "p10_ms": kd["p10_ms"], "p90_ms": kd["p90_ms"], "source_sha256_16": kernel_source_hash(dom_sources)},
+        "warmup_calls": warm_steps,
+        "warmup_ms": round(warm_ms, 1),
         "roofline": {
             **roof,
             "traffic": traffic,

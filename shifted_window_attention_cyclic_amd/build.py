@@ -29,15 +29,19 @@ def hipcc_flags():
 def build(verbose: bool = False) -> str:
     """Compiles every HIP source and links the shared library (always)."""
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    objs = []
+    objs, procs = [], []
+    # the sources compile independently, side by side
     for src in SOURCES:
         obj = os.path.join(CSRC, os.path.basename(src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         cmd = [hipcc] + hipcc_flags() + lang + ["-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        procs.append((subprocess.Popen(cmd), cmd))
         objs.append(obj)
+    failed = [cmd for p, cmd in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
     cmd = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", LIBRARY + ".tmp"] + objs
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -1737,8 +1737,12 @@ static Bf16Variant bf16_variant_for(const Geometry& g, bool stream) {
 }
 
 bool bf16_block_fits(const Geometry& g) {
-    // the general per-unit variant takes up to 8 waves x 4 tiles = 512 tokens
-    return g.N <= 512 && bf16_lds(g).total <= (size_t)kLdsBytes;
+    const int64_t rows = (int64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
+    const int64_t wrows = g.windows * g.N;
+    // the general per-unit variant takes up to 8 waves x 4 tiles = 512 tokens; row + 1
+    // of the real-token layout (fused) or of the window slots (staged) fits the 28 bits
+    // of the packed table word
+    return g.N <= 512 && bf16_lds(g).total <= (size_t)kLdsBytes && (rows > wrows ? rows : wrows) < kRowMask;
 }
 
 bool bf16_stream_fits(const Geometry& g) {

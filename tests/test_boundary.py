@@ -157,3 +157,27 @@ def test_binding_refuses_cpu_tensors():
     t = torch.zeros(4)
     with pytest.raises(ValueError):
         binding._dev(t, "q")
+
+
+# Every bf16 schedule packs source row + 1 of a token into the 28 low bits of a
+# table word, so a bf16 problem with 2^28 - 1 or more token rows (real tokens,
+# or window slots in the staged layout) is refused before any device call.
+# 180x360 grids with one 32-wide head: 64,800 tokens per batch item.
+ROW_LIMIT = (1 << 28) - 1
+C2 = WORKLOADS["c2_bf16_180x360"]
+
+
+@pytest.mark.parametrize("variant", ["fused", "staged"])
+def test_bf16_row_word_limit_refused(lib, variant):
+    p = C2.with_(batch=4200, heads=1)  # 272,160,000 tokens: past the 28-bit row word
+    assert p.tokens >= ROW_LIMIT and p.window_tokens <= 512
+    st, msg = create_status(lib, p, variant)
+    assert st == binding.SWA_ERR_UNSUPPORTED, (st, msg)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_bf16_row_word_limit_just_below_is_valid(lib):
+    p = C2.with_(batch=4100, heads=1)  # 265,680,000 tokens: inside the 28-bit row word
+    assert p.tokens < ROW_LIMIT
+    st, msg = create_status(lib, p)
+    assert st == binding.SWA_ERR_HIP, (st, msg)  # valid: only the missing device stops it

@@ -10,6 +10,7 @@ import torch
 
 import oracle
 from helpers import TOL, host_f32, rel_err
+from oracle_pool import pooled_backward_errors
 from shifted_window_attention_cyclic_amd import SwaError, WindowAttention
 from shifted_window_attention_cyclic_amd.inputs import WORKLOADS, Problem, make_inputs
 from test_gpu_parity import EDGE, LARGE, SMALL
@@ -72,28 +73,24 @@ def test_backward_small_grid(name):
         assert torch.isfinite(g_gpu.float()).all(), gname
 
 
-def test_backward_full_size_sampled_windows():
-    """540x1080 at full size: the gradients of every token of a sample of
-    windows (first and last window rows and columns, the latitude wrap, and
-    random ones) against the oracle."""
-    p = WORKLOADS["c3_bf16_540x1080"]
+@pytest.mark.parametrize("name", ["c3_bf16_540x1080", "c4_bf16_181x360_pad190", "c5_bf16_4x180x360_3d",
+                                  "c6_bf16_180x360_pad184_d128"])
+def test_backward_full_size_every_window(name):
+    """The workload at its full size: dq, dk, dv of every token and the table
+    gradient (a sum over every window and batch item) against the oracle's
+    per-window backward over all windows, split across host processes."""
+    p = WORKLOADS[name]
     x = make_inputs(p)
     dout = _dout(p)
-    dq, dk, dv, dtable = _run(p, x, dout)
-    nwy, nwx = p.padded[1] // p.window[1], p.padded[2] // p.window[2]
-    rng = np.random.default_rng(0)
-    rows = sorted({0, 1, nwy - 2, nwy - 1} | set(rng.integers(0, nwy, 4).tolist()))
-    cols = sorted({0, 1, nwx - 1} | set(rng.integers(0, nwx, 3).tolist()))
-    wins = [r * nwx + c for r in rows for c in cols]
-    say(f"[backward full] {len(wins)} windows")
-    ref = oracle.literal_backward(p, host_f32(x["q"]), host_f32(x["k"]), host_f32(x["v"]),
-                                  host_f32(x["table"]), host_f32(dout), windows=wins)
-    mine = np.isin(oracle.token_windows(p), wins)[None]  # [1, T, H, W]
-    for gname, g_gpu, g_ref in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
-        err = rel_err(host_f32(g_gpu)[mine], g_ref[mine])
-        say(f"  {gname}: rel err {err:.3e} over {int(mine.sum())} tokens")
-        assert err <= TOL["bf16"], gname
-    for g in (dq, dk, dv, dtable):
+    got = _run(p, x, dout)
+    say(f"[backward full] {name}: {p.windows} windows")
+    host = {n: host_f32(x[n]) for n in ("q", "k", "v", "table")}
+    host["dout"] = host_f32(dout)
+    errs = pooled_backward_errors(p, host, [host_f32(g) for g in got])
+    for gname in ("dq", "dk", "dv", "dtable"):
+        say(f"  {gname}: rel err {errs[gname]:.3e}")
+        assert errs[gname] <= TOL["bf16"], gname
+    for g in got:
         assert torch.isfinite(g.float()).all()
 
 
@@ -123,10 +120,11 @@ def test_backward_is_bitwise_reproducible():
         assert torch.equal(ga, gb)
 
 
-@pytest.mark.parametrize("name", ["c5_bf16_4x180x360_3d", "c7_bf16_180x384_pad192_d128_w32"])
+@pytest.mark.parametrize("name", ["c7_bf16_180x384_pad192_d128_w32"])
 def test_backward_big_windows_full_size_sampled(name):
-    """The big-window kernels at full size (2x12x12 and 32x32 windows): every
-    token's gradients in a few sampled windows (first, last, latitude wrap)."""
+    """The 32x32-window kernels at full size (each window takes the fp64 oracle
+    over a minute): every token's gradients in a few sampled windows (first,
+    last, latitude wrap)."""
     p = WORKLOADS[name]
     x = make_inputs(p)
     dout = _dout(p)

@@ -129,6 +129,24 @@ def test_parity_full_size_sampled(name):
         assert err4 <= TOL[p.dtype]
 
 
+@pytest.mark.parametrize("name", ["c2_bf16_180x360", "c3_bf16_540x1080", "c4_bf16_181x360_pad190",
+                                  "c5_bf16_4x180x360_3d", "c6_bf16_180x360_pad184_d128"])
+def test_parity_full_grid_every_token(name):
+    """The workload at its full size, in the launch configuration the benchmark
+    times: every real token and head against the oracle's direct form (C,
+    OpenMP over the host cores)."""
+    p = WORKLOADS[name]
+    say(f"[full grid] {name} seed={p.seed}")
+    x, d = device_inputs(p)
+    out = run(p, d, "fused")
+    del d
+    ref = oracle_full(p, x)
+    err = rel_err(host_f32(out), ref)
+    say(f"  {p.tokens} tokens x {p.heads} heads, rel err {err:.3e}")
+    assert err <= TOL[p.dtype]
+    assert torch.isfinite(out.float()).all()
+
+
 def test_fp32_full_workload_matches_oracle_everywhere():
     p = WORKLOADS["c1_f32_16x32"]
     x, d = device_inputs(p)
