@@ -179,6 +179,32 @@ swa_status swa_backward(swa_handle* h, const void* q, const void* k, const void*
                         void* stream);
 
 /*
+ * swa_backward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight training or serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as swa_backward, without the
+ * workspace: the per-(window, head) table-gradient shares (and, for
+ * backward_schedule 2, the per-query statistics) go to a fixed scratch array
+ * of 32 MiB in device memory that the library holds on each device it runs on
+ * (looked up in swa_create, kept until the process ends).  The windows are
+ * processed in passes of whole chunks of 1/64 of the windows each, as many
+ * chunks per pass as the scratch holds, and the table gradient is summed chunk
+ * by chunk in the order swa_backward sums it, so dq, dk, dv and (with
+ * backward_schedule 1) dtable equal swa_backward's bit for bit.  Queues only
+ * kernel launches on `stream` (no allocation, no memset, no host
+ * synchronisation).  Every call on one device shares that device's scratch:
+ * calls that overlap in time on one device (other streams, other threads,
+ * other handles) race and give wrong gradients.  The handle must have been
+ * created on the current device.
+ * Errors: as swa_backward; also UNSUPPORTED when one chunk of windows needs
+ * more than the 32 MiB scratch (about 2^23 / ((heads * table entries) per
+ * window) * 64 windows; swa_backward takes any size), INVALID_ARGUMENT when
+ * the current device is not the handle's.
+ */
+swa_status swa_backward_noalloc(swa_handle* h, const void* q, const void* k, const void* v,
+                                const float* bias_table, const void* dout, void* dq, void* dk, void* dv,
+                                float* dtable, void* stream);
+
+/*
  * The window attention inside its Swin block's projections (TERRA page,
  * abstract: the models are stacks of Swin blocks; Table V: embedding width
  * d = N_h * head_dim).  With C = heads * head_dim:

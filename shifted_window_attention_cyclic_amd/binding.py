@@ -19,7 +19,7 @@ SWA_SCHEDULE_AUTO, SWA_SCHEDULE_STREAM, SWA_SCHEDULE_BLOCK, SWA_SCHEDULE_KEYBLOC
 SCHEDULES = {"auto": SWA_SCHEDULE_AUTO, "stream": SWA_SCHEDULE_STREAM, "block": SWA_SCHEDULE_BLOCK,
              "keyblock": SWA_SCHEDULE_KEYBLOCK}
 
-EXPORTS = ("swa_create", "swa_forward", "swa_backward", "swa_layer_forward", "swa_projection", "swa_destroy",
+EXPORTS = ("swa_create", "swa_forward", "swa_backward", "swa_backward_noalloc", "swa_layer_forward", "swa_projection", "swa_destroy",
            "swa_get_info", "swa_status_string",
            "swa_last_error", "swa_gather", "swa_scatter", "swa_debug_visibility")
 
@@ -69,6 +69,8 @@ def load_library(path: str = LIBRARY):
     lib.swa_forward.restype = st
     lib.swa_backward.argtypes = [vp] * 12
     lib.swa_backward.restype = st
+    lib.swa_backward_noalloc.argtypes = [vp] * 11
+    lib.swa_backward_noalloc.restype = st
     lib.swa_layer_forward.argtypes = [vp] * 10
     lib.swa_layer_forward.restype = st
     i32, i64 = ctypes.c_int32, ctypes.c_int64
@@ -169,6 +171,14 @@ def swa_backward(handle, q, k, v, table, dout, dq, dk, dv, dtable, workspace, st
                                        _dev(dq, "dq", dt), _dev(dk, "dk", dt), _dev(dv, "dv", dt),
                                        _dev(dtable, "dtable", torch.float32), _dev(workspace, "workspace"),
                                        _stream(stream)))
+
+
+def swa_backward_noalloc(handle, q, k, v, table, dout, dq, dk, dv, dtable, stream=None) -> None:
+    dt = q.dtype
+    _check(load_library().swa_backward_noalloc(handle, _dev(q, "q"), _dev(k, "k", dt), _dev(v, "v", dt),
+                                               _dev(table, "table", torch.float32), _dev(dout, "dout", dt),
+                                               _dev(dq, "dq", dt), _dev(dk, "dk", dt), _dev(dv, "dv", dt),
+                                               _dev(dtable, "dtable", torch.float32), _stream(stream)))
 
 
 def swa_layer_forward(handle, x, w_qkv, b_qkv, table, w_o, b_o, y, workspace, stream=None) -> None:

@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -28,9 +29,21 @@ struct swa_handle {
     float* bias_hm;     // key-blocked schedule: head-major copy of the bias table
 };
 
+// Scratch of swa_backward_noalloc: file-scope device memory, so that the call
+// needs no allocation.  Each device holds its own copy from the moment its
+// address is first looked up until the process ends.  In host code the name
+// stands for a host-side shadow, never a device address: only the address
+// hipGetSymbolAddress returns for the current device is passed to kernels.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices]; // device address of `scratch` on each device, once looked up
 
 swa_status fail(swa_status s, const std::string& msg) {
     g_last_error = msg;
@@ -145,6 +158,24 @@ swa_status validate(const swa_config* c, swa::Geometry* g, int* elem_bytes) {
     return SWA_OK;
 }
 
+// The device address of `scratch` on device dev, which must be current; looked
+// up once per device.
+swa_status scratch_for_device(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(SWA_ERR_UNSUPPORTED, "device index beyond the scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(SWA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SWA_OK;
+}
+
 size_t io_bytes(const swa_handle* h) {
     return (size_t)h->g.batch * h->g.ext[0] * h->g.ext[1] * h->g.ext[2] * h->g.row * h->elem_bytes;
 }
@@ -208,6 +239,12 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
         return fail(SWA_ERR_UNSUPPORTED, buf);
     }
     if ((e = swa::prepare_kernels(max_lds)) != hipSuccess) return fail_hip(e, "hipFuncSetAttribute");
+    {
+        // set-up of swa_backward_noalloc on this device (once per device)
+        void* sp = nullptr;
+        const swa_status ss = scratch_for_device(dev, &sp);
+        if (ss != SWA_OK) return ss;
+    }
     if ((e = swa::prepare_backward_kernels(max_lds)) != hipSuccess) return fail_hip(e, "hipFuncSetAttribute");
     int schedule = 0, blocks = 0;
     if (cfg->dtype == SWA_BF16) {
@@ -364,6 +401,47 @@ swa_status swa_backward(swa_handle* h, const void* q, const void* k, const void*
                 return fail(SWA_ERR_INVALID_ARGUMENT, "a gradient or the workspace overlaps another argument");
     hipError_t e = swa::launch_backward(g, bf16, q, k, v, bias_table, dout, dq, dk, dv, dtable, workspace,
                                         (hipStream_t)stream);
+    return e == hipSuccess ? SWA_OK : fail_hip(e, "backward launch");
+}
+
+swa_status swa_backward_noalloc(swa_handle* h, const void* q, const void* k, const void* v,
+                                const float* bias_table, const void* dout, void* dq, void* dk, void* dv,
+                                float* dtable, void* stream) {
+    if (!h || !q || !k || !v || !bias_table || !dout || !dq || !dk || !dv || !dtable)
+        return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    const void* tensors[] = {q, k, v, dout, dq, dk, dv};
+    for (const void* p : tensors)
+        if (!aligned(p, 16)) return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned pointer (tensors need 16 bytes)");
+    if (!aligned(bias_table, 4) || !aligned(dtable, 4)) return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned table");
+    const swa::Geometry& g = h->g;
+    const bool bf16 = h->cfg.dtype == SWA_BF16;
+    if (!swa::backward_fits(g, bf16))
+        return fail(SWA_ERR_UNSUPPORTED, "the backward kernels do not take this window");
+    const size_t need = swa::backward_scratch_bytes(g, bf16);
+    if (need > kScratchBytes) {
+        char buf[200];
+        snprintf(buf, sizeof buf,
+                 "one chunk of windows needs %zu bytes of scratch, above the %zu of swa_backward_noalloc "
+                 "(swa_backward takes a workspace of any size)", need, kScratchBytes);
+        return fail(SWA_ERR_UNSUPPORTED, buf);
+    }
+    const size_t n = io_bytes(h);
+    const size_t nt = (size_t)g.table_size * g.heads * sizeof(float);
+    const void* all[] = {q, k, v, dout, bias_table, dq, dk, dv, dtable};
+    const size_t len[] = {n, n, n, n, nt, n, n, n, nt};
+    for (int i = 5; i < 9; i++)
+        for (int j = 0; j < 9; j++)
+            if (j != i && overlap(all[i], len[i], all[j], len[j]))
+                return fail(SWA_ERR_INVALID_ARGUMENT, "a gradient overlaps another argument");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    if (dev != h->device) return fail(SWA_ERR_INVALID_ARGUMENT, "the handle was created on another device");
+    void* sp = nullptr;
+    const swa_status st = scratch_for_device(dev, &sp); // looked up in swa_create: no runtime call here
+    if (st != SWA_OK) return st;
+    e = swa::launch_backward_scratch(g, bf16, q, k, v, bias_table, dout, dq, dk, dv, dtable, sp, kScratchBytes,
+                                     (hipStream_t)stream);
     return e == hipSuccess ? SWA_OK : fail_hip(e, "backward launch");
 }
 

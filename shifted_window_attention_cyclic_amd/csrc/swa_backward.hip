@@ -84,7 +84,8 @@ template <int D, bool BIAS_VEC>
 __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
     Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ dtab_units) {
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ dtab_units, uint32_t work0,
+    uint32_t count) {
     constexpr int THREADS = kBwdWaves * 64;
     constexpr int KSTEPS = D / 32, DT = D / 16, CH = D / 8, RPC = 64 / CH;
     constexpr int KB = kBwdMaxTiles;
@@ -98,8 +99,8 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;
 
-    const uint32_t total = (uint32_t)(g.windows * g.heads);
-    const uint32_t work = (uint32_t)xcd_work_index(blockIdx.x, total);
+    // units work0 .. work0 + count - 1 (all of them, or one pass of the no-workspace entry)
+    const uint32_t work = work0 + (uint32_t)xcd_work_index(blockIdx.x, count);
     const uint32_t wi = fdiv(g.fd_heads, work);
     const int h = (int)(work - wi * (uint32_t)g.heads);
     const int b = (int)fdiv(g.fd_nW, wi);
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
     // are masked or involve pad hold dS = 0).  Two balanced stages when the
     // partial sums fit in the P region (free once pass 2 is done): per
     // (query row, key row, x offset) along x, then per entry over the rows.
-    float* dst = dtab_units + (size_t)work * g.table_size;
+    float* dst = dtab_units + (size_t)(work - work0) * g.table_size;
     const uint16_t* dSm = (const uint16_t*)(smem + L.dsm);
     auto ds_at = [&](int n, int m) __attribute__((always_inline)) {
         return __builtin_bit_cast(float, (unsigned)dSm[(size_t)n * NP + m] << 16);
@@ -596,7 +597,7 @@ template <int D, int QW>
 __global__ __launch_bounds__((QW + kBwdLoaders) * 64) void attn_bf16_bwd_q_kernel(
     Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
-    float* __restrict__ stats) {
+    float* __restrict__ stats, uint32_t work0, uint32_t count) {
     constexpr int THREADS = (QW + kBwdLoaders) * 64;
     constexpr int KSTEPS = D / 32, DT = D / 16;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -612,10 +613,11 @@ __global__ __launch_bounds__((QW + kBwdLoaders) * 64) void attn_bf16_bwd_q_kerne
     const int col = lane & 15, grp = lane >> 4;
 
     const int QB = (N + QW * 16 - 1) / (QW * 16);
-    const uint32_t total = (uint32_t)(g.windows * g.heads) * (uint32_t)QB;
+    const uint32_t total = count * (uint32_t)QB; // units work0 .. work0 + count - 1
     const uint32_t work = (uint32_t)xcd_work_index(blockIdx.x, total);
-    const uint32_t unit = work / (uint32_t)QB;
-    const int qblk = (int)(work - unit * (uint32_t)QB);
+    const uint32_t ul = work / (uint32_t)QB;
+    const uint32_t unit = work0 + ul;
+    const int qblk = (int)(work - ul * (uint32_t)QB);
     int h, b, wc[3];
     uint32_t wi;
     unit_coords(g, unit, h, b, wc, wi);
@@ -745,7 +747,7 @@ __global__ __launch_bounds__((QW + kBwdLoaders) * 64) void attn_bf16_bwd_q_kerne
     // statistics per query: lse2 (log2 of the softmax normaliser) and D; a pad
     // query gets lse2 = +inf, so that every P it would take is 0
     if (grp == 0 && in_window) {
-        float* st = stats + (size_t)unit * 2 * NPX;
+        float* st = stats + (size_t)ul * 2 * NPX;
         st[n] = pscale == 0.f ? INFINITY : lse2;
         st[NPX + n] = dsum;
     }
@@ -799,7 +801,8 @@ __global__ __launch_bounds__((KW + kBwdLoaders) * 64)
 __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kernel(
     Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, const float* __restrict__ stats, float* __restrict__ dtab_units) {
+    uint16_t* __restrict__ dv, const float* __restrict__ stats, float* __restrict__ dtab_units, uint32_t work0,
+    uint32_t count) {
     static_assert(KW <= kBwdKWaves, "diagonal scratch per compute wave");
     constexpr int THREADS = (KW + kBwdLoaders) * 64;
     constexpr int KSTEPS = D / 32, DT = D / 16;
@@ -819,8 +822,8 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;
 
-    const uint32_t units = (uint32_t)(g.windows * g.heads);
-    const uint32_t unit = (uint32_t)xcd_work_index(blockIdx.x, units);
+    const uint32_t ul = (uint32_t)xcd_work_index(blockIdx.x, count); // unit work0 + ul
+    const uint32_t unit = work0 + ul;
     int h, b, wc[3];
     uint32_t wi;
     unit_coords(g, unit, h, b, wc, wi);
@@ -832,7 +835,7 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
         dtab[i] = 0.f;
     }
     {
-        const float* st = stats + (size_t)unit * 2 * NPX;
+        const float* st = stats + (size_t)ul * 2 * NPX;
         for (int i = tid; i < NPX; i += THREADS) {
             lse[i] = i < N ? st[i] : INFINITY; // slots past N: P = 0
             dd[i] = i < N ? st[NPX + i] : 0.f;
@@ -1028,7 +1031,7 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
         }
         bwd_compute_barrier(); // final: every atomic of the table share has landed
     }
-    float* dst = dtab_units + (size_t)unit * g.table_size;
+    float* dst = dtab_units + (size_t)ul * g.table_size;
     for (int e = tid; e < g.table_size; e += THREADS) dst[e] = dtab[e];
 }
 
@@ -1044,7 +1047,7 @@ template <int D>
 __global__ __launch_bounds__(kF32BwdThreads) void attn_f32_bwd_kernel(
     Geometry g, const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ table, const float* __restrict__ dout, float* __restrict__ dq, float* __restrict__ dk,
-    float* __restrict__ dv, float* __restrict__ dtab_units) {
+    float* __restrict__ dv, float* __restrict__ dtab_units, uint32_t work0, uint32_t count) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int N = g.N;
     float* Qs = (float*)smem;
@@ -1058,8 +1061,7 @@ __global__ __launch_bounds__(kF32BwdThreads) void attn_f32_bwd_kernel(
     int* qword = kword + N;
     int* rowi = qword + N;
 
-    const int64_t total = g.windows * g.heads;
-    const int64_t work = xcd_work_index(blockIdx.x, total);
+    const int64_t work = (int64_t)work0 + xcd_work_index(blockIdx.x, count);
     const int64_t wi = work / g.heads;
     const int h = (int)(work - wi * g.heads);
 
@@ -1152,7 +1154,7 @@ __global__ __launch_bounds__(kF32BwdThreads) void attn_f32_bwd_kernel(
         }
     }
     // this unit's share of the table gradient, an entry per thread (see the bf16 kernel)
-    float* dst = dtab_units + (size_t)work * g.table_size;
+    float* dst = dtab_units + (size_t)(work - work0) * g.table_size;
     for (int e = threadIdx.x; e < g.table_size; e += blockDim.x) {
         const int et = e / (g.tdy * g.tdx), r0 = e - et * (g.tdy * g.tdx);
         const int ey = r0 / g.tdx, ex = r0 - ey * g.tdx;
@@ -1225,7 +1227,7 @@ size_t backward_workspace_bytes(const Geometry& g) {
 }
 
 typedef void (*bwd_bf16_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
-                           const uint16_t*, uint16_t*, uint16_t*, uint16_t*, float*);
+                           const uint16_t*, uint16_t*, uint16_t*, uint16_t*, float*, uint32_t, uint32_t);
 
 static bwd_bf16_t bwd_bf16_variant(const Geometry& g) {
     const bool bv = g.win[2] % 4 == 0;
@@ -1270,21 +1272,21 @@ hipError_t prepare_backward_kernels(int max_lds) {
     return hipSuccess;
 }
 
-hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
-                           const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
-                           void* workspace, hipStream_t s) {
-    const dim3 grid((unsigned)(g.windows * g.heads));
-    float* units = (float*)workspace;
-    float* chunks = units + (size_t)(g.windows * g.heads) * g.table_size;
-    float* stats = chunks + (size_t)kDtableChunks * g.heads * g.table_size;
+// The attention gradients of units work0 .. work0 + count - 1: dq, dk, dv of
+// their tokens, their table-gradient shares at units[(unit - work0) * ts] and,
+// for big windows, their per-query statistics at stats[(unit - work0) * 2 NPX].
+static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
+                                        const float* table, const void* dout, void* dq, void* dk, void* dv,
+                                        uint32_t work0, uint32_t count, float* units, float* stats, hipStream_t s) {
+    const dim3 grid(count);
     if (bf16 && !bwd_small_fits(g)) {
         const BwdBigLds L = bwd_big_lds(g, bwd_kv_waves(g.head_dim));
         const int QW = bwd_q_waves(g);
-        const dim3 qgrid((unsigned)(g.windows * g.heads * ((g.N + QW * 16 - 1) / (QW * 16))));
+        const dim3 qgrid(count * (unsigned)((g.N + QW * 16 - 1) / (QW * 16)));
         typedef void (*qk_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
-                             const uint16_t*, uint16_t*, float*);
+                             const uint16_t*, uint16_t*, float*, uint32_t, uint32_t);
         typedef void (*kv_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
-                             const uint16_t*, uint16_t*, uint16_t*, const float*, float*);
+                             const uint16_t*, uint16_t*, uint16_t*, const float*, float*, uint32_t, uint32_t);
         const qk_t fq = g.head_dim == 128 ? (QW == 6 ? attn_bf16_bwd_q_kernel<128, 6> : attn_bf16_bwd_q_kernel<128, 4>)
                         : g.head_dim == 64
                             ? (QW == 8   ? attn_bf16_bwd_q_kernel<64, 8>
@@ -1297,26 +1299,36 @@ hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const vo
         const kv_t fk = g.head_dim == 32 ? attn_bf16_bwd_kv_kernel<32, 6>
                         : g.head_dim == 64 ? attn_bf16_bwd_kv_kernel<64, 6> : attn_bf16_bwd_kv_kernel<128, 8>;
         hipLaunchKernelGGL(fq, qgrid, dim3((QW + kBwdLoaders) * 64), L.total_q, s, g, (const uint16_t*)q, (const uint16_t*)k,
-                           (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dq, stats);
+                           (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dq, stats, work0, count);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(fk, grid, dim3((KW + kBwdLoaders) * 64), L.total_k, s, g, (const uint16_t*)q, (const uint16_t*)k,
                            (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dk, (uint16_t*)dv,
-                           (const float*)stats, units);
+                           (const float*)stats, units, work0, count);
     } else if (bf16) {
         hipLaunchKernelGGL(bwd_bf16_variant(g), grid, dim3(kBwdWaves * 64), bwd_lds(g).total, s, g,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, table, (const uint16_t*)dout,
-                           (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, units);
+                           (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, units, work0, count);
     } else if (g.head_dim == 32) {
         hipLaunchKernelGGL(attn_f32_bwd_kernel<32>, grid, dim3(kF32BwdThreads), f32_bwd_lds_bytes(g), s, g,
                            (const float*)q, (const float*)k, (const float*)v, table, (const float*)dout, (float*)dq,
-                           (float*)dk, (float*)dv, units);
+                           (float*)dk, (float*)dv, units, work0, count);
     } else {
         hipLaunchKernelGGL(attn_f32_bwd_kernel<64>, grid, dim3(kF32BwdThreads), f32_bwd_lds_bytes(g), s, g,
                            (const float*)q, (const float*)k, (const float*)v, table, (const float*)dout, (float*)dq,
-                           (float*)dk, (float*)dv, units);
+                           (float*)dk, (float*)dv, units, work0, count);
     }
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
+                           const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
+                           void* workspace, hipStream_t s) {
+    float* units = (float*)workspace;
+    float* chunks = units + (size_t)(g.windows * g.heads) * g.table_size;
+    float* stats = chunks + (size_t)kDtableChunks * g.heads * g.table_size;
+    hipError_t e = launch_backward_units(g, bf16, q, k, v, table, dout, dq, dk, dv, 0,
+                                         (uint32_t)(g.windows * g.heads), units, stats, s);
     if (e != hipSuccess) return e;
     const int n = g.heads * g.table_size;
     hipLaunchKernelGGL(dtable_chunk_kernel, dim3((n + 255) / 256, kDtableChunks), dim3(256), 0, s, g.windows,
@@ -1325,6 +1337,78 @@ hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const vo
     hipLaunchKernelGGL(dtable_sum_kernel, dim3((n + 255) / 256), dim3(256), 0, s, g.heads, g.table_size,
                        (const float*)chunks, dtable);
     return hipGetLastError();
+}
+
+// ---- the backward pass through a fixed scratch buffer, in passes over runs
+// of whole window chunks (the chunks of dtable_chunk_kernel).  After each pass
+// the chunks it covered are summed and added to the running table gradient,
+// chunk by chunk in order, which is exactly the sum dtable_sum_kernel forms:
+// the results equal the workspace path's bit for bit.
+
+// Bytes of scratch one window needs: its heads' table shares (and per-query
+// statistics of big windows).
+static size_t scratch_per_window(const Geometry& g, bool bf16) {
+    size_t per_unit = (size_t)g.table_size;
+    if (bf16 && !bwd_small_fits(g)) per_unit += 2 * (size_t)bwd_big_lds(g, bwd_kv_waves(g.head_dim)).NPX;
+    return per_unit * g.heads * sizeof(float);
+}
+
+static int64_t chunk_window(const Geometry& g, int c) { return g.windows * c / kDtableChunks; }
+
+size_t backward_scratch_bytes(const Geometry& g, bool bf16) {
+    int64_t most = 0; // windows of the largest chunk
+    for (int c = 0; c < kDtableChunks; c++) {
+        const int64_t n = chunk_window(g, c + 1) - chunk_window(g, c);
+        most = n > most ? n : most;
+    }
+    return (size_t)most * scratch_per_window(g, bf16);
+}
+
+// dtable[e][h] = (c0 == 0 ? 0 : dtable[e][h]) + chunk sums c0 .. c1 - 1 in order;
+// the shares of windows w0 .. are at units[(w - w0) * heads * ts].
+__global__ __launch_bounds__(256) void dtable_accumulate_kernel(int64_t windows, int heads, int ts, int c0, int c1,
+                                                                int64_t w0, const float* __restrict__ units,
+                                                                float* __restrict__ dtable) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x; // h * ts + e
+    if (idx >= heads * ts) return;
+    const int h = idx / ts, e = idx - h * ts;
+    float run = c0 == 0 ? 0.f : dtable[(size_t)e * heads + h];
+    for (int c = c0; c < c1; c++) {
+        const int64_t a = windows * c / kDtableChunks, b = windows * (c + 1) / kDtableChunks;
+        float acc = 0.f;
+        for (int64_t w = a; w < b; w++) acc += units[(size_t)(w - w0) * heads * ts + idx];
+        run += acc;
+    }
+    dtable[(size_t)e * heads + h] = run;
+}
+
+hipError_t launch_backward_scratch(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
+                                   const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
+                                   void* scratch, size_t scratch_bytes, hipStream_t s) {
+    const size_t per_window = scratch_per_window(g, bf16);
+    const int n = g.heads * g.table_size;
+    int c0 = 0;
+    while (c0 < kDtableChunks) {
+        // the longest run of chunks whose windows' shares fit the scratch
+        int c1 = c0 + 1;
+        while (c1 < kDtableChunks &&
+               (size_t)(chunk_window(g, c1 + 1) - chunk_window(g, c0)) * per_window <= scratch_bytes)
+            c1++;
+        const int64_t w0 = chunk_window(g, c0), w1 = chunk_window(g, c1);
+        float* units = (float*)scratch;
+        float* stats = units + (size_t)(w1 - w0) * g.heads * g.table_size;
+        hipError_t e;
+        if (w1 > w0) {
+            e = launch_backward_units(g, bf16, q, k, v, table, dout, dq, dk, dv, (uint32_t)(w0 * g.heads),
+                                      (uint32_t)((w1 - w0) * g.heads), units, stats, s);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(dtable_accumulate_kernel, dim3((n + 255) / 256), dim3(256), 0, s, g.windows, g.heads,
+                           g.table_size, c0, c1, w0, (const float*)units, dtable);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        c0 = c1;
+    }
+    return hipSuccess;
 }
 
 } // namespace swa

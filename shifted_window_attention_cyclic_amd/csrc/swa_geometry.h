@@ -177,5 +177,12 @@ hipError_t prepare_backward_kernels(int max_lds);
 hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
                            const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
                            void* workspace, hipStream_t s);
+// The same gradients through a fixed scratch buffer of scratch_bytes, in
+// passes over runs of window chunks (bitwise equal to launch_backward), and
+// the least scratch that takes (one chunk of windows).
+size_t backward_scratch_bytes(const Geometry& g, bool bf16);
+hipError_t launch_backward_scratch(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
+                                   const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
+                                   void* scratch, size_t scratch_bytes, hipStream_t s);
 
 } // namespace swa
