@@ -39,11 +39,17 @@ PROJ_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_projection.hip",
                 "shifted_window_attention_cyclic_amd/csrc/swa_projection.h",
                 "shifted_window_attention_cyclic_amd/csrc/swa_device.h",
                 "shifted_window_attention_cyclic_amd/csrc/swa_geometry.h"]
+LAYER_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_layer.hip",
+                 "shifted_window_attention_cyclic_amd/csrc/swa_layer.h",
+                 "shifted_window_attention_cyclic_amd/csrc/swa_stream.h",
+                 "shifted_window_attention_cyclic_amd/csrc/swa_device.h",
+                 "shifted_window_attention_cyclic_amd/csrc/swa_geometry.h"]
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 MALL_BYTES = 256 << 20     # Infinity Cache; rotate inputs until the working set is 3x this
 KERNEL_SOURCES = ["shifted_window_attention_cyclic_amd/csrc/swa_kernels.hip",
+                  "shifted_window_attention_cyclic_amd/csrc/swa_stream.h",
                   "shifted_window_attention_cyclic_amd/csrc/swa_device.h",
                   "shifted_window_attention_cyclic_amd/csrc/swa_geometry.h"]
 SCHEDULE_STREAM, SCHEDULE_BLOCK, SCHEDULE_KEYBLOCK = 1, 2, 3  # swa_info.schedule
@@ -197,6 +203,8 @@ def main():
                     help="after timing, run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward", "layer"],
                     help="time swa_forward (default), swa_backward or swa_layer_forward")
+    ap.add_argument("--layer", default="auto", choices=["auto", "fused", "unfused"],
+                    help="the path of swa_layer_forward (--pass layer)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -400,12 +408,14 @@ def cpu_baseline_layer(p, x, y_gpu, rows):
 def run_layer(args):
     import torch
 
-    from shifted_window_attention_cyclic_amd import WindowAttention, swa_forward, swa_layer_forward, swa_projection
+    from shifted_window_attention_cyclic_amd import (WindowAttention, swa_forward, swa_layer_attention,
+                                                      swa_layer_forward, swa_projection)
     from shifted_window_attention_cyclic_amd.inputs import WORKLOADS, make_layer_inputs
 
     p = WORKLOADS[args.workload]
-    att = WindowAttention(p, args.variant)
+    att = WindowAttention(p, args.variant, layer=args.layer)
     info = att.info
+    fused = info.layer_path == 1  # SWA_LAYER_FUSED
     C = att.channels
     M = info.tokens
     eb = p.elem_bytes
@@ -419,7 +429,11 @@ def run_layer(args):
         d["y"] = torch.empty_like(d["x"])
         sets.append(d)
     ws = att.layer_workspace()
-    q, k, v, o = (ws[i * M * C:(i + 1) * M * C] for i in range(4))
+    if fused:
+        o = ws[:M * C]
+        q = k = v = None
+    else:
+        q, k, v, o = (ws[i * M * C:(i + 1) * M * C] for i in range(4))
 
     def step(i):
         s = sets[i % nsets]
@@ -432,7 +446,7 @@ def run_layer(args):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # the three kernels of a step, each timed alone through its own entry point
+    # the kernels of a step, each timed alone through its own entry point
     # on the same inputs and stream
     def proj_qkv(i):
         s = sets[i % nsets]
@@ -446,17 +460,31 @@ def run_layer(args):
         s = sets[i % nsets]
         swa_projection(o.view(M, C), s["w_o"], s["b_o"], [s["y"].view(-1)])
 
+    def qkv_attention(i):
+        s = sets[i % nsets]
+        swa_layer_attention(att.handle, s["x"], s["w_qkv"], s["b_qkv"], s["table"], o.view(att.io_shape))
+
     proj_flops_qkv = 2.0 * M * C * 3 * C
     proj_flops_out = 2.0 * M * C * C
     proj_name = "proj_bf16_kernel" if p.dtype == "bf16" else "proj_f32_kernel"
     # name: (call, kernel, flops, algorithmic bytes, kernel sources); projection
-    # bytes: x and the weights read, the outputs written, the fp32 bias read
-    kernels = {
-        "proj_qkv": (proj_qkv, proj_name, proj_flops_qkv, (M * C + 3 * C * C + 3 * M * C) * eb + 12.0 * C,
-                     PROJ_SOURCES),
-        "attention": (attention, kernel_name(p, info), info.nominal_flops, info.algorithmic_bytes, KERNEL_SOURCES),
-        "proj_out": (proj_out, proj_name, proj_flops_out, (2 * M * C + C * C) * eb + 4.0 * C, PROJ_SOURCES),
-    }
+    # bytes: x and the weights read, the outputs written, the fp32 bias read;
+    # the fused kernel reads x and the weights and writes the attention output
+    if fused:
+        kernels = {
+            "qkv_attention": (qkv_attention, "layer_qkv_attn_kernel", proj_flops_qkv + info.nominal_flops,
+                              (2 * M * C + 3 * C * C) * eb + 12.0 * C + 4.0 * math.prod(p.table_shape),
+                              LAYER_SOURCES),
+            "proj_out": (proj_out, proj_name, proj_flops_out, (2 * M * C + C * C) * eb + 4.0 * C, PROJ_SOURCES),
+        }
+    else:
+        kernels = {
+            "proj_qkv": (proj_qkv, proj_name, proj_flops_qkv, (M * C + 3 * C * C + 3 * M * C) * eb + 12.0 * C,
+                         PROJ_SOURCES),
+            "attention": (attention, kernel_name(p, info), info.nominal_flops, info.algorithmic_bytes,
+                          KERNEL_SOURCES),
+            "proj_out": (proj_out, proj_name, proj_flops_out, (2 * M * C + C * C) * eb + 4.0 * C, PROJ_SOURCES),
+        }
     per_kernel = {}
     for name, (fn, kname, flops, nbytes, _) in kernels.items():
         warm_up(fn, args.warmup, args.warmup_ms / 3)
@@ -498,6 +526,7 @@ def run_layer(args):
             "workload": p.name, "batch": p.batch, "grid_thw": list(p.extent), "padded_thw": list(p.padded),
             "window": list(p.window), "shift": list(p.shift), "heads": p.heads, "head_dim": p.head_dim,
             "channels": C, "variant": args.variant, "pass": "layer", "input_sets_rotated": nsets,
+            "layer_path": "fused" if fused else "unfused",
         },
         "tokens_per_s": round(M / (ms_per_step * 1e-3), 1),
         "mfma_peak_frac": round(tflops / peak_tf, 5),

@@ -89,6 +89,15 @@ typedef enum swa_schedule {
                                  bias slice and token tables leave LDS room for the ring */
 } swa_schedule;
 
+typedef enum swa_layer_path {
+    SWA_LAYER_AUTO = 0,   /* UNFUSED (the faster path on every shape measured) */
+    SWA_LAYER_FUSED = 1,  /* bf16: q, k, v projected per window inside the attention kernel (they never
+                             reach device memory), then the output projection GEMM: two launches and a
+                             quarter of the workspace */
+    SWA_LAYER_UNFUSED = 2 /* projection GEMM, swa_forward, projection GEMM: three launches, q, k, v and
+                             the attention output through the workspace */
+} swa_layer_path;
+
 typedef struct swa_config {
     int batch;     /* B >= 1 */
     int heads;     /* N_h >= 1 (TERRA, Table V) */
@@ -102,6 +111,7 @@ typedef struct swa_config {
     float scale;   /* logit scale, > 0; 0 selects 1/sqrt(head_dim) */
     swa_variant variant;
     swa_schedule schedule; /* bf16 kernel schedule; ignored for SWA_F32 */
+    swa_layer_path layer;  /* how swa_layer_forward runs */
 } swa_config;
 
 typedef struct swa_handle swa_handle;
@@ -127,6 +137,7 @@ typedef struct swa_info {
     int32_t backward_schedule;       /* 0: no backward pass; 1: one workgroup per (window, head), the
                                         whole window in LDS (fp32 always); 2: bf16 key-blocked kernels
                                         for windows beyond that (32-token blocks streamed) */
+    int32_t layer_path;              /* the path swa_layer_forward takes: SWA_LAYER_FUSED or _UNFUSED */
 } swa_info;
 
 /*
@@ -213,16 +224,22 @@ swa_status swa_backward_noalloc(swa_handle* h, const void* q, const void* k, con
  *   y   = o w_o^T + b_o
  * Channels are head-major (head h owns channels h*head_dim .. +head_dim-1),
  * so q, k, v and o have exactly the [B][T][H][W][heads][head_dim] layout of
- * swa_forward.  x, y: [B][T][H][W][C] in the handle's dtype.  w_qkv: [3C][C]
+ * swa_forward.  info.layer_path says how it runs: SWA_LAYER_FUSED projects
+ * each window's q, k, v head by head inside the attention kernel, so they
+ * never reach device memory (bf16; head_dim 32 or 64 with windows of up to
+ * 144 tokens, or 128 with up to 80; C a multiple of 32 of at least 96), then runs
+ * the output projection; SWA_LAYER_UNFUSED runs three launches.  Both give
+ * the same y bit for bit (the fused kernel keeps the projection's operand and
+ * reduction order and the attention's arithmetic).  x, y: [B][T][H][W][C] in the handle's dtype.  w_qkv: [3C][C]
  * and w_o: [C][C], the handle's dtype, row-major (a linear layer's
  * [out_features][in_features]).  b_qkv: [3C] and b_o: [C], fp32.  bf16: the
  * products run on bf16 matrix cores with fp32 accumulation; the bias is added
  * in fp32 and q, k, v, o, y are rounded to bf16 once.  x, y, the weights and
  * the workspace are device pointers, 16-byte aligned; biases and table
- * 4-byte aligned.  workspace: info.layer_workspace_bytes bytes, caller-owned,
- * receiving q, k, v and o in that order (each tokens * C elements); its
- * contents on entry do not matter, and on return it holds those four
- * tensors.  y must not overlap any other argument, nor the workspace any
+ * 4-byte aligned.  workspace: info.layer_workspace_bytes bytes, caller-owned;
+ * its contents on entry do not matter.  On return it holds o (fused path:
+ * tokens * C elements), or q, k, v and o in that order (unfused path: each
+ * tokens * C elements).  y must not overlap any other argument, nor the workspace any
  * input.  Asynchronous on `stream`; allocates nothing.
  * Errors: INVALID_ARGUMENT (NULL handle or pointer, misalignment, overlap),
  * UNSUPPORTED (C above 10912: 3C output features exceed the projection's
@@ -231,6 +248,20 @@ swa_status swa_backward_noalloc(swa_handle* h, const void* q, const void* k, con
 swa_status swa_layer_forward(swa_handle* h, const void* x, const void* w_qkv, const float* b_qkv,
                              const float* bias_table, const void* w_o, const float* b_o, void* y,
                              void* workspace, void* stream);
+
+/*
+ * The first launch of swa_layer_forward's fused path alone: the attention
+ * output o = swa_forward(q, k, v) with q, k, v = x w_qkv^T + b_qkv projected
+ * window by window inside the kernel (TERRA page, abstract: Swin blocks).
+ * Same x, w_qkv, b_qkv and bias_table as swa_layer_forward; out: [B][T][H][W]
+ * [heads][head_dim] in the handle's dtype, 16-byte aligned, every real token
+ * written; it must not overlap an input.  Equals the unfused path's o bit for
+ * bit.  Asynchronous on `stream`; allocates nothing.
+ * Errors: INVALID_ARGUMENT (NULL handle or pointer, misalignment, overlap),
+ * UNSUPPORTED (info.layer_path is not SWA_LAYER_FUSED), HIP (launch failure).
+ */
+swa_status swa_layer_attention(swa_handle* h, const void* x, const void* w_qkv, const float* b_qkv,
+                               const float* bias_table, void* out, void* stream);
 
 /*
  * The projection step of swa_layer_forward alone, on any token count:

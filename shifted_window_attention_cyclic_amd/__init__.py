@@ -6,12 +6,12 @@ ctypes binding with the same entry-point names.
 """
 from .binding import (EXPORTS, SwaError, WindowAttention, load_library, make_config,
                       swa_backward, swa_backward_noalloc, swa_create, swa_debug_visibility, swa_destroy, swa_forward, swa_gather,
-                      swa_get_info, swa_layer_forward, swa_projection, swa_scatter,
+                      swa_get_info, swa_layer_attention, swa_layer_forward, swa_projection, swa_scatter,
                       swa_status_string)
 
 __all__ = [
     "EXPORTS", "SwaError", "WindowAttention", "load_library", "make_config", "swa_backward",
     "swa_backward_noalloc", "swa_create",
     "swa_debug_visibility", "swa_destroy", "swa_forward", "swa_gather", "swa_get_info",
-    "swa_layer_forward", "swa_projection", "swa_scatter", "swa_status_string",
+    "swa_layer_attention", "swa_layer_forward", "swa_projection", "swa_scatter", "swa_status_string",
 ]

@@ -18,9 +18,11 @@ SWA_VARIANT_FUSED, SWA_VARIANT_STAGED = 0, 1
 SWA_SCHEDULE_AUTO, SWA_SCHEDULE_STREAM, SWA_SCHEDULE_BLOCK, SWA_SCHEDULE_KEYBLOCK = 0, 1, 2, 3
 SCHEDULES = {"auto": SWA_SCHEDULE_AUTO, "stream": SWA_SCHEDULE_STREAM, "block": SWA_SCHEDULE_BLOCK,
              "keyblock": SWA_SCHEDULE_KEYBLOCK}
+SWA_LAYER_AUTO, SWA_LAYER_FUSED, SWA_LAYER_UNFUSED = 0, 1, 2
+LAYER_PATHS = {"auto": SWA_LAYER_AUTO, "fused": SWA_LAYER_FUSED, "unfused": SWA_LAYER_UNFUSED}
 
-EXPORTS = ("swa_create", "swa_forward", "swa_backward", "swa_backward_noalloc", "swa_layer_forward", "swa_projection", "swa_destroy",
-           "swa_get_info", "swa_status_string",
+EXPORTS = ("swa_create", "swa_forward", "swa_backward", "swa_backward_noalloc", "swa_layer_forward",
+           "swa_layer_attention", "swa_projection", "swa_destroy", "swa_get_info", "swa_status_string",
            "swa_last_error", "swa_gather", "swa_scatter", "swa_debug_visibility")
 
 
@@ -30,7 +32,7 @@ class swa_config(ctypes.Structure):
         ("grid", ctypes.c_int * 3), ("padded", ctypes.c_int * 3), ("window", ctypes.c_int * 3),
         ("shift", ctypes.c_int * 3), ("cyclic", ctypes.c_int * 3),
         ("dtype", ctypes.c_int), ("scale", ctypes.c_float), ("variant", ctypes.c_int),
-        ("schedule", ctypes.c_int),
+        ("schedule", ctypes.c_int), ("layer", ctypes.c_int),
     ]
 
 
@@ -42,6 +44,7 @@ class swa_info(ctypes.Structure):
         ("schedule", ctypes.c_int32), ("workgroups", ctypes.c_int32),
         ("backward_workspace_bytes", ctypes.c_size_t), ("layer_workspace_bytes", ctypes.c_size_t),
         ("layer_flops", ctypes.c_double), ("backward_schedule", ctypes.c_int32),
+        ("layer_path", ctypes.c_int32),
     ]
 
 
@@ -73,6 +76,8 @@ def load_library(path: str = LIBRARY):
     lib.swa_backward_noalloc.restype = st
     lib.swa_layer_forward.argtypes = [vp] * 10
     lib.swa_layer_forward.restype = st
+    lib.swa_layer_attention.argtypes = [vp] * 7
+    lib.swa_layer_attention.restype = st
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.swa_projection.argtypes = [st, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp]
     lib.swa_projection.restype = st
@@ -101,7 +106,7 @@ def _check(status):
                                f"{lib.swa_last_error().decode()}")
 
 
-def make_config(problem, variant: str = "fused", schedule: str = "auto") -> swa_config:
+def make_config(problem, variant: str = "fused", schedule: str = "auto", layer: str = "auto") -> swa_config:
     """swa_config from a problem description (attributes batch, heads, head_dim,
     extent, padded, window, shift, cyclic, dtype ("f32"/"bf16"), scale)."""
     c = swa_config()
@@ -116,6 +121,7 @@ def make_config(problem, variant: str = "fused", schedule: str = "auto") -> swa_
     c.scale = float(problem.scale or 0.0)
     c.variant = {"fused": SWA_VARIANT_FUSED, "staged": SWA_VARIANT_STAGED}[variant]
     c.schedule = SCHEDULES[schedule]
+    c.layer = LAYER_PATHS[layer]
     return c
 
 
@@ -189,6 +195,14 @@ def swa_layer_forward(handle, x, w_qkv, b_qkv, table, w_o, b_o, y, workspace, st
                                             _dev(y, "y", dt), _dev(workspace, "workspace"), _stream(stream)))
 
 
+def swa_layer_attention(handle, x, w_qkv, b_qkv, table, out, stream=None) -> None:
+    dt = x.dtype
+    f32 = torch.float32
+    _check(load_library().swa_layer_attention(handle, _dev(x, "x"), _dev(w_qkv, "w_qkv", dt),
+                                              _dev(b_qkv, "b_qkv", f32), _dev(table, "table", f32),
+                                              _dev(out, "out", dt), _stream(stream)))
+
+
 def swa_projection(x, w, bias, outputs, split=None, stream=None) -> None:
     """outputs[n // split][m, n % split] = (x @ w.T + bias)[m, n]; x [rows, in],
     w [out, in], bias [out] fp32, outputs: 1 to 3 tensors of rows * split
@@ -231,10 +245,10 @@ def swa_debug_visibility(handle, window_index: int, dev_out, stream=None) -> Non
 class WindowAttention:
     """Owns one handle for a problem; checks tensor shapes before each call."""
 
-    def __init__(self, problem, variant: str = "fused", schedule: str = "auto"):
+    def __init__(self, problem, variant: str = "fused", schedule: str = "auto", layer: str = "auto"):
         self.problem = problem
         self.dtype = torch.float32 if problem.dtype == "f32" else torch.bfloat16
-        self.handle = swa_create(make_config(problem, variant, schedule))
+        self.handle = swa_create(make_config(problem, variant, schedule, layer))
         self.info = swa_get_info(self.handle)
 
     @property
@@ -282,7 +296,8 @@ class WindowAttention:
         return self.problem.heads * self.problem.head_dim
 
     def layer_workspace(self, device="cuda"):
-        """A workspace for layer_forward (q, k, v and o of the layer, in that order)."""
+        """A workspace for layer_forward (o of the layer on the fused path; q, k, v and o
+        on the unfused one)."""
         n = self.info.layer_workspace_bytes
         return torch.empty(n // (2 if self.dtype == torch.bfloat16 else 4), dtype=self.dtype, device=device)
 

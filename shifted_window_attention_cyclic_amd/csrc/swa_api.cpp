@@ -14,6 +14,7 @@
 #include <string>
 
 #include "swa_geometry.h"
+#include "swa_layer.h"
 #include "swa_projection.h"
 #include "swa_backward.h"
 
@@ -24,6 +25,7 @@ struct swa_handle {
     int device;
     int schedule;       // bf16: SWA_SCHEDULE_STREAM, _BLOCK or _KEYBLOCK; fp32: 0
     int blocks;         // bf16: workgroups per attention launch
+    int layer_path;     // SWA_LAYER_FUSED or SWA_LAYER_UNFUSED
     size_t wm_bytes;    // bytes of one window-major tensor
     void* workspace;    // staged variant: q, k, v, o window-major tensors
     float* bias_hm;     // key-blocked schedule: head-major copy of the bias table
@@ -63,6 +65,8 @@ swa_status validate(const swa_config* c, swa::Geometry* g, int* elem_bytes) {
     if (c->schedule != SWA_SCHEDULE_AUTO && c->schedule != SWA_SCHEDULE_STREAM && c->schedule != SWA_SCHEDULE_BLOCK &&
         c->schedule != SWA_SCHEDULE_KEYBLOCK)
         return fail(SWA_ERR_INVALID_ARGUMENT, "unknown schedule");
+    if (c->layer != SWA_LAYER_AUTO && c->layer != SWA_LAYER_FUSED && c->layer != SWA_LAYER_UNFUSED)
+        return fail(SWA_ERR_INVALID_ARGUMENT, "unknown layer path");
     if (c->head_dim < 1) return fail(SWA_ERR_INVALID_ARGUMENT, "head_dim must be >= 1");
     if (!(isfinite(c->scale)) || c->scale < 0.f)
         return fail(SWA_ERR_INVALID_ARGUMENT, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
@@ -246,6 +250,10 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
         if (ss != SWA_OK) return ss;
     }
     if ((e = swa::prepare_backward_kernels(max_lds)) != hipSuccess) return fail_hip(e, "hipFuncSetAttribute");
+    if ((e = swa::prepare_layer_kernels(max_lds)) != hipSuccess) return fail_hip(e, "hipFuncSetAttribute");
+    const bool fused_layer = cfg->dtype == SWA_BF16 && swa::layer_fused_fits(g);
+    if (cfg->layer == SWA_LAYER_FUSED && !fused_layer)
+        return fail(SWA_ERR_UNSUPPORTED, "the fused layer kernel does not take this problem");
     int schedule = 0, blocks = 0;
     if (cfg->dtype == SWA_BF16) {
         // AUTO: the streaming schedule, else the per-unit one, else the key-blocked one,
@@ -277,6 +285,8 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
     h->device = dev;
     h->schedule = schedule;
     h->blocks = blocks;
+    // AUTO takes the unfused layer: it is the faster one on every measured shape
+    h->layer_path = fused_layer && cfg->layer == SWA_LAYER_FUSED ? SWA_LAYER_FUSED : SWA_LAYER_UNFUSED;
     h->wm_bytes = (size_t)g.windows * g.N * g.row * eb;
     h->workspace = nullptr;
     h->bias_hm = nullptr;
@@ -330,7 +340,8 @@ swa_status swa_get_info(const swa_handle* h, swa_info* info) {
     info->workgroups = bf16 ? h->blocks : 0;
     info->backward_workspace_bytes = swa::backward_fits(g, bf16) ? swa::backward_workspace_bytes(g) : 0;
     info->backward_schedule = swa::backward_schedule(g, bf16);
-    info->layer_workspace_bytes = 4 * io_bytes(h);
+    info->layer_path = h->layer_path;
+    info->layer_workspace_bytes = (h->layer_path == SWA_LAYER_FUSED ? 1 : 4) * io_bytes(h);
     info->layer_flops = 8.0 * (double)info->tokens * g.row * (double)g.row + info->nominal_flops;
     return SWA_OK;
 }
@@ -464,25 +475,53 @@ swa_status swa_layer_forward(swa_handle* h, const void* x, const void* w_qkv, co
     const size_t nt = (size_t)g.table_size * g.heads * sizeof(float);
     // y is disjoint from every other argument; the workspace from every input
     const void* all[] = {x, w_qkv, b_qkv, bias_table, w_o, b_o, y, workspace};
+    const size_t nws = (h->layer_path == SWA_LAYER_FUSED ? 1 : 4) * n;
     const size_t len[] = {n, 3 * (size_t)C * C * eb, 3 * (size_t)C * 4, nt, (size_t)C * C * eb, (size_t)C * 4, n,
-                          4 * n};
+                          nws};
     for (int i = 6; i < 8; i++)
         for (int j = 0; j < 8; j++)
             if (j != i && overlap(all[i], len[i], all[j], len[j]))
                 return fail(SWA_ERR_INVALID_ARGUMENT, "y or the workspace overlaps another argument");
     hipStream_t s = (hipStream_t)stream;
+    const bool bf16 = h->cfg.dtype == SWA_BF16;
+    if (h->layer_path == SWA_LAYER_FUSED) {
+        // q, k, v projected inside the attention kernel; o through the workspace
+        hipError_t e = swa::launch_layer_qkv_attention(g, (const uint16_t*)x, (const uint16_t*)w_qkv, b_qkv,
+                                                       bias_table, (uint16_t*)workspace, s);
+        if (e != hipSuccess) return fail_hip(e, "fused layer launch");
+        e = swa::launch_projection(true, workspace, w_o, b_o, M, C, C, C, y, y, y, s);
+        return e == hipSuccess ? SWA_OK : fail_hip(e, "projection launch");
+    }
     char* ws = (char*)workspace;
     void* q = ws;
     void* k = ws + n;
     void* v = ws + 2 * n;
     void* o = ws + 3 * n;
-    const bool bf16 = h->cfg.dtype == SWA_BF16;
     hipError_t e = swa::launch_projection(bf16, x, w_qkv, b_qkv, M, 3 * C, C, C, q, k, v, s);
     if (e != hipSuccess) return fail_hip(e, "projection launch");
     swa_status st = swa_forward(h, q, k, v, bias_table, o, stream);
     if (st != SWA_OK) return st;
     e = swa::launch_projection(bf16, o, w_o, b_o, M, C, C, C, y, y, y, s);
     return e == hipSuccess ? SWA_OK : fail_hip(e, "projection launch");
+}
+
+swa_status swa_layer_attention(swa_handle* h, const void* x, const void* w_qkv, const float* b_qkv,
+                               const float* bias_table, void* out, void* stream) {
+    if (!h || !x || !w_qkv || !b_qkv || !bias_table || !out) return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (!aligned(x, 16) || !aligned(w_qkv, 16) || !aligned(out, 16) || !aligned(b_qkv, 4) || !aligned(bias_table, 4))
+        return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned pointer (x, w_qkv and out need 16 bytes)");
+    if (h->layer_path != SWA_LAYER_FUSED) return fail(SWA_ERR_UNSUPPORTED, "the handle's layer path is not fused");
+    const swa::Geometry& g = h->g;
+    const int C = g.row;
+    const size_t n = io_bytes(h);
+    const size_t nt = (size_t)g.table_size * g.heads * sizeof(float);
+    const void* ins[] = {x, w_qkv, b_qkv, bias_table};
+    const size_t len[] = {n, 3 * (size_t)C * C * 2, 3 * (size_t)C * 4, nt};
+    for (int j = 0; j < 4; j++)
+        if (overlap(out, n, ins[j], len[j])) return fail(SWA_ERR_INVALID_ARGUMENT, "out overlaps an input");
+    const hipError_t e = swa::launch_layer_qkv_attention(g, (const uint16_t*)x, (const uint16_t*)w_qkv, b_qkv,
+                                                         bias_table, (uint16_t*)out, (hipStream_t)stream);
+    return e == hipSuccess ? SWA_OK : fail_hip(e, "fused layer launch");
 }
 
 swa_status swa_projection(swa_dtype dtype, const void* x, const void* w, const float* bias, int64_t rows,

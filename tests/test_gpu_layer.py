@@ -3,7 +3,12 @@ oracle (oracle.layer_forward): y element by element, and the q, k, v the
 query/key/value projection leaves in the workspace, with the attention's
 metric max|G_gpu - G_ref| / max|G_ref| <= 1e-2 for bf16 and <= 1e-5 for fp32.
 Grids are chosen so that the 256-token and 256-feature tiles of the
-projection kernel end ragged (partial last tiles in both directions)."""
+projection kernel end ragged (partial last tiles in both directions).
+
+The layer runs on two paths: unfused (projection GEMM, attention, projection
+GEMM) and fused (q, k, v projected per window inside the attention kernel,
+then the output projection).  The fused path must give the unfused path's y
+and attention output bit for bit, besides matching the oracle."""
 import ctypes
 
 import numpy as np
@@ -12,7 +17,9 @@ import torch
 
 import oracle
 from helpers import TOL, host_f32, rel_err, sample_tokens
-from shifted_window_attention_cyclic_amd import SwaError, WindowAttention, load_library, swa_projection
+from shifted_window_attention_cyclic_amd import (SwaError, WindowAttention, load_library, swa_layer_attention,
+                                                  swa_projection)
+from shifted_window_attention_cyclic_amd.binding import SWA_LAYER_FUSED, SWA_LAYER_UNFUSED
 from shifted_window_attention_cyclic_amd.inputs import WORKLOADS, Problem, make_layer_inputs
 from test_gpu_parity import EDGE, SMALL
 
@@ -38,8 +45,8 @@ def _host(x):
     return {n: host_f32(t) for n, t in x.items()}
 
 
-def _run(p, x, variant="fused"):
-    att = WindowAttention(p, variant)
+def _run(p, x, variant="fused", layer="auto"):
+    att = WindowAttention(p, variant, layer=layer)
     d = {n: t.cuda() for n, t in x.items()}
     ws = att.layer_workspace()
     y = att.layer_forward(d["x"], d["w_qkv"], d["b_qkv"], d["table"], d["w_o"], d["b_o"], workspace=ws)
@@ -58,7 +65,7 @@ def test_layer_small_grid(name):
     say(f"[layer] {name} dtype={p.dtype} B={p.batch} grid={p.extent} pad={p.padded} win={p.window} "
         f"shift={p.shift} heads={p.heads}x{p.head_dim}")
     x = make_layer_inputs(p)
-    att, d, y, ws = _run(p, x)
+    att, d, y, ws = _run(p, x, layer="unfused")
     h = _host(x)
     ref = oracle.layer_forward(p, h["x"], h["w_qkv"], h["b_qkv"], h["table"], h["w_o"], h["b_o"])
     err = rel_err(host_f32(y), ref)
@@ -75,19 +82,72 @@ def test_layer_small_grid(name):
     # o is the attention forward pass of those q, k, v, bit for bit
     assert torch.equal(o, att.forward(q, k, v, d["table"]))
     att.close()
+    # the fused path, where it takes the problem: the same y and o bit for bit
+    try:
+        af, _, yf, wsf = _run(p, x, layer="fused")
+    except SwaError:
+        # the fused kernel takes bf16 windows of up to 9 query tiles (5 for 128-wide
+        # heads) when C is a multiple of its stage depth (64 channels; 32 for 128-wide heads)
+        stage = 32 if p.head_dim == 128 else 64
+        tiles = (p.window_tokens + 15) // 16
+        takes = (p.dtype == "bf16" and tiles <= (5 if p.head_dim == 128 else 9)
+                 and (p.heads * p.head_dim) % stage == 0)
+        assert not takes, "the fused kernel should take this problem"
+        return
+    assert af.info.layer_path == SWA_LAYER_FUSED
+    say(f"  fused path: y {'==' if torch.equal(yf, y) else '!='} unfused y")
+    assert torch.equal(wsf[:o.numel()].view(o.shape), o)
+    assert torch.equal(yf, y)
+    # the fused path's first launch alone
+    o2 = torch.full_like(o, float("nan"))
+    swa_layer_attention(af.handle, d["x"], d["w_qkv"], d["b_qkv"], d["table"], o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o)
+    af.close()
 
 
-def test_layer_full_size_180x360():
-    """180x360 at full size: every token against the oracle."""
-    p = WORKLOADS["c2_bf16_180x360"]
+@pytest.mark.parametrize("name", ["c2_bf16_180x360", "c3_bf16_540x1080", "c6_bf16_180x360_pad184_d128"])
+def test_layer_full_size_every_token(name):
+    """Full size, fused path: every token against the oracle, and the
+    unfused path's y bit for bit."""
+    p = WORKLOADS[name]
     x = make_layer_inputs(p)
-    att, _, y, _ = _run(p, x)
+    att, _, y, _ = _run(p, x, layer="fused")
+    assert att.info.layer_path == SWA_LAYER_FUSED
+    att.close()
     h = _host(x)
     ref = oracle.layer_forward(p, h["x"], h["w_qkv"], h["b_qkv"], h["table"], h["w_o"], h["b_o"])
     err = rel_err(host_f32(y), ref)
-    say(f"[layer full 180x360] rel err {err:.3e}")
+    say(f"[layer full {name}] rel err {err:.3e}")
     assert err <= TOL["bf16"]
-    att.close()
+    del ref
+    au, _, yu, _ = _run(p, x, layer="unfused")
+    assert torch.equal(y, yu)
+    au.close()
+
+
+def test_layer_path_reported():
+    """AUTO takes the unfused layer; an explicit fused request is honoured where
+    the kernel takes the problem (windows of up to 144 tokens, bf16) and
+    refused elsewhere.  The fused path needs a quarter of the workspace."""
+    fused_ok = {"c2_bf16_180x360": True, "c3_bf16_540x1080": True, "c4_bf16_181x360_pad190": True,
+                "c6_bf16_180x360_pad184_d128": True, "c5_bf16_4x180x360_3d": False,
+                "c7_bf16_180x384_pad192_d128_w32": False, "c1_f32_16x32": False}
+    for name, ok in fused_ok.items():
+        p = WORKLOADS[name]
+        n = p.tokens * p.heads * p.head_dim * p.elem_bytes
+        att = WindowAttention(p)
+        assert att.info.layer_path == SWA_LAYER_UNFUSED, name
+        assert att.info.layer_workspace_bytes == 4 * n, name
+        att.close()
+        if ok:
+            att = WindowAttention(p, layer="fused")
+            assert att.info.layer_path == SWA_LAYER_FUSED, name
+            assert att.info.layer_workspace_bytes == n, name
+            att.close()
+        else:
+            with pytest.raises(SwaError):
+                WindowAttention(p, layer="fused")
 
 
 @pytest.mark.parametrize("name", ["c3_bf16_540x1080", "c4_bf16_181x360_pad190", "c5_bf16_4x180x360_3d",
