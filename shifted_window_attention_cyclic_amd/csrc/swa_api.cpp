@@ -154,9 +154,10 @@ swa_status validate(const swa_config* c, swa::Geometry* g, int* elem_bytes) {
     *elem_bytes = c->dtype == SWA_F32 ? 4 : 2;
 
     if (c->dtype == SWA_BF16) {
-        if (!swa::bf16_stream_fits(G) && !swa::bf16_block_fits(G) && !swa::bf16_kblock_fits(G))
+        if (!swa::bf16_stream_fits(G, c->variant == SWA_VARIANT_STAGED) && !swa::bf16_block_fits(G) &&
+            !swa::bf16_kblock_fits(G))
             return fail(SWA_ERR_UNSUPPORTED, "window too large for the LDS of every bf16 schedule");
-    } else if (swa::attention_lds_bytes(G, false) > 160 * 1024) {
+    } else if (swa::attention_lds_bytes(G, false, false) > 160 * 1024) {
         return fail(SWA_ERR_UNSUPPORTED, "window too large for the LDS of one workgroup");
     }
     return SWA_OK;
@@ -236,7 +237,8 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
     int max_lds = optin > per_cu ? optin : per_cu;
     if (max_lds < 64 * 1024) max_lds = 64 * 1024;
     if (max_lds > 160 * 1024) max_lds = 160 * 1024;
-    const size_t need = swa::attention_lds_bytes(g, cfg->dtype == SWA_BF16);
+    const bool staged = cfg->variant == SWA_VARIANT_STAGED;
+    const size_t need = swa::attention_lds_bytes(g, cfg->dtype == SWA_BF16, staged);
     if (need > (size_t)max_lds) {
         char buf[160];
         snprintf(buf, sizeof buf, "window needs %zu bytes of LDS, the device allows %d", need, max_lds);
@@ -258,7 +260,8 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
     if (cfg->dtype == SWA_BF16) {
         // AUTO: the streaming schedule, else the per-unit one, else the key-blocked one,
         // each only when its workgroup fits and can be resident
-        const bool fit[4] = {false, swa::bf16_stream_fits(g), swa::bf16_block_fits(g), swa::bf16_kblock_fits(g)};
+        const bool fit[4] = {false, swa::bf16_stream_fits(g, staged), swa::bf16_block_fits(g),
+                             swa::bf16_kblock_fits(g)};
         const int order[3] = {SWA_SCHEDULE_STREAM, SWA_SCHEDULE_BLOCK, SWA_SCHEDULE_KEYBLOCK};
         for (int sc : order) {
             if (cfg->schedule != SWA_SCHEDULE_AUTO && cfg->schedule != sc) continue;

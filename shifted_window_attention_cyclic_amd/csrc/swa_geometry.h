@@ -148,9 +148,10 @@ hipError_t launch_attention_bf16(const Geometry& g, bool stream, int blocks, boo
                                  uint16_t* out, hipStream_t s);
 // LDS bytes the attention kernels need for g (bf16: the smallest among the
 // schedules that take the window; (size_t)-1 when none does).
-size_t attention_lds_bytes(const Geometry& g, bool bf16);
-// Whether the streaming bf16 schedule (persistent blocks, two LDS stages) fits.
-bool bf16_stream_fits(const Geometry& g);
+size_t attention_lds_bytes(const Geometry& g, bool bf16, bool staged);
+// Whether the streaming bf16 schedule (persistent blocks, two LDS stages) fits,
+// for the fused or the staged variant.
+bool bf16_stream_fits(const Geometry& g, bool staged);
 // Whether the per-unit bf16 schedule (a window's K and V in one workgroup's LDS) fits.
 bool bf16_block_fits(const Geometry& g);
 // Workgroups one bf16 attention launch uses (0: the kernel does not fit).

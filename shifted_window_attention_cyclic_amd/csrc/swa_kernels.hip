@@ -650,8 +650,6 @@ attn_bf16_stream_kernel(
         constexpr int MAXC = loader_max_copies<D, KT_FIXED, NL>();
         constexpr int NCOPY = KT_FIXED * 16 * (D / 8) / 64; // copies per tensor (fixed tile counts)
         constexpr bool EX = KT_FIXED > 0 && NCOPY % NL == 0;
-        const __amdgpu_buffer_rsrc_t ors =
-            __builtin_amdgcn_make_buffer_rsrc((void*)out, 0, (int)stream_tensor_bytes(g, staged), kBufferWord3);
         const int j = wave - NWAVES;
         const LoaderRange R = loader_range(g, L, j, NL);
         // copies with a unit's K and Q, with its V, and O stores (one per 1 KB of rows)
@@ -685,7 +683,7 @@ attn_bf16_stream_kernel(
             loader_barrier();
             if (has_next) stream_issue<D, MAXC, EX>(R, head(un), ov, v, smem + L.v0 + ((iter + 1) % kBufs) * L.tb);
             if (iter >= 1) // O of the previous unit, staged by the compute waves before A
-                stream_store_o<D, MAXC, EX>(g, L, smem, ors, R, lane, u - per, (iter - 1) % kTableSlots, staged);
+                stream_store_o<D, MAXC, EX>(g, L, smem, out, R, lane, u - per, (iter - 1) % kTableSlots, staged);
             if (un2 < uend) stream_offsets<D, MAXC, EX>(g, L, smem, R, lane, (iter + 2) % kTableSlots, okq);
             // B: V of unit u has landed once at most O(u-2) stores, K/Q(un), V(un)
             // and O(u-1) stores remain
@@ -702,7 +700,7 @@ attn_bf16_stream_kernel(
         }
         // O of the last unit, staged before the final barrier
         loader_barrier();
-        stream_store_o<D, MAXC, EX>(g, L, smem, ors, R, lane, u, (int)((uend - 1 - u0) / per) % kTableSlots, staged);
+        stream_store_o<D, MAXC, EX>(g, L, smem, out, R, lane, u, (int)((uend - 1 - u0) / per) % kTableSlots, staged);
     } else {
         // ---- compute waves
         const int KT = KT_FIXED > 0 ? KT_FIXED : NP / 16;
@@ -1151,11 +1149,11 @@ hipError_t launch_attention_kblock(const Geometry& g, bool staged, const uint16_
     return hipGetLastError();
 }
 
-size_t attention_lds_bytes(const Geometry& g, bool bf16) {
+size_t attention_lds_bytes(const Geometry& g, bool bf16, bool staged) {
     if (!bf16) return f32_lds_bytes(g);
     // the smallest footprint among the bf16 schedules that can take the window
     size_t best = (size_t)-1;
-    if (bf16_stream_fits(g)) best = stream_lds(g).total;
+    if (bf16_stream_fits(g, staged)) best = stream_lds(g).total;
     if (bf16_block_fits(g) && bf16_lds(g).total < best) best = bf16_lds(g).total;
     if (bf16_kblock_fits(g) && kb_lds(g).total < best) best = kb_lds(g).total;
     return best;
@@ -1240,14 +1238,15 @@ bool bf16_block_fits(const Geometry& g) {
     return g.N <= 512 && bf16_lds(g).total <= (size_t)kLdsBytes && (rows > wrows ? rows : wrows) < kRowMask;
 }
 
-bool bf16_stream_fits(const Geometry& g) {
-    const int64_t rows = (int64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
-    const int64_t wrows = g.windows * g.N;
+bool bf16_stream_fits(const Geometry& g, bool staged) {
+    // the layout the kernel reads and writes: real tokens (fused) or window slots (staged)
+    const int64_t rows = staged ? g.windows * g.N : (int64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
     const int KT = (g.N + 15) / 16;
-    // rows + 1 fit the packed table word; buffer offsets of both layouts stay below 2^31
+    // row + 1 fits the packed table word; the loaders' element offsets fit 32 bits; the
+    // O stores' buffer offsets, from the start of the unit's batch item, stay below 2^31
     return stream_lds(g).total <= (size_t)kLdsBytes && KT <= (g.head_dim == 128 ? kStreamMaxTiles128 : kStreamMaxTiles) &&
-           (rows > wrows ? rows : wrows) < kRowMask && stream_tensor_bytes(g, false) < kOutOfRange &&
-           stream_tensor_bytes(g, true) < kOutOfRange;
+           rows < kRowMask && (uint64_t)rows * (uint64_t)g.row < ((uint64_t)1 << 32) &&
+           stream_item_bytes(g, staged) < kOutOfRange;
 }
 
 hipError_t bf16_plan(const Geometry& g, bool stream, int* blocks) {

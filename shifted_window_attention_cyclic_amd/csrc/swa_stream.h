@@ -472,19 +472,33 @@ __device__ inline void stream_pv(const StreamLds& L, unsigned char* smem, int la
     }
 }
 
+// Rows of one batch item in the tensors the streaming schedule reads and
+// writes (real-token layout, or window-major when staged), and its bytes.
+__host__ __device__ inline uint64_t stream_item_rows(const Geometry& g, bool staged) {
+    return staged ? (uint64_t)g.nW * g.N : (uint64_t)g.ext[0] * g.ext[1] * g.ext[2];
+}
+__host__ __device__ inline uint64_t stream_item_bytes(const Geometry& g, bool staged) {
+    return stream_item_rows(g, staged) * (uint64_t)g.row * 2;
+}
+
 // Loader j's stores of a unit's O (table in slot s) from the LDS staging
 // buffer: whole 128-byte token rows of its own row range, to the real token or,
 // in the staged layout, also to pad slots (zeros); other lanes store out of
-// range, which the buffer range check drops.
+// range, which the buffer range check drops.  The buffer resource starts at
+// the unit's batch item, so offsets stay below 2^31 whatever the batch.
 template <int D, int MAXC, bool EXACT>
 __device__ inline void stream_store_o(const Geometry& g, const StreamLds& L, const unsigned char* smem,
-                                      __amdgpu_buffer_rsrc_t ors, LoaderRange R, int lane, uint32_t uu, int s,
+                                      uint16_t* __restrict__ out, LoaderRange R, int lane, uint32_t uu, int s,
                                       int staged) {
     constexpr int CH = D / 8;
     constexpr int RPC = 64 / CH;
     const int* tw = (const int*)(smem + L.slot0 + s * L.slot_bytes);
     const uint16_t* Os = (const uint16_t*)(smem + L.o0);
     const Unit U = decode_unit(g, uu);
+    const uint64_t item_rows = stream_item_rows(g, staged);
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(out + (uint64_t)U.b * item_rows * (uint32_t)g.row), 0, (int)stream_item_bytes(g, staged), kBufferWord3);
+    const int row0 = (int)((uint64_t)U.b * item_rows); // first row of the batch item
     const int c = lane % CH;
     u32x4 val[MAXC];
     int rm[MAXC];
@@ -501,18 +515,12 @@ __device__ inline void stream_store_o(const Geometry& g, const StreamLds& L, con
         if (EXACT || R.c0 + i < R.c1) {
             const int m = (R.c0 + i) * RPC + lane / CH;
             const int orow = rm[i] >= 0 ? rm[i] : (staged && m < g.N ? (int)(U.wi * (uint32_t)g.N + m) : -1);
-            const uint32_t ob = orow >= 0 ? ((uint32_t)orow * (uint32_t)g.row + U.h * D + c * 8) * 2 : kOutOfRange;
+            const uint32_t ob =
+                orow >= 0 ? ((uint32_t)(orow - row0) * (uint32_t)g.row + U.h * D + c * 8) * 2 : kOutOfRange;
             __builtin_amdgcn_raw_buffer_store_b128(val[i], ors, ob, 0, kNonTemporal);
         }
     }
 }
 
-// Bytes of each tensor the streaming schedule writes through a buffer
-// resource (real-token layout, or window-major when staged).
-__host__ __device__ inline uint64_t stream_tensor_bytes(const Geometry& g, bool staged) {
-    const uint64_t rows = staged ? (uint64_t)g.windows * g.N
-                                 : (uint64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
-    return rows * (uint64_t)g.row * 2;
-}
 
 } // namespace swa

@@ -93,6 +93,9 @@ WORKLOADS = {
     "c7_bf16_180x384_pad192_d128_w32": Problem("c7_bf16_180x384_pad192_d128_w32", "bf16", 1, 64, 128,
                                                (1, 180, 384), (1, 192, 384), (1, 32, 32), (0, 16, 16),
                                                seed=1006),
+    # the 1/12 degree field with a batch of 4: 2.39 GB per tensor, past 2^31 bytes
+    "c3b4_bf16_540x1080": Problem("c3b4_bf16_540x1080", "bf16", 4, 8, 64, (1, 540, 1080),
+                                  (1, 540, 1080), (1, 12, 12), (0, 6, 6), seed=1007),
 }
 ORDER = list(WORKLOADS)
 

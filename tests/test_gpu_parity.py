@@ -147,6 +147,34 @@ def test_parity_full_grid_every_token(name):
     assert torch.isfinite(out.float()).all()
 
 
+def test_batch_past_2gib_keeps_the_streaming_schedule():
+    """540x1080 with a batch of 4 (2.39 GB per tensor): the streaming schedule
+    still takes it (its O stores address each batch item from that item's
+    start), sampled tokens of every batch item match the oracle, and every
+    token of the last batch item does."""
+    p = WORKLOADS["c3b4_bf16_540x1080"]
+    x, d = device_inputs(p)
+    att = WindowAttention(p)
+    assert att.info.schedule == 1  # SWA_SCHEDULE_STREAM
+    out = att.forward(d["q"], d["k"], d["v"], d["table"])
+    torch.cuda.synchronize()
+    att.close()
+    del d
+    per = p.tokens // p.batch
+    idx = np.concatenate([sample_tokens(p.with_(batch=1), count=128) + b * per for b in range(p.batch)])
+    ref = oracle_at(p, x, idx)
+    got = host_f32(out).reshape(p.tokens, p.heads, p.head_dim)[idx]
+    err = rel_err(got, ref)
+    say(f"[batch 4] {idx.size} sampled tokens, rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    last = np.arange((p.batch - 1) * per, p.batch * per)
+    ref = oracle_at(p, x, last)
+    err = rel_err(host_f32(out).reshape(p.tokens, p.heads, p.head_dim)[last], ref)
+    say(f"  last batch item, every token: rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert torch.isfinite(out.float()).all()
+
+
 def test_fp32_full_workload_matches_oracle_everywhere():
     p = WORKLOADS["c1_f32_16x32"]
     x, d = device_inputs(p)
