@@ -50,6 +50,10 @@ EDGE = {
     "lat_cyclic_too": _edge("latcyc", "bf16", 1, 4, 32, (1, 24, 24), (1, 24, 24), (1, 8, 8), (0, 4, 4), (0, 1, 1)),
     "shift_not_half": _edge("s3", "bf16", 1, 2, 64, (1, 20, 30), (1, 20, 30), (1, 10, 10), (0, 3, 7)),
     "d32_n288_3d": _edge("d32n288", "bf16", 1, 3, 32, (4, 24, 24), (4, 24, 24), (2, 12, 12), (1, 6, 6)),
+    # 32-wide heads, an even head count: 7-tile windows, width 10 (no 4-key bias runs), latitude padded
+    "d32_n100_pad": _edge("d32p100", "bf16", 2, 4, 32, (1, 17, 30), (1, 20, 30), (1, 10, 10), (0, 5, 5)),
+    # and an odd head count
+    "d32_odd_heads": _edge("d32odd", "bf16", 1, 5, 32, (1, 24, 36), (1, 24, 36), (1, 12, 12), (0, 6, 6)),
     "n512_3d_pad": _edge("n512", "bf16", 1, 2, 64, (3, 16, 32), (4, 16, 32), (2, 16, 16), (1, 8, 8)),
     "time_pad": _edge("tpad", "bf16", 2, 2, 64, (3, 12, 24), (4, 12, 24), (2, 6, 6), (1, 3, 3)),
     "f32_d64_3d_pad": _edge("f32d64", "f32", 2, 2, 64, (3, 10, 16), (4, 12, 16), (2, 4, 8), (1, 2, 4)),
