@@ -195,6 +195,8 @@ def main():
                          "passed, so that clocks have settled before the timed steps")
     ap.add_argument("--workload", default="c3_bf16_540x1080")
     ap.add_argument("--variant", default="fused", choices=["fused", "staged"])
+    ap.add_argument("--schedule", default="auto", choices=["auto", "stream", "block", "keyblock"],
+                    help="the bf16 attention schedule (forward and backward passes)")
     ap.add_argument("--cpu-rows", type=int, default=1 << 30,
                     help="latitude rows in the CPU-baseline sample (default: all that keep it "
                          "near 4e11 nominal FLOPs)")
@@ -225,7 +227,7 @@ def main():
         return run_layer(args)
     p = WORKLOADS[args.workload]
     x = make_inputs(p)
-    att = WindowAttention(p, args.variant)
+    att = WindowAttention(p, args.variant, args.schedule)
     info = att.info
     set_bytes = info.algorithmic_bytes
     nsets = max(1, min(8, math.ceil(3 * MALL_BYTES / set_bytes)))
