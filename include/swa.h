@@ -299,23 +299,37 @@ const char* swa_status_string(swa_status s);
 const char* swa_last_error(void);
 
 /*
- * The route into the window layout alone (pad, roll by -shift, partition):
- * src [B][T][H][W][heads][head_dim] -> dst window-major (pad slots zeroed).
- * Same pointer rules as swa_forward; dst holds info.window_major_elems elements.
+ * The route into the window layout alone (TERRA page, abstract: tokens leave
+ * the spatial layout for window layouts; Fig. 5 caption: shift token routes;
+ * Table I: the padded resolution H^, W^ the windows tile): pad, roll by
+ * -shift, partition.  src [B][T][H][W][heads][head_dim] -> dst window-major
+ * (pad slots zeroed).  Same pointer rules as swa_forward; dst holds
+ * info.window_major_elems elements.  For tests and for callers that want the
+ * window layout itself.
+ * Errors: INVALID_ARGUMENT (NULL handle or pointer, misalignment, overlap),
+ * HIP (launch failure).
  */
 swa_status swa_gather(swa_handle* h, const void* src, void* dst_window_major, void* stream);
 
 /*
- * The route back alone (un-partition, roll by +shift, crop): window-major src
- * -> dst [B][T][H][W][heads][head_dim].  Pad slots of src are not read.
+ * The route back alone (TERRA page, abstract: tokens return from the window
+ * layout to the spatial layout): un-partition, roll by +shift, crop to the
+ * real resolution (Table I).  Window-major src -> dst
+ * [B][T][H][W][heads][head_dim].  Pad slots of src are not read.
+ * Errors: as swa_gather.
  */
 swa_status swa_scatter(swa_handle* h, const void* src_window_major, void* dst, void* stream);
 
 /*
- * The attention mask of one window, as the attention kernels evaluate it:
- * dev_out[n * N + m] = 1 when key m may be attended by query n of window
- * `window_index` (0 <= window_index < info.windows), else 0; pad queries get
- * all-zero rows.  dev_out: device buffer of N * N bytes.
+ * The attention mask of one window, as the attention kernels evaluate it
+ * (TERRA page, abstract: shifted-window execution; Table I: pad tokens of
+ * the padded resolution): dev_out[n * N + m] = 1 when key m may be attended
+ * by query n of window `window_index` (0 <= window_index < info.windows), that
+ * is when neither is pad and they lie on the same side of the wrap of every
+ * masked axis, else 0; pad queries get all-zero rows.  dev_out: device buffer
+ * of N * N bytes, owned by the caller.
+ * Errors: INVALID_ARGUMENT (NULL handle or pointer, window index out of
+ * range), HIP (launch failure).
  */
 swa_status swa_debug_visibility(swa_handle* h, int64_t window_index, uint8_t* dev_out,
                                 void* stream);
