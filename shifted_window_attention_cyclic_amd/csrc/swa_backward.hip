@@ -796,7 +796,10 @@ __global__ __launch_bounds__((QW + kBwdLoaders) * 64) void attn_bf16_bwd_q_kerne
 }
 
 // KW = bwd_kv_waves(D) compute waves, a 16-key tile each.
-template <int D, int KW>
+// RUNS: how a diagonal of a 16 x 16 tile splits into runs of one table entry:
+// 0, never (the window width is a multiple of 16); 1, at row starts (width of
+// at least 8); 2, wherever the entry changes (any width).
+template <int D, int KW, int RUNS>
 __global__ __launch_bounds__((KW + kBwdLoaders) * 64)
 __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kernel(
     Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -865,7 +868,6 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
             return tr_read(base + row * (D * 2) + k_slot<D>(row, d >> 3) * 16 + (d & 7) * 2);
         };
         float* sc = diag + wave * 2 * DIAG;     // [tile][slot][diagonal + slot]
-        const bool rowtile = g.win[2] % 16 == 0; // 16-token tiles never straddle a window row
         const int dl = lane & 31, tt = lane >> 5; // the diagonal and the tile this lane sums
 
         int slot = 0;
@@ -970,7 +972,7 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
                         if (dl < 31 && n0 < N) {
                             // slot a of this diagonal pairs query n0 + a with key m0 + a - dgl
                             const float* sd = sc + tt * DIAG;
-                            if (rowtile) {
+                            if (RUNS == 0) {
                                 float x[16];
 #pragma unroll
                                 for (int a = 0; a < 16; a++) x[a] = sd[49 * a + dl];
@@ -978,6 +980,60 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
 #pragma unroll
                                 for (int a = 0; a < 16; a++) run += x[a];
                                 atomicAdd(&dtab[qbo[n0] - kbo[m0] + dgl], run);
+                            } else if (RUNS == 1) {
+                                // A window row holds at least 8 tokens, so at most two row
+                                // starts of the queries and two of the keys fall strictly
+                                // inside the diagonal: they cut it into at most five runs
+                                // of one entry each.  The prefix sums of the diagonal go
+                                // back into its own slots (the others stay 0); a run's sum
+                                // is the difference of the prefix sums at its ends, its
+                                // entry the table words at its first slot.
+                                float* sdw = sc + tt * DIAG;
+                                const int alo = dgl > 0 ? dgl : 0, ahi = dgl < 0 ? 16 + dgl : 16;
+                                float pre = 0.f;
+#pragma unroll
+                                for (int half = 0; half < 2; half++) {
+                                    float x[8];
+#pragma unroll
+                                    for (int c = 0; c < 8; c++) x[c] = sd[49 * (8 * half + c) + dl];
+#pragma unroll
+                                    for (int c = 0; c < 8; c++) {
+                                        const int a = 8 * half + c;
+                                        if (a >= alo && a < ahi) sdw[49 * a + dl] = pre;
+                                        pre += x[c];
+                                    }
+                                }
+                                // row starts inside (alo, ahi): the query n0 + a or the key
+                                // m0 + a - dgl at a multiple of the window width
+                                const int w2 = g.win[2];
+                                const int rq = n0 % w2, rk = ((m0 - dgl) % w2 + w2) % w2;
+                                int c[4];
+                                c[0] = rq == 0 ? w2 : w2 - rq;
+                                c[1] = c[0] + w2;
+                                c[2] = rk == 0 ? w2 : w2 - rk;
+                                c[3] = c[2] + w2;
+#pragma unroll
+                                for (int i = 0; i < 4; i++) c[i] = c[i] > alo && c[i] < ahi ? c[i] : ahi;
+                                auto order = [&](int i, int j) __attribute__((always_inline)) {
+                                    const int lo = min(c[i], c[j]), hi = max(c[i], c[j]);
+                                    c[i] = lo;
+                                    c[j] = hi;
+                                };
+                                order(0, 1);
+                                order(2, 3);
+                                order(0, 2);
+                                order(1, 3);
+                                order(1, 2);
+                                float pc[4];
+#pragma unroll
+                                for (int i = 0; i < 4; i++) pc[i] = c[i] < ahi ? sd[49 * c[i] + dl] : pre;
+                                const int st[5] = {alo, c[0], c[1], c[2], c[3]};
+                                const int en[5] = {c[0], c[1], c[2], c[3], ahi};
+                                const float sum[5] = {pc[0], pc[1] - pc[0], pc[2] - pc[1], pc[3] - pc[2], pre - pc[3]};
+#pragma unroll
+                                for (int r = 0; r < 5; r++)
+                                    if (st[r] < en[r])
+                                        atomicAdd(&dtab[qbo[n0 + st[r]] - kbo[m0 + st[r] - dgl]], sum[r]);
                             } else {
                                 float run = 0.f;
                                 int ecur = -1;
@@ -1263,13 +1319,35 @@ hipError_t prepare_backward_kernels(int max_lds) {
                         (const void*)attn_bf16_bwd_q_kernel<128, 4>,  (const void*)attn_bf16_bwd_q_kernel<32, 8>,
                         (const void*)attn_bf16_bwd_q_kernel<64, 8>,   (const void*)attn_bf16_bwd_q_kernel<128, 6>,
                         (const void*)attn_bf16_bwd_q_kernel<32, 6>,   (const void*)attn_bf16_bwd_q_kernel<64, 6>,
-                        (const void*)attn_bf16_bwd_kv_kernel<32, 6>,
-                        (const void*)attn_bf16_bwd_kv_kernel<64, 6>,  (const void*)attn_bf16_bwd_kv_kernel<128, 8>};
+                        (const void*)attn_bf16_bwd_kv_kernel<32, 6, 0>,  (const void*)attn_bf16_bwd_kv_kernel<32, 6, 1>,
+                        (const void*)attn_bf16_bwd_kv_kernel<32, 6, 2>,  (const void*)attn_bf16_bwd_kv_kernel<64, 6, 0>,
+                        (const void*)attn_bf16_bwd_kv_kernel<64, 6, 1>,  (const void*)attn_bf16_bwd_kv_kernel<64, 6, 2>,
+                        (const void*)attn_bf16_bwd_kv_kernel<128, 8, 0>, (const void*)attn_bf16_bwd_kv_kernel<128, 8, 1>,
+                        (const void*)attn_bf16_bwd_kv_kernel<128, 8, 2>};
     for (const void* f : fs) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// The key kernel for g: the head width, and how a tile diagonal of the table
+// gradient splits into runs (window widths that are multiples of 16 never
+// split it; widths of at least 8 split it at row starts only).
+typedef void (*kv_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*, const uint16_t*,
+                     uint16_t*, uint16_t*, const float*, float*, uint32_t, uint32_t);
+
+template <int D, int KW>
+static kv_t bwd_kv_runs(const Geometry& g) {
+    if (g.win[2] % 16 == 0) return attn_bf16_bwd_kv_kernel<D, KW, 0>;
+    if (g.win[2] >= 8) return attn_bf16_bwd_kv_kernel<D, KW, 1>;
+    return attn_bf16_bwd_kv_kernel<D, KW, 2>;
+}
+
+static kv_t bwd_kv_variant(const Geometry& g) {
+    if (g.head_dim == 32) return bwd_kv_runs<32, 6>(g);
+    if (g.head_dim == 64) return bwd_kv_runs<64, 6>(g);
+    return bwd_kv_runs<128, 8>(g);
 }
 
 // The attention gradients of units work0 .. work0 + count - 1: dq, dk, dv of
@@ -1285,8 +1363,6 @@ static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void
         const dim3 qgrid(count * (unsigned)((g.N + QW * 16 - 1) / (QW * 16)));
         typedef void (*qk_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
                              const uint16_t*, uint16_t*, float*, uint32_t, uint32_t);
-        typedef void (*kv_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
-                             const uint16_t*, uint16_t*, uint16_t*, const float*, float*, uint32_t, uint32_t);
         const qk_t fq = g.head_dim == 128 ? (QW == 6 ? attn_bf16_bwd_q_kernel<128, 6> : attn_bf16_bwd_q_kernel<128, 4>)
                         : g.head_dim == 64
                             ? (QW == 8   ? attn_bf16_bwd_q_kernel<64, 8>
@@ -1296,8 +1372,7 @@ static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void
                                : QW == 6 ? attn_bf16_bwd_q_kernel<32, 6>
                                          : attn_bf16_bwd_q_kernel<32, 4>);
         const int KW = bwd_kv_waves(g.head_dim);
-        const kv_t fk = g.head_dim == 32 ? attn_bf16_bwd_kv_kernel<32, 6>
-                        : g.head_dim == 64 ? attn_bf16_bwd_kv_kernel<64, 6> : attn_bf16_bwd_kv_kernel<128, 8>;
+        const kv_t fk = bwd_kv_variant(g);
         hipLaunchKernelGGL(fq, qgrid, dim3((QW + kBwdLoaders) * 64), L.total_q, s, g, (const uint16_t*)q, (const uint16_t*)k,
                            (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dq, stats, work0, count);
         hipError_t e = hipGetLastError();

@@ -51,7 +51,11 @@ CASES = {**SMALL, **EDGE, **LARGE,
          # 16 x 20 windows (320 tokens, 5 blocks of 4 query waves with no idle slot;
          # a width of 20 splits diagonal runs at window rows), latitude padded 30 -> 32
          "n320_w20_pad": Problem("n320", "bf16", 1, 2, 64, (1, 30, 40), (1, 32, 40), (1, 16, 20), (0, 8, 10),
-                                 seed=32)}
+                                 seed=32),
+         # the narrowest width whose diagonal runs split at row starts only (8), and a
+         # narrower one (5), whose runs split wherever the table entry changes
+         "n192_w8": Problem("n192w8", "bf16", 1, 2, 64, (1, 48, 24), (1, 48, 24), (1, 24, 8), (0, 12, 4), seed=33),
+         "n200_w5": Problem("n200w5", "bf16", 1, 2, 64, (1, 40, 20), (1, 40, 20), (1, 40, 5), (0, 20, 2), seed=34)}
 
 
 @pytest.mark.parametrize("name", list(CASES))
