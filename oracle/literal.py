@@ -138,3 +138,21 @@ def literal_forward(prob, q, k, v, table):
     p = np.divide(e, den, out=np.zeros_like(e), where=den > 0)
     ow = np.einsum("bwhnm,bwmhe->bwnhe", p, vw)
     return literal_unwindows(prob, ow)
+
+
+def literal_lse(prob, q, k, table):
+    """Steps 1-6 up to the softmax's normaliser: fp64 log-sum-exp (natural log)
+    of each real query's logits over its visible keys, [B, T, H, W, heads].
+    The softmax weight of a visible key is exp(logit - lse)."""
+    qw, kw = literal_windows(prob, q), literal_windows(prob, k)  # [B, nW, N, h, d]
+    bias = literal_bias(prob, table)  # [h, N, N]
+    vis = literal_visibility(prob)  # [nW, N, N]
+    logits = np.einsum("bwnhe,bwmhe->bwhnm", qw, kw) * _scale(prob) + bias[None, None]
+    logits = np.where(vis[None, :, None], logits, -np.inf)
+    has_key = vis.any(axis=-1)[None, :, None, :]  # [1, nW, 1, N]
+    mx = np.where(has_key, logits.max(axis=-1), 0.0)
+    den = np.where(vis[None, :, None], np.exp(logits - mx[..., None]), 0.0).sum(axis=-1)
+    with np.errstate(divide="ignore"):
+        lse = np.where(den > 0, mx + np.log(np.where(den > 0, den, 1.0)), -np.inf)  # [B, nW, h, N]
+    return literal_unwindows(prob, np.moveaxis(lse, 2, 3))
+

@@ -467,3 +467,100 @@ def test_pad_values_do_not_matter(oracle_lib, monkeypatch):
     monkeypatch.setattr(literal, "_pad", noisy_pad)
     noisy = run_literal(oracle_lib, p, x)
     assert np.array_equal(noisy, base)
+
+
+# --------------------------------------------------------------------------- log-sum-exp
+
+
+def test_lse_single_window_shift0_is_logsumexp(oracle_lib):
+    """One window with shift 0 is global attention: the log-sum-exp of a query is
+    torch's logsumexp over all its logits (scaled products plus the bias of the
+    raw coordinate differences), in float64 on the CPU."""
+    p = P((2, 3, 4), (2, 3, 4), (2, 3, 4), (0, 0, 0), heads=3, head_dim=16, batch=2)
+    x = make_inputs(p, seed=41)
+    x["table"] = torch.randn(p.table_shape, generator=torch.Generator().manual_seed(6), dtype=torch.float32)
+    got = oracle_lib.literal_lse(p, f64(x["q"]), f64(x["k"]), f64(x["table"]))
+    T, H, W = p.extent
+    coords = torch.stack(torch.meshgrid(torch.arange(T), torch.arange(H), torch.arange(W),
+                                        indexing="ij"), -1).reshape(-1, 3)
+    rel = coords[:, None, :] - coords[None, :, :] + torch.tensor(p.window) - 1
+    bias = x["table"].double()[rel[..., 0], rel[..., 1], rel[..., 2]].permute(2, 0, 1)  # [h, n, m]
+    n = T * H * W
+    q = x["q"].double().reshape(p.batch, n, p.heads, p.head_dim).permute(0, 2, 1, 3)
+    k = x["k"].double().reshape(p.batch, n, p.heads, p.head_dim).permute(0, 2, 1, 3)
+    logits = q @ k.transpose(-1, -2) / math.sqrt(p.head_dim) + bias[None]
+    ref = torch.logsumexp(logits, dim=-1).permute(0, 2, 1).reshape(got.shape).numpy()
+    assert np.abs(got - ref).max() < 1e-12
+
+
+def test_lse_brute_force_over_hand_segments(oracle_lib):
+    """The tiny padded grid: each query's log-sum-exp by plain Python arithmetic
+    over its hand-derived key set."""
+    ax = golden_axes()
+    lat, lon = ax["tiny_lat_pad"], ax["tiny_lon_cyclic"]
+    p = P((1, 7, 8), (1, 8, 8), (1, 4, 4), (0, 2, 2), heads=2, head_dim=3)
+    x = make_inputs(p, seed=27)
+    got = oracle_lib.literal_lse(p, f64(x["q"]), f64(x["k"]), f64(x["table"]))
+    q, k, tab = (f64(x[n]) for n in ("q", "k", "table"))
+    seg_y = {c: seg for seg in lat["segments"] for c in seg}
+    seg_x = {c: seg for seg in lon["segments"] for c in seg}
+    ly = {int(kk): val for kk, val in lat["local"].items()}
+    lx = {int(kk): val for kk, val in lon["local"].items()}
+    sc = 1.0 / math.sqrt(3)
+    for y in range(7):
+        for xx in range(8):
+            for h in range(2):
+                logits = []
+                for y2 in seg_y[y]:
+                    for x2 in seg_x[xx]:
+                        dot = sum(q[0, 0, y, xx, h, e] * k[0, 0, y2, x2, h, e] for e in range(3))
+                        logits.append(dot * sc + tab[0, ly[y] - ly[y2] + 3, lx[xx] - lx[x2] + 3, h])
+                m = max(logits)
+                want = m + math.log(sum(math.exp(l - m) for l in logits))
+                assert abs(got[0, 0, y, xx, h] - want) < 1e-13
+
+
+def test_lse_uniform_logits_count_the_key_set(oracle_lib):
+    """Q = 0 and a constant table c make every logit c: the log-sum-exp is
+    c + log(size of the key set), the sizes fixed by the hand derivation
+    (ragged 181 -> 190 latitude, window 10x10, shift 5; longitude 360)."""
+    base = WORKLOADS["c4_bf16_181x360_pad190"]
+    p = base.with_(dtype="f32", heads=2, head_dim=4, batch=1)
+    x = make_inputs(p, seed=28)
+    x["q"].zero_()
+    x["table"].fill_(0.25)
+    got = oracle_lib.literal_lse(p, f64(x["q"]), f64(x["k"]), f64(x["table"]))
+    ax = golden_axes()
+    lat = ax["ragged_lat_181_pad190_w10_s5"]["segments_of"]
+    lon = ax["lon_360_w10_s5"]["segments_of"]
+    for y, xx in [(0, 0), (4, 359), (180, 200), (100, 5), (175, 0)]:
+        size = len(expand(*lat[str(y)], 181)) * len(expand(*lon[str(xx)], 360))
+        assert np.abs(got[0, 0, y, xx] - (0.25 + math.log(size))).max() < 1e-13
+
+
+def test_lse_gives_the_forward_weights(oracle_lib):
+    """exp(logit - lse) are the weights of the forward output: with V the one-hot
+    code of each key, the literal forward returns them, and they sum to 1."""
+    p = P((1, 6, 8), (1, 8, 8), (1, 4, 4), (0, 2, 2), heads=2, head_dim=5, cyclic=(0, 0, 1))
+    x = make_inputs(p, seed=29)
+    lse = oracle_lib.literal_lse(p, f64(x["q"]), f64(x["k"]), f64(x["table"]))
+    out = run_literal(oracle_lib, p, x)
+    # a ones vector for V makes the forward return the weight sum (1 for every real query)
+    x1 = dict(x)
+    x1["v"] = torch.ones_like(x["v"])
+    ones = run_literal(oracle_lib, p, x1)
+    assert np.abs(ones - 1.0).max() < 1e-12
+    # and the output equals sum_k exp(logit - lse) v_k over the visible keys, by brute force
+    # through the literal form's own windows for one query
+    import oracle as O
+    qw, kw, vw = (O.literal_windows(p, f64(x[n])) for n in ("q", "k", "v"))
+    bias = O.literal_bias(p, f64(x["table"]))
+    vis = O.literal_visibility(p)
+    lw = O.literal_windows(p, lse[..., None])[..., 0]  # [B, nW, N, h]
+    b, w, n, h = 0, 1, 5, 1
+    logit = (qw[b, w, n, h] @ kw[b, w, :, h].T) / math.sqrt(5) + bias[h, n]
+    wts = np.where(vis[w, n], np.exp(logit - lw[b, w, n, h]), 0.0)
+    assert abs(wts.sum() - 1.0) < 1e-12
+    o = wts @ vw[b, w, :, h]
+    ow = O.literal_windows(p, out)
+    assert np.abs(o - ow[b, w, n, h]).max() < 1e-12
