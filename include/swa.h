@@ -163,6 +163,20 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
                        const float* bias_table, void* out, void* stream);
 
 /*
+ * swa_forward that also keeps the softmax normaliser of every query for the
+ * backward pass (the models are trained: TERRA page, abstract): lse[r * heads
+ * + h] = log of the sum of exp(logit) over the keys real token r sees in head
+ * h (natural log, the logits of the forward pass above), so that each
+ * softmax weight is exp(logit - lse).  lse: device buffer of B*T*H*W*heads
+ * fp32 values, 4-byte aligned, owned by the caller, overlapping no other
+ * argument; one value per real token and head is written.  out is as
+ * swa_forward writes it, bit for bit.  The fused variant only.
+ * Errors: as swa_forward; UNSUPPORTED for a staged handle.
+ */
+swa_status swa_forward_lse(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
+                           void* out, float* lse, void* stream);
+
+/*
  * Gradients of the forward pass (the pages' models are trained: TERRA page,
  * abstract and Table V).  Given dout = dL/d(out) in the layout of out, writes
  * dq, dk, dv = dL/dq, dL/dk, dL/dv (layout and dtype of q, k, v; every real
@@ -188,6 +202,23 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
 swa_status swa_backward(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
                         const void* dout, void* dq, void* dk, void* dv, float* dtable, void* workspace,
                         void* stream);
+
+/*
+ * swa_backward from the forward pass's output and statistics (out and lse as
+ * swa_forward_lse wrote them for the same q, k, v and table; the fused
+ * layout): with backward_schedule 2 the query kernel takes each query's
+ * softmax normaliser from lse and D = rowsum(dout * out) from out instead of
+ * recomputing both in a first pass over the window's keys, so it reads K and
+ * V once.  backward_schedule 1 and fp32 form their statistics in LDS as
+ * swa_backward does and ignore out and lse: there the results equal
+ * swa_backward's bit for bit.  With schedule 2 they differ from it by
+ * rounding (out is the bf16-rounded output).  out: 16-byte aligned; lse:
+ * 4-byte aligned; both are only read.
+ * Errors: as swa_backward; INVALID_ARGUMENT also for NULL out or lse.
+ */
+swa_status swa_backward_lse(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
+                            const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            float* dtable, void* workspace, void* stream);
 
 /*
  * swa_backward for callers that cannot allocate device memory: code under

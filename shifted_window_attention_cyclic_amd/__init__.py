@@ -5,13 +5,14 @@ The computation lives in the HIP library ``libswa.so`` (C ABI in
 ctypes binding with the same entry-point names.
 """
 from .binding import (EXPORTS, SwaError, WindowAttention, load_library, make_config,
-                      swa_backward, swa_backward_noalloc, swa_create, swa_debug_visibility, swa_destroy, swa_forward, swa_gather,
+                      swa_backward, swa_backward_lse, swa_backward_noalloc, swa_create, swa_debug_visibility,
+                      swa_destroy, swa_forward, swa_forward_lse, swa_gather,
                       swa_get_info, swa_layer_attention, swa_layer_forward, swa_projection, swa_scatter,
                       swa_status_string)
 
 __all__ = [
     "EXPORTS", "SwaError", "WindowAttention", "load_library", "make_config", "swa_backward",
-    "swa_backward_noalloc", "swa_create",
+    "swa_backward_lse", "swa_backward_noalloc", "swa_create", "swa_forward_lse",
     "swa_debug_visibility", "swa_destroy", "swa_forward", "swa_gather", "swa_get_info",
     "swa_layer_attention", "swa_layer_forward", "swa_projection", "swa_scatter", "swa_status_string",
 ]

@@ -21,7 +21,8 @@ SCHEDULES = {"auto": SWA_SCHEDULE_AUTO, "stream": SWA_SCHEDULE_STREAM, "block": 
 SWA_LAYER_AUTO, SWA_LAYER_FUSED, SWA_LAYER_UNFUSED = 0, 1, 2
 LAYER_PATHS = {"auto": SWA_LAYER_AUTO, "fused": SWA_LAYER_FUSED, "unfused": SWA_LAYER_UNFUSED}
 
-EXPORTS = ("swa_create", "swa_forward", "swa_backward", "swa_backward_noalloc", "swa_layer_forward",
+EXPORTS = ("swa_create", "swa_forward", "swa_forward_lse", "swa_backward", "swa_backward_lse",
+           "swa_backward_noalloc", "swa_layer_forward",
            "swa_layer_attention", "swa_projection", "swa_destroy", "swa_get_info", "swa_status_string",
            "swa_last_error", "swa_gather", "swa_scatter", "swa_debug_visibility")
 
@@ -70,8 +71,12 @@ def load_library(path: str = LIBRARY):
     lib.swa_create.restype = st
     lib.swa_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.swa_forward.restype = st
+    lib.swa_forward_lse.argtypes = [vp] * 8
+    lib.swa_forward_lse.restype = st
     lib.swa_backward.argtypes = [vp] * 12
     lib.swa_backward.restype = st
+    lib.swa_backward_lse.argtypes = [vp] * 14
+    lib.swa_backward_lse.restype = st
     lib.swa_backward_noalloc.argtypes = [vp] * 11
     lib.swa_backward_noalloc.restype = st
     lib.swa_layer_forward.argtypes = [vp] * 10
@@ -168,6 +173,23 @@ def swa_forward(handle, q, k, v, table, out, stream=None) -> None:
     _check(load_library().swa_forward(handle, _dev(q, "q"), _dev(k, "k", dt), _dev(v, "v", dt),
                                       _dev(table, "table", torch.float32), _dev(out, "out", dt),
                                       _stream(stream)))
+
+
+def swa_forward_lse(handle, q, k, v, table, out, lse, stream=None) -> None:
+    dt = q.dtype
+    _check(load_library().swa_forward_lse(handle, _dev(q, "q"), _dev(k, "k", dt), _dev(v, "v", dt),
+                                          _dev(table, "table", torch.float32), _dev(out, "out", dt),
+                                          _dev(lse, "lse", torch.float32), _stream(stream)))
+
+
+def swa_backward_lse(handle, q, k, v, table, out, lse, dout, dq, dk, dv, dtable, workspace, stream=None) -> None:
+    dt = q.dtype
+    _check(load_library().swa_backward_lse(handle, _dev(q, "q"), _dev(k, "k", dt), _dev(v, "v", dt),
+                                           _dev(table, "table", torch.float32), _dev(out, "out", dt),
+                                           _dev(lse, "lse", torch.float32), _dev(dout, "dout", dt),
+                                           _dev(dq, "dq", dt), _dev(dk, "dk", dt), _dev(dv, "dv", dt),
+                                           _dev(dtable, "dtable", torch.float32), _dev(workspace, "workspace"),
+                                           _stream(stream)))
 
 
 def swa_backward(handle, q, k, v, table, dout, dq, dk, dv, dtable, workspace, stream=None) -> None:
@@ -276,6 +298,17 @@ class WindowAttention:
         swa_forward(self.handle, q, k, v, table, out, stream)
         return out
 
+    def forward_lse(self, q, k, v, table, out=None, lse=None, stream=None):
+        """forward() that also returns each query's log-sum-exp [B, T, H, W, heads] (fp32)."""
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            self._shape(t, self.io_shape, name)
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty(self.io_shape[:-1], dtype=torch.float32, device=q.device)
+        swa_forward_lse(self.handle, q, k, v, table, out, lse, stream)
+        return out, lse
+
     def backward(self, q, k, v, table, dout, stream=None):
         """Gradients (dq, dk, dv, dtable) of sum(dout * forward(q, k, v, table))."""
         for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
@@ -289,6 +322,20 @@ class WindowAttention:
         dtable = torch.empty_like(table)
         ws = torch.empty((nws + 15) // 16 * 4, dtype=torch.float32, device=q.device)
         swa_backward(self.handle, q, k, v, table, dout, dq, dk, dv, dtable, ws, stream)
+        return dq, dk, dv, dtable
+
+    def backward_lse(self, q, k, v, table, out, lse, dout, stream=None):
+        """backward() from the forward's output and log-sum-exp (forward_lse)."""
+        for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+            self._shape(t, self.io_shape, name)
+        self._shape(lse, self.io_shape[:-1], "lse")
+        nws = self.info.backward_workspace_bytes
+        if nws == 0:
+            raise SwaError(SWA_ERR_UNSUPPORTED, "the backward kernels do not take this window")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dtable = torch.empty_like(table)
+        ws = torch.empty((nws + 15) // 16 * 4, dtype=torch.float32, device=q.device)
+        swa_backward_lse(self.handle, q, k, v, table, out, lse, dout, dq, dk, dv, dtable, ws, stream)
         return dq, dk, dv, dtable
 
     @property

@@ -349,15 +349,9 @@ swa_status swa_get_info(const swa_handle* h, swa_info* info) {
     return SWA_OK;
 }
 
-swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* v,
-                       const float* bias_table, void* out, void* stream) {
-    if (!h || !q || !k || !v || !bias_table || !out) return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(bias_table, 4))
-        return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned pointer (q, k, v, out need 16 bytes)");
-    const size_t n = io_bytes(h);
-    const size_t nt = (size_t)h->g.table_size * h->g.heads * sizeof(float);
-    if (overlap(out, n, q, n) || overlap(out, n, k, n) || overlap(out, n, v, n) || overlap(out, n, bias_table, nt))
-        return fail(SWA_ERR_INVALID_ARGUMENT, "out overlaps an input");
+// The forward pass after argument checks; lse (fused variant only) may be null.
+static swa_status forward(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
+                          void* out, float* lse, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     const swa::Geometry& g = h->g;
     const bool bf16 = h->cfg.dtype == SWA_BF16;
@@ -365,13 +359,13 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
     auto attention = [&](bool staged, const void* aq, const void* ak, const void* av, void* ao) {
         if (!bf16)
             return swa::launch_attention_f32(g, staged, (const float*)aq, (const float*)ak, (const float*)av,
-                                             bias_table, (float*)ao, s);
+                                             bias_table, (float*)ao, lse, s);
         if (h->schedule == SWA_SCHEDULE_KEYBLOCK)
             return swa::launch_attention_kblock(g, staged, (const uint16_t*)aq, (const uint16_t*)ak,
-                                                (const uint16_t*)av, bias_table, h->bias_hm, (uint16_t*)ao, s);
+                                                (const uint16_t*)av, bias_table, h->bias_hm, (uint16_t*)ao, lse, s);
         return swa::launch_attention_bf16(g, h->schedule == SWA_SCHEDULE_STREAM, h->blocks, staged,
                                           (const uint16_t*)aq, (const uint16_t*)ak, (const uint16_t*)av, bias_table,
-                                          (uint16_t*)ao, s);
+                                          (uint16_t*)ao, lse, s);
     };
     if (h->cfg.variant == SWA_VARIANT_FUSED) {
         e = attention(false, q, k, v, out);
@@ -390,15 +384,60 @@ swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* 
     return SWA_OK;
 }
 
-swa_status swa_backward(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
-                        const void* dout, void* dq, void* dk, void* dv, float* dtable, void* workspace,
-                        void* stream) {
+static swa_status forward_args(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
+                               void* out) {
+    if (!h || !q || !k || !v || !bias_table || !out) return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(bias_table, 4))
+        return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned pointer (q, k, v, out need 16 bytes)");
+    const size_t n = io_bytes(h);
+    const size_t nt = (size_t)h->g.table_size * h->g.heads * sizeof(float);
+    if (overlap(out, n, q, n) || overlap(out, n, k, n) || overlap(out, n, v, n) || overlap(out, n, bias_table, nt))
+        return fail(SWA_ERR_INVALID_ARGUMENT, "out overlaps an input");
+    return SWA_OK;
+}
+
+// bytes of a log-sum-exp tensor: one float per real token and head
+static size_t lse_bytes(const swa_handle* h) {
+    const swa::Geometry& g = h->g;
+    return (size_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2] * g.heads * sizeof(float);
+}
+
+swa_status swa_forward(swa_handle* h, const void* q, const void* k, const void* v,
+                       const float* bias_table, void* out, void* stream) {
+    const swa_status st = forward_args(h, q, k, v, bias_table, out);
+    return st != SWA_OK ? st : forward(h, q, k, v, bias_table, out, nullptr, stream);
+}
+
+swa_status swa_forward_lse(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
+                           void* out, float* lse, void* stream) {
+    swa_status st = forward_args(h, q, k, v, bias_table, out);
+    if (st != SWA_OK) return st;
+    if (!lse) return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (!aligned(lse, 4)) return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned lse");
+    if (h->cfg.variant != SWA_VARIANT_FUSED)
+        return fail(SWA_ERR_UNSUPPORTED, "the statistics come with the fused variant only");
+    const size_t n = io_bytes(h);
+    const size_t nt = (size_t)h->g.table_size * h->g.heads * sizeof(float);
+    const size_t nl = lse_bytes(h);
+    if (overlap(lse, nl, q, n) || overlap(lse, nl, k, n) || overlap(lse, nl, v, n) || overlap(lse, nl, out, n) ||
+        overlap(lse, nl, bias_table, nt))
+        return fail(SWA_ERR_INVALID_ARGUMENT, "lse overlaps another argument");
+    return forward(h, q, k, v, bias_table, out, lse, stream);
+}
+
+// Argument checks of the backward passes and the launch; o and lse (the
+// forward's output and statistics) may both be null.
+static swa_status backward(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* dtable, void* workspace, void* stream) {
     if (!h || !q || !k || !v || !bias_table || !dout || !dq || !dk || !dv || !dtable || !workspace)
         return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
     const void* tensors[] = {q, k, v, dout, dq, dk, dv, workspace};
     for (const void* p : tensors)
         if (!aligned(p, 16)) return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned pointer (tensors and workspace need 16 bytes)");
     if (!aligned(bias_table, 4) || !aligned(dtable, 4)) return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned table");
+    if ((o && !aligned(o, 16)) || (lse && !aligned(lse, 4)))
+        return fail(SWA_ERR_INVALID_ARGUMENT, "misaligned out or lse");
     const swa::Geometry& g = h->g;
     const bool bf16 = h->cfg.dtype == SWA_BF16;
     if (!swa::backward_fits(g, bf16))
@@ -406,16 +445,30 @@ swa_status swa_backward(swa_handle* h, const void* q, const void* k, const void*
     const size_t n = io_bytes(h);
     const size_t nt = (size_t)g.table_size * g.heads * sizeof(float);
     const size_t nw = swa::backward_workspace_bytes(g);
+    const size_t nl = lse_bytes(h);
     // every buffer written must be disjoint from every other argument
-    const void* all[] = {q, k, v, dout, bias_table, dq, dk, dv, dtable, workspace};
-    const size_t len[] = {n, n, n, n, nt, n, n, n, nt, nw};
-    for (int i = 5; i < 10; i++)
-        for (int j = 0; j < 10; j++)
-            if (j != i && overlap(all[i], len[i], all[j], len[j]))
+    const void* all[] = {q, k, v, dout, bias_table, o, lse, dq, dk, dv, dtable, workspace};
+    const size_t len[] = {n, n, n, n, nt, o ? n : 0, lse ? nl : 0, n, n, n, nt, nw};
+    for (int i = 7; i < 12; i++)
+        for (int j = 0; j < 12; j++)
+            if (j != i && all[j] && overlap(all[i], len[i], all[j], len[j]))
                 return fail(SWA_ERR_INVALID_ARGUMENT, "a gradient or the workspace overlaps another argument");
-    hipError_t e = swa::launch_backward(g, bf16, q, k, v, bias_table, dout, dq, dk, dv, dtable, workspace,
+    hipError_t e = swa::launch_backward(g, bf16, q, k, v, bias_table, dout, dq, dk, dv, dtable, workspace, o, lse,
                                         (hipStream_t)stream);
     return e == hipSuccess ? SWA_OK : fail_hip(e, "backward launch");
+}
+
+swa_status swa_backward(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
+                        const void* dout, void* dq, void* dk, void* dv, float* dtable, void* workspace,
+                        void* stream) {
+    return backward(h, q, k, v, bias_table, nullptr, nullptr, dout, dq, dk, dv, dtable, workspace, stream);
+}
+
+swa_status swa_backward_lse(swa_handle* h, const void* q, const void* k, const void* v, const float* bias_table,
+                            const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            float* dtable, void* workspace, void* stream) {
+    if (!out || !lse) return fail(SWA_ERR_INVALID_ARGUMENT, "NULL argument");
+    return backward(h, q, k, v, bias_table, out, lse, dout, dq, dk, dv, dtable, workspace, stream);
 }
 
 swa_status swa_backward_noalloc(swa_handle* h, const void* q, const void* k, const void* v,

@@ -593,11 +593,14 @@ __device__ inline int copy_block(const Geometry& g, const uint16_t* src, int h, 
     return issued;
 }
 
+// With lse (and o, the forward's output) the statistics come from the forward
+// pass: lse2 = log2(e) * lse and D = rowsum(dO * O), and K and V stream once.
 template <int D, int QW>
 __global__ __launch_bounds__((QW + kBwdLoaders) * 64) void attn_bf16_bwd_q_kernel(
     Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
-    float* __restrict__ stats, uint32_t work0, uint32_t count) {
+    float* __restrict__ stats, uint32_t work0, uint32_t count, const uint16_t* __restrict__ o,
+    const float* __restrict__ lse) {
     constexpr int THREADS = (QW + kBwdLoaders) * 64;
     constexpr int KSTEPS = D / 32, DT = D / 16;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -627,9 +630,10 @@ __global__ __launch_bounds__((QW + kBwdLoaders) * 64) void attn_bf16_bwd_q_kerne
     for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)i * g.heads + h];
     __syncthreads();
 
+    const int passes = lse != nullptr ? 1 : 2;
     if (wave >= QW) { // loader waves: K and V blocks, once per pass
         const int li = wave - QW;
-        bwd_stream(2 * NB, 2 * block_copies_of<D>(li, kBwdLoaders), [&](int s, int slot) {
+        bwd_stream(passes * NB, 2 * block_copies_of<D>(li, kBwdLoaders), [&](int s, int slot) {
             const int j = s < NB ? s : s - NB;
             unsigned char* dst = ring + (size_t)slot * 2 * L.buf_bytes;
             copy_block<D>(g, k, h, tw, j * kBwdBlk, dst, li, kBwdLoaders);
@@ -702,10 +706,11 @@ __global__ __launch_bounds__((QW + kBwdLoaders) * 64) void attn_bf16_bwd_q_kerne
     // ---- pass 1: the softmax statistics and D = rowsum(P * dP) at once.  Per
     // lane, over its keys: the running max m, l = sum 2^(logit - m) and
     // dsum = sum 2^(logit - m) dP, both rescaled when m grows; then across the
-    // query's 4 lanes.  D = dsum / l.
+    // query's 4 lanes.  D = dsum / l.  Skipped when the forward's statistics
+    // are given.
     float m_run = -INFINITY, l_run = 0.f, d_run = 0.f;
     int slot = 0;
-    for (int j = 0; j < NB; j++) {
+    for (int j = 0; j < (passes == 2 ? NB : 0); j++) {
         bwd_compute_barrier(); // block j is in its slot
         f32x4 s[2], dp[2];
         block_products(slot, j, s, dp);
@@ -741,9 +746,29 @@ __global__ __launch_bounds__((QW + kBwdLoaders) * 64) void attn_bf16_bwd_q_kerne
     d_all += __shfl_xor(d_all, 16);
     d_all += __shfl_xor(d_all, 32);
     // P = qvalid * exp2(logit - lse2); a query with no visible key (pad) gets P = 0
-    const float lse2 = l_all > 0.f ? m_all + log2f(l_all) : 0.f;
-    const float pscale = l_all > 0.f ? qvalid : 0.f;
-    const float dsum = pscale == 0.f ? 0.f : d_all / l_all;
+    float lse2 = l_all > 0.f ? m_all + log2f(l_all) : 0.f;
+    float pscale = l_all > 0.f ? qvalid : 0.f;
+    float dsum = pscale == 0.f ? 0.f : d_all / l_all;
+    if (passes == 1) {
+        // the forward's statistics: every real query sees itself, so its sum is
+        // positive; D over the head slice, this lane's 8 d per step and then
+        // across the query's 4 lanes
+        float part = 0.f;
+        if (r >= 0) {
+            const uint64_t base = (uint64_t)(uint32_t)r * (uint32_t)g.row + h * D + grp * 8;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ks++) {
+                const bf16x8 of = __builtin_bit_cast(bf16x8, *(const u32x4*)(o + base + ks * 32));
+#pragma unroll
+                for (int e = 0; e < 8; e++) part = fmaf((float)df[ks][e], (float)of[e], part);
+            }
+        }
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        lse2 = r >= 0 ? lse[(uint64_t)(uint32_t)r * (uint32_t)g.heads + h] * kLog2e : 0.f;
+        pscale = qvalid;
+        dsum = r >= 0 ? part : 0.f;
+    }
     // statistics per query: lse2 (log2 of the softmax normaliser) and D; a pad
     // query gets lse2 = +inf, so that every P it would take is 0
     if (grp == 0 && in_window) {
@@ -1355,14 +1380,15 @@ static kv_t bwd_kv_variant(const Geometry& g) {
 // for big windows, their per-query statistics at stats[(unit - work0) * 2 NPX].
 static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
                                         const float* table, const void* dout, void* dq, void* dk, void* dv,
-                                        uint32_t work0, uint32_t count, float* units, float* stats, hipStream_t s) {
+                                        uint32_t work0, uint32_t count, float* units, float* stats, const void* o,
+                                        const float* lse, hipStream_t s) {
     const dim3 grid(count);
     if (bf16 && !bwd_small_fits(g)) {
         const BwdBigLds L = bwd_big_lds(g, bwd_kv_waves(g.head_dim));
         const int QW = bwd_q_waves(g);
         const dim3 qgrid(count * (unsigned)((g.N + QW * 16 - 1) / (QW * 16)));
         typedef void (*qk_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
-                             const uint16_t*, uint16_t*, float*, uint32_t, uint32_t);
+                             const uint16_t*, uint16_t*, float*, uint32_t, uint32_t, const uint16_t*, const float*);
         const qk_t fq = g.head_dim == 128 ? (QW == 6 ? attn_bf16_bwd_q_kernel<128, 6> : attn_bf16_bwd_q_kernel<128, 4>)
                         : g.head_dim == 64
                             ? (QW == 8   ? attn_bf16_bwd_q_kernel<64, 8>
@@ -1374,7 +1400,8 @@ static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void
         const int KW = bwd_kv_waves(g.head_dim);
         const kv_t fk = bwd_kv_variant(g);
         hipLaunchKernelGGL(fq, qgrid, dim3((QW + kBwdLoaders) * 64), L.total_q, s, g, (const uint16_t*)q, (const uint16_t*)k,
-                           (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dq, stats, work0, count);
+                           (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dq, stats, work0, count,
+                           (const uint16_t*)o, lse);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(fk, grid, dim3((KW + kBwdLoaders) * 64), L.total_k, s, g, (const uint16_t*)q, (const uint16_t*)k,
@@ -1398,12 +1425,12 @@ static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void
 
 hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
                            const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
-                           void* workspace, hipStream_t s) {
+                           void* workspace, const void* o, const float* lse, hipStream_t s) {
     float* units = (float*)workspace;
     float* chunks = units + (size_t)(g.windows * g.heads) * g.table_size;
     float* stats = chunks + (size_t)kDtableChunks * g.heads * g.table_size;
     hipError_t e = launch_backward_units(g, bf16, q, k, v, table, dout, dq, dk, dv, 0,
-                                         (uint32_t)(g.windows * g.heads), units, stats, s);
+                                         (uint32_t)(g.windows * g.heads), units, stats, o, lse, s);
     if (e != hipSuccess) return e;
     const int n = g.heads * g.table_size;
     hipLaunchKernelGGL(dtable_chunk_kernel, dim3((n + 255) / 256, kDtableChunks), dim3(256), 0, s, g.windows,
@@ -1475,7 +1502,7 @@ hipError_t launch_backward_scratch(const Geometry& g, bool bf16, const void* q, 
         hipError_t e;
         if (w1 > w0) {
             e = launch_backward_units(g, bf16, q, k, v, table, dout, dq, dk, dv, (uint32_t)(w0 * g.heads),
-                                      (uint32_t)((w1 - w0) * g.heads), units, stats, s);
+                                      (uint32_t)((w1 - w0) * g.heads), units, stats, nullptr, nullptr, s);
             if (e != hipSuccess) return e;
         }
         hipLaunchKernelGGL(dtable_accumulate_kernel, dim3((n + 255) / 256), dim3(256), 0, s, g.windows, g.heads,

@@ -141,11 +141,13 @@ hipError_t launch_gather(const Geometry& g, int elem_bytes, const void* src, voi
 hipError_t launch_scatter(const Geometry& g, int elem_bytes, const void* src, void* dst,
                           hipStream_t s);
 hipError_t launch_visibility(const Geometry& g, int64_t window, uint8_t* out, hipStream_t s);
+// With lse (fused layout only; may be null) every real query's log-sum-exp of
+// its logits also goes to lse[row * heads + head].
 hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, const float* k,
-                                const float* v, const float* table, float* out, hipStream_t s);
+                                const float* v, const float* table, float* out, float* lse, hipStream_t s);
 hipError_t launch_attention_bf16(const Geometry& g, bool stream, int blocks, bool staged, const uint16_t* q,
                                  const uint16_t* k, const uint16_t* v, const float* table,
-                                 uint16_t* out, hipStream_t s);
+                                 uint16_t* out, float* lse, hipStream_t s);
 // LDS bytes the attention kernels need for g (bf16: the smallest among the
 // schedules that take the window; (size_t)-1 when none does).
 size_t attention_lds_bytes(const Geometry& g, bool bf16, bool staged);
@@ -164,7 +166,7 @@ size_t bf16_kblock_workspace_bytes(const Geometry& g);
 hipError_t kblock_plan(const Geometry& g, int* blocks);
 hipError_t launch_attention_kblock(const Geometry& g, bool staged, const uint16_t* q, const uint16_t* k,
                                    const uint16_t* v, const float* table, float* bias_hm, uint16_t* out,
-                                   hipStream_t s);
+                                   float* lse, hipStream_t s);
 // Lets every attention kernel take up to max_lds bytes of dynamic LDS.
 hipError_t prepare_kernels(int max_lds);
 
@@ -175,9 +177,11 @@ hipError_t prepare_kernels(int max_lds);
 bool backward_fits(const Geometry& g, bool bf16);
 size_t backward_workspace_bytes(const Geometry& g);
 hipError_t prepare_backward_kernels(int max_lds);
+// With lse and o (the forward's statistics and output; both may be null) the
+// big-window kernels take the softmax statistics from the forward pass.
 hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
                            const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
-                           void* workspace, hipStream_t s);
+                           void* workspace, const void* o, const float* lse, hipStream_t s);
 // The same gradients through a fixed scratch buffer of scratch_bytes, in
 // passes over runs of window chunks (bitwise equal to launch_backward), and
 // the least scratch that takes (one chunk of windows).

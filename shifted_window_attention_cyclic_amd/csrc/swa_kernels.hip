@@ -157,7 +157,8 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(Geometry g, int s
                                                                const float* __restrict__ k,
                                                                const float* __restrict__ v,
                                                                const float* __restrict__ table,
-                                                               float* __restrict__ out) {
+                                                               float* __restrict__ out,
+                                                               float* __restrict__ lse) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int N = g.N;
     float* Ks = (float*)smem;
@@ -224,21 +225,22 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(Geometry g, int s
             for (int e = 0; e < D; e++) acc[e] = fmaf(p, Vs[m * D + e], acc[e]);
         }
         float inv = 1.f / den;
+        if (lse != nullptr) lse[(int64_t)r * g.heads + h] = mx + logf(den);
         float* o = out + (int64_t)r * g.row + (int64_t)h * D;
         for (int e = 0; e < D; e++) o[e] = acc[e] * inv;
     }
 }
 
 hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, const float* k,
-                                const float* v, const float* table, float* out, hipStream_t s) {
+                                const float* v, const float* table, float* out, float* lse, hipStream_t s) {
     size_t lds = f32_lds_bytes(g);
     dim3 grid((unsigned)(g.windows * g.heads));
     if (g.head_dim == 32)
         hipLaunchKernelGGL(attn_f32_kernel<32>, grid, dim3(kF32Threads), lds, s, g, (int)staged, q,
-                           k, v, table, out);
+                           k, v, table, out, lse);
     else
         hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(kF32Threads), lds, s, g, (int)staged, q,
-                           k, v, table, out);
+                           k, v, table, out, lse);
     return hipGetLastError();
 }
 
@@ -305,7 +307,8 @@ __host__ __device__ inline Bf16Lds bf16_lds(const Geometry& g) {
 template <int D, int NWAVES, int QT_MAX, int KT_FIXED, bool BIAS_VEC>
 __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
     Geometry g, int staged, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ table, uint16_t* __restrict__ out) {
+    const uint16_t* __restrict__ v, const float* __restrict__ table, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
     constexpr int THREADS = NWAVES * 64;
     constexpr int KSTEPS = D / 32; // 32-deep steps of K Q^T
     constexpr int DT = D / 16;     // 16-row d tiles of O^T
@@ -588,6 +591,10 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 
         int orow = r;
         if (r < 0 && staged) orow = (int)(wi * (uint32_t)N + n); // staged: pad slots of O are zeros
+        // the log-sum-exp of a real query's logits: reference (mrun, natural units)
+        // plus the log of the row sum
+        if (lse != nullptr && r >= 0 && grp == 0)
+            lse[(uint64_t)(uint32_t)r * (uint32_t)g.heads + h] = mrun + log2f(osum[0]) * kLn2;
         if (orow >= 0 && n < N) {
             const float inv = r >= 0 ? __builtin_amdgcn_rcpf(osum[0]) : 0.f;
             uint16_t* op = out + (uint64_t)(uint32_t)orow * (uint32_t)g.row + h * D + grp * 4;
@@ -609,7 +616,8 @@ __global__ __launch_bounds__((NWAVES + NL) * 64)
 __attribute__((amdgpu_waves_per_eu(D == 32 && BIAS_VEC && KT_FIXED == 9 && NWAVES + NL == 12 ? 6 : 1))) void
 attn_bf16_stream_kernel(
     Geometry g, int staged, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ table, uint16_t* __restrict__ out) {
+    const uint16_t* __restrict__ v, const float* __restrict__ table, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
     constexpr int THREADS = (NWAVES + NL) * 64;
     static_assert(KT_FIXED <= NWAVES, "one query tile per compute wave");
     extern __shared__ __align__(16) unsigned char smem[];
@@ -715,7 +723,9 @@ attn_bf16_stream_kernel(
             lds_barrier(); // A
             if (active) stream_qk<D, KT_FIXED, BIAS_VEC>(g, L, smem, wave, lane, u, s, b, bo, ts);
             lds_barrier(); // B
-            if (active) stream_pv<D, KT_FIXED>(L, smem, lane, b, ts);
+            if (active)
+                stream_pv<D, KT_FIXED>(L, smem, lane, b, ts, lse, (int)(u - fdiv(g.fd_heads, u) * (uint32_t)g.heads),
+                                       g.heads);
             u += per;
             if (u >= uend) break;
         }
@@ -725,7 +735,7 @@ attn_bf16_stream_kernel(
 
 // bf16 attention kernels share one signature: (geometry, staged, q, k, v, table, out)
 typedef void (*bf16_kernel_t)(Geometry, int, const uint16_t*, const uint16_t*, const uint16_t*,
-                              const float*, uint16_t*);
+                              const float*, uint16_t*, float*);
 
 // --------------------------------------------------------------------------
 // bf16 attention, key-blocked schedule: windows whose K and V do not fit in
@@ -805,7 +815,8 @@ __global__ __launch_bounds__(256) void bias_head_major_kernel(int table_size, in
 template <int D, bool BIAS_VEC>
 __global__ __launch_bounds__((kKbComputeWaves + kKbLoaders) * 64) void attn_bf16_kblock_kernel(
     Geometry g, int staged, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ bias_hm, uint16_t* __restrict__ out) {
+    const uint16_t* __restrict__ v, const float* __restrict__ bias_hm, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
     constexpr int THREADS = (kKbComputeWaves + kKbLoaders) * 64;
     constexpr int KSTEPS = D / 32, DT = D / 16, CH = D / 8, RPC = 64 / CH;
     constexpr int KCOPIES = kKbKeys * CH / 64;        // 1 KB copies per tensor per block
@@ -1077,6 +1088,10 @@ __global__ __launch_bounds__((kKbComputeWaves + kKbLoaders) * 64) void attn_bf16
 #pragma unroll
     for (int t = 0; t < 2; t++) {
         const float inv = qr[t] >= 0 ? __builtin_amdgcn_rcpf(osum[t][0]) : 0.f;
+        // the log-sum-exp of a real query's logits: reference (log2 units) plus the
+        // log of the row sum
+        if (lse != nullptr && qr[t] >= 0 && grp == 0)
+            lse[(uint64_t)(uint32_t)qr[t] * (uint32_t)g.heads + h] = (mref[t] + log2f(osum[t][0])) * kLn2;
         const int m = t * 16 + col;
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
@@ -1136,7 +1151,7 @@ hipError_t kblock_plan(const Geometry& g, int* blocks) {
 
 hipError_t launch_attention_kblock(const Geometry& g, bool staged, const uint16_t* q, const uint16_t* k,
                                    const uint16_t* v, const float* table, float* bias_hm, uint16_t* out,
-                                   hipStream_t s) {
+                                   float* lse, hipStream_t s) {
     const int64_t n = (int64_t)g.table_size * g.heads;
     const int64_t tb = (n + 255) / 256;
     hipLaunchKernelGGL(bias_head_major_kernel, dim3((unsigned)(tb < 1024 ? tb : 1024)), dim3(256), 0, s,
@@ -1145,7 +1160,7 @@ hipError_t launch_attention_kblock(const Geometry& g, bool staged, const uint16_
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kblock_variant_for(g), dim3((unsigned)kblock_workgroups(g)),
                        dim3((kKbComputeWaves + kKbLoaders) * 64), kb_lds(g).total, s, g, (int)staged, q, k, v,
-                       (const float*)bias_hm, out);
+                       (const float*)bias_hm, out, lse);
     return hipGetLastError();
 }
 
@@ -1273,11 +1288,11 @@ hipError_t bf16_plan(const Geometry& g, bool stream, int* blocks) {
 
 hipError_t launch_attention_bf16(const Geometry& g, bool stream, int blocks, bool staged, const uint16_t* q,
                                  const uint16_t* k, const uint16_t* v, const float* table,
-                                 uint16_t* out, hipStream_t s) {
+                                 uint16_t* out, float* lse, hipStream_t s) {
     const Bf16Variant var = bf16_variant_for(g, stream);
     const size_t lds = stream ? stream_lds(g).total : bf16_lds(g).total;
     hipLaunchKernelGGL(var.f, dim3((unsigned)blocks), dim3(var.waves * 64), lds, s, g,
-                       (int)staged, q, k, v, table, out);
+                       (int)staged, q, k, v, table, out, lse);
     return hipGetLastError();
 }
 

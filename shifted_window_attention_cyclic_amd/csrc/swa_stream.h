@@ -271,6 +271,7 @@ template <int KT>
 struct TileState {
     unsigned pk[KT][2]; // bf16 P: 4 keys per tile in two dwords
     int n, r;           // query index in the window; its source row (or -1)
+    float mc;           // the exponents' reference (the row max, log2 units)
 };
 
 // Byte offsets, within a head's bias slice, of the biases a lane adds: they
@@ -398,6 +399,7 @@ __device__ inline void stream_qk(const Geometry& g, const StreamLds& L, const un
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
     const float mc = (bmax == -INFINITY ? 0.f : bmax) * kLog2e;
+    ts.mc = mc;
 #pragma unroll
     for (int kt = 0; kt < KB; kt++) {
         float p[4];
@@ -410,10 +412,12 @@ __device__ inline void stream_qk(const Geometry& g, const StreamLds& L, const un
 
 // Second half: O^T = V^T P^T from V in buffer b, divide by the sum and leave
 // the O tile in this tile's rows of the LDS staging buffer (the loader waves
-// store it).
+// store it).  With lse, each real query's log-sum-exp of its logits goes to
+// lse[row * heads + hh] (natural log), from the reference and the row sum.
 template <int D, int KT_FIXED>
 __device__ inline void stream_pv(const StreamLds& L, unsigned char* smem, int lane, int b,
-                                 const TileState<(KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles)>& ts) {
+                                 const TileState<(KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles)>& ts,
+                                 float* __restrict__ lse = nullptr, int hh = 0, int heads = 0) {
     constexpr int DT = D / 16;
     constexpr int KB = KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles;
     const int col = lane & 15, grp = lane >> 4;
@@ -464,6 +468,8 @@ __device__ inline void stream_pv(const StreamLds& L, unsigned char* smem, int la
     // O tile into the staging rows of this tile (same swizzle)
     const int n = ts.n;
     const float inv = ts.r >= 0 ? __builtin_amdgcn_rcpf(osum[0]) : 0.f;
+    if (lse != nullptr && ts.r >= 0 && grp == 0)
+        lse[(uint64_t)(uint32_t)ts.r * (uint32_t)heads + hh] = (ts.mc + log2f(osum[0])) * kLn2;
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) {
         const u32x2 w = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};

@@ -71,6 +71,8 @@ def test_null_handles(lib):
     assert lib.swa_backward_noalloc(*([None] * 11)) == binding.SWA_ERR_INVALID_ARGUMENT
     assert lib.swa_layer_forward(*([None] * 10)) == binding.SWA_ERR_INVALID_ARGUMENT
     assert lib.swa_layer_attention(*([None] * 7)) == binding.SWA_ERR_INVALID_ARGUMENT
+    assert lib.swa_forward_lse(*([None] * 8)) == binding.SWA_ERR_INVALID_ARGUMENT
+    assert lib.swa_backward_lse(*([None] * 14)) == binding.SWA_ERR_INVALID_ARGUMENT
     # NULL pointers, an unknown dtype and a bad shape are refused before any device call
     assert lib.swa_projection(binding.SWA_BF16, None, None, None, 1, 8, 32, 8, None, None, None,
                               None) == binding.SWA_ERR_INVALID_ARGUMENT
