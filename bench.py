@@ -5,9 +5,12 @@
 A step is one swa_forward call over the whole workload (gather, window
 attention with bias and mask, softmax, PV and scatter), inputs already in HBM.
 With --pass backward a step is one swa_backward call (dq, dk, dv and the
-bias-table gradient of the same workload).  With --pass layer a step is one
-swa_layer_forward call: the query/key/value projection of the token
-embeddings, the window attention and the output projection.
+bias-table gradient of the same workload); with --from-forward it is one
+swa_backward_lse call, which takes the softmax statistics and the output that
+swa_forward_lse produced (once per input set, before the timed steps).
+With --pass layer a step is one swa_layer_forward call: the
+query/key/value projection of the token embeddings, the window attention
+and the output projection.
 Default workload: bf16, B=1, 540x1080 grid (1/12 degree field at patch 4),
 8 heads x 64, window 12x12, shift 6.  Prints one JSON line.
 
@@ -203,6 +206,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--from-forward", action="store_true",
+                    help="--pass backward: time swa_backward_lse from swa_forward_lse's output and statistics")
     ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward", "layer"],
                     help="time swa_forward (default), swa_backward or swa_layer_forward")
     ap.add_argument("--layer", default="auto", choices=["auto", "fused", "unfused"],
@@ -218,7 +223,8 @@ def main():
 
     import torch
 
-    from shifted_window_attention_cyclic_amd import WindowAttention, swa_backward, swa_forward
+    from shifted_window_attention_cyclic_amd import (WindowAttention, swa_backward, swa_backward_lse, swa_forward,
+                                                     swa_forward_lse)
     from shifted_window_attention_cyclic_amd.inputs import WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
@@ -249,10 +255,17 @@ def main():
             s["dout"] = dout_host.cuda()
             s["dq"], s["dk"], s["dv"] = (torch.empty_like(s["q"]) for _ in range(3))
             s["dtable"] = torch.empty_like(s["table"])
+            if args.from_forward:
+                s["lse"] = torch.empty(att.io_shape[:-1], dtype=torch.float32, device="cuda")
+                swa_forward_lse(att.handle, s["q"], s["k"], s["v"], s["table"], s["out"], s["lse"])
+        torch.cuda.synchronize()
 
     def step(i):
         s = sets[i % nsets]
-        if backward:
+        if backward and args.from_forward:
+            swa_backward_lse(att.handle, s["q"], s["k"], s["v"], s["table"], s["out"], s["lse"], s["dout"], s["dq"],
+                             s["dk"], s["dv"], s["dtable"], ws)
+        elif backward:
             swa_backward(att.handle, s["q"], s["k"], s["v"], s["table"], s["dout"], s["dq"], s["dk"], s["dv"],
                          s["dtable"], ws)
         else:
@@ -286,13 +299,17 @@ def main():
     nominal_flops = info.nominal_flops * flop_mul
     table_bytes = 4.0 * math.prod(p.table_shape)
     tensor_bytes = (info.algorithmic_bytes - table_bytes) / 4
-    alg_bytes = (7 * tensor_bytes + 2 * table_bytes) if backward else info.algorithmic_bytes
+    # from the forward's statistics the backward also reads out and lse (one float per token and head)
+    lse_bytes = 4.0 * info.tokens * p.heads
+    alg_bytes = ((8 * tensor_bytes + lse_bytes if args.from_forward else 7 * tensor_bytes) + 2 * table_bytes
+                 if backward else info.algorithmic_bytes)
     tflops = nominal_flops / (ms_per_step * 1e-3) / 1e12
     useful = 4.0 * useful_pairs(p) * p.head_dim * p.heads * flop_mul
     achieved_gbs = alg_bytes / (avg_launch_ms * 1e-3) / 1e9
     kernel_tflops = nominal_flops / (avg_launch_ms * 1e-3) / 1e12
     peak_tf = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = traffic_from_profiles(p.name, backward) if args.variant == "fused" else None
+    traffic = (traffic_from_profiles(p.name, backward, tag="bwdlse_" if args.from_forward else None)
+               if args.variant == "fused" else None)
     # the roof that binds: HBM below the ridge (peak FLOP/s over peak bytes/s), MFMA above it
     intensity = nominal_flops / alg_bytes
     mfma_bound = intensity > peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -317,6 +334,7 @@ def main():
             "workload": p.name, "batch": p.batch, "grid_thw": list(p.extent),
             "padded_thw": list(p.padded), "window": list(p.window), "shift": list(p.shift),
             "heads": p.heads, "head_dim": p.head_dim, "variant": args.variant, "pass": args.which,
+            **({"statistics": "forward" if args.from_forward else "recomputed"} if backward else {}),
             "input_sets_rotated": nsets,
         },
         "tokens_per_s": round(info.tokens / (ms_per_step * 1e-3), 1),

@@ -17,7 +17,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kXcds = 8; // MI355X: workgroups are dealt to 8 XCDs round-robin
 
 // Blocks are dealt to the XCDs round-robin (block i to XCD i % 8).  This maps

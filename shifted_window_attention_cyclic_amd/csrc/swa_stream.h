@@ -51,6 +51,7 @@ namespace swa {
 // reads V^T fragments with ds_read_b64_tr_b16, which hands lane i of each
 // 16-lane group element i of the 4 rows its group addresses.
 // --------------------------------------------------------------------------
+constexpr float kLn2 = 0.6931471805599453f; // natural log of 2: log-sum-exp from log2 units
 constexpr int kBufs = 2;       // buffers each of K, Q and V
 constexpr int kTableSlots = 4; // token tables of units i .. i+3
 constexpr int kStreamMaxTiles = 9;
