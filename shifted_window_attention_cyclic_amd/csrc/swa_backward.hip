@@ -39,6 +39,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "swa_backward.h"
 #include "swa_device.h"
 #include "swa_geometry.h"
@@ -374,25 +376,76 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
     __syncthreads(); // pass 2 is done with P
     if ((size_t)items * 4 <= (size_t)NP * NP * 2) {
         float* part = (float*)(smem + L.pm);
-        for (int it = tid; it < items; it += THREADS) {
-            const int ex = it % g.tdx, rr = it / g.tdx;
-            const int rk = rr % R, rq = rr / R;
+        // A thread takes one (key row, x offset) and a share of the query rows,
+        // so the integer divisions that place it happen once, not per sum;
+        // neighbouring lanes take neighbouring key rows, whose reads sit a window
+        // row apart in one dS row and so spread over the banks.
+        const int cols = R * g.tdx;
+        const int split = cols < THREADS ? THREADS / cols : 1;
+        for (int t = tid; t < cols * split; t += THREADS) {
+            const int rk = t % R, rest = t / R;
+            const int ex = rest % g.tdx, first = rest / g.tdx;
             const int dx = ex - (wx - 1);
-            const int n0 = rq * wx + dx, m0 = rk * wx;
-            float acc = 0.f;
-            for (int kx = dx < 0 ? -dx : 0; kx < wx - (dx > 0 ? dx : 0); kx++) acc += ds_at(n0 + kx, m0 + kx);
-            part[it] = acc;
+            const int lo = dx < 0 ? -dx : 0, hi = wx - (dx > 0 ? dx : 0);
+            const int m0 = rk * wx;
+            // the thread's query rows (up to G at a time, G the thread's row count
+            // rounded up to 2, 4 or 8) share the loop over x, so their reads are
+            // independent and in flight together; each sum still adds its terms in
+            // x order
+            auto rows = [&](auto gtag) __attribute__((always_inline)) {
+                constexpr int G = decltype(gtag)::value;
+                for (int rq0 = first; rq0 < R; rq0 += G * split) {
+                    int n0[G];
+                    float acc[G];
+#pragma unroll
+                    for (int u = 0; u < G; u++) {
+                        const int rq = rq0 + u * split;
+                        n0[u] = (rq < R ? rq : first) * wx + dx;
+                        acc[u] = 0.f;
+                    }
+                    for (int kx = lo; kx < hi; kx++) {
+                        float x[G];
+#pragma unroll
+                        for (int u = 0; u < G; u++) x[u] = ds_at(n0[u] + kx, m0 + kx);
+#pragma unroll
+                        for (int u = 0; u < G; u++) acc[u] += x[u];
+                    }
+#pragma unroll
+                    for (int u = 0; u < G; u++) {
+                        const int rq = rq0 + u * split;
+                        if (rq < R) part[(rq * R + rk) * g.tdx + ex] = acc[u];
+                    }
+                }
+            };
+            const int most = (R - 1) / split + 1; // the most query rows a thread takes
+            if (most <= 2)
+                rows(std::integral_constant<int, 2>());
+            else if (most <= 4)
+                rows(std::integral_constant<int, 4>());
+            else
+                rows(std::integral_constant<int, 8>());
         }
         __syncthreads();
         for (int e = tid; e < g.table_size; e += THREADS) {
             const int et = e / (g.tdy * g.tdx), r0 = e - et * (g.tdy * g.tdx);
             const int ey = r0 / g.tdx, ex = r0 - ey * g.tdx;
             const int dt = et - (g.win[0] - 1), dy = ey - (g.win[1] - 1);
+            // four reads in flight at a time, all issued: a step past the end
+            // re-reads the last term and adds +0, which leaves the sum exact (a sum
+            // that starts at +0 is never -0)
+            const int ylo = dy < 0 ? -dy : 0, yhi = g.win[1] - (dy > 0 ? dy : 0);
             float acc = 0.f;
             for (int kt = dt < 0 ? -dt : 0; kt < g.win[0] - (dt > 0 ? dt : 0); kt++)
-                for (int ky = dy < 0 ? -dy : 0; ky < g.win[1] - (dy > 0 ? dy : 0); ky++) {
-                    const int rq = (kt + dt) * g.win[1] + ky + dy, rk = kt * g.win[1] + ky;
-                    acc += part[(rq * R + rk) * g.tdx + ex];
+                for (int ky = ylo; ky < yhi; ky += 4) {
+                    float x[4];
+#pragma unroll
+                    for (int u = 0; u < 4; u++) {
+                        const int yy = ky + u < yhi ? ky + u : yhi - 1;
+                        const int rq = (kt + dt) * g.win[1] + yy + dy, rk = kt * g.win[1] + yy;
+                        x[u] = part[(rq * R + rk) * g.tdx + ex];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; u++) acc += ky + u < yhi ? x[u] : 0.f;
                 }
             dst[e] = acc;
         }
