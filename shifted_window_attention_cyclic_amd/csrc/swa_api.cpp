@@ -25,6 +25,7 @@ struct swa_handle {
     int device;
     int schedule;       // bf16: SWA_SCHEDULE_STREAM, _BLOCK or _KEYBLOCK; fp32: 0
     int blocks;         // bf16: workgroups per attention launch
+    int bwd_blocks;     // workgroups of the persistent backward kernel, 0: one-shot kernels
     int layer_path;     // SWA_LAYER_FUSED or SWA_LAYER_UNFUSED
     size_t wm_bytes;    // bytes of one window-major tensor
     void* workspace;    // staged variant: q, k, v, o window-major tensors
@@ -279,6 +280,9 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
         }
         if (schedule == 0) return fail(SWA_ERR_UNSUPPORTED, "attention kernel does not fit on a compute unit");
     }
+    int bwd_blocks = 0;
+    if ((e = swa::backward_plan(g, cfg->dtype == SWA_BF16, &bwd_blocks)) != hipSuccess)
+        return fail_hip(e, "occupancy query");
 
     swa_handle* h = new (std::nothrow) swa_handle();
     if (!h) return fail(SWA_ERR_OUT_OF_MEMORY, "host allocation");
@@ -288,6 +292,7 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
     h->device = dev;
     h->schedule = schedule;
     h->blocks = blocks;
+    h->bwd_blocks = bwd_blocks;
     // AUTO takes the unfused layer: it is the faster one on every measured shape
     h->layer_path = fused_layer && cfg->layer == SWA_LAYER_FUSED ? SWA_LAYER_FUSED : SWA_LAYER_UNFUSED;
     h->wm_bytes = (size_t)g.windows * g.N * g.row * eb;
@@ -454,7 +459,7 @@ static swa_status backward(swa_handle* h, const void* q, const void* k, const vo
             if (j != i && all[j] && overlap(all[i], len[i], all[j], len[j]))
                 return fail(SWA_ERR_INVALID_ARGUMENT, "a gradient or the workspace overlaps another argument");
     hipError_t e = swa::launch_backward(g, bf16, q, k, v, bias_table, dout, dq, dk, dv, dtable, workspace, o, lse,
-                                        (hipStream_t)stream);
+                                        h->bwd_blocks, (hipStream_t)stream);
     return e == hipSuccess ? SWA_OK : fail_hip(e, "backward launch");
 }
 
@@ -508,7 +513,7 @@ swa_status swa_backward_noalloc(swa_handle* h, const void* q, const void* k, con
     const swa_status st = scratch_for_device(dev, &sp); // looked up in swa_create: no runtime call here
     if (st != SWA_OK) return st;
     e = swa::launch_backward_scratch(g, bf16, q, k, v, bias_table, dout, dq, dk, dv, dtable, sp, kScratchBytes,
-                                     (hipStream_t)stream);
+                                     h->bwd_blocks, (hipStream_t)stream);
     return e == hipSuccess ? SWA_OK : fail_hip(e, "backward launch");
 }
 

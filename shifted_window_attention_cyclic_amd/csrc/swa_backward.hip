@@ -19,14 +19,20 @@
 // single-workgroup backward pass is therefore bitwise reproducible.
 //
 // Kernels:
-//   attn_bf16_bwd_kernel  one workgroup per unit, windows of up to 9 query
-//                         tiles.  Pass 1, a query tile per wave: recompute the
-//                         logits and P on MFMA, dP^T = V dO^T, dS and
-//                         dQ^T = K^T dS^T; P and dS go to LDS as [query][key]
-//                         bf16.  Pass 2, a key tile per wave: dV^T = dO^T P and
-//                         dK^T = Q^T dS, with the operands fetched by
-//                         transposing LDS reads.  Then the unit's share of the
-//                         table gradient, an entry per thread.
+//   attn_bf16_bwd_pkernel windows of up to 9 query tiles: persistent
+//                         workgroups, 9 compute waves that take unit after
+//                         unit and 2 loader waves that copy the next unit's
+//                         Q, K, V and dO into LDS as this one's are done with.
+//                         Per unit (bwd_unit): pass 1, a query tile per wave:
+//                         recompute the logits and P on MFMA, dP^T = V dO^T, dS
+//                         and dQ^T = K^T dS^T; P and dS go to LDS as
+//                         [query][key] bf16.  Pass 2, a key tile per wave:
+//                         dV^T = dO^T P and dK^T = Q^T dS, with the operands
+//                         fetched by transposing LDS reads.  Then the unit's
+//                         share of the table gradient, gathered.
+//   attn_bf16_bwd_kernel  the same per unit, one workgroup per unit, where the
+//                         persistent kernel's LDS (second table and bias
+//                         slots) does not fit.
 //   attn_f32_bwd_kernel   the fp32 counterpart: one thread per query, then one
 //                         per key.
 //   attn_bf16_bwd_q_kernel, attn_bf16_bwd_kv_kernel
@@ -82,86 +88,94 @@ __device__ inline u32x2 tr_read(const unsigned char* p) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)p));
 }
 
-template <int D, bool BIAS_VEC>
-__global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
-    Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ dtab_units, uint32_t work0,
-    uint32_t count) {
+// Block barriers of a workgroup whose loader waves issue LDS copies while
+// its compute waves read LDS.  The compute waves' barrier fences LDS only
+// (they issue no copies, so nothing of theirs is in flight into LDS).  The
+// loader waves' barrier has no release fence, which would make the compiler
+// wait for every copy in flight; their only other LDS writes are table words
+// (covered by the lgkmcnt wait), and the empty asm statements keep the
+// compiler from moving LDS accesses across it.
+__device__ inline void bwd_compute_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__device__ inline void bwd_loader_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// unit -> head, batch item and window coordinates
+struct BwdUnit {
+    int h, b, wc[3];
+};
+__device__ inline BwdUnit bwd_decode(const Geometry& g, uint32_t work) {
+    BwdUnit U;
+    const uint32_t wi = fdiv(g.fd_heads, work);
+    U.h = (int)(work - wi * (uint32_t)g.heads);
+    U.b = (int)fdiv(g.fd_nW, wi);
+    const uint32_t r = wi - (uint32_t)U.b * (uint32_t)g.nW;
+    const uint32_t r2 = fdiv(g.fd_nwin2, r);
+    U.wc[2] = (int)(r - r2 * (uint32_t)g.nwin[2]);
+    U.wc[0] = (int)fdiv(g.fd_nwin1, r2);
+    U.wc[1] = (int)(r2 - (uint32_t)U.wc[0] * (uint32_t)g.nwin[1]);
+    return U;
+}
+
+// Token word of local token n of a window (batch item b, window coordinates
+// wc): source row + 1 (0 for pad and for slots past N) | mask field << 28;
+// and the token's key bias offset.
+template <bool BIAS_VEC>
+__device__ inline void bwd_token(const Geometry& g, int b, const int wc[3], int n, int& word, uint16_t& kbo) {
+    if (n < g.N) {
+        int l[3];
+        local_coords(g, n, l[0], l[1], l[2]);
+        int region = 0, tok = b;
+        bool is_pad = false;
+#pragma unroll
+        for (int a = 0; a < 3; a++) {
+            const int cr = wc[a] * g.win[a] + l[a];
+            int c = cr + g.shift[a];
+            if (c >= g.pad[a]) c -= g.pad[a];
+            is_pad |= c >= g.ext[a];
+            if (!g.cyc[a] && cr >= g.pad[a] - g.shift[a]) region |= 1 << a;
+            tok = tok * g.ext[a] + c;
+        }
+        word = ((is_pad ? -1 : tok) + 1) | ((region | (is_pad ? 8 : 0)) << 28);
+        kbo = (uint16_t)((l[0] * g.tdy + l[1]) * g.tdx + l[2]);
+    } else {
+        word = 15 << 28;
+        kbo = BIAS_VEC ? 3 : 0; // keeps qb - kb (- 3) inside the table
+    }
+}
+
+// Whether the table-gradient share is gathered in two stages: when the
+// per-(query row, key row, x offset) partial sums fit the P region.
+__host__ __device__ inline bool bwd_gather_staged(const Geometry& g) {
+    const size_t R = (size_t)g.win[0] * g.win[1];
+    const size_t NP = (size_t)(g.N + 15) / 16 * 16;
+    return R * R * g.tdx * 4 <= NP * NP * 2;
+}
+
+// Pass 1, pass 2 and the table-gradient share of one unit whose Q, K, V and
+// dO ([token][d], swizzled), token table tw, key bias offsets kb and bias
+// slice are in LDS, into dq, dk, dv and the share dst.  Run by waves 0 ..
+// kBwdWaves - 1; barrier() is the block barrier, which any other wave of the
+// workgroup meets as often: twice, three times when bwd_gather_staged(g).
+template <int D, bool BIAS_VEC, typename Barrier>
+__device__ __forceinline__ void bwd_unit(const Geometry& g, unsigned char* smem, const BwdLds& L,
+                                         const float* bias, const int* tw, const uint16_t* kb, int h,
+                                         bool masked_window, uint16_t* __restrict__ dq, uint16_t* __restrict__ dk,
+                                         uint16_t* __restrict__ dv, float* __restrict__ dst, Barrier&& barrier) {
     constexpr int THREADS = kBwdWaves * 64;
-    constexpr int KSTEPS = D / 32, DT = D / 16, CH = D / 8, RPC = 64 / CH;
+    constexpr int KSTEPS = D / 32, DT = D / 16;
     constexpr int KB = kBwdMaxTiles;
-    extern __shared__ __align__(16) unsigned char smem[];
-    const BwdLds L = bwd_lds(g);
     const int N = g.N, NP = L.NP, KT = NP / 16;
-    float* bias = (float*)(smem + L.bias);
-    int* tw = (int*)(smem + L.tw);
-    uint16_t* kb = (uint16_t*)(smem + L.kb);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;
-
-    // units work0 .. work0 + count - 1 (all of them, or one pass of the no-workspace entry)
-    const uint32_t work = work0 + (uint32_t)xcd_work_index(blockIdx.x, count);
-    const uint32_t wi = fdiv(g.fd_heads, work);
-    const int h = (int)(work - wi * (uint32_t)g.heads);
-    const int b = (int)fdiv(g.fd_nW, wi);
-    int wc[3];
-    {
-        const uint32_t r = wi - (uint32_t)b * (uint32_t)g.nW;
-        const uint32_t r2 = fdiv(g.fd_nwin2, r);
-        wc[2] = (int)(r - r2 * (uint32_t)g.nwin[2]);
-        wc[0] = (int)fdiv(g.fd_nwin1, r2);
-        wc[1] = (int)(r2 - (uint32_t)wc[0] * (uint32_t)g.nwin[1]);
-    }
-    const bool masked_window = window_maybe_masked(g, wc);
-
-    // ---- token table (packed word: source row + 1 | mask field << 28), key
-    // bias offsets, this head's bias slice
-    for (int n = tid; n < NP; n += THREADS) {
-        if (n < N) {
-            int l[3];
-            local_coords(g, n, l[0], l[1], l[2]);
-            int region = 0, tok = b;
-            bool is_pad = false;
-#pragma unroll
-            for (int a = 0; a < 3; a++) {
-                const int cr = wc[a] * g.win[a] + l[a];
-                int c = cr + g.shift[a];
-                if (c >= g.pad[a]) c -= g.pad[a];
-                is_pad |= c >= g.ext[a];
-                if (!g.cyc[a] && cr >= g.pad[a] - g.shift[a]) region |= 1 << a;
-                tok = tok * g.ext[a] + c;
-            }
-            tw[n] = ((is_pad ? -1 : tok) + 1) | ((region | (is_pad ? 8 : 0)) << 28);
-            kb[n] = (uint16_t)((l[0] * g.tdy + l[1]) * g.tdx + l[2]);
-        } else {
-            tw[n] = 15 << 28;
-            kb[n] = BIAS_VEC ? 3 : 0; // keeps qb - kb (- 3) inside the table
-        }
-    }
-    for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)i * g.heads + h];
-    __syncthreads();
-
-    // ---- Q, K, V, dO of the window into LDS ([token][d], swizzled; pad rows copy
-    // row 0: their weights are 0, and pad queries are excluded below)
-    {
-        const int ncopy = NP * CH / 64;
-        const int m0 = lane / CH;
-        const uint16_t* src[4] = {q, k, v, dout};
-        const size_t dst[4] = {L.qs, L.ks, L.vs, L.dos};
-        for (int c = wave; c < 4 * ncopy; c += kBwdWaves) {
-            const int tsr = c / ncopy, cc = c - tsr * ncopy;
-            const int r1 = tw[cc * RPC + m0] & kRowMask;
-            const uint64_t off = (uint64_t)(uint32_t)(r1 == 0 ? 0 : r1 - 1) * (uint32_t)g.row + h * D +
-                                 copy_chunk<D>(cc * RPC + m0, lane) * 8;
-            __builtin_amdgcn_global_load_lds((const void*)(src[tsr] + off), (lds_void*)(smem + dst[tsr] + cc * 1024),
-                                             16, 0, 0);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); // this wave's copies have landed
-    __syncthreads();
-
     const uint16_t* Qs = (const uint16_t*)(smem + L.qs);
     const uint16_t* Ks = (const uint16_t*)(smem + L.ks);
     const uint16_t* Vs = (const uint16_t*)(smem + L.vs);
@@ -318,7 +332,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
                                                 pack_bf16x2(acc[dt][2] * g.scale, acc[dt][3] * g.scale)};
         }
     }
-    __syncthreads();
+    barrier(); // P and dS complete
 
     // ---- pass 2: key tile wave; contraction over the queries in pairs of tiles
     if (wave < KT) {
@@ -366,15 +380,13 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
     // are masked or involve pad hold dS = 0).  Two balanced stages when the
     // partial sums fit in the P region (free once pass 2 is done): per
     // (query row, key row, x offset) along x, then per entry over the rows.
-    float* dst = dtab_units + (size_t)(work - work0) * g.table_size;
     const uint16_t* dSm = (const uint16_t*)(smem + L.dsm);
     auto ds_at = [&](int n, int m) __attribute__((always_inline)) {
         return __builtin_bit_cast(float, (unsigned)dSm[(size_t)n * NP + m] << 16);
     };
     const int wx = g.win[2], R = g.win[0] * g.win[1]; // tokens per window row; rows (t, y) per window
-    const int items = R * R * g.tdx;
-    __syncthreads(); // pass 2 is done with P
-    if ((size_t)items * 4 <= (size_t)NP * NP * 2) {
+    barrier(); // pass 2 is done with P
+    if (bwd_gather_staged(g)) {
         float* part = (float*)(smem + L.pm);
         // A thread takes one (key row, x offset) and a share of the query rows,
         // so the integer divisions that place it happen once, not per sum;
@@ -425,7 +437,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
             else
                 rows(std::integral_constant<int, 8>());
         }
-        __syncthreads();
+        barrier(); // stage 1 complete
         for (int e = tid; e < g.table_size; e += THREADS) {
             const int et = e / (g.tdy * g.tdx), r0 = e - et * (g.tdy * g.tdx);
             const int ey = r0 / g.tdx, ex = r0 - ey * g.tdx;
@@ -467,6 +479,193 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
     }
 }
 
+// One workgroup per unit: the token table, the bias slice and the unit's Q,
+// K, V and dO into LDS, then bwd_unit.
+template <int D, bool BIAS_VEC>
+__global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
+    Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ dtab_units, uint32_t work0,
+    uint32_t count) {
+    constexpr int THREADS = kBwdWaves * 64;
+    constexpr int CH = D / 8, RPC = 64 / CH;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const BwdLds L = bwd_lds(g);
+    const int NP = L.NP;
+    float* bias = (float*)(smem + L.bias);
+    int* tw = (int*)(smem + L.tw);
+    uint16_t* kb = (uint16_t*)(smem + L.kb);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // units work0 .. work0 + count - 1 (all of them, or one pass of the no-workspace entry)
+    const uint32_t work = work0 + (uint32_t)xcd_work_index(blockIdx.x, count);
+    const BwdUnit U = bwd_decode(g, work);
+
+    for (int n = tid; n < NP; n += THREADS) {
+        int word;
+        uint16_t kbo;
+        bwd_token<BIAS_VEC>(g, U.b, U.wc, n, word, kbo);
+        tw[n] = word;
+        kb[n] = kbo;
+    }
+    for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)i * g.heads + U.h];
+    __syncthreads();
+
+    // ---- Q, K, V, dO of the window into LDS ([token][d], swizzled; pad rows copy
+    // row 0: their weights are 0, and pad queries are excluded)
+    {
+        const int ncopy = NP * CH / 64;
+        const int m0 = lane / CH;
+        const uint16_t* src[4] = {q, k, v, dout};
+        const size_t dst[4] = {L.qs, L.ks, L.vs, L.dos};
+        for (int c = wave; c < 4 * ncopy; c += kBwdWaves) {
+            const int tsr = c / ncopy, cc = c - tsr * ncopy;
+            const int r1 = tw[cc * RPC + m0] & kRowMask;
+            const uint64_t off = (uint64_t)(uint32_t)(r1 == 0 ? 0 : r1 - 1) * (uint32_t)g.row + U.h * D +
+                                 copy_chunk<D>(cc * RPC + m0, lane) * 8;
+            __builtin_amdgcn_global_load_lds((const void*)(src[tsr] + off), (lds_void*)(smem + dst[tsr] + cc * 1024),
+                                             16, 0, 0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); // this wave's copies have landed
+    __syncthreads();
+    bwd_unit<D, BIAS_VEC>(g, smem, L, bias, tw, kb, U.h, window_maybe_masked(g, U.wc), dq, dk, dv,
+                          dtab_units + (size_t)(work - work0) * g.table_size, [] { bwd_compute_barrier(); });
+}
+
+// ---- the same computation in persistent workgroups (one per compute unit):
+// 9 compute waves run bwd_unit on unit after unit, and two loader waves fill
+// the LDS for the next unit behind them.  The next unit's token table and
+// bias slice go to the other of two slots while the compute waves run pass 1;
+// its K and V replace this unit's once pass 1 is done with them, its Q and dO
+// once pass 2 is; the copies land while the table gradient is gathered.  The
+// loader waves build the token words of the rows they copy themselves, so
+// they need no barrier of their own.
+constexpr int kBwdPLoaders = 2;
+
+struct BwdPLds {
+    BwdLds L;      // Q, K, V, dO, P and dS as in the one-shot kernel
+    size_t bias, tw, kb, bias_stride, tw_stride, kb_stride, total; // slot 0 and slot strides
+};
+
+__host__ __device__ inline BwdPLds bwd_plds(const Geometry& g) {
+    BwdPLds P;
+    P.L = bwd_lds(g);
+    P.bias_stride = ((size_t)g.table_size + 63) / 64 * 256; // whole 64-float copies
+    P.tw_stride = (size_t)P.L.NP * 4;
+    P.kb_stride = ((size_t)P.L.NP * 2 + 15) / 16 * 16;
+    P.bias = P.L.bias;
+    P.tw = P.bias + 2 * P.bias_stride;
+    P.kb = P.tw + 2 * P.tw_stride;
+    P.total = P.kb + 2 * P.kb_stride;
+    return P;
+}
+
+template <int D, bool BIAS_VEC>
+__global__ __launch_bounds__((kBwdWaves + kBwdPLoaders) * 64) void attn_bf16_bwd_pkernel(
+    Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ dtab_units, uint32_t work0,
+    uint32_t count) {
+    constexpr int CH = D / 8, RPC = 64 / CH;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const BwdPLds P = bwd_plds(g);
+    const int NP = P.L.NP;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool staged = bwd_gather_staged(g);
+
+    // units work0 + u, u = 0 .. count - 1: each XCD takes a contiguous range,
+    // its workgroups in turn
+    const uint32_t per = gridDim.x / kXcds, xcd = blockIdx.x % kXcds;
+    const uint32_t uend = (uint32_t)((uint64_t)count * (xcd + 1) / kXcds);
+    const uint32_t u0 = (uint32_t)((uint64_t)count * xcd / kXcds) + blockIdx.x / kXcds;
+    if (u0 >= uend) return;
+
+    if (wave >= kBwdWaves) {
+        // ---- loader waves: copy cc = j, j + 2, ... of each tensor (RPC rows of
+        // 1 KB each); the lanes of a row also write its token word and bias offset
+        const int j = wave - kBwdWaves;
+        constexpr int MAXC = (kBwdMaxTiles * 16 * CH / 64 + kBwdPLoaders - 1) / kBwdPLoaders;
+        const int ncopy = NP * CH / 64;
+        const int mine = (ncopy - j + kBwdPLoaders - 1) / kBwdPLoaders;
+        uint64_t off[MAXC]; // source offsets of this wave's copies of the next unit
+        auto prepare = [&](uint32_t u, int slot) __attribute__((always_inline)) {
+            const BwdUnit U = bwd_decode(g, work0 + u);
+            int* tws = (int*)(smem + P.tw + slot * P.tw_stride);
+            uint16_t* kbs = (uint16_t*)(smem + P.kb + slot * P.kb_stride);
+#pragma unroll
+            for (int i = 0; i < MAXC; i++) {
+                if (i < mine) {
+                    const int n = (j + i * kBwdPLoaders) * RPC + lane / CH;
+                    int word;
+                    uint16_t kbo;
+                    bwd_token<BIAS_VEC>(g, U.b, U.wc, n, word, kbo);
+                    if (lane % CH == 0) {
+                        tws[n] = word;
+                        kbs[n] = kbo;
+                    }
+                    const int r1 = word & kRowMask;
+                    off[i] = (uint64_t)(uint32_t)(r1 == 0 ? 0 : r1 - 1) * (uint32_t)g.row + U.h * D +
+                             copy_chunk<D>(n, lane) * 8;
+                }
+            }
+            float* bs = (float*)(smem + P.bias + slot * P.bias_stride);
+            for (int i0 = j * 64; i0 < g.table_size; i0 += kBwdPLoaders * 64) {
+                const int i = i0 + lane;
+                const float* src = table + (i < g.table_size ? (size_t)i * g.heads + U.h : 0);
+                __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(bs + i0), 4, 0, 0);
+            }
+        };
+        auto issue = [&](const uint16_t* src, size_t dst) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < MAXC; i++)
+                if (i < mine)
+                    __builtin_amdgcn_global_load_lds((const void*)(src + off[i]),
+                                                     (lds_void*)(smem + dst + (j + i * kBwdPLoaders) * 1024), 16, 0, 0);
+        };
+        prepare(u0, 0);
+        issue(q, P.L.qs);
+        issue(k, P.L.ks);
+        issue(v, P.L.vs);
+        issue(dout, P.L.dos);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        bwd_loader_barrier(); // the first unit is in LDS
+        int it = 0;
+        for (uint32_t u = u0; u < uend; u += per, it++) {
+            const bool next = u + per < uend;
+            if (next) prepare(u + per, (it + 1) & 1); // the slot the unit before this one used
+            bwd_loader_barrier();                     // pass 1 done with K and V
+            if (next) {
+                issue(k, P.L.ks);
+                issue(v, P.L.vs);
+            }
+            bwd_loader_barrier(); // pass 2 done with Q and dO
+            if (next) {
+                issue(q, P.L.qs);
+                issue(dout, P.L.dos);
+            }
+            if (staged) bwd_loader_barrier(); // the gather's first stage
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            bwd_loader_barrier(); // the unit is done, the next one is in LDS
+        }
+        return;
+    }
+
+    bwd_compute_barrier(); // the first unit is in LDS
+    int it = 0;
+    for (uint32_t u = u0; u < uend; u += per, it++) {
+        const int slot = it & 1;
+        const BwdUnit U = bwd_decode(g, work0 + u);
+        bwd_unit<D, BIAS_VEC>(g, smem, P.L, (const float*)(smem + P.bias + slot * P.bias_stride),
+                              (const int*)(smem + P.tw + slot * P.tw_stride),
+                              (const uint16_t*)(smem + P.kb + slot * P.kb_stride), U.h, window_maybe_masked(g, U.wc),
+                              dq, dk, dv, dtab_units + (size_t)u * g.table_size, [] { bwd_compute_barrier(); });
+        bwd_compute_barrier(); // the unit is done, the next one is in LDS
+    }
+}
+
 // ---- bf16 backward for windows beyond the single-workgroup kernel (more than
 // 9 query tiles, e.g. 2x12x12 or 32x32): nothing of size N x N is kept.  Two
 // kernels, both streaming 32-token blocks of the other side through an LDS
@@ -505,25 +704,6 @@ __device__ inline void bwd_wait_vm(int n) {
     case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
     default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
     }
-}
-
-// Block barrier of the compute waves, which issue no LDS copies: the fence
-// orders LDS accesses only.
-__device__ inline void bwd_compute_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Block barrier of the loader waves.  Their only LDS writes are copies they
-// have waited for with vmcnt; a release fence would make the compiler wait
-// for every copy in flight.  The empty asm statements keep the compiler from
-// moving LDS accesses across the barrier.
-__device__ inline void bwd_loader_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
 }
 
 // The loader waves' side of a stream of T blocks through the ring.  Block s
@@ -1370,6 +1550,32 @@ static bwd_bf16_t bwd_bf16_variant(const Geometry& g) {
     return bv ? attn_bf16_bwd_kernel<64, true> : attn_bf16_bwd_kernel<64, false>;
 }
 
+static bwd_bf16_t bwd_bf16_pvariant(const Geometry& g) {
+    const bool bv = g.win[2] % 4 == 0;
+    if (g.head_dim == 32) return bv ? attn_bf16_bwd_pkernel<32, true> : attn_bf16_bwd_pkernel<32, false>;
+    if (g.head_dim == 128) return bv ? attn_bf16_bwd_pkernel<128, true> : attn_bf16_bwd_pkernel<128, false>;
+    return bv ? attn_bf16_bwd_pkernel<64, true> : attn_bf16_bwd_pkernel<64, false>;
+}
+
+#ifndef SWA_BWD_PERSISTENT
+#define SWA_BWD_PERSISTENT 1
+#endif
+
+hipError_t backward_plan(const Geometry& g, bool bf16, int* blocks) {
+    *blocks = 0;
+    if (!SWA_BWD_PERSISTENT || !bf16 || !bwd_small_fits(g) || bwd_plds(g).total > (size_t)kLdsBytes)
+        return hipSuccess;
+    int per_cu = 0, dev = 0, cus = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)bwd_bf16_pvariant(g),
+                                                                (kBwdWaves + kBwdPLoaders) * 64, bwd_plds(g).total);
+    if (e != hipSuccess) return e;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int n = per_cu * cus / kXcds * kXcds;
+    *blocks = n > 0 ? n : 0;
+    return hipSuccess;
+}
+
 // Compute waves of the query kernel (16 queries each).  Heads of up to 64:
 // whichever of 4, 6 and 8 waves leaves the fewest idle query slots in the
 // last block, ties to more waves (fewer re-reads of K and V).  128-wide heads:
@@ -1389,7 +1595,10 @@ static int bwd_q_waves(const Geometry& g) {
 }
 
 hipError_t prepare_backward_kernels(int max_lds) {
-    const void* fs[] = {(const void*)attn_bf16_bwd_kernel<32, true>,  (const void*)attn_bf16_bwd_kernel<32, false>,
+    const void* fs[] = {(const void*)attn_bf16_bwd_pkernel<32, true>, (const void*)attn_bf16_bwd_pkernel<32, false>,
+                        (const void*)attn_bf16_bwd_pkernel<64, true>, (const void*)attn_bf16_bwd_pkernel<64, false>,
+                        (const void*)attn_bf16_bwd_pkernel<128, true>, (const void*)attn_bf16_bwd_pkernel<128, false>,
+                        (const void*)attn_bf16_bwd_kernel<32, true>,  (const void*)attn_bf16_bwd_kernel<32, false>,
                         (const void*)attn_bf16_bwd_kernel<64, true>,  (const void*)attn_bf16_bwd_kernel<64, false>,
                         (const void*)attn_bf16_bwd_kernel<128, true>, (const void*)attn_bf16_bwd_kernel<128, false>,
                         (const void*)attn_f32_bwd_kernel<32>,         (const void*)attn_f32_bwd_kernel<64>,
@@ -1434,7 +1643,7 @@ static kv_t bwd_kv_variant(const Geometry& g) {
 static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
                                         const float* table, const void* dout, void* dq, void* dk, void* dv,
                                         uint32_t work0, uint32_t count, float* units, float* stats, const void* o,
-                                        const float* lse, hipStream_t s) {
+                                        const float* lse, int blocks, hipStream_t s) {
     const dim3 grid(count);
     if (bf16 && !bwd_small_fits(g)) {
         const BwdBigLds L = bwd_big_lds(g, bwd_kv_waves(g.head_dim));
@@ -1460,6 +1669,10 @@ static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void
         hipLaunchKernelGGL(fk, grid, dim3((KW + kBwdLoaders) * 64), L.total_k, s, g, (const uint16_t*)q, (const uint16_t*)k,
                            (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dk, (uint16_t*)dv,
                            (const float*)stats, units, work0, count);
+    } else if (bf16 && blocks > 0) {
+        hipLaunchKernelGGL(bwd_bf16_pvariant(g), dim3((unsigned)blocks), dim3((kBwdWaves + kBwdPLoaders) * 64),
+                           bwd_plds(g).total, s, g, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, table,
+                           (const uint16_t*)dout, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, units, work0, count);
     } else if (bf16) {
         hipLaunchKernelGGL(bwd_bf16_variant(g), grid, dim3(kBwdWaves * 64), bwd_lds(g).total, s, g,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, table, (const uint16_t*)dout,
@@ -1478,12 +1691,12 @@ static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void
 
 hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
                            const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
-                           void* workspace, const void* o, const float* lse, hipStream_t s) {
+                           void* workspace, const void* o, const float* lse, int blocks, hipStream_t s) {
     float* units = (float*)workspace;
     float* chunks = units + (size_t)(g.windows * g.heads) * g.table_size;
     float* stats = chunks + (size_t)kDtableChunks * g.heads * g.table_size;
     hipError_t e = launch_backward_units(g, bf16, q, k, v, table, dout, dq, dk, dv, 0,
-                                         (uint32_t)(g.windows * g.heads), units, stats, o, lse, s);
+                                         (uint32_t)(g.windows * g.heads), units, stats, o, lse, blocks, s);
     if (e != hipSuccess) return e;
     const int n = g.heads * g.table_size;
     hipLaunchKernelGGL(dtable_chunk_kernel, dim3((n + 255) / 256, kDtableChunks), dim3(256), 0, s, g.windows,
@@ -1539,7 +1752,7 @@ __global__ __launch_bounds__(256) void dtable_accumulate_kernel(int64_t windows,
 
 hipError_t launch_backward_scratch(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
                                    const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
-                                   void* scratch, size_t scratch_bytes, hipStream_t s) {
+                                   void* scratch, size_t scratch_bytes, int blocks, hipStream_t s) {
     const size_t per_window = scratch_per_window(g, bf16);
     const int n = g.heads * g.table_size;
     int c0 = 0;
@@ -1555,7 +1768,7 @@ hipError_t launch_backward_scratch(const Geometry& g, bool bf16, const void* q, 
         hipError_t e;
         if (w1 > w0) {
             e = launch_backward_units(g, bf16, q, k, v, table, dout, dq, dk, dv, (uint32_t)(w0 * g.heads),
-                                      (uint32_t)((w1 - w0) * g.heads), units, stats, nullptr, nullptr, s);
+                                      (uint32_t)((w1 - w0) * g.heads), units, stats, nullptr, nullptr, blocks, s);
             if (e != hipSuccess) return e;
         }
         hipLaunchKernelGGL(dtable_accumulate_kernel, dim3((n + 255) / 256), dim3(256), 0, s, g.windows, g.heads,
