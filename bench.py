@@ -341,10 +341,11 @@ def main():
         "mfma_peak_frac": round(tflops / peak_tf, 5),
         "useful_tflops": round(useful / (ms_per_step * 1e-3) / 1e12, 3),
         "kernel": {"name": (("attn_f32_bwd_kernel" if p.dtype == "f32" else
-                             "attn_bf16_bwd_kernel" if info.backward_schedule == 1 else
+                             ("attn_bf16_bwd_pkernel" if info.backward_workgroups > 0 else "attn_bf16_bwd_kernel")
+                             if info.backward_schedule == 1 else
                              "attn_bf16_bwd_q_kernel+attn_bf16_bwd_kv_kernel") if backward
                             else kernel_name(p, info) if args.variant == "fused" else "gather+attn+scatter"),
-                   "workgroups": info.workgroups,
+                   "workgroups": info.backward_workgroups if backward else info.workgroups,
                    **launch_stats(launch_ms),
                    "source_sha256_16": kernel_source_hash(BWD_SOURCES if backward else None)},
         "warmup_calls": warm_steps,

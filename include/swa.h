@@ -138,6 +138,9 @@ typedef struct swa_info {
                                         whole window in LDS (fp32 always); 2: bf16 key-blocked kernels
                                         for windows beyond that (32-token blocks streamed) */
     int32_t layer_path;              /* the path swa_layer_forward takes: SWA_LAYER_FUSED or _UNFUSED */
+    int32_t backward_workgroups;     /* bf16 backward schedule 1: workgroups of the persistent kernel
+                                        (whole units per workgroup, the next unit's inputs copied
+                                        behind the current one); 0: one workgroup per (window, head) */
 } swa_info;
 
 /*

@@ -45,7 +45,7 @@ class swa_info(ctypes.Structure):
         ("schedule", ctypes.c_int32), ("workgroups", ctypes.c_int32),
         ("backward_workspace_bytes", ctypes.c_size_t), ("layer_workspace_bytes", ctypes.c_size_t),
         ("layer_flops", ctypes.c_double), ("backward_schedule", ctypes.c_int32),
-        ("layer_path", ctypes.c_int32),
+        ("layer_path", ctypes.c_int32), ("backward_workgroups", ctypes.c_int32),
     ]
 
 

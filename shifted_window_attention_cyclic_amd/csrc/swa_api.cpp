@@ -348,6 +348,7 @@ swa_status swa_get_info(const swa_handle* h, swa_info* info) {
     info->workgroups = bf16 ? h->blocks : 0;
     info->backward_workspace_bytes = swa::backward_fits(g, bf16) ? swa::backward_workspace_bytes(g) : 0;
     info->backward_schedule = swa::backward_schedule(g, bf16);
+    info->backward_workgroups = h->bwd_blocks;
     info->layer_path = h->layer_path;
     info->layer_workspace_bytes = (h->layer_path == SWA_LAYER_FUSED ? 1 : 4) * io_bytes(h);
     info->layer_flops = 8.0 * (double)info->tokens * g.row * (double)g.row + info->nominal_flops;
