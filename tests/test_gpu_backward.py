@@ -154,6 +154,11 @@ def test_backward_schedule_reported(name, schedule):
     att = WindowAttention(WORKLOADS[name])
     assert att.info.backward_schedule == schedule
     assert att.info.backward_workspace_bytes > 0
+    # bf16 schedule 1 runs persistent workgroups, a whole number per XCD; the
+    # fp32 kernel and the big-window kernels take one workgroup per unit or block
+    persistent = schedule == 1 and WORKLOADS[name].dtype == "bf16"
+    wg = att.info.backward_workgroups
+    assert (wg > 0 and wg % 8 == 0) if persistent else wg == 0
     att.close()
 
 
