@@ -343,7 +343,8 @@ def main():
         "kernel": {"name": (("attn_f32_bwd_kernel" if p.dtype == "f32" else
                              ("attn_bf16_bwd_pkernel" if info.backward_workgroups > 0 else "attn_bf16_bwd_kernel")
                              if info.backward_schedule == 1 else
-                             "attn_bf16_bwd_q_kernel+attn_bf16_bwd_kv_kernel") if backward
+                             ("attn_bf16_bwd_q_kernel+attn_bf16_bwd_kvp_kernel" if info.backward_workgroups > 0
+                              else "attn_bf16_bwd_q_kernel+attn_bf16_bwd_kv_kernel")) if backward
                             else kernel_name(p, info) if args.variant == "fused" else "gather+attn+scatter"),
                    "workgroups": info.backward_workgroups if backward else info.workgroups,
                    **launch_stats(launch_ms),

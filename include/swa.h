@@ -140,7 +140,10 @@ typedef struct swa_info {
     int32_t layer_path;              /* the path swa_layer_forward takes: SWA_LAYER_FUSED or _UNFUSED */
     int32_t backward_workgroups;     /* bf16 backward schedule 1: workgroups of the persistent kernel
                                         (whole units per workgroup, the next unit's inputs copied
-                                        behind the current one); 0: one workgroup per (window, head) */
+                                        behind the current one); schedule 2 with windows of up to 288
+                                        tokens and head_dim 32 or 64: workgroups of the persistent key
+                                        kernel (one head, one group of 4 key tiles, a run of windows);
+                                        0: one workgroup per (window, head) or query block */
 } swa_info;
 
 /*
@@ -196,7 +199,11 @@ swa_status swa_forward_lse(swa_handle* h, const void* q, const void* k, const vo
  * fixed order, so the results are bitwise reproducible, and the table
  * gradient sums bf16-rounded dS terms in fp32.  backward_schedule 2 (larger
  * bf16 windows): dq, dk, dv are still reproducible; the table gradient sums
- * fp32 dS terms with LDS atomics, in an order that may differ between runs.
+ * fp32 dS terms.  Where backward_workgroups > 0 (windows of up to 288 tokens,
+ * head_dim 32 or 64) it first sums them over windows per window-local
+ * (query, key) pair and then over each entry's pairs, in a fixed order
+ * (reproducible); otherwise it sums each window's terms with LDS atomics, in
+ * an order that may differ between runs.
  * Asynchronous on `stream`, like swa_forward.
  * Errors: INVALID_ARGUMENT (NULL handle or pointer, misalignment, a buffer
  * written that overlaps another argument), UNSUPPORTED (the window is beyond

@@ -12,7 +12,8 @@ bool backward_fits(const Geometry& g, bool bf16);
 size_t backward_workspace_bytes(const Geometry& g);
 hipError_t prepare_backward_kernels(int max_lds);
 // Workgroups of the persistent small-window backward kernel for g (a multiple
-// of the XCD count), or 0 where the one-shot kernels run; after
+// of the XCD count), of the persistent big-window key kernel (heads * key
+// groups * runs of windows), or 0 where the one-shot kernels run; after
 // prepare_backward_kernels, on the device the launches will use.
 hipError_t backward_plan(const Geometry& g, bool bf16, int* blocks);
 // blocks: backward_plan's.  With lse and o (the forward's statistics and

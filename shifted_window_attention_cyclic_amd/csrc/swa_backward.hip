@@ -35,9 +35,12 @@
 //                         slots) does not fit.
 //   attn_f32_bwd_kernel   the fp32 counterpart: one thread per query, then one
 //                         per key.
-//   attn_bf16_bwd_q_kernel, attn_bf16_bwd_kv_kernel
+//   attn_bf16_bwd_q_kernel, attn_bf16_bwd_kv_kernel, attn_bf16_bwd_kvp_kernel
 //                         bf16 windows the single-workgroup kernel does not
-//                         take (see below).
+//                         take (see below); the persistent key kernel
+//                         attn_bf16_bwd_kvp_kernel where it fits (129 .. 288
+//                         tokens, heads of 32 or 64), with pair_runs_kernel
+//                         and dtable_pairs_kernel for its table gradient.
 //   dtable_chunk_kernel,
 //   dtable_sum_kernel     the table gradient: per-chunk sums over windows,
 //                         then the sum of the chunks.
@@ -766,33 +769,45 @@ __host__ __device__ inline BwdBigLds bwd_big_lds(const Geometry& g, int kw) {
     return L;
 }
 
-// token table of a unit for the big-window kernels: tw (row + 1 | mask field
-// << 28, as the single-workgroup kernel), key and query bias offsets
+// token word of slot n of window (b, wc): row + 1 | mask field << 28, as the
+// single-workgroup kernel; a slot past N gets a field no query has
+__device__ inline int big_token_word(const Geometry& g, const int wc[3], int b, int n) {
+    if (n >= g.N) return 15 << 28;
+    int l[3];
+    local_coords(g, n, l[0], l[1], l[2]);
+    int region = 0, tok = b;
+    bool is_pad = false;
+#pragma unroll
+    for (int a = 0; a < 3; a++) {
+        const int cr = wc[a] * g.win[a] + l[a];
+        int c = cr + g.shift[a];
+        if (c >= g.pad[a]) c -= g.pad[a];
+        is_pad |= c >= g.ext[a];
+        if (!g.cyc[a] && cr >= g.pad[a] - g.shift[a]) region |= 1 << a;
+        tok = tok * g.ext[a] + c;
+    }
+    return ((is_pad ? -1 : tok) + 1) | ((region | (is_pad ? 8 : 0)) << 28);
+}
+
+// key and query bias offsets of slot n (the same in every window)
+__device__ inline void big_bias_offsets(const Geometry& g, int n, int& kb, int& qb) {
+    if (n < g.N) {
+        int l[3];
+        local_coords(g, n, l[0], l[1], l[2]);
+        kb = (l[0] * g.tdy + l[1]) * g.tdx + l[2];
+        qb = kb + g.c0;
+    } else {
+        kb = 0;
+        qb = g.table_size - 1; // qb - kb stays inside the table
+    }
+}
+
+// token table of a unit for the big-window kernels: tw, key and query bias offsets
 __device__ inline void big_token_table(const Geometry& g, const int wc[3], int b, int NPX, int* tw, int* kbo,
                                        int* qbo, int nthreads) {
     for (int n = threadIdx.x; n < NPX; n += nthreads) {
-        if (n < g.N) {
-            int l[3];
-            local_coords(g, n, l[0], l[1], l[2]);
-            int region = 0, tok = b;
-            bool is_pad = false;
-#pragma unroll
-            for (int a = 0; a < 3; a++) {
-                const int cr = wc[a] * g.win[a] + l[a];
-                int c = cr + g.shift[a];
-                if (c >= g.pad[a]) c -= g.pad[a];
-                is_pad |= c >= g.ext[a];
-                if (!g.cyc[a] && cr >= g.pad[a] - g.shift[a]) region |= 1 << a;
-                tok = tok * g.ext[a] + c;
-            }
-            tw[n] = ((is_pad ? -1 : tok) + 1) | ((region | (is_pad ? 8 : 0)) << 28);
-            kbo[n] = (l[0] * g.tdy + l[1]) * g.tdx + l[2];
-            qbo[n] = kbo[n] + g.c0;
-        } else {
-            tw[n] = 15 << 28; // a field no query has: never visible
-            kbo[n] = 0;
-            qbo[n] = g.table_size - 1; // qb - kb stays inside the table
-        }
+        tw[n] = big_token_word(g, wc, b, n);
+        big_bias_offsets(g, n, kbo[n], qbo[n]);
     }
 }
 
@@ -1349,6 +1364,423 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
     for (int e = tid; e < g.table_size; e += THREADS) dst[e] = dtab[e];
 }
 
+// ---- attn_bf16_bwd_kvp_kernel: the key kernel with the table gradient summed
+// over windows before it is summed over offsets.
+//
+// A table entry depends only on the window-local positions of its query and
+// key, so dtable[e] = sum, over the local pairs (n, m) of entry e, of
+// S[n][m] = sum over windows of dS[n][m].  A workgroup takes one head, one
+// group of kKvpTiles key tiles and a run of consecutive windows.  Each of its
+// compute waves owns a key tile and one 16-query half of every 32-query
+// block, and adds each window's dS of its pairs into registers: one add per
+// term, where attn_bf16_bwd_kv_kernel parks the terms in LDS and adds runs of
+// each tile diagonal with atomics.  At the end every wave writes its pair
+// sums; pair_runs_kernel adds the runs of windows in order and
+// dtable_pairs_kernel sums each entry's pairs in query order, so this table
+// gradient is bitwise reproducible.
+//
+// The two halves of a key tile each hold a share of its dK and dV; at the end
+// of a window the second half leaves its share in LDS and the first adds it
+// after the next barrier and stores both.  Four loader waves stream the Q
+// and dO blocks of the current window through the ring, two blocks per step
+// (one barrier per step), and, from the start of a window on, build the next
+// window's token words and copy its statistics, K and V (the group's keys)
+// into the other of two window buffers.  Eight compute waves (4 key tiles)
+// keep the workgroup at 159 VGPRs, 3 waves per SIMD; 12 (6 key tiles) need
+// more than the 128 of 4 waves per SIMD and spill.
+constexpr int kKvpTiles = 4;                              // key tiles per group
+constexpr int kKvpWaves = 2 * kKvpTiles;                  // compute waves: (key tile, query half)
+constexpr int kKvpLoaders = 4;
+constexpr int kKvpBlocks = 9;                             // 32-query blocks per window, at most
+constexpr int kKvpWorkgroups = 256;                       // aimed at: one per compute unit
+constexpr int kKvpSums = kKvpWaves * kKvpBlocks * 4 * 64; // pair sums per workgroup (floats)
+
+struct KvpLds {
+    int NPX;
+    size_t kbo, qbo, bias, win, win_bytes, tw, stat, kt, vt, ring, buf_bytes, exch, total;
+};
+
+__host__ __device__ inline KvpLds kvp_lds(const Geometry& g) {
+    KvpLds L;
+    const size_t D = (size_t)g.head_dim;
+    L.NPX = (g.N + kBwdBlk - 1) / kBwdBlk * kBwdBlk;
+    L.kbo = 0;                                                  // int per slot: key bias offset
+    L.qbo = L.kbo + (size_t)L.NPX * 4;                          // int per slot: query bias offset
+    L.bias = L.qbo + (size_t)L.NPX * 4;                         // the head's table slice
+    L.win = L.bias + ((size_t)g.table_size * 4 + 15) / 16 * 16; // two window buffers
+    L.tw = 0;                                                   // per window: token words,
+    L.stat = L.tw + (size_t)L.NPX * 4;                          //   lse2 and D per query,
+    L.kt = L.stat + (size_t)L.NPX * 8;                          //   K and V of the group's keys
+    L.vt = L.kt + (size_t)kKvpTiles * 16 * D * 2;
+    L.win_bytes = L.vt + (size_t)kKvpTiles * 16 * D * 2;
+    L.ring = L.win + 2 * L.win_bytes;                           // kBwdStages slots of a step: two
+    L.buf_bytes = (size_t)kBwdBlk * D * 2;                      //   blocks of Q and dO each
+    L.exch = L.ring + 4 * kBwdStages * L.buf_bytes;             // per key tile: the second half's dV, dK
+    L.total = L.exch + (size_t)kKvpTiles * 2 * (D / 16) * 64 * 16;
+    return L;
+}
+
+// Waits until at most n (wave-uniform) vector-memory operations of this wave
+// are outstanding; past 15 it waits for all of them.
+__device__ inline void bwd_wait_vm_n(int n) {
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(vmcnt_imm(9)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(vmcnt_imm(10)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(vmcnt_imm(11)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); break;
+    case 13: __builtin_amdgcn_s_waitcnt(vmcnt_imm(13)); break;
+    case 14: __builtin_amdgcn_s_waitcnt(vmcnt_imm(14)); break;
+    case 15: __builtin_amdgcn_s_waitcnt(vmcnt_imm(15)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    }
+}
+
+// global window index -> batch item and window coordinates
+__device__ inline void window_of(const Geometry& g, uint32_t wi, int& b, int wc[3]) {
+    b = (int)fdiv(g.fd_nW, wi);
+    const uint32_t r = wi - (uint32_t)b * (uint32_t)g.nW;
+    const uint32_t r2 = fdiv(g.fd_nwin2, r);
+    wc[2] = (int)(r - r2 * (uint32_t)g.nwin[2]);
+    wc[0] = (int)fdiv(g.fd_nwin1, r2);
+    wc[1] = (int)(r2 - (uint32_t)wc[0] * (uint32_t)g.nwin[1]);
+}
+
+// copy_block with each lane's source row computed from the window instead of
+// read from a token table in LDS
+template <int D>
+__device__ inline int copy_block_rows(const Geometry& g, const uint16_t* src, int h, const int wc[3], int b, int t0,
+                                      unsigned char* dst, int wave, int nwaves) {
+    constexpr int CH = D / 8, RPC = 64 / CH, NC = kBwdBlk / RPC;
+    const int lane = threadIdx.x & 63, m0 = lane / CH;
+    int issued = 0;
+    for (int c = wave; c < NC; c += nwaves) {
+        const int r1 = big_token_word(g, wc, b, t0 + c * RPC + m0) & kRowMask;
+        const uint64_t off = (uint64_t)(uint32_t)(r1 == 0 ? 0 : r1 - 1) * (uint32_t)g.row + h * D +
+                             copy_chunk<D>(c * RPC + m0, lane) * 8;
+        __builtin_amdgcn_global_load_lds((const void*)(src + off), (lds_void*)(dst + c * 1024), 16, 0, 0);
+        issued++;
+    }
+    return issued;
+}
+
+// Workgroup wg of heads * runs * groups (run of windows, key group), over
+// windows w0 .. w0 + nw - 1 (the units whose statistics are at
+// stats[((w - w0) * heads + h) * 2 NPX]); pair sums to sums[wg * kKvpSums].
+template <int D>
+__global__ __launch_bounds__((kKvpWaves + kKvpLoaders) * 64) void attn_bf16_bwd_kvp_kernel(
+    Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, const float* __restrict__ stats, float* __restrict__ sums, uint32_t w0, uint32_t nw,
+    int runs, int groups) {
+    constexpr int THREADS = (kKvpWaves + kKvpLoaders) * 64;
+    constexpr int KSTEPS = D / 32, DT = D / 16;
+    static_assert(kKvpTiles * 16 % kBwdBlk == 0, "a group's keys copy as whole blocks");
+    extern __shared__ __align__(16) unsigned char smem[];
+    const KvpLds L = kvp_lds(g);
+    const int N = g.N, NPX = L.NPX, NB = NPX / kBwdBlk;
+    int* kbo = (int*)(smem + L.kbo);
+    int* qbo = (int*)(smem + L.qbo);
+    float* bias = (float*)(smem + L.bias);
+    unsigned char* ring = smem + L.ring;
+    f32x4* exch = (f32x4*)(smem + L.exch);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+
+    // workgroup -> (head, run, key group): the groups of a run are neighbours
+    // on one XCD, so the Q and dO blocks that each of them streams share its L2
+    const int wg = (int)xcd_work_index(blockIdx.x, (int64_t)g.heads * runs * groups);
+    const int kg = wg % groups;
+    const int run = (wg / groups) % runs;
+    const int h = wg / (groups * runs);
+    const uint32_t wbeg = w0 + (uint32_t)((uint64_t)nw * run / runs);
+    const int nwin = (int)(w0 + (uint32_t)((uint64_t)nw * (run + 1) / runs) - wbeg);
+
+    for (int n = tid; n < NPX; n += THREADS) big_bias_offsets(g, n, kbo[n], qbo[n]);
+    for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)i * g.heads + h];
+    if (nwin > 0) {
+        int b, wc[3];
+        window_of(g, wbeg, b, wc);
+        int* tw0 = (int*)(smem + L.win + L.tw);
+        for (int n = tid; n < NPX; n += THREADS) tw0[n] = big_token_word(g, wc, b, n);
+    }
+    __syncthreads();
+
+    // A step takes two 32-query blocks of a window (the last step of an odd
+    // count one); every window's NS steps stream through the ring.
+    const int NS = (NB + 1) / 2, T = nwin * NS;
+    if (wave >= kKvpWaves) {
+        const int li = wave - kKvpWaves;
+        const int per_block = 2 * block_copies_of<D>(li, kKvpLoaders); // this loader's copies per block
+        auto own = [&](int s) __attribute__((always_inline)) {         // ... per step s
+            const int js = s % NS;
+            return (2 * js + 1 < NB ? 2 : 1) * per_block;
+        };
+        // window i's token words (unless written already), K and V of the
+        // group's keys, and its statistics, into window buffer i & 1; returns
+        // the copies issued
+        auto prologue = [&](int i, bool words) __attribute__((always_inline)) {
+            int b, wc[3];
+            window_of(g, wbeg + i, b, wc);
+            unsigned char* wb = smem + L.win + (size_t)(i & 1) * L.win_bytes;
+            if (words) {
+                int* tw = (int*)(wb + L.tw);
+                for (int n = li * 64 + lane; n < NPX; n += kKvpLoaders * 64) tw[n] = big_token_word(g, wc, b, n);
+            }
+            int issued = 0;
+            for (int c = 0; c < kKvpTiles * 16 / kBwdBlk; c++) {
+                const int t0 = kg * kKvpTiles * 16 + c * kBwdBlk;
+                issued += copy_block_rows<D>(g, k, h, wc, b, t0, wb + L.kt + c * L.buf_bytes, li, kKvpLoaders);
+                issued += copy_block_rows<D>(g, v, h, wc, b, t0, wb + L.vt + c * L.buf_bytes, li, kKvpLoaders);
+            }
+            // lse2 and D: 2 NPX floats, 16 bytes per lane (lane 0 of every copy is in range)
+            const float* st = stats + ((size_t)(wbeg + i - w0) * g.heads + h) * 2 * NPX;
+            const int bytes = NPX * 8;
+            for (int c = li; c * 1024 < bytes; c += kKvpLoaders) {
+                if (c * 1024 + lane * 16 < bytes)
+                    __builtin_amdgcn_global_load_lds((const void*)(st + c * 256 + lane * 4),
+                                                     (lds_void*)(wb + L.stat + c * 1024), 16, 0, 0);
+                issued++;
+            }
+            return issued;
+        };
+        auto issue_step = [&](int s) __attribute__((always_inline)) {
+            const int i = s / NS, js = s - i * NS;
+            const int* tw = (const int*)(smem + L.win + (size_t)(i & 1) * L.win_bytes + L.tw);
+            unsigned char* dst = ring + (size_t)(s % kBwdStages) * 4 * L.buf_bytes;
+            for (int u = 0; u < 2 && 2 * js + u < NB; u++) {
+                const int j = 2 * js + u;
+                copy_block<D>(g, q, h, tw, j * kBwdBlk, dst + u * 2 * L.buf_bytes, li, kKvpLoaders);
+                copy_block<D>(g, dout, h, tw, j * kBwdBlk, dst + (u * 2 + 1) * L.buf_bytes, li, kKvpLoaders);
+            }
+        };
+        // Issue order: window 0's prologue, steps 0 and 1; after barrier s,
+        // the next window's prologue when s starts a window, then step s + 2.
+        // Before barrier s a loader waits for its copies of step s; the ones
+        // issued after them are step s + 1 and the prologue of step s - 1.
+        // Window i + 1's first steps are issued at steps (i + 1) NS - 2 and
+        // - 1, after the barrier that follows the prologue writing its token
+        // words (NS >= 3).
+        if (nwin > 0) prologue(0, false);
+        for (int s = 0; s < kBwdStages - 1 && s < T; s++) issue_step(s);
+        int pro = 0; // prologue copies issued at the previous step
+        for (int s = 0; s < T; s++) {
+            bwd_wait_vm_n(pro + (s + 1 < T ? own(s + 1) : 0));
+            bwd_loader_barrier();
+            const int i = s / NS;
+            pro = (s == i * NS && i + 1 < nwin) ? prologue(i + 1, true) : 0;
+            if (s + kBwdStages - 1 < T) issue_step(s + kBwdStages - 1);
+        }
+        bwd_loader_barrier(); // final: the last window's dV and dK shares
+        return;
+    }
+
+    // compute wave: key tile kg * kKvpTiles + kk, queries 16 th .. 16 th + 15 of each block
+    const int kk = wave >> 1, th = wave & 1;
+    const int m = (kg * kKvpTiles + kk) * 16 + col; // the lane's key slot
+    const bool active = (kg * kKvpTiles + kk) * 16 < NPX;
+    const bool key_in = active && m < N; // slots past N are masked in every block
+    const int kbm = key_in ? kbo[m] : 0;
+    const int krow = kk * 16 + col;      // its row in the window buffer's K and V
+    // transposed 4 x 16 read of a [32][D] block: rows t0 + 4 grp + 0..3, d = 16 dt + col
+    auto tr_blk = [&](const unsigned char* base, int t0, int dt) __attribute__((always_inline)) {
+        const int row = t0 + grp * 4 + (col >> 2);
+        const int d = dt * 16 + (col & 3) * 4;
+        return tr_read(base + row * (D * 2) + k_slot<D>(row, d >> 3) * 16 + (d & 7) * 2);
+    };
+    f32x4* ex = exch + (size_t)kk * 2 * DT * 64;
+    f32x4 acc[kKvpBlocks]; // pair sums: block j, queries 32 j + 16 th + 4 grp + 0..3, key m
+#pragma unroll
+    for (int j = 0; j < kKvpBlocks; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 av[DT], ak[DT]; // dV^T and dK^T shares: lane (key m, d = 16 dt + 4 grp + 0..3)
+    // the first half adds the second's share and stores the key tile's dV, dK
+    auto finish = [&](int kr) __attribute__((always_inline)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            av[dt] += ex[dt * 64 + lane];
+            ak[dt] += ex[(DT + dt) * 64 + lane];
+        }
+        if (kr >= 0) {
+            const uint64_t base = (uint64_t)(uint32_t)kr * (uint32_t)g.row + h * D + grp * 4;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                *(u32x2*)(dv + base + dt * 16) =
+                    u32x2{pack_bf16x2(av[dt][0], av[dt][1]), pack_bf16x2(av[dt][2], av[dt][3])};
+                *(u32x2*)(dk + base + dt * 16) = u32x2{pack_bf16x2(ak[dt][0] * g.scale, ak[dt][1] * g.scale),
+                                                       pack_bf16x2(ak[dt][2] * g.scale, ak[dt][3] * g.scale)};
+            }
+        }
+    };
+    int slot = 0, kr = -1;
+    for (int i = 0; i < nwin; i++) {
+        const unsigned char* wb = smem + L.win + (size_t)(i & 1) * L.win_bytes;
+        const int* tw = (const int*)(wb + L.tw);
+        const float* lse = (const float*)(wb + L.stat);
+        const float* dd = lse + NPX;
+        const uint16_t* Kt = (const uint16_t*)(wb + L.kt);
+        const uint16_t* Vt = (const uint16_t*)(wb + L.vt);
+        int b, wc[3];
+        window_of(g, wbeg + i, b, wc);
+        const bool masked_window = window_maybe_masked(g, wc);
+        unsigned kreg = 15;
+        for (int js = 0; js < NS; js++) {
+            {
+                bwd_compute_barrier(); // step js of window i is in its slot
+                if (js == 0) {
+                    if (th == 0 && active && i > 0) finish(kr); // the previous window's key tile
+#pragma unroll
+                    for (int dt = 0; dt < DT; dt++) {
+                        av[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        ak[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+                    const int kword = active ? tw[m] : (15 << 28);
+                    kreg = (unsigned)kword >> 28;
+                    kr = (kword & kRowMask) - 1;
+                }
+#pragma unroll
+                for (int u = 0; u < 2; u++) {
+                    const int j = 2 * js + u;
+                    if (!active || j >= NB) continue;
+                    const unsigned char* Qb = ring + (size_t)slot * 4 * L.buf_bytes + u * 2 * L.buf_bytes;
+                    const unsigned char* Ob = Qb + L.buf_bytes;
+                    const uint16_t* Qs = (const uint16_t*)Qb;
+                    const uint16_t* dOs = (const uint16_t*)Ob;
+                    const int nb = j * kBwdBlk, qrow = th * 16 + col;
+                    // S = Q K^T and dP = dO V^T: lane (key m, queries nb + 16 th + 4 grp + 0..3)
+                    f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, dp4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KSTEPS; ks++) {
+                        const int kc = k_slot<D>(krow, ks * 4 + grp) * 8, qc = k_slot<D>(qrow, ks * 4 + grp) * 8;
+                        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kt + krow * D + kc));
+                        const bf16x8 vf = __builtin_bit_cast(bf16x8, *(const u32x4*)(Vt + krow * D + kc));
+                        s4 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(Qs + qrow * D + qc)), kf, s4);
+                        dp4 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(dOs + qrow * D + qc)), vf, dp4);
+                    }
+                    const int n4 = nb + th * 16 + grp * 4;
+                    const u32x4 qb4 = *(const u32x4*)(qbo + n4);
+                    const f32x4 ls4 = *(const f32x4*)(lse + n4);
+                    const f32x4 dd4 = *(const f32x4*)(dd + n4);
+                    float lg[4];
+#pragma unroll
+                    for (int ii = 0; ii < 4; ii++) lg[ii] = bias[(int)qb4[ii] - kbm];
+                    f32x4 p, ds;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ii++) {
+                        const float x = key_in ? fmaf(s4[ii], g.scale, lg[ii]) * kLog2e : -INFINITY;
+                        p[ii] = __builtin_amdgcn_exp2f(x - ls4[ii]);
+                        ds[ii] = p[ii] * (dp4[ii] - dd4[ii]);
+                    }
+                    if (masked_window || nb + kBwdBlk > N) { // wave-uniform
+                        // queries of another region, pad queries, and slots past N (whose
+                        // statistics are not written) take no weight
+                        const u32x4 tw4 = *(const u32x4*)(tw + n4);
+#pragma unroll
+                        for (int ii = 0; ii < 4; ii++) {
+                            const bool vis = key_in && (tw4[ii] >> 28) == kreg;
+                            p[ii] = vis ? p[ii] : 0.f;
+                            ds[ii] = vis ? ds[ii] : 0.f;
+                        }
+                    }
+                    // acc[j] += ds, with j a register index (the loop is not unrolled)
+                    switch (j) {
+                    case 0: acc[0] += ds; break;
+                    case 1: acc[1] += ds; break;
+                    case 2: acc[2] += ds; break;
+                    case 3: acc[3] += ds; break;
+                    case 4: acc[4] += ds; break;
+                    case 5: acc[5] += ds; break;
+                    case 6: acc[6] += ds; break;
+                    case 7: acc[7] += ds; break;
+                    default: acc[8] += ds; break;
+                    }
+                    const bf16x8 bp = __builtin_bit_cast(
+                        bf16x8, u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), 0u, 0u});
+                    const bf16x8 bs = __builtin_bit_cast(
+                        bf16x8, u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), 0u, 0u});
+                    // dV^T += dO^T P and dK^T += Q^T dS over this half's 16 queries (the
+                    // 32-deep product with its other half zero: one opcode per chain)
+#pragma unroll
+                    for (int dt = 0; dt < DT; dt++) {
+                        const u32x2 o = tr_blk(Ob, th * 16, dt), qq = tr_blk(Qb, th * 16, dt);
+                        av[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{o[0], o[1], 0u, 0u}), bp, av[dt]);
+                        ak[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{qq[0], qq[1], 0u, 0u}), bs, ak[dt]);
+                    }
+                }
+                slot = slot + 1 == kBwdStages ? 0 : slot + 1;
+                if (js == NS - 1 && th == 1 && active) { // this half's share for the first half
+#pragma unroll
+                    for (int dt = 0; dt < DT; dt++) {
+                        ex[dt * 64 + lane] = av[dt];
+                        ex[(DT + dt) * 64 + lane] = ak[dt];
+                    }
+                }
+            }
+        }
+    }
+    bwd_compute_barrier(); // final: the last window's second-half shares
+    if (th == 0 && active && nwin > 0) finish(kr);
+    float* dst = sums + (size_t)wg * kKvpSums + (size_t)wave * kKvpBlocks * 4 * 64;
+#pragma unroll
+    for (int j = 0; j < kKvpBlocks; j++)
+#pragma unroll
+        for (int ii = 0; ii < 4; ii++) dst[(j * 4 + ii) * 64 + lane] = acc[j][ii];
+}
+
+// pairs[(h * groups + kg) * kKvpSums + x] = sum over runs r, in order, of the
+// workgroup sums of (h, r, kg)
+__global__ __launch_bounds__(256) void pair_runs_kernel(int heads, int runs, int groups, const float* __restrict__ sums,
+                                                        float* __restrict__ pairs) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)heads * groups * kKvpSums) return;
+    const int x = (int)(idx % kKvpSums), hg = (int)(idx / kKvpSums);
+    const int h = hg / groups, kg = hg - h * groups;
+    float acc = 0.f;
+    for (int r = 0; r < runs; r++) acc += sums[((size_t)(h * runs + r) * groups + kg) * kKvpSums + x];
+    pairs[idx] = acc;
+}
+
+// dtable[e][h] = (accumulate ? dtable[e][h] : 0) + the sum of the pair sums
+// of (n, m), m the key at offset e from query n (entry e = ((dt + w_t - 1) tdy
+// + dy + w_y - 1) tdx + dx + w_x - 1 for the local offset (dt, dy, dx) = query
+// - key).  A wave per entry: lane l adds queries l, l + 64, ... in order, then
+// the lanes' sums are added in a fixed butterfly order.
+__global__ __launch_bounds__(256) void dtable_pairs_kernel(Geometry g, int groups, const float* __restrict__ pairs,
+                                                           float* __restrict__ dtable, int accumulate) {
+    const int idx = blockIdx.x * 4 + (threadIdx.x >> 6); // h * ts + e
+    const int lane = threadIdx.x & 63;
+    if (idx >= g.heads * g.table_size) return; // wave-uniform
+    const int h = idx / g.table_size, e = idx - h * g.table_size;
+    const int ex = e % g.tdx, r = e / g.tdx;
+    const int oy = r % g.tdy - (g.win[1] - 1), ot = r / g.tdy - (g.win[0] - 1), ox = ex - (g.win[2] - 1);
+    const float* ph = pairs + (size_t)h * groups * kKvpSums;
+    float acc = 0.f;
+    for (int n = lane; n < g.N; n += 64) {
+        int lt, ly, lx;
+        local_coords(g, n, lt, ly, lx);
+        const int mt = lt - ot, my = ly - oy, mx = lx - ox;
+        if (mt < 0 || mt >= g.win[0] || my < 0 || my >= g.win[1] || mx < 0 || mx >= g.win[2]) continue;
+        const int m = (mt * g.win[1] + my) * g.win[2] + mx;
+        const int kg = (m >> 4) / kKvpTiles, kk = (m >> 4) - kg * kKvpTiles;
+        const int wave = 2 * kk + ((n >> 4) & 1), l = ((n >> 2) & 3) * 16 + (m & 15);
+        acc += ph[(size_t)kg * kKvpSums + ((size_t)(wave * kKvpBlocks + (n >> 5)) * 4 + (n & 3)) * 64 + l];
+    }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) acc += __shfl_xor(acc, sh);
+    if (lane == 0) {
+        const size_t o = (size_t)e * g.heads + h;
+        dtable[o] = (accumulate ? dtable[o] : 0.f) + acc;
+    }
+}
+
 // ---- fp32 backward: one block per unit, a thread per query, then per key
 constexpr int kF32BwdThreads = 256;
 
@@ -1520,6 +1952,39 @@ static bool bwd_big_fits(const Geometry& g) {
     return L.total_q <= (size_t)kLdsBytes && L.total_k <= (size_t)kLdsBytes;
 }
 
+#ifndef SWA_BWD_KVP
+#define SWA_BWD_KVP 1
+#endif
+
+// The persistent key kernel (pair sums over windows): big windows of 5 to 9
+// query blocks (129 to 288 tokens) with heads of 32 or 64.
+static bool bwd_kvp_fits(const Geometry& g) {
+    if (!SWA_BWD_KVP || bwd_small_fits(g) || !bwd_big_fits(g)) return false;
+    if (g.head_dim != 32 && g.head_dim != 64) return false;
+    const int NB = kvp_lds(g).NPX / kBwdBlk;
+    return NB >= 5 && NB <= kKvpBlocks && kvp_lds(g).total <= (size_t)kLdsBytes;
+}
+
+// Key groups of a window, and runs of windows per (head, group): enough
+// workgroups for one per compute unit, never more runs than windows.
+struct KvpPlan {
+    int groups, runs;
+};
+static KvpPlan kvp_plan(const Geometry& g, int64_t windows) {
+    KvpPlan p;
+    p.groups = (kvp_lds(g).NPX / 16 + kKvpTiles - 1) / kKvpTiles;
+    const int64_t r = kKvpWorkgroups / ((int64_t)g.heads * p.groups);
+    p.runs = (int)(r < 1 ? 1 : r > windows ? (windows < 1 ? 1 : windows) : r);
+    return p;
+}
+// floats of the kernel's workgroup sums and of their sums over runs
+static size_t kvp_sums_floats(const Geometry& g, const KvpPlan& p) {
+    return (size_t)g.heads * p.groups * p.runs * kKvpSums;
+}
+static size_t kvp_pairs_floats(const Geometry& g, const KvpPlan& p) {
+    return p.runs > 1 ? (size_t)g.heads * p.groups * kKvpSums : 0;
+}
+
 bool backward_fits(const Geometry& g, bool bf16) {
     if (!bf16) return g.head_dim <= 64 && f32_bwd_lds_bytes(g) <= (size_t)kLdsBytes;
     const int64_t rows = (int64_t)g.batch * g.ext[0] * g.ext[1] * g.ext[2];
@@ -1532,6 +1997,11 @@ int backward_schedule(const Geometry& g, bool bf16) {
 }
 
 size_t backward_workspace_bytes(const Geometry& g) {
+    if (bwd_kvp_fits(g)) { // per-query statistics, workgroup sums, their sums over runs
+        const KvpPlan p = kvp_plan(g, g.windows);
+        return ((size_t)(g.windows * g.heads) * 2 * kvp_lds(g).NPX + kvp_sums_floats(g, p) +
+                kvp_pairs_floats(g, p)) * sizeof(float);
+    }
     const size_t units = (size_t)(g.windows * g.heads) * g.table_size;
     const size_t chunks = (size_t)kDtableChunks * g.heads * g.table_size;
     // big windows: per query, lse2 and D
@@ -1563,6 +2033,11 @@ static bwd_bf16_t bwd_bf16_pvariant(const Geometry& g) {
 
 hipError_t backward_plan(const Geometry& g, bool bf16, int* blocks) {
     *blocks = 0;
+    if (bf16 && bwd_kvp_fits(g)) { // the persistent key kernel's workgroups
+        const KvpPlan p = kvp_plan(g, g.windows);
+        *blocks = g.heads * p.groups * p.runs;
+        return hipSuccess;
+    }
     if (!SWA_BWD_PERSISTENT || !bf16 || !bwd_small_fits(g) || bwd_plds(g).total > (size_t)kLdsBytes)
         return hipSuccess;
     int per_cu = 0, dev = 0, cus = 0;
@@ -1610,7 +2085,8 @@ hipError_t prepare_backward_kernels(int max_lds) {
                         (const void*)attn_bf16_bwd_kv_kernel<32, 6, 2>,  (const void*)attn_bf16_bwd_kv_kernel<64, 6, 0>,
                         (const void*)attn_bf16_bwd_kv_kernel<64, 6, 1>,  (const void*)attn_bf16_bwd_kv_kernel<64, 6, 2>,
                         (const void*)attn_bf16_bwd_kv_kernel<128, 8, 0>, (const void*)attn_bf16_bwd_kv_kernel<128, 8, 1>,
-                        (const void*)attn_bf16_bwd_kv_kernel<128, 8, 2>};
+                        (const void*)attn_bf16_bwd_kv_kernel<128, 8, 2>, (const void*)attn_bf16_bwd_kvp_kernel<32>,
+                        (const void*)attn_bf16_bwd_kvp_kernel<64>};
     for (const void* f : fs) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
         if (e != hipSuccess) return e;
@@ -1640,6 +2116,59 @@ static kv_t bwd_kv_variant(const Geometry& g) {
 // The attention gradients of units work0 .. work0 + count - 1: dq, dk, dv of
 // their tokens, their table-gradient shares at units[(unit - work0) * ts] and,
 // for big windows, their per-query statistics at stats[(unit - work0) * 2 NPX].
+// The big-window query kernel over units work0 .. work0 + count - 1: dq, and
+// each unit's per-query statistics at stats[(unit - work0) * 2 NPX].
+static hipError_t launch_big_query(const Geometry& g, const void* q, const void* k, const void* v, const float* table,
+                                   const void* dout, void* dq, uint32_t work0, uint32_t count, float* stats,
+                                   const void* o, const float* lse, hipStream_t s) {
+    const BwdBigLds L = bwd_big_lds(g, bwd_kv_waves(g.head_dim));
+    const int QW = bwd_q_waves(g);
+    const dim3 qgrid(count * (unsigned)((g.N + QW * 16 - 1) / (QW * 16)));
+    typedef void (*qk_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
+                         const uint16_t*, uint16_t*, float*, uint32_t, uint32_t, const uint16_t*, const float*);
+    const qk_t fq = g.head_dim == 128 ? (QW == 6 ? attn_bf16_bwd_q_kernel<128, 6> : attn_bf16_bwd_q_kernel<128, 4>)
+                    : g.head_dim == 64
+                        ? (QW == 8   ? attn_bf16_bwd_q_kernel<64, 8>
+                           : QW == 6 ? attn_bf16_bwd_q_kernel<64, 6>
+                                     : attn_bf16_bwd_q_kernel<64, 4>)
+                        : (QW == 8   ? attn_bf16_bwd_q_kernel<32, 8>
+                           : QW == 6 ? attn_bf16_bwd_q_kernel<32, 6>
+                                     : attn_bf16_bwd_q_kernel<32, 4>);
+    hipLaunchKernelGGL(fq, qgrid, dim3((QW + kBwdLoaders) * 64), L.total_q, s, g, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dq, stats,
+                       work0, count, (const uint16_t*)o, lse);
+    return hipGetLastError();
+}
+
+// The persistent key kernel over windows w0 .. w0 + nw - 1 (statistics of
+// their units at stats, as launch_big_query leaves them), then the table
+// gradient from its pair sums: dtable = (accumulate ? dtable : 0) + the
+// windows' share.  sums: kvp_sums_floats, pairs: kvp_pairs_floats (runs > 1).
+static hipError_t launch_kvp(const Geometry& g, const void* q, const void* k, const void* v, const float* table,
+                             const void* dout, void* dk, void* dv, float* dtable, const float* stats, float* sums,
+                             float* pairs, uint32_t w0, uint32_t nw, const KvpPlan& p, int accumulate,
+                             hipStream_t s) {
+    const unsigned wgs = (unsigned)(g.heads * p.runs * p.groups);
+    hipLaunchKernelGGL(g.head_dim == 32 ? attn_bf16_bwd_kvp_kernel<32> : attn_bf16_bwd_kvp_kernel<64>, dim3(wgs),
+                       dim3((kKvpWaves + kKvpLoaders) * 64), kvp_lds(g).total, s, g, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dk,
+                       (uint16_t*)dv, stats, sums, w0, nw, p.runs, p.groups);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const float* ps = sums;
+    if (p.runs > 1) {
+        const int64_t n = (int64_t)g.heads * p.groups * kKvpSums;
+        hipLaunchKernelGGL(pair_runs_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g.heads, p.runs,
+                           p.groups, (const float*)sums, pairs);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        ps = pairs;
+    }
+    const int n = g.heads * g.table_size; // a wave per entry, four per block
+    hipLaunchKernelGGL(dtable_pairs_kernel, dim3((n + 3) / 4), dim3(256), 0, s, g, p.groups, ps, dtable,
+                       accumulate);
+    return hipGetLastError();
+}
+
 static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
                                         const float* table, const void* dout, void* dq, void* dk, void* dv,
                                         uint32_t work0, uint32_t count, float* units, float* stats, const void* o,
@@ -1647,24 +2176,9 @@ static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void
     const dim3 grid(count);
     if (bf16 && !bwd_small_fits(g)) {
         const BwdBigLds L = bwd_big_lds(g, bwd_kv_waves(g.head_dim));
-        const int QW = bwd_q_waves(g);
-        const dim3 qgrid(count * (unsigned)((g.N + QW * 16 - 1) / (QW * 16)));
-        typedef void (*qk_t)(Geometry, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
-                             const uint16_t*, uint16_t*, float*, uint32_t, uint32_t, const uint16_t*, const float*);
-        const qk_t fq = g.head_dim == 128 ? (QW == 6 ? attn_bf16_bwd_q_kernel<128, 6> : attn_bf16_bwd_q_kernel<128, 4>)
-                        : g.head_dim == 64
-                            ? (QW == 8   ? attn_bf16_bwd_q_kernel<64, 8>
-                               : QW == 6 ? attn_bf16_bwd_q_kernel<64, 6>
-                                         : attn_bf16_bwd_q_kernel<64, 4>)
-                            : (QW == 8   ? attn_bf16_bwd_q_kernel<32, 8>
-                               : QW == 6 ? attn_bf16_bwd_q_kernel<32, 6>
-                                         : attn_bf16_bwd_q_kernel<32, 4>);
         const int KW = bwd_kv_waves(g.head_dim);
         const kv_t fk = bwd_kv_variant(g);
-        hipLaunchKernelGGL(fq, qgrid, dim3((QW + kBwdLoaders) * 64), L.total_q, s, g, (const uint16_t*)q, (const uint16_t*)k,
-                           (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dq, stats, work0, count,
-                           (const uint16_t*)o, lse);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_big_query(g, q, k, v, table, dout, dq, work0, count, stats, o, lse, s);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(fk, grid, dim3((KW + kBwdLoaders) * 64), L.total_k, s, g, (const uint16_t*)q, (const uint16_t*)k,
                            (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dk, (uint16_t*)dv,
@@ -1692,6 +2206,17 @@ static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void
 hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
                            const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
                            void* workspace, const void* o, const float* lse, int blocks, hipStream_t s) {
+    if (bf16 && bwd_kvp_fits(g)) {
+        const KvpPlan p = kvp_plan(g, g.windows);
+        float* stats = (float*)workspace;
+        float* sums = stats + (size_t)(g.windows * g.heads) * 2 * kvp_lds(g).NPX;
+        float* pairs = sums + kvp_sums_floats(g, p);
+        hipError_t e = launch_big_query(g, q, k, v, table, dout, dq, 0, (uint32_t)(g.windows * g.heads), stats, o,
+                                        lse, s);
+        if (e != hipSuccess) return e;
+        return launch_kvp(g, q, k, v, table, dout, dk, dv, dtable, stats, sums, pairs, 0, (uint32_t)g.windows, p, 0,
+                          s);
+    }
     float* units = (float*)workspace;
     float* chunks = units + (size_t)(g.windows * g.heads) * g.table_size;
     float* stats = chunks + (size_t)kDtableChunks * g.heads * g.table_size;
@@ -1723,7 +2248,21 @@ static size_t scratch_per_window(const Geometry& g, bool bf16) {
 
 static int64_t chunk_window(const Geometry& g, int c) { return g.windows * c / kDtableChunks; }
 
+// The persistent key kernel through the scratch: passes over runs of windows,
+// each with the statistics of its units, the workgroup sums and their sums.
+// The runs per (head, group) are halved until a pass holds at least two
+// windows per run; the smallest layout is one run of one window.
+static size_t kvp_window_bytes(const Geometry& g) { return (size_t)g.heads * 2 * kvp_lds(g).NPX * sizeof(float); }
+static size_t kvp_fixed_bytes(const Geometry& g, const KvpPlan& p) {
+    return (kvp_sums_floats(g, p) + kvp_pairs_floats(g, p)) * sizeof(float);
+}
+
 size_t backward_scratch_bytes(const Geometry& g, bool bf16) {
+    if (bf16 && bwd_kvp_fits(g)) {
+        KvpPlan p = kvp_plan(g, 1);
+        p.runs = 1;
+        return kvp_window_bytes(g) + kvp_fixed_bytes(g, p);
+    }
     int64_t most = 0; // windows of the largest chunk
     for (int c = 0; c < kDtableChunks; c++) {
         const int64_t n = chunk_window(g, c + 1) - chunk_window(g, c);
@@ -1753,6 +2292,33 @@ __global__ __launch_bounds__(256) void dtable_accumulate_kernel(int64_t windows,
 hipError_t launch_backward_scratch(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
                                    const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
                                    void* scratch, size_t scratch_bytes, int blocks, hipStream_t s) {
+    if (bf16 && bwd_kvp_fits(g)) {
+        KvpPlan p = kvp_plan(g, g.windows);
+        int64_t per_pass = 0;
+        for (;;) {
+            const size_t fixed = kvp_fixed_bytes(g, p);
+            per_pass = fixed < scratch_bytes ? (int64_t)((scratch_bytes - fixed) / kvp_window_bytes(g)) : 0;
+            if (per_pass >= g.windows || per_pass >= 2 * (int64_t)p.runs || p.runs == 1) break;
+            p.runs = p.runs / 2;
+        }
+        if (per_pass < 1) return hipErrorInvalidValue; // the caller checks backward_scratch_bytes first
+        per_pass = per_pass < g.windows ? per_pass : g.windows;
+        for (int64_t w0 = 0; w0 < g.windows; w0 += per_pass) {
+            const int64_t nw = g.windows - w0 < per_pass ? g.windows - w0 : per_pass;
+            KvpPlan pp = p;
+            pp.runs = (int)(pp.runs < nw ? pp.runs : nw);
+            float* stats = (float*)scratch;
+            float* sums = stats + (size_t)nw * g.heads * 2 * kvp_lds(g).NPX;
+            float* pairs = sums + kvp_sums_floats(g, pp);
+            hipError_t e = launch_big_query(g, q, k, v, table, dout, dq, (uint32_t)(w0 * g.heads),
+                                            (uint32_t)(nw * g.heads), stats, nullptr, nullptr, s);
+            if (e != hipSuccess) return e;
+            e = launch_kvp(g, q, k, v, table, dout, dk, dv, dtable, stats, sums, pairs, (uint32_t)w0, (uint32_t)nw,
+                           pp, w0 > 0, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     const size_t per_window = scratch_per_window(g, bf16);
     const int n = g.heads * g.table_size;
     int c0 = 0;

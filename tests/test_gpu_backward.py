@@ -55,7 +55,11 @@ CASES = {**SMALL, **EDGE, **LARGE,
          # the narrowest width whose diagonal runs split at row starts only (8), and a
          # narrower one (5), whose runs split wherever the table entry changes
          "n192_w8": Problem("n192w8", "bf16", 1, 2, 64, (1, 48, 24), (1, 48, 24), (1, 24, 8), (0, 12, 4), seed=33),
-         "n200_w5": Problem("n200w5", "bf16", 1, 2, 64, (1, 40, 20), (1, 40, 20), (1, 40, 5), (0, 20, 2), seed=34)}
+         "n200_w5": Problem("n200w5", "bf16", 1, 2, 64, (1, 40, 20), (1, 40, 20), (1, 40, 5), (0, 20, 2), seed=34),
+         # 32-wide heads in 160-token windows (the persistent key kernel's 32-wide
+         # variant: 5 query blocks, key groups of 4, 4 and 2 tiles), masked latitude
+         "n160_d32": Problem("n160d32", "bf16", 1, 4, 32, (1, 40, 48), (1, 40, 48), (1, 10, 16), (0, 5, 8),
+                             seed=35)}
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -124,6 +128,24 @@ def test_backward_is_bitwise_reproducible():
         assert torch.equal(ga, gb)
 
 
+@pytest.mark.parametrize("name", ["b2_n288_3d_pad", "n200_w5"])
+def test_backward_big_windows_bitwise_reproducible(name):
+    """The persistent big-window key kernel sums the table gradient per pair
+    over windows, then per entry, each in a fixed order: two runs agree bit for
+    bit (b2_n288_3d_pad: more runs of windows than windows, one window per
+    workgroup; n200_w5: 7 query blocks, a last key group of 2 tiles)."""
+    p = CASES[name]
+    att = WindowAttention(p)
+    assert att.info.backward_workgroups > 0
+    att.close()
+    x = make_inputs(p)
+    dout = _dout(p)
+    a = _run(p, x, dout)
+    b = _run(p, x, dout)
+    for gname, ga, gb in zip(("dq", "dk", "dv", "dtable"), a, b):
+        assert torch.equal(ga, gb), gname
+
+
 @pytest.mark.parametrize("name", ["c7_bf16_180x384_pad192_d128_w32"])
 def test_backward_big_windows_full_size_sampled(name):
     """The 32x32-window kernels at full size (each window takes the fp64 oracle
@@ -154,11 +176,18 @@ def test_backward_schedule_reported(name, schedule):
     att = WindowAttention(WORKLOADS[name])
     assert att.info.backward_schedule == schedule
     assert att.info.backward_workspace_bytes > 0
-    # bf16 schedule 1 runs persistent workgroups, a whole number per XCD; the
-    # fp32 kernel and the big-window kernels take one workgroup per unit or block
-    persistent = schedule == 1 and WORKLOADS[name].dtype == "bf16"
+    # bf16 schedule 1 runs persistent workgroups, a whole number per XCD; so
+    # does the big-window key kernel for 2x12x12 windows (288 tokens, 64-wide
+    # heads): heads * 5 key groups * runs of windows, about one per CU.  The fp32
+    # kernel and 32x32 windows take one workgroup per unit or block.
+    p = WORKLOADS[name]
     wg = att.info.backward_workgroups
-    assert (wg > 0 and wg % 8 == 0) if persistent else wg == 0
+    if schedule == 1 and p.dtype == "bf16":
+        assert wg > 0 and wg % 8 == 0
+    elif name == "c5_bf16_4x180x360_3d":
+        assert wg == p.heads * 5 * (256 // (p.heads * 5))
+    else:
+        assert wg == 0
     att.close()
 
 

@@ -5,9 +5,10 @@ problem is smaller than the first.
 
 dq, dk, dv must match bit for bit (the same kernels compute every unit), and
 so must the table gradient of the single-workgroup schedule (its chunk sums
-run in swa_backward's order); the big-window schedule's table gradient sums
-with LDS atomics, whose order may vary between runs, so there it is held to
-the bf16 tolerance.  Each pair also checks the no-allocation result against
+run in swa_backward's order).  The big-window schedule's table gradient is
+held to the bf16 tolerance: through the scratch its per-pair sums cover
+shorter runs of windows (passes sized to the scratch), which changes the
+order of the fp32 additions.  Each pair also checks the no-allocation result against
 the fp64 oracle on the smaller problem.
 """
 import numpy as np
