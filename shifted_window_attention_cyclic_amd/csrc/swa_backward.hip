@@ -1382,18 +1382,24 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
 // The two halves of a key tile each hold a share of its dK and dV; at the end
 // of a window the second half leaves its share in LDS and the first adds it
 // after the next barrier and stores both.  Four loader waves stream the Q
-// and dO blocks of the current window through the ring, two blocks per step
-// (one barrier per step), and, from the start of a window on, build the next
-// window's token words and copy its statistics, K and V (the group's keys)
-// into the other of two window buffers.  Eight compute waves (4 key tiles)
-// keep the workgroup at 159 VGPRs, 3 waves per SIMD; 12 (6 key tiles) need
-// more than the 128 of 4 waves per SIMD and spill.
+// and dO blocks of the current window through the ring, two or three blocks
+// per step (one barrier per step), and, from the start of a window on, build
+// the next window's token words and copy its statistics, K and V (the
+// group's keys) into the other of two window buffers; the compute waves take
+// their key tile's K and V fragments into registers at the window's start.
+// Eight compute waves (4 key tiles) keep the workgroup at 159 VGPRs, 3 waves
+// per SIMD; 12 (6 key tiles) need more than the 128 of 4 waves per SIMD and
+// spill.
 constexpr int kKvpTiles = 4;                              // key tiles per group
 constexpr int kKvpWaves = 2 * kKvpTiles;                  // compute waves: (key tile, query half)
 constexpr int kKvpLoaders = 4;
 constexpr int kKvpBlocks = 9;                             // 32-query blocks per window, at most
 constexpr int kKvpWorkgroups = 256;                       // aimed at: one per compute unit
 constexpr int kKvpSums = kKvpWaves * kKvpBlocks * 4 * 64; // pair sums per workgroup (floats)
+
+// blocks per step: three where a window has at least 7 blocks (3 steps or
+// more, which the loaders' token words need), else two
+__host__ __device__ constexpr int kvp_step_blocks(int nb) { return nb >= 7 ? 3 : 2; }
 
 struct KvpLds {
     int NPX;
@@ -1414,8 +1420,9 @@ __host__ __device__ inline KvpLds kvp_lds(const Geometry& g) {
     L.vt = L.kt + (size_t)kKvpTiles * 16 * D * 2;
     L.win_bytes = L.vt + (size_t)kKvpTiles * 16 * D * 2;
     L.ring = L.win + 2 * L.win_bytes;                           // kBwdStages slots of a step: two
-    L.buf_bytes = (size_t)kBwdBlk * D * 2;                      //   blocks of Q and dO each
-    L.exch = L.ring + 4 * kBwdStages * L.buf_bytes;             // per key tile: the second half's dV, dK
+    L.buf_bytes = (size_t)kBwdBlk * D * 2;                      //   or three blocks of Q and dO each
+    L.exch = L.ring + 2 * kvp_step_blocks(L.NPX / kBwdBlk) * kBwdStages * L.buf_bytes;
+                                                                // per key tile: the second half's dV, dK
     L.total = L.exch + (size_t)kKvpTiles * 2 * (D / 16) * 64 * 16;
     return L;
 }
@@ -1475,7 +1482,7 @@ __device__ inline int copy_block_rows(const Geometry& g, const uint16_t* src, in
 // Workgroup wg of heads * runs * groups (run of windows, key group), over
 // windows w0 .. w0 + nw - 1 (the units whose statistics are at
 // stats[((w - w0) * heads + h) * 2 NPX]); pair sums to sums[wg * kKvpSums].
-template <int D>
+template <int D, int SB>
 __global__ __launch_bounds__((kKvpWaves + kKvpLoaders) * 64) void attn_bf16_bwd_kvp_kernel(
     Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ table, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
@@ -1515,15 +1522,15 @@ __global__ __launch_bounds__((kKvpWaves + kKvpLoaders) * 64) void attn_bf16_bwd_
     }
     __syncthreads();
 
-    // A step takes two 32-query blocks of a window (the last step of an odd
-    // count one); every window's NS steps stream through the ring.
-    const int NS = (NB + 1) / 2, T = nwin * NS;
+    // A step takes SB 32-query blocks of a window (the last step the rest);
+    // every window's NS steps stream through the ring.
+    const int NS = (NB + SB - 1) / SB, T = nwin * NS;
     if (wave >= kKvpWaves) {
         const int li = wave - kKvpWaves;
         const int per_block = 2 * block_copies_of<D>(li, kKvpLoaders); // this loader's copies per block
         auto own = [&](int s) __attribute__((always_inline)) {         // ... per step s
             const int js = s % NS;
-            return (2 * js + 1 < NB ? 2 : 1) * per_block;
+            return (NB - SB * js < SB ? NB - SB * js : SB) * per_block;
         };
         // window i's token words (unless written already), K and V of the
         // group's keys, and its statistics, into window buffer i & 1; returns
@@ -1556,9 +1563,9 @@ __global__ __launch_bounds__((kKvpWaves + kKvpLoaders) * 64) void attn_bf16_bwd_
         auto issue_step = [&](int s) __attribute__((always_inline)) {
             const int i = s / NS, js = s - i * NS;
             const int* tw = (const int*)(smem + L.win + (size_t)(i & 1) * L.win_bytes + L.tw);
-            unsigned char* dst = ring + (size_t)(s % kBwdStages) * 4 * L.buf_bytes;
-            for (int u = 0; u < 2 && 2 * js + u < NB; u++) {
-                const int j = 2 * js + u;
+            unsigned char* dst = ring + (size_t)(s % kBwdStages) * 2 * SB * L.buf_bytes;
+            for (int u = 0; u < SB && SB * js + u < NB; u++) {
+                const int j = SB * js + u;
                 copy_block<D>(g, q, h, tw, j * kBwdBlk, dst + u * 2 * L.buf_bytes, li, kKvpLoaders);
                 copy_block<D>(g, dout, h, tw, j * kBwdBlk, dst + (u * 2 + 1) * L.buf_bytes, li, kKvpLoaders);
             }
@@ -1621,6 +1628,7 @@ __global__ __launch_bounds__((kKvpWaves + kKvpLoaders) * 64) void attn_bf16_bwd_
         }
     };
     int slot = 0, kr = -1;
+    bf16x8 kf[KSTEPS], vf[KSTEPS]; // B operands of the key tile: key m, d = 32 ks + 8 grp + 0..7
     for (int i = 0; i < nwin; i++) {
         const unsigned char* wb = smem + L.win + (size_t)(i & 1) * L.win_bytes;
         const int* tw = (const int*)(wb + L.tw);
@@ -1643,14 +1651,20 @@ __global__ __launch_bounds__((kKvpWaves + kKvpLoaders) * 64) void attn_bf16_bwd_
                         ak[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
                     }
                     const int kword = active ? tw[m] : (15 << 28);
+#pragma unroll
+                    for (int ks = 0; ks < KSTEPS; ks++) {
+                        const int kc = k_slot<D>(krow, ks * 4 + grp) * 8;
+                        kf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kt + krow * D + kc));
+                        vf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Vt + krow * D + kc));
+                    }
                     kreg = (unsigned)kword >> 28;
                     kr = (kword & kRowMask) - 1;
                 }
 #pragma unroll
-                for (int u = 0; u < 2; u++) {
-                    const int j = 2 * js + u;
+                for (int u = 0; u < SB; u++) {
+                    const int j = SB * js + u;
                     if (!active || j >= NB) continue;
-                    const unsigned char* Qb = ring + (size_t)slot * 4 * L.buf_bytes + u * 2 * L.buf_bytes;
+                    const unsigned char* Qb = ring + (size_t)slot * 2 * SB * L.buf_bytes + u * 2 * L.buf_bytes;
                     const unsigned char* Ob = Qb + L.buf_bytes;
                     const uint16_t* Qs = (const uint16_t*)Qb;
                     const uint16_t* dOs = (const uint16_t*)Ob;
@@ -1659,11 +1673,9 @@ __global__ __launch_bounds__((kKvpWaves + kKvpLoaders) * 64) void attn_bf16_bwd_
                     f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, dp4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KSTEPS; ks++) {
-                        const int kc = k_slot<D>(krow, ks * 4 + grp) * 8, qc = k_slot<D>(qrow, ks * 4 + grp) * 8;
-                        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kt + krow * D + kc));
-                        const bf16x8 vf = __builtin_bit_cast(bf16x8, *(const u32x4*)(Vt + krow * D + kc));
-                        s4 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(Qs + qrow * D + qc)), kf, s4);
-                        dp4 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(dOs + qrow * D + qc)), vf, dp4);
+                        const int qc = k_slot<D>(qrow, ks * 4 + grp) * 8;
+                        s4 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(Qs + qrow * D + qc)), kf[ks], s4);
+                        dp4 = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)(dOs + qrow * D + qc)), vf[ks], dp4);
                     }
                     const int n4 = nb + th * 16 + grp * 4;
                     const u32x4 qb4 = *(const u32x4*)(qbo + n4);
@@ -2085,8 +2097,9 @@ hipError_t prepare_backward_kernels(int max_lds) {
                         (const void*)attn_bf16_bwd_kv_kernel<32, 6, 2>,  (const void*)attn_bf16_bwd_kv_kernel<64, 6, 0>,
                         (const void*)attn_bf16_bwd_kv_kernel<64, 6, 1>,  (const void*)attn_bf16_bwd_kv_kernel<64, 6, 2>,
                         (const void*)attn_bf16_bwd_kv_kernel<128, 8, 0>, (const void*)attn_bf16_bwd_kv_kernel<128, 8, 1>,
-                        (const void*)attn_bf16_bwd_kv_kernel<128, 8, 2>, (const void*)attn_bf16_bwd_kvp_kernel<32>,
-                        (const void*)attn_bf16_bwd_kvp_kernel<64>};
+                        (const void*)attn_bf16_bwd_kv_kernel<128, 8, 2>, (const void*)attn_bf16_bwd_kvp_kernel<32, 2>,
+                        (const void*)attn_bf16_bwd_kvp_kernel<32, 3>, (const void*)attn_bf16_bwd_kvp_kernel<64, 2>,
+                        (const void*)attn_bf16_bwd_kvp_kernel<64, 3>};
     for (const void* f : fs) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
         if (e != hipSuccess) return e;
@@ -2149,7 +2162,10 @@ static hipError_t launch_kvp(const Geometry& g, const void* q, const void* k, co
                              float* pairs, uint32_t w0, uint32_t nw, const KvpPlan& p, int accumulate,
                              hipStream_t s) {
     const unsigned wgs = (unsigned)(g.heads * p.runs * p.groups);
-    hipLaunchKernelGGL(g.head_dim == 32 ? attn_bf16_bwd_kvp_kernel<32> : attn_bf16_bwd_kvp_kernel<64>, dim3(wgs),
+    const bool sb3 = kvp_step_blocks(kvp_lds(g).NPX / kBwdBlk) == 3;
+    hipLaunchKernelGGL(g.head_dim == 32 ? (sb3 ? attn_bf16_bwd_kvp_kernel<32, 3> : attn_bf16_bwd_kvp_kernel<32, 2>)
+                                        : (sb3 ? attn_bf16_bwd_kvp_kernel<64, 3> : attn_bf16_bwd_kvp_kernel<64, 2>),
+                       dim3(wgs),
                        dim3((kKvpWaves + kKvpLoaders) * 64), kvp_lds(g).total, s, g, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, table, (const uint16_t*)dout, (uint16_t*)dk,
                        (uint16_t*)dv, stats, sums, w0, nw, p.runs, p.groups);
