@@ -189,10 +189,10 @@ swa_status swa_forward_lse(swa_handle* h, const void* q, const void* k, const vo
  * token) and dtable = dL/d(bias_table) (fp32, the table's layout); all four
  * are overwritten.  The pad tokens of a window have no output, so they add
  * nothing.  workspace: device buffer of info.backward_workspace_bytes bytes,
- * 16-byte aligned, owned by the caller (per-(window, head) shares of the
- * table gradient and their partial sums; with backward_schedule 2 also each
- * query's softmax normaliser and D = rowsum(P * dP); its contents on entry
- * do not matter).  The pass reads and writes the spatial layout whatever the
+ * 16-byte aligned, owned by the caller (a head-major copy of the bias table,
+ * per-(window, head) shares of the table gradient and their partial sums;
+ * with backward_schedule 2 also each query's softmax normaliser and
+ * D = rowsum(P * dP); its contents on entry do not matter).  The pass reads and writes the spatial layout whatever the
  * variant and allocates nothing.  backward_schedule 1 (bf16 windows whose
  * Q, K, V, dO and two N x N matrices fit one workgroup's LDS: up to 144
  * tokens with head_dim <= 64, fewer at 128; and fp32): every sum runs in a
@@ -234,8 +234,9 @@ swa_status swa_backward_lse(swa_handle* h, const void* q, const void* k, const v
  * swa_backward for callers that cannot allocate device memory: code under
  * HIP graph capture, tight training or serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, results and errors as swa_backward, without the
- * workspace: the per-(window, head) table-gradient shares (and, for
- * backward_schedule 2, the per-query statistics) go to a fixed scratch array
+ * workspace: a head-major copy of the bias table, the per-(window, head)
+ * table-gradient shares (and, for backward_schedule 2, the per-query
+ * statistics) go to a fixed scratch array
  * of 32 MiB in device memory that the library holds on each device it runs on
  * (looked up in swa_create, kept until the process ends).  The windows are
  * processed in passes of whole chunks of 1/64 of the windows each, as many

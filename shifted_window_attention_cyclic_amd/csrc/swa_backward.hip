@@ -512,7 +512,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void attn_bf16_bwd_kernel(
         tw[n] = word;
         kb[n] = kbo;
     }
-    for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)i * g.heads + U.h];
+    for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)U.h * g.table_size + i];
     __syncthreads();
 
     // ---- Q, K, V, dO of the window into LDS ([token][d], swizzled; pad rows copy
@@ -617,7 +617,7 @@ __global__ __launch_bounds__((kBwdWaves + kBwdPLoaders) * 64) void attn_bf16_bwd
             float* bs = (float*)(smem + P.bias + slot * P.bias_stride);
             for (int i0 = j * 64; i0 < g.table_size; i0 += kBwdPLoaders * 64) {
                 const int i = i0 + lane;
-                const float* src = table + (i < g.table_size ? (size_t)i * g.heads + U.h : 0);
+                const float* src = table + (size_t)U.h * g.table_size + (i < g.table_size ? i : 0);
                 __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(bs + i0), 4, 0, 0);
             }
         };
@@ -875,7 +875,7 @@ __global__ __launch_bounds__((QW + kBwdLoaders) * 64) void attn_bf16_bwd_q_kerne
     const bool masked_window = window_maybe_masked(g, wc);
 
     big_token_table(g, wc, b, NPX, tw, kbo, qbo, THREADS);
-    for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)i * g.heads + h];
+    for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)h * g.table_size + i];
     __syncthreads();
 
     const int passes = lse != nullptr ? 1 : 2;
@@ -1107,7 +1107,7 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
 
     big_token_table(g, wc, b, NPX, tw, kbo, qbo, THREADS);
     for (int i = tid; i < g.table_size; i += THREADS) {
-        bias[i] = table[(size_t)i * g.heads + h];
+        bias[i] = table[(size_t)h * g.table_size + i];
         dtab[i] = 0.f;
     }
     {
@@ -1513,7 +1513,7 @@ __global__ __launch_bounds__((kKvpWaves + kKvpLoaders) * 64) void attn_bf16_bwd_
     const int nwin = (int)(w0 + (uint32_t)((uint64_t)nw * (run + 1) / runs) - wbeg);
 
     for (int n = tid; n < NPX; n += THREADS) big_bias_offsets(g, n, kbo[n], qbo[n]);
-    for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)i * g.heads + h];
+    for (int i = tid; i < g.table_size; i += THREADS) bias[i] = table[(size_t)h * g.table_size + i];
     if (nwin > 0) {
         int b, wc[3];
         window_of(g, wbeg, b, wc);
@@ -1824,7 +1824,7 @@ __global__ __launch_bounds__(kF32BwdThreads) void attn_f32_bwd_kernel(
     const int h = (int)(work - wi * g.heads);
 
     fill_token_tables(g, wi, false, N, kword, qword, rowi);
-    for (int i = threadIdx.x; i < g.table_size; i += blockDim.x) bias[i] = table[(int64_t)i * g.heads + h];
+    for (int i = threadIdx.x; i < g.table_size; i += blockDim.x) bias[i] = table[(int64_t)h * g.table_size + i];
     __syncthreads();
     for (int i = threadIdx.x; i < N * D; i += blockDim.x) {
         const int m = i / D, e = i % D;
@@ -1953,7 +1953,27 @@ __global__ __launch_bounds__(256) void dtable_sum_kernel(int heads, int ts, cons
     dtable[(size_t)e * heads + h] = acc;
 }
 
+// hm[h][e] = table[e][h]: the bias table head-major, so that a unit's slice is
+// contiguous for the backward kernels, which read it as `table`
+__global__ __launch_bounds__(256) void bias_heads_kernel(int ts, int heads, const float* __restrict__ table,
+                                                         float* __restrict__ hm) {
+    const int idx = blockIdx.x * 256 + threadIdx.x; // h * ts + e
+    if (idx >= ts * heads) return;
+    const int h = idx / ts, e = idx - h * ts;
+    hm[idx] = table[(size_t)e * heads + h];
+}
+
 // ---- host side
+// bytes of the head-major table copy at the front of the workspace or scratch
+static size_t bias_heads_bytes(const Geometry& g) {
+    return ((size_t)g.heads * g.table_size * sizeof(float) + 255) / 256 * 256;
+}
+static hipError_t launch_bias_heads(const Geometry& g, const float* table, float* hm, hipStream_t s) {
+    const int n = g.heads * g.table_size;
+    hipLaunchKernelGGL(bias_heads_kernel, dim3((n + 255) / 256), dim3(256), 0, s, g.table_size, g.heads, table, hm);
+    return hipGetLastError();
+}
+
 // the single-workgroup bf16 kernel, or else the two big-window kernels
 static bool bwd_small_fits(const Geometry& g) {
     return (g.N + 15) / 16 <= kBwdMaxTiles && bwd_lds(g).total <= (size_t)kLdsBytes;
@@ -2008,7 +2028,13 @@ int backward_schedule(const Geometry& g, bool bf16) {
     return !bf16 || bwd_small_fits(g) ? 1 : 2;
 }
 
+static size_t backward_work_bytes(const Geometry& g);
 size_t backward_workspace_bytes(const Geometry& g) {
+    return bias_heads_bytes(g) + backward_work_bytes(g);
+}
+
+// the workspace after the head-major table
+static size_t backward_work_bytes(const Geometry& g) {
     if (bwd_kvp_fits(g)) { // per-query statistics, workgroup sums, their sums over runs
         const KvpPlan p = kvp_plan(g, g.windows);
         return ((size_t)(g.windows * g.heads) * 2 * kvp_lds(g).NPX + kvp_sums_floats(g, p) +
@@ -2220,8 +2246,14 @@ static hipError_t launch_backward_units(const Geometry& g, bool bf16, const void
 }
 
 hipError_t launch_backward(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
-                           const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
-                           void* workspace, const void* o, const float* lse, int blocks, hipStream_t s) {
+                           const float* table_in, const void* dout, void* dq, void* dk, void* dv, float* dtable,
+                           void* workspace_in, const void* o, const float* lse, int blocks, hipStream_t s) {
+    float* table = (float*)workspace_in; // the head-major copy that every kernel below reads
+    void* workspace = (unsigned char*)workspace_in + bias_heads_bytes(g);
+    {
+        const hipError_t e = launch_bias_heads(g, table_in, table, s);
+        if (e != hipSuccess) return e;
+    }
     if (bf16 && bwd_kvp_fits(g)) {
         const KvpPlan p = kvp_plan(g, g.windows);
         float* stats = (float*)workspace;
@@ -2273,7 +2305,10 @@ static size_t kvp_fixed_bytes(const Geometry& g, const KvpPlan& p) {
     return (kvp_sums_floats(g, p) + kvp_pairs_floats(g, p)) * sizeof(float);
 }
 
-size_t backward_scratch_bytes(const Geometry& g, bool bf16) {
+static size_t scratch_work_bytes(const Geometry& g, bool bf16);
+size_t backward_scratch_bytes(const Geometry& g, bool bf16) { return bias_heads_bytes(g) + scratch_work_bytes(g, bf16); }
+
+static size_t scratch_work_bytes(const Geometry& g, bool bf16) {
     if (bf16 && bwd_kvp_fits(g)) {
         KvpPlan p = kvp_plan(g, 1);
         p.runs = 1;
@@ -2306,8 +2341,17 @@ __global__ __launch_bounds__(256) void dtable_accumulate_kernel(int64_t windows,
 }
 
 hipError_t launch_backward_scratch(const Geometry& g, bool bf16, const void* q, const void* k, const void* v,
-                                   const float* table, const void* dout, void* dq, void* dk, void* dv, float* dtable,
-                                   void* scratch, size_t scratch_bytes, int blocks, hipStream_t s) {
+                                   const float* table_in, const void* dout, void* dq, void* dk, void* dv,
+                                   float* dtable, void* scratch_in, size_t scratch_in_bytes, int blocks,
+                                   hipStream_t s) {
+    if (scratch_in_bytes < bias_heads_bytes(g)) return hipErrorInvalidValue; // checked by the caller
+    float* table = (float*)scratch_in; // the head-major copy that every kernel below reads
+    void* scratch = (unsigned char*)scratch_in + bias_heads_bytes(g);
+    const size_t scratch_bytes = scratch_in_bytes - bias_heads_bytes(g);
+    {
+        const hipError_t e = launch_bias_heads(g, table_in, table, s);
+        if (e != hipSuccess) return e;
+    }
     if (bf16 && bwd_kvp_fits(g)) {
         KvpPlan p = kvp_plan(g, g.windows);
         int64_t per_pass = 0;
