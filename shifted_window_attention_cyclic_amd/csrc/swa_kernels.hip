@@ -8,7 +8,8 @@
 //   gather_kernel      spatial layout -> window-major layout (pad, roll, partition)
 //   scatter_kernel     window-major layout -> spatial layout (reverse)
 //   visibility_kernel  the attention mask of one window, as the kernels use it
-//   attn_f32_kernel    fp32 window attention (VALU), one block per (window, head)
+//   attn_f32_kernel    fp32 window attention (VALU), one block per (window, head),
+//                      four lanes per query
 //   attn_bf16_stream_kernel
 //                      bf16 window attention on MFMA with fp32 accumulation,
 //                      windows of up to 9 query tiles: persistent workgroups,
@@ -141,10 +142,15 @@ hipError_t launch_visibility(const Geometry& g, int64_t window, uint8_t* out, hi
 }
 
 // --------------------------------------------------------------------------
-// fp32 attention: one block per (window, head), one thread per query, online
-// softmax over the window's keys held in LDS.
+// fp32 attention: one block per (window, head).  Each query takes four
+// lanes of a quad; lane j runs an online softmax over the keys m with
+// m % 4 == j (K and V rows from LDS, 16 bytes per read), and the quad then
+// merges its four partial states (max, sum, weighted V) with shuffles.  So a
+// 64-token window keeps all four waves busy where a thread per query would
+// leave three idle and run 64 keys in series.
 // --------------------------------------------------------------------------
 constexpr int kF32Threads = 256;
+constexpr int kF32Split = 4; // lanes per query
 
 __host__ __device__ inline size_t f32_lds_bytes(const Geometry& g) {
     return (size_t)g.N * g.head_dim * 2 * sizeof(float) + (size_t)g.table_size * sizeof(float) +
@@ -159,6 +165,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(Geometry g, int s
                                                                const float* __restrict__ table,
                                                                float* __restrict__ out,
                                                                float* __restrict__ lse) {
+    static_assert(D % 16 == 0, "rows read 16 bytes at a time, each lane writes a quarter of a row");
     extern __shared__ __align__(16) unsigned char smem[];
     const int N = g.N;
     float* Ks = (float*)smem;
@@ -177,57 +184,110 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(Geometry g, int s
     for (int i = threadIdx.x; i < g.table_size; i += blockDim.x)
         bias[i] = table[(int64_t)i * g.heads + h];
     __syncthreads();
-    for (int i = threadIdx.x; i < N * D; i += blockDim.x) {
-        int m = i / D, e = i % D;
-        int r = rowi[m];
-        float kv = 0.f, vv = 0.f;
+    for (int i = threadIdx.x; i < N * D / 4; i += blockDim.x) {
+        const int m = i / (D / 4), e4 = i % (D / 4);
+        const int r = rowi[m];
+        float4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
         if (r >= 0) {
-            int64_t off = (int64_t)r * g.row + (int64_t)h * D + e;
-            kv = k[off];
-            vv = v[off];
+            const int64_t off = (int64_t)r * g.row + (int64_t)h * D + e4 * 4;
+            kv = *(const float4*)(k + off);
+            vv = *(const float4*)(v + off);
         }
-        Ks[i] = kv;
-        Vs[i] = vv;
+        ((float4*)Ks)[i] = kv;
+        ((float4*)Vs)[i] = vv;
     }
     __syncthreads();
 
-    for (int n = threadIdx.x; n < N; n += blockDim.x) {
-        int r = rowi[n];
-        int qw = qword[n];
-        if (r < 0) {
+    const int j = threadIdx.x % kF32Split; // this lane's keys: m % kF32Split == j
+    // every lane of a quad runs the loop the same number of times (the shuffles need all four)
+    for (int n0 = threadIdx.x / kF32Split; n0 < (N + kF32Threads / kF32Split - 1) / (kF32Threads / kF32Split) *
+                                                     (kF32Threads / kF32Split);
+         n0 += kF32Threads / kF32Split) {
+        const int n = n0 < N ? n0 : N - 1;
+        const int r = rowi[n];
+        const int qw = qword[n];
+        float qv[D], acc[D];
+        const float* qp = q + (int64_t)(r < 0 ? 0 : r) * g.row + (int64_t)h * D;
+#pragma unroll
+        for (int e = 0; e < D; e += 4) {
+            const float4 x = *(const float4*)(qp + e);
+            qv[e] = x.x;
+            qv[e + 1] = x.y;
+            qv[e + 2] = x.z;
+            qv[e + 3] = x.w;
+        }
+#pragma unroll
+        for (int e = 0; e < D; e++) acc[e] = 0.f;
+        float mx = -INFINITY, den = 0.f;
+        for (int m = j; m < N; m += kF32Split) {
+            const int kw = kword[m];
+            if (!visible(qw, kw)) continue;
+            const float4* kr = (const float4*)(Ks + m * D);
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < D; e += 4) {
+                const float4 x = kr[e / 4];
+                dot = fmaf(qv[e], x.x, dot);
+                dot = fmaf(qv[e + 1], x.y, dot);
+                dot = fmaf(qv[e + 2], x.z, dot);
+                dot = fmaf(qv[e + 3], x.w, dot);
+            }
+            const float sc = dot * g.scale + bias[(qw & 0xFFFF) - (kw & 0xFFFF)];
+            if (sc > mx) {
+                const float alpha = expf(mx - sc); // 0 on the first visible key
+                den *= alpha;
+#pragma unroll
+                for (int e = 0; e < D; e++) acc[e] *= alpha;
+                mx = sc;
+            }
+            const float p = expf(sc - mx);
+            den += p;
+            const float4* vr = (const float4*)(Vs + m * D);
+#pragma unroll
+            for (int e = 0; e < D; e += 4) {
+                const float4 x = vr[e / 4];
+                acc[e] = fmaf(p, x.x, acc[e]);
+                acc[e + 1] = fmaf(p, x.y, acc[e + 1]);
+                acc[e + 2] = fmaf(p, x.z, acc[e + 2]);
+                acc[e + 3] = fmaf(p, x.w, acc[e + 3]);
+            }
+        }
+        // merge the quad's partial states: the common max, each part scaled to it
+        float m4 = fmaxf(mx, __shfl_xor(mx, 1));
+        m4 = fmaxf(m4, __shfl_xor(m4, 2));
+        const float w = mx == -INFINITY ? 0.f : expf(mx - m4); // a lane that saw no visible key adds 0
+        float d4 = den * w;
+        d4 += __shfl_xor(d4, 1);
+        d4 += __shfl_xor(d4, 2);
+#pragma unroll
+        for (int e = 0; e < D; e++) {
+            float a = acc[e] * w;
+            a += __shfl_xor(a, 1);
+            a += __shfl_xor(a, 2);
+            acc[e] = a;
+        }
+        if (n0 >= N) continue; // a padding iteration of the loop: nothing to write
+        if (r < 0) {           // pad query: no output (staged: its slot is zero)
             if (staged) {
                 float* o = out + ((wi * N + n) * (int64_t)g.row + (int64_t)h * D);
-                for (int e = 0; e < D; e++) o[e] = 0.f;
+#pragma unroll
+                for (int e = 0; e < D / kF32Split; e++) o[j * (D / kF32Split) + e] = 0.f;
             }
             continue;
         }
-        float qv[D], acc[D];
-        const float* qp = q + (int64_t)r * g.row + (int64_t)h * D;
-        for (int e = 0; e < D; e++) {
-            qv[e] = qp[e];
-            acc[e] = 0.f;
-        }
-        float mx = -INFINITY, den = 0.f;
-        for (int m = 0; m < N; m++) {
-            int kw = kword[m];
-            if (!visible(qw, kw)) continue;
-            float dot = 0.f;
-            for (int e = 0; e < D; e++) dot = fmaf(qv[e], Ks[m * D + e], dot);
-            float s = dot * g.scale + bias[(qw & 0xFFFF) - (kw & 0xFFFF)];
-            if (s > mx) {
-                float alpha = expf(mx - s); // 0 on the first visible key
-                den *= alpha;
-                for (int e = 0; e < D; e++) acc[e] *= alpha;
-                mx = s;
-            }
-            float p = expf(s - mx);
-            den += p;
-            for (int e = 0; e < D; e++) acc[e] = fmaf(p, Vs[m * D + e], acc[e]);
-        }
-        float inv = 1.f / den;
-        if (lse != nullptr) lse[(int64_t)r * g.heads + h] = mx + logf(den);
+        const float inv = 1.f / d4;
+        if (lse != nullptr && j == 0) lse[(int64_t)r * g.heads + h] = m4 + logf(d4);
         float* o = out + (int64_t)r * g.row + (int64_t)h * D;
-        for (int e = 0; e < D; e++) o[e] = acc[e] * inv;
+        // lane j writes elements j D/4 .. (j + 1) D/4 - 1 (register indices stay static)
+#pragma unroll
+        for (int jj = 0; jj < kF32Split; jj++) {
+            if (jj != j) continue;
+#pragma unroll
+            for (int e = 0; e < D / kF32Split; e += 4)
+                *(float4*)(o + jj * (D / kF32Split) + e) =
+                    float4{acc[jj * (D / kF32Split) + e] * inv, acc[jj * (D / kF32Split) + e + 1] * inv,
+                           acc[jj * (D / kF32Split) + e + 2] * inv, acc[jj * (D / kF32Split) + e + 3] * inv};
+        }
     }
 }
 
