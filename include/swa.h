@@ -122,7 +122,8 @@ typedef struct swa_info {
     int32_t window_tokens;      /* N = w_t * w_y * w_x */
     int64_t tokens;             /* real tokens B * T * H * W */
     int64_t window_major_elems; /* windows * N * heads * head_dim */
-    size_t workspace_bytes;     /* device bytes owned by the handle (staged variant, key-blocked bias copy) */
+    size_t workspace_bytes;     /* device bytes owned by the handle (staged variant; head-major bias copy of
+                                   the key-blocked and per-unit schedules) */
     double nominal_flops;       /* 4 * N^2 * head_dim per (window, head), all windows */
     double algorithmic_bytes;   /* q, k, v read and out written once, real tokens, plus the table */
     int32_t schedule;           /* bf16: the schedule in use (_STREAM, _BLOCK or _KEYBLOCK); fp32: 0 */
@@ -148,8 +149,8 @@ typedef struct swa_info {
 
 /*
  * Validates cfg, checks that the current HIP device is a gfx950, and creates
- * a handle.  The workspaces (staged variant; key-blocked schedule) are
- * allocated here.  On failure *out is set to NULL.
+ * a handle.  The workspaces (staged variant; the head-major bias copy of the
+ * key-blocked and per-unit schedules) are allocated here.  On failure *out is set to NULL.
  * Errors: INVALID_ARGUMENT (NULL pointers, malformed tiling, unknown enum),
  * UNSUPPORTED (head_dim or window size outside the kernels' range, or an
  * explicit schedule that cannot take the window),

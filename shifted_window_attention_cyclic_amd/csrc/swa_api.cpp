@@ -29,7 +29,7 @@ struct swa_handle {
     int layer_path;     // SWA_LAYER_FUSED or SWA_LAYER_UNFUSED
     size_t wm_bytes;    // bytes of one window-major tensor
     void* workspace;    // staged variant: q, k, v, o window-major tensors
-    float* bias_hm;     // key-blocked schedule: head-major copy of the bias table
+    float* bias_hm;     // key-blocked and per-unit schedules: head-major copy of the bias table
 };
 
 // Scratch of swa_backward_noalloc: file-scope device memory, so that the call
@@ -306,7 +306,7 @@ swa_status swa_create(const swa_config* cfg, swa_handle** out) {
             return fail(SWA_ERR_OUT_OF_MEMORY, "staged workspace");
         }
     }
-    if (schedule == SWA_SCHEDULE_KEYBLOCK) {
+    if (schedule == SWA_SCHEDULE_KEYBLOCK || schedule == SWA_SCHEDULE_BLOCK) {
         e = hipMalloc((void**)&h->bias_hm, swa::bf16_kblock_workspace_bytes(g));
         if (e != hipSuccess) {
             (void)hipGetLastError();
@@ -371,7 +371,7 @@ static swa_status forward(swa_handle* h, const void* q, const void* k, const voi
                                                 (const uint16_t*)av, bias_table, h->bias_hm, (uint16_t*)ao, lse, s);
         return swa::launch_attention_bf16(g, h->schedule == SWA_SCHEDULE_STREAM, h->blocks, staged,
                                           (const uint16_t*)aq, (const uint16_t*)ak, (const uint16_t*)av, bias_table,
-                                          (uint16_t*)ao, lse, s);
+                                          h->bias_hm, (uint16_t*)ao, lse, s);
     };
     if (h->cfg.variant == SWA_VARIANT_FUSED) {
         e = attention(false, q, k, v, out);

@@ -145,8 +145,10 @@ hipError_t launch_visibility(const Geometry& g, int64_t window, uint8_t* out, hi
 // its logits also goes to lse[row * heads + head].
 hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, const float* k,
                                 const float* v, const float* table, float* out, float* lse, hipStream_t s);
+// The per-unit schedule (stream false) first refreshes bias_hm, a head-major
+// copy of table (bf16_kblock_workspace_bytes), and reads its slices from it.
 hipError_t launch_attention_bf16(const Geometry& g, bool stream, int blocks, bool staged, const uint16_t* q,
-                                 const uint16_t* k, const uint16_t* v, const float* table,
+                                 const uint16_t* k, const uint16_t* v, const float* table, float* bias_hm,
                                  uint16_t* out, float* lse, hipStream_t s);
 // LDS bytes the attention kernels need for g (bf16: the smallest among the
 // schedules that take the window; (size_t)-1 when none does).

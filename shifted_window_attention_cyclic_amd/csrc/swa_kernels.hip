@@ -24,7 +24,8 @@
 //                      streamed in 32-key blocks, blocks masked for all of a
 //                      wave's queries skipped
 //   bias_head_major_kernel
-//                      the head-major bias copy the key-blocked kernel reads
+//                      the head-major bias copy the key-blocked and per-unit
+//                      kernels read
 // Every bf16 kernel reads Q/K/V straight from the spatial layout and writes O
 // back to it (fused), or works on window-major buffers (staged).
 #include <hip/hip_runtime.h>
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_bf16_kernel(
 #pragma unroll
         for (int u = 0; u < BIAS_UNROLL; u++) {
             const int i = base + u * THREADS + tid;
-            bv[u] = i < g.table_size ? table[i * g.heads + h] : 0.f;
+            bv[u] = i < g.table_size ? table[(size_t)h * g.table_size + i] : 0.f; // head-major copy
         }
 #pragma unroll
         for (int u = 0; u < BIAS_UNROLL; u++) {
@@ -860,7 +861,7 @@ __host__ __device__ inline KbLds kb_lds(const Geometry& g) {
     return L;
 }
 
-// dst[h][i] = table[i][h] / scale
+// dst[h][i] = table[i][h] / scale (scale 1: an exact copy)
 __global__ __launch_bounds__(256) void bias_head_major_kernel(int table_size, int heads, float scale,
                                                               const float* __restrict__ table,
                                                               float* __restrict__ dst) {
@@ -1347,10 +1348,19 @@ hipError_t bf16_plan(const Geometry& g, bool stream, int* blocks) {
 }
 
 hipError_t launch_attention_bf16(const Geometry& g, bool stream, int blocks, bool staged, const uint16_t* q,
-                                 const uint16_t* k, const uint16_t* v, const float* table,
+                                 const uint16_t* k, const uint16_t* v, const float* table, float* bias_hm,
                                  uint16_t* out, float* lse, hipStream_t s) {
     const Bf16Variant var = bf16_variant_for(g, stream);
     const size_t lds = stream ? stream_lds(g).total : bf16_lds(g).total;
+    if (!stream) { // the per-unit kernel reads its head's bias slice from a head-major copy
+        const int64_t n = (int64_t)g.table_size * g.heads;
+        const int64_t tb = (n + 255) / 256;
+        hipLaunchKernelGGL(bias_head_major_kernel, dim3((unsigned)(tb < 1024 ? tb : 1024)), dim3(256), 0, s,
+                           g.table_size, g.heads, 1.0f, table, bias_hm);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        table = bias_hm;
+    }
     hipLaunchKernelGGL(var.f, dim3((unsigned)blocks), dim3(var.waves * 64), lds, s, g,
                        (int)staged, q, k, v, table, out, lse);
     return hipGetLastError();
