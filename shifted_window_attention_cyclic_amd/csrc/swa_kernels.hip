@@ -697,7 +697,8 @@ attn_bf16_stream_kernel(
     const uint32_t u0 = ubeg + blockIdx.x / kXcds;
     if (u0 >= uend) return;
 
-    // ---- window-independent tables; every head's bias when resident
+    // ---- window-independent tables (every head's bias, when resident, is the
+    // compute waves' part of the prologue: below)
     for (int n = tid; n < NP; n += THREADS) {
         if (n < N) {
             int lt, ly, lx;
@@ -706,10 +707,6 @@ attn_bf16_stream_kernel(
         } else {
             kb4[n] = BIAS_VEC ? 12 : 0; // keeps qb - kb (- 3) inside the table
         }
-    }
-    if (L.bias_resident) {
-        for (int hh = 0; hh < g.heads; hh++)
-            for (int i = tid; i < g.table_size; i += THREADS) bias_lds[hh * L.TSP + i] = table[i * g.heads + hh];
     }
 
     if (wave >= NWAVES) {
@@ -771,7 +768,16 @@ attn_bf16_stream_kernel(
         loader_barrier();
         stream_store_o<D, MAXC, EX>(g, L, smem, out, R, lane, u, (int)((uend - 1 - u0) / per) % kTableSlots, staged);
     } else {
-        // ---- compute waves
+        // ---- compute waves.  Every head's bias slice when resident, from the
+        // table read in its own order (coalesced), while the loaders already
+        // build the first units' tables and issue their copies.
+        if (L.bias_resident) {
+            const uint32_t n = (uint32_t)g.table_size * (uint32_t)g.heads;
+            for (uint32_t e = (uint32_t)tid; e < n; e += NWAVES * 64) {
+                const uint32_t i = fdiv(g.fd_heads, e);
+                bias_lds[(e - i * (uint32_t)g.heads) * L.TSP + i] = table[e];
+            }
+        }
         const int KT = KT_FIXED > 0 ? KT_FIXED : NP / 16;
         const bool active = wave < KT;
         TileState<(KT_FIXED > 0 ? KT_FIXED : kStreamMaxTiles)> ts;
