@@ -237,21 +237,25 @@ swa_status swa_backward_lse(swa_handle* h, const void* q, const void* k, const v
  * hipMalloc.  Same arguments, results and errors as swa_backward, without the
  * workspace: a head-major copy of the bias table, the per-(window, head)
  * table-gradient shares (and, for backward_schedule 2, the per-query
- * statistics) go to a fixed scratch array
- * of 32 MiB in device memory that the library holds on each device it runs on
- * (looked up in swa_create, kept until the process ends).  The windows are
- * processed in passes of whole chunks of 1/64 of the windows each, as many
- * chunks per pass as the scratch holds, and the table gradient is summed chunk
- * by chunk in the order swa_backward sums it, so dq, dk, dv and (with
- * backward_schedule 1) dtable equal swa_backward's bit for bit.  Queues only
+ * statistics and the per-pair sums) go to a fixed scratch array of 32 MiB in
+ * device memory that the library holds on each device it runs on (looked up
+ * in swa_create, kept until the process ends).  The windows are processed in
+ * passes: of whole chunks of 1/64 of the windows each, as many chunks per
+ * pass as the scratch holds, with the table gradient summed chunk by chunk in
+ * the order swa_backward sums it; or, where backward_workgroups > 0, of runs
+ * of windows sized to the scratch, whose per-pair sums are added to dtable
+ * pass by pass.  dq, dk, dv and (with backward_schedule 1) dtable equal
+ * swa_backward's bit for bit; otherwise dtable agrees with it to rounding.
+ * Queues only
  * kernel launches on `stream` (no allocation, no memset, no host
  * synchronisation).  Every call on one device shares that device's scratch:
  * calls that overlap in time on one device (other streams, other threads,
  * other handles) race and give wrong gradients.  The handle must have been
  * created on the current device.
- * Errors: as swa_backward; also UNSUPPORTED when one chunk of windows needs
- * more than the 32 MiB scratch (about 2^23 / ((heads * table entries) per
- * window) * 64 windows; swa_backward takes any size), INVALID_ARGUMENT when
+ * Errors: as swa_backward; also UNSUPPORTED when one pass's smallest layout
+ * needs more than the 32 MiB scratch (one chunk of windows: about
+ * 2^23 / ((heads * table entries) per window) * 64 windows; swa_backward takes
+ * any size), INVALID_ARGUMENT when
  * the current device is not the handle's.
  */
 swa_status swa_backward_noalloc(swa_handle* h, const void* q, const void* k, const void* v,
