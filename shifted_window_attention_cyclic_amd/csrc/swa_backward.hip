@@ -1387,7 +1387,7 @@ __attribute__((amdgpu_waves_per_eu(KW == 6 ? 4 : 1))) void attn_bf16_bwd_kv_kern
 // the next window's token words and copy its statistics, K and V (the
 // group's keys) into the other of two window buffers; the compute waves take
 // their key tile's K and V fragments into registers at the window's start.
-// Eight compute waves (4 key tiles) keep the workgroup at 159 VGPRs, 3 waves
+// Eight compute waves (4 key tiles) keep the workgroup at about 160 VGPRs, 3 waves
 // per SIMD; 12 (6 key tiles) need more than the 128 of 4 waves per SIMD and
 // spill.
 constexpr int kKvpTiles = 4;                              // key tiles per group

@@ -8,8 +8,8 @@
 //   gather_kernel      spatial layout -> window-major layout (pad, roll, partition)
 //   scatter_kernel     window-major layout -> spatial layout (reverse)
 //   visibility_kernel  the attention mask of one window, as the kernels use it
-//   attn_f32_kernel    fp32 window attention (VALU), one block per (window, head),
-//                      four lanes per query
+//   attn_f32_kernel    fp32 window attention (VALU), one block per (window, head,
+//                      32 queries), eight lanes per query
 //   attn_bf16_stream_kernel
 //                      bf16 window attention on MFMA with fp32 accumulation,
 //                      windows of up to 9 query tiles: persistent workgroups,
@@ -143,15 +143,17 @@ hipError_t launch_visibility(const Geometry& g, int64_t window, uint8_t* out, hi
 }
 
 // --------------------------------------------------------------------------
-// fp32 attention: one block per (window, head).  Each query takes four
-// lanes of a quad; lane j runs an online softmax over the keys m with
-// m % 4 == j (K and V rows from LDS, 16 bytes per read), and the quad then
-// merges its four partial states (max, sum, weighted V) with shuffles.  So a
-// 64-token window keeps all four waves busy where a thread per query would
-// leave three idle and run 64 keys in series.
+// fp32 attention: one block per (window, head, block of 32 queries).  Each
+// query takes kF32Split lanes; lane j runs an online softmax over the keys m
+// with m % kF32Split == j (K and V rows from LDS, 16 bytes per read), and the
+// lanes then merge their partial states (max, sum, weighted V) with
+// shuffles.  So a 64-token window runs on two blocks of four busy waves,
+// where a thread per query would leave three waves idle and run 64 keys in
+// series.
 // --------------------------------------------------------------------------
 constexpr int kF32Threads = 256;
-constexpr int kF32Split = 4; // lanes per query
+constexpr int kF32Split = 8;                        // lanes per query
+constexpr int kF32Queries = kF32Threads / kF32Split; // queries per block
 
 __host__ __device__ inline size_t f32_lds_bytes(const Geometry& g) {
     return (size_t)g.N * g.head_dim * 2 * sizeof(float) + (size_t)g.table_size * sizeof(float) +
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(Geometry g, int s
                                                                const float* __restrict__ table,
                                                                float* __restrict__ out,
                                                                float* __restrict__ lse) {
-    static_assert(D % 16 == 0, "rows read 16 bytes at a time, each lane writes a quarter of a row");
+    static_assert(D % (4 * kF32Split) == 0, "rows read 16 bytes at a time, each lane writes 16-byte pieces of a row");
     extern __shared__ __align__(16) unsigned char smem[];
     const int N = g.N;
     float* Ks = (float*)smem;
@@ -176,10 +178,15 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(Geometry g, int s
     int* qword = kword + N;
     int* rowi = qword + N;
 
-    const int64_t total = g.windows * g.heads;
+    // block -> (window, head, query block); the query blocks of a unit are
+    // neighbours on one XCD and read its K and V from that XCD's L2
+    const int QB = (N + kF32Queries - 1) / kF32Queries;
+    const int64_t total = g.windows * g.heads * QB;
     const int64_t work = xcd_work_index(blockIdx.x, total);
-    const int64_t wi = work / g.heads;
-    const int h = (int)(work - wi * g.heads);
+    const int64_t unit = work / QB;
+    const int qblk = (int)(work - unit * QB);
+    const int64_t wi = unit / g.heads;
+    const int h = (int)(unit - wi * g.heads);
 
     fill_token_tables(g, wi, staged != 0, N, kword, qword, rowi);
     for (int i = threadIdx.x; i < g.table_size; i += blockDim.x)
@@ -200,10 +207,9 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(Geometry g, int s
     __syncthreads();
 
     const int j = threadIdx.x % kF32Split; // this lane's keys: m % kF32Split == j
-    // every lane of a quad runs the loop the same number of times (the shuffles need all four)
-    for (int n0 = threadIdx.x / kF32Split; n0 < (N + kF32Threads / kF32Split - 1) / (kF32Threads / kF32Split) *
-                                                     (kF32Threads / kF32Split);
-         n0 += kF32Threads / kF32Split) {
+    {
+        // the lanes of a query all run this (the shuffles need every one of them)
+        const int n0 = qblk * kF32Queries + threadIdx.x / kF32Split;
         const int n = n0 < N ? n0 : N - 1;
         const int r = rowi[n];
         const int qw = qword[n];
@@ -253,33 +259,34 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(Geometry g, int s
                 acc[e + 3] = fmaf(p, x.w, acc[e + 3]);
             }
         }
-        // merge the quad's partial states: the common max, each part scaled to it
-        float m4 = fmaxf(mx, __shfl_xor(mx, 1));
-        m4 = fmaxf(m4, __shfl_xor(m4, 2));
+        // merge the query's partial states: the common max, each part scaled to it
+        float m4 = mx;
+#pragma unroll
+        for (int sh = 1; sh < kF32Split; sh <<= 1) m4 = fmaxf(m4, __shfl_xor(m4, sh));
         const float w = mx == -INFINITY ? 0.f : expf(mx - m4); // a lane that saw no visible key adds 0
         float d4 = den * w;
-        d4 += __shfl_xor(d4, 1);
-        d4 += __shfl_xor(d4, 2);
+#pragma unroll
+        for (int sh = 1; sh < kF32Split; sh <<= 1) d4 += __shfl_xor(d4, sh);
 #pragma unroll
         for (int e = 0; e < D; e++) {
             float a = acc[e] * w;
-            a += __shfl_xor(a, 1);
-            a += __shfl_xor(a, 2);
+#pragma unroll
+            for (int sh = 1; sh < kF32Split; sh <<= 1) a += __shfl_xor(a, sh);
             acc[e] = a;
         }
-        if (n0 >= N) continue; // a padding iteration of the loop: nothing to write
-        if (r < 0) {           // pad query: no output (staged: its slot is zero)
+        if (n0 >= N) return; // a query slot past the window: nothing to write
+        if (r < 0) {         // pad query: no output (staged: its slot is zero)
             if (staged) {
                 float* o = out + ((wi * N + n) * (int64_t)g.row + (int64_t)h * D);
 #pragma unroll
                 for (int e = 0; e < D / kF32Split; e++) o[j * (D / kF32Split) + e] = 0.f;
             }
-            continue;
+            return;
         }
         const float inv = 1.f / d4;
         if (lse != nullptr && j == 0) lse[(int64_t)r * g.heads + h] = m4 + logf(d4);
         float* o = out + (int64_t)r * g.row + (int64_t)h * D;
-        // lane j writes elements j D/4 .. (j + 1) D/4 - 1 (register indices stay static)
+        // lane j writes elements j D/kF32Split .. (j + 1) D/kF32Split - 1 (register indices stay static)
 #pragma unroll
         for (int jj = 0; jj < kF32Split; jj++) {
             if (jj != j) continue;
@@ -295,7 +302,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(Geometry g, int s
 hipError_t launch_attention_f32(const Geometry& g, bool staged, const float* q, const float* k,
                                 const float* v, const float* table, float* out, float* lse, hipStream_t s) {
     size_t lds = f32_lds_bytes(g);
-    dim3 grid((unsigned)(g.windows * g.heads));
+    dim3 grid((unsigned)(g.windows * g.heads * ((g.N + kF32Queries - 1) / kF32Queries)));
     if (g.head_dim == 32)
         hipLaunchKernelGGL(attn_f32_kernel<32>, grid, dim3(kF32Threads), lds, s, g, (int)staged, q,
                            k, v, table, out, lse);
